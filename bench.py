@@ -1,0 +1,332 @@
+"""Decode throughput of the DeltaLog path on one MI355X.
+
+One step = one dl_decode_step over every (sequence, head) tile of the
+workload: base + log reads, output, append, and the fold on steps that fill
+the log.  Default workload: GDN, batch 64, 32 heads, dk = dv = 128, L = 16,
+all logs starting empty, inputs resident in HBM (a pool of 64 drawn steps,
+cycled).  Prints one JSON line.
+
+Also measured in the same run: the eager comparator (dl_eager_step, read and
+write the whole state every step) on the same inputs, a cache-cold variant
+(three independent pools used in turn, 480 MB, more than the 256 MB
+last-level cache), and the fp64 CPU oracle on the host cores.
+
+  python bench.py [--gpus 1] [--steps 1024] [--warmup 32] [--workload 2]
+                  [--no-cpu-baseline] [--graph] [--only deltalog|eager|copy]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from inputs import VARIANT_NAMES, WORKLOADS, make_inputs  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published figure
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["linear_attention_recurrent_amd/csrc/decode.hip",
+                  "linear_attention_recurrent_amd/csrc/dl_device.hpp"]
+
+
+# ------------------------------------------------------------ byte model ----
+def entry_bytes(variant: int, dk: int, dv: int) -> int:
+    """Bytes of one log entry: key (bf16), factor (fp32; RWKV6: v in bf16), cumulative decay."""
+    if variant == 0:
+        return 2 * dk + 4 * dv + 4
+    if variant == 1:
+        return 2 * dk + 4 * dv + 4 * dk
+    return 2 * dk + 2 * dv + 4 * dk
+
+
+def input_bytes(variant: int, dk: int, dv: int, batch: int) -> float:
+    """q, k, v (bf16), decay, beta (fp32) per state-step; RWKV6's bonus is per head."""
+    b = 2 * dk * 2 + 2 * dv
+    if variant == 0:
+        b += 4 + 4
+    elif variant == 1:
+        b += 4 * dk + 4
+    else:
+        b += 4 * dk + 4 * dk / batch
+    return b
+
+
+def deltalog_bytes_per_state_step(variant, dk, dv, L, batch) -> dict:
+    """Algorithmic HBM bytes per (sequence, head, token), averaged over a period of L steps."""
+    E = entry_bytes(variant, dk, dv)
+    state = 4 * dk * dv
+    parts = dict(
+        base_read=state,
+        inputs=input_bytes(variant, dk, dv, batch),
+        log_read=(L - 1) / 2 * E,           # the n entries present, n uniform over 0..L-1
+        fill=8,
+        output=4 * dv,
+        append=(L - 1) / L * E,             # every step but the folding one
+        fold_write=state / L,               # the folding step rewrites the base
+    )
+    parts["total"] = sum(parts.values())
+    parts["state_writes"] = parts["append"] + parts["fold_write"]
+    return parts
+
+
+def eager_bytes_per_state_step(variant, dk, dv, batch) -> dict:
+    state = 4 * dk * dv
+    parts = dict(state_read=state, state_write=state, inputs=input_bytes(variant, dk, dv, batch), output=4 * dv)
+    parts["total"] = sum(parts.values())
+    parts["state_writes"] = state
+    return parts
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_counter_profile(workload_name: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    path = os.path.join(PROFILE_DIR, f"decode_{workload_name}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return vals
+
+
+# ----------------------------------------------------------- CPU baseline ---
+def _cpu_worker(args):
+    workload, tiles, steps = args
+    import oracle  # the fp64 oracle, timed as it stands
+    inp = make_inputs(workload, steps, pool=steps, batch=WORKLOADS[workload]["batch"])
+    sel = tiles
+    t0 = time.perf_counter()
+    oracle.run_eager(inp, steps, sel=sel, keep_outputs=False)
+    return time.perf_counter() - t0, len(sel) * steps
+
+
+def cpu_baseline(workload: int, target_s: float = 12.0) -> dict:
+    """Time the fp64 eager oracle on the host cores over a bounded sample of the workload."""
+    import multiprocessing as mp
+
+    import oracle
+    w = WORKLOADS[workload]
+    B, H = w["batch"], w["heads"]
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    # calibrate on one core: seconds per tile-step
+    inp = make_inputs(workload, 2, pool=2, batch=1, heads=min(H, 8))
+    sel = [(0, h) for h in range(inp.heads)]
+    t0 = time.perf_counter()
+    oracle.run_eager(inp, 2, sel=sel, keep_outputs=False)
+    per = (time.perf_counter() - t0) / (2 * len(sel))
+    all_tiles = [(b, h) for b in range(B) for h in range(H)]
+    steps = max(2, int(target_s / (per * len(all_tiles) / cores)))
+    steps = min(steps, 64)
+    chunks = [all_tiles[i::cores] for i in range(cores)]
+    # the sample: `steps` steps on the workload's full batch, tiles split over the cores
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as p:
+        res = p.map(_cpu_worker, [(workload, c, steps) for c in chunks])
+    wall = time.perf_counter() - t0
+    work = sum(r[1] for r in res)
+    return {"value": work / wall, "unit": "state-steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 NumPy eager oracle, {steps} steps x {B}x{H} tiles of the same workload "
+                      f"split over {cores} forked workers, {wall:.1f} s wall (incl. input generation)"}
+
+
+# -------------------------------------------------------------- GPU legs ----
+def gpu_setup(workload, pool_slots, log_len=None):
+    import torch
+
+    from linear_attention_recurrent_amd import deltalog as dl
+    w = WORKLOADS[workload]
+    inp = make_inputs(workload, pool_slots, pool=pool_slots, log_len=log_len)
+    dev = torch.device("cuda", 0)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    T = dict(q=bf(inp.q), k=bf(inp.k), v=bf(inp.v), decay=torch.from_numpy(inp.decay).to(dev),
+             beta=None if inp.beta is None else torch.from_numpy(inp.beta).to(dev),
+             bonus=None if inp.bonus is None else torch.from_numpy(inp.bonus).to(dev),
+             s0=torch.from_numpy(inp.s0).to(dev),
+             out=torch.empty((inp.batch, inp.heads, inp.dv), dtype=torch.float32, device=dev))
+    ios = [dl.make_step_io(inp.variant, inp.batch, inp.heads, inp.dk, inp.dv, dev, T["q"][p], T["k"][p],
+                           T["v"][p], T["decay"][p], None if T["beta"] is None else T["beta"][p],
+                           T["bonus"], T["out"]) for p in range(pool_slots)]
+    return inp, T, ios, w
+
+
+def time_loop(fn, steps, warmup, graph_chunk=0):
+    """Run fn(t) for warmup untimed steps then `steps` timed ones; returns seconds (events)."""
+    import torch
+    for t in range(warmup):
+        fn(t)
+    torch.cuda.synchronize()
+    if graph_chunk:
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for t in range(graph_chunk):
+                    fn(warmup + t)
+        torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    if graph_chunk:
+        for _ in range(steps // graph_chunk):
+            g.replay()
+    else:
+        for t in range(steps):
+            fn(warmup + t)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4])
+    ap.add_argument("--log-len", type=int, default=None)
+    ap.add_argument("--pool-slots", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay the step loop as a HIP graph")
+    ap.add_argument("--only", choices=["deltalog", "eager", "copy"], default=None,
+                    help="run one leg only (for profiling runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Decode tiles are independent, so N GPUs would each run this same kernel on their own "
+              "share of sequences with no communication.", file=sys.stderr)
+        sys.exit(2)
+
+    cpu = None
+    if not args.no_cpu_baseline and args.only is None:
+        cpu = cpu_baseline(args.workload)  # before any GPU work: forked workers never touch the GPU
+
+    import torch
+
+    from linear_attention_recurrent_amd import deltalog as dl
+    dl.load_library()
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = torch.device("cuda", 0)
+
+    if args.only == "copy":
+        # plain copy of known size, for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters
+        n = 256 << 20
+        a = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n, "launches": 5}))
+        return
+
+    inp, T, ios, w = gpu_setup(args.workload, args.pool_slots, args.log_len)
+    B, H, dk, dv, L, var = inp.batch, inp.heads, inp.dk, inp.dv, inp.log_len, inp.variant
+    P = args.pool_slots
+    tiles = B * H
+    K, W = args.steps, args.warmup
+    chunk = 0
+    if args.graph:
+        chunk = L * max(1, 64 // L)
+        K = max(chunk, (K // chunk) * chunk)
+
+    result = {}
+    if args.only in (None, "deltalog"):
+        pool = dl.DeltaLogPool(var, B, H, dk, dv, L, dev)
+        dl.dl_init_state(pool, T["s0"], inp.fill0)
+        # W warmup steps, then K timed steps; both start the timed window at the same phase
+        W_al = ((W + L - 1) // L) * L
+        secs = time_loop(lambda t: dl.dl_decode_step(pool, ios[t % P]), K, W_al, chunk)
+        result["deltalog"] = secs
+    if args.only in (None, "eager"):
+        state = T["s0"].clone()
+        secs_e = time_loop(lambda t: dl.dl_eager_step(var, state, ios[t % P]), K, W, chunk)
+        result["eager"] = secs_e
+    if args.only is not None:
+        print(json.dumps({k: v / K * 1e3 for k, v in result.items()} | {"unit": "ms per step"}))
+        return
+
+    # cache-cold variant: three independent pools used in turn
+    pools = [dl.DeltaLogPool(var, B, H, dk, dv, L, dev) for _ in range(3)]
+    for p_ in pools:
+        dl.dl_init_state(p_, T["s0"], inp.fill0)
+    W_al = ((W + 3 * L - 1) // (3 * L)) * (3 * L)
+    Kc = (K // (3 * L)) * (3 * L) or 3 * L
+    secs_c = time_loop(lambda t: dl.dl_decode_step(pools[t % 3], ios[t % P]), Kc, W_al)
+    del pools
+
+    mdl = deltalog_bytes_per_state_step(var, dk, dv, L, B)
+    eag = eager_bytes_per_state_step(var, dk, dv, B)
+    t_step = result["deltalog"] / K
+    t_eager = result["eager"] / K
+    t_cold = secs_c / Kc
+    value = tiles / t_step
+    achieved = mdl["total"] * tiles / t_step / 1e9
+    prof = read_counter_profile(w["name"])
+    traffic = None
+    counter_write = None
+    if prof is not None:
+        traffic = float(prof["fetch_bytes_per_launch"]) + float(prof["write_bytes_per_launch"])
+        counter_write = {"deltalog": float(prof["write_bytes_per_launch"]) / tiles,
+                         "eager": float(prof.get("eager_write_bytes_per_launch", "nan")) / tiles,
+                         "source": f"profiles/decode_{w['name']}_counters.txt"}
+
+    line = {
+        "metric": "decode state-steps/s (B×H per s)",
+        "value": value,
+        "unit": "state-steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{VARIANT_NAMES[var]} decode B={B} H={H} dk={dk} dv={dv} L={L}",
+                   "variant": VARIANT_NAMES[var], "batch": B, "heads": H, "dk": dk, "dv": dv,
+                   "log_len": L, "initial_fill": "0 for every sequence" if not np.any(inp.fill0) else "ragged",
+                   "input_pool_steps": P, "hip_graph": bool(chunk)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+        "cpu_baseline": cpu,
+        "hbm_gbs_algorithmic": achieved,
+        "bytes_per_state_step_model": {"deltalog": mdl["total"], "eager": eag["total"]},
+        "state_write_bytes_per_state_step": {
+            "deltalog_model": mdl["state_writes"], "eager_model": eag["state_writes"],
+            "cut_model": eag["state_writes"] / mdl["state_writes"], "counters": counter_write},
+        "eager": {"value": tiles / t_eager, "ms_per_step": t_eager * 1e3,
+                  "hbm_gbs_algorithmic": eag["total"] * tiles / t_eager / 1e9,
+                  "deltalog_speedup": t_eager / t_step},
+        "cold_three_pools": {"value": tiles / t_cold, "ms_per_step": t_cold * 1e3,
+                             "hbm_gbs_algorithmic": mdl["total"] * tiles / t_cold / 1e9,
+                             "frac": mdl["total"] * tiles / t_cold / 1e9 / HBM_PEAK_GBS},
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

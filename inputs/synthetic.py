@@ -141,7 +141,8 @@ def _l2n(x: np.ndarray) -> np.ndarray:
 def make_inputs(workload: int, steps: Optional[int] = None, *, batch: Optional[int] = None,
                 heads: Optional[int] = None, log_len: Optional[int] = None,
                 pool: Optional[int] = None, seed: Optional[int] = None,
-                fill0: Optional[np.ndarray] = None, layer: int = 0) -> DecodeInputs:
+                fill0: Optional[np.ndarray] = None, layer: int = 0, dk: Optional[int] = None,
+                dv: Optional[int] = None) -> DecodeInputs:
     """Draw the inputs of a decode workload (see WORKLOADS).
 
     steps:   number of decode steps the run will take (default: the workload's).
@@ -152,12 +153,14 @@ def make_inputs(workload: int, steps: Optional[int] = None, *, batch: Optional[i
     fill0:   explicit initial fills [batch]; default zeros, or U{0..L-1} per
              sequence for ragged workloads.
     layer:   layer index for multi-layer workloads (separate streams per layer).
+    dk, dv:  override the head sizes (edge-case shapes; distributions unchanged).
     """
     w = WORKLOADS[workload]
     variant = w["variant"]
     B = w["batch"] if batch is None else int(batch)
     H = w["heads"] if heads is None else int(heads)
-    dk, dv = w["dk"], w["dv"]
+    dk = w["dk"] if dk is None else int(dk)
+    dv = w["dv"] if dv is None else int(dv)
     L = w["log_len"] if log_len is None else int(log_len)
     T = w["steps"] if steps is None else int(steps)
     P = min(T, 256) if pool is None else int(pool)

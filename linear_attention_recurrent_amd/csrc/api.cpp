@@ -1,0 +1,130 @@
+// C ABI of the DeltaLog decode library: host-side argument checks and the
+// launch sequence.  The operations, layouts and status codes are documented in
+// include/deltalog.h.  Every check runs before anything is enqueued.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/deltalog.h"
+#include "launch.hpp"
+
+namespace {
+
+// Arrays read or written with 16-byte vector accesses need 16-byte alignment;
+// arrays of one scalar per tile (and the output) need 4.
+bool misaligned(const void* ptr, uintptr_t align = 16) {
+  return (reinterpret_cast<uintptr_t>(ptr) & (align - 1)) != 0;
+}
+
+int check_dims(const dl_dims* d) {
+  if (d == nullptr) return DL_EINVAL;
+  if (d->variant < DL_GDN || d->variant > DL_RWKV6) return DL_EINVAL;
+  if (d->batch < 0 || d->heads < 1) return DL_EINVAL;
+  if (d->log_len < 1 || d->log_len > DL_MAX_LOG_LEN) return DL_EINVAL;
+  if (static_cast<int64_t>(d->batch) * d->heads > INT32_MAX) return DL_EINVAL;
+  if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128)) return DL_EUNSUPPORTED;
+  return DL_OK;
+}
+
+int check_pool(const dl_pool* p, int variant) {
+  if (p == nullptr) return DL_EINVAL;
+  if (!p->base || !p->log_k || !p->log_u || !p->log_c || !p->fill) return DL_EINVAL;
+  if (misaligned(p->base) || misaligned(p->log_k) || misaligned(p->log_u) ||
+      misaligned(p->log_c, variant == DL_GDN ? 4 : 16) || misaligned(p->fill, 4))
+    return DL_EALIGN;
+  return DL_OK;
+}
+
+int check_io(const dl_dims* d, const dl_step_io* io) {
+  if (io == nullptr) return DL_EINVAL;
+  if (!io->q || !io->k || !io->v || !io->decay || !io->out) return DL_EINVAL;
+  const bool rwkv = d->variant == DL_RWKV6;
+  if (rwkv && (io->beta != nullptr || io->bonus == nullptr)) return DL_EUNSUPPORTED;
+  if (!rwkv && (io->beta == nullptr || io->bonus != nullptr)) return DL_EUNSUPPORTED;
+  if (misaligned(io->q) || misaligned(io->k) || misaligned(io->v) ||
+      misaligned(io->decay, rwkv || d->variant == DL_KDA ? 16 : 4) || misaligned(io->out, 4) ||
+      (io->beta && misaligned(io->beta, 4)) || (io->bonus && misaligned(io->bonus)))
+    return DL_EALIGN;
+  return DL_OK;
+}
+
+dl::PoolArgs pool_args(const dl_dims* d, const dl_pool* p) {
+  return dl::PoolArgs{p->base, p->log_k, p->log_u, p->log_c, p->fill, d->heads, d->log_len};
+}
+
+dl::StepArgs step_args(const dl_step_io* io) {
+  return dl::StepArgs{io->q, io->k, io->v, io->decay, io->beta, io->bonus, io->out};
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DL_OK : DL_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int dl_init_state(const dl_dims* dims, const dl_pool* pool, const float* init_base,
+                  const int32_t* init_fill, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != DL_OK || dims->batch == 0) return rc;
+  if ((rc = check_pool(pool, dims->variant)) != DL_OK) return rc;
+  if (init_base && misaligned(init_base)) return DL_EALIGN;
+  const int batch = dims->batch, heads = dims->heads;
+  std::vector<int32_t> fills(static_cast<size_t>(batch) * heads, 0);
+  if (init_fill) {
+    for (int b = 0; b < batch; ++b) {
+      if (init_fill[b] < 0 || init_fill[b] >= dims->log_len) return DL_EINVAL;
+      for (int h = 0; h < heads; ++h) fills[static_cast<size_t>(b) * heads + h] = init_fill[b];
+    }
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(pool->fill, fills.data(), fills.size() * sizeof(int32_t),
+                                hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return DL_EHIP;
+  e = dl::launch_init(dims->variant, dims->dk, dims->dv, batch * heads, pool_args(dims, pool), init_base, st);
+  if (e != hipSuccess) return DL_EHIP;
+  return hip_status(hipStreamSynchronize(st));
+}
+
+int dl_decode_step(const dl_dims* dims, const dl_pool* pool, const dl_step_io* io, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != DL_OK || dims->batch == 0) return rc;
+  if ((rc = check_pool(pool, dims->variant)) != DL_OK) return rc;
+  if ((rc = check_io(dims, io)) != DL_OK) return rc;
+  return hip_status(dl::launch_decode(dims->variant, dims->dk, dims->dv, dims->batch * dims->heads,
+                                      pool_args(dims, pool), step_args(io),
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int dl_merge(const dl_dims* dims, const dl_pool* pool, int32_t min_fill, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != DL_OK) return rc;
+  if (min_fill < 1 || min_fill > dims->log_len) return DL_EINVAL;
+  if (dims->batch == 0) return DL_OK;
+  if ((rc = check_pool(pool, dims->variant)) != DL_OK) return rc;
+  return hip_status(dl::launch_merge(dims->variant, dims->dk, dims->dv, dims->batch * dims->heads,
+                                     pool_args(dims, pool), min_fill, static_cast<hipStream_t>(stream)));
+}
+
+int dl_eager_step(const dl_dims* dims, float* state, const dl_step_io* io, void* stream) {
+  int rc = check_dims(dims);
+  if (rc != DL_OK || dims->batch == 0) return rc;
+  if ((rc = check_io(dims, io)) != DL_OK) return rc;
+  if (state == nullptr) return DL_EINVAL;
+  if (misaligned(state)) return DL_EALIGN;
+  return hip_status(dl::launch_eager(dims->variant, dims->dk, dims->dv, dims->batch * dims->heads,
+                                     dims->heads, state, step_args(io), static_cast<hipStream_t>(stream)));
+}
+
+const char* dl_status_string(int status) {
+  switch (status) {
+    case DL_OK: return "DL_OK: success";
+    case DL_EINVAL: return "DL_EINVAL: invalid argument (null pointer, dims, log length or fill out of range)";
+    case DL_EUNSUPPORTED: return "DL_EUNSUPPORTED: unsupported head size or variant/pointer combination";
+    case DL_EALIGN: return "DL_EALIGN: a device pointer is not aligned as required";
+    case DL_EHIP: return "DL_EHIP: the HIP runtime reported an error";
+    default: return "unknown deltalog status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,202 @@
+"""Python binding of libdeltalog.so: argument marshalling only.
+
+The four calls have the C names and meanings declared in include/deltalog.h
+(dl_init_state, dl_decode_step, dl_merge, dl_eager_step).  PyTorch supplies
+device memory and the stream; every step of the decode path runs in the HIP
+kernels of libdeltalog.so.  There is no CPU fallback: if the library is not
+built, or no GPU is present, these calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # imported first so the library binds to the HIP runtime torch already loaded
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdeltalog.so")
+
+GDN, KDA, RWKV6 = 0, 1, 2
+DL_OK, DL_EINVAL, DL_EUNSUPPORTED, DL_EALIGN, DL_EHIP = 0, -1, -2, -3, -4
+MAX_LOG_LEN = 128
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("log_len", ctypes.c_int32)]
+
+
+class Pool(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("log_k", ctypes.c_void_p), ("log_u", ctypes.c_void_p),
+                ("log_c", ctypes.c_void_p), ("fill", ctypes.c_void_p)]
+
+
+class StepIO(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("decay", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("bonus", ctypes.c_void_p),
+                ("out", ctypes.c_void_p)]
+
+
+class DeltaLogError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libdeltalog.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built; run `python -m linear_attention_recurrent_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp = ctypes.c_void_p
+    lib.dl_init_state.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Pool), vp,
+                                  ctypes.POINTER(ctypes.c_int32), vp]
+    lib.dl_decode_step.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Pool), ctypes.POINTER(StepIO), vp]
+    lib.dl_merge.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Pool), ctypes.c_int32, vp]
+    lib.dl_eager_step.argtypes = [ctypes.POINTER(Dims), vp, ctypes.POINTER(StepIO), vp]
+    lib.dl_status_string.argtypes = [ctypes.c_int]
+    lib.dl_status_string.restype = ctypes.c_char_p
+    for f in (lib.dl_init_state, lib.dl_decode_step, lib.dl_merge, lib.dl_eager_step):
+        f.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().dl_status_string(int(status)).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != DL_OK:
+        raise DeltaLogError(rc, what)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, shape: tuple, dtype: torch.dtype, device) -> None:
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {shape}, "
+                         f"got {t.dtype} {tuple(t.shape)}")
+
+
+class DeltaLogPool:
+    """One layer's state pool: the device tensors of dl_pool plus its dims.
+
+    base  fp32 [B][H][dk][dv]; log_k bf16 [B][H][L][dk];
+    log_u fp32 (GDN/KDA) or bf16 (RWKV6) [B][H][L][dv];
+    log_c fp32 [B][H][L][1 or dk]; fill int32 [B][H].
+    """
+
+    def __init__(self, variant: int, batch: int, heads: int, dk: int, dv: int, log_len: int,
+                 device="cuda"):
+        self.device = torch.device(device)
+        if self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        self.variant, self.batch, self.heads = int(variant), int(batch), int(heads)
+        self.dk, self.dv, self.log_len = int(dk), int(dv), int(log_len)
+        B, H, L = self.batch, self.heads, self.log_len
+        g = 1 if variant == GDN else dk
+        kw = dict(device=self.device)
+        self.base = torch.empty((B, H, dk, dv), dtype=torch.float32, **kw)
+        self.log_k = torch.empty((B, H, L, dk), dtype=torch.bfloat16, **kw)
+        self.log_u = torch.empty((B, H, L, dv), dtype=torch.bfloat16 if variant == RWKV6 else torch.float32,
+                                 **kw)
+        self.log_c = torch.empty((B, H, L, g), dtype=torch.float32, **kw)
+        self.fill = torch.empty((B, H), dtype=torch.int32, **kw)
+        self.c_dims = Dims(self.variant, B, H, self.dk, self.dv, L)
+        self.c_pool = Pool(self.base.data_ptr(), self.log_k.data_ptr(), self.log_u.data_ptr(),
+                           self.log_c.data_ptr(), self.fill.data_ptr())
+
+    def tensors(self) -> dict:
+        return dict(base=self.base, log_k=self.log_k, log_u=self.log_u, log_c=self.log_c, fill=self.fill)
+
+    def clone(self) -> "DeltaLogPool":
+        other = DeltaLogPool(self.variant, self.batch, self.heads, self.dk, self.dv, self.log_len, self.device)
+        for name, t in self.tensors().items():
+            getattr(other, name).copy_(t)
+        return other
+
+    def step_io(self, q, k, v, decay, beta, bonus, out) -> StepIO:
+        """Check the step tensors against this pool's shape and pack them into a StepIO."""
+        return make_step_io(self.variant, self.batch, self.heads, self.dk, self.dv, self.device,
+                            q, k, v, decay, beta, bonus, out)
+
+
+def make_step_io(variant, batch, heads, dk, dv, device, q, k, v, decay, beta, bonus, out) -> StepIO:
+    B, H = batch, heads
+    _need(q, "q", (B, H, dk), torch.bfloat16, device)
+    _need(k, "k", (B, H, dk), torch.bfloat16, device)
+    _need(v, "v", (B, H, dv), torch.bfloat16, device)
+    _need(decay, "decay", (B, H) if variant == GDN else (B, H, dk), torch.float32, device)
+    if variant == RWKV6:
+        _need(bonus, "bonus", (H, dk), torch.float32, device)
+        if beta is not None:
+            raise ValueError("beta must be None for RWKV6")
+    else:
+        _need(beta, "beta", (B, H), torch.float32, device)
+        if bonus is not None:
+            raise ValueError("bonus must be None for GDN/KDA")
+    _need(out, "out", (B, H, dv), torch.float32, device)
+    return StepIO(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta), _ptr(bonus), _ptr(out))
+
+
+# ------------------------------------------------------------- the C calls --
+def dl_init_state(pool: DeltaLogPool, init_base: Optional[torch.Tensor] = None,
+                  init_fill=None, stream=None) -> None:
+    """Start the pool from `init_base` (or zeros) with per-sequence log fills `init_fill`."""
+    if init_base is not None:
+        _need(init_base, "init_base", tuple(pool.base.shape), torch.float32, pool.device)
+    fill_arr = None
+    if init_fill is not None:
+        vals = [int(x) for x in init_fill]
+        if len(vals) != pool.batch:
+            raise ValueError(f"init_fill must have {pool.batch} entries")
+        fill_arr = (ctypes.c_int32 * max(len(vals), 1))(*vals)
+    rc = load_library().dl_init_state(ctypes.byref(pool.c_dims), ctypes.byref(pool.c_pool),
+                                      _ptr(init_base), fill_arr, _stream(stream))
+    _check(rc, "dl_init_state")
+
+
+def dl_decode_step(pool: DeltaLogPool, io: StepIO, stream=None) -> None:
+    """One decode step (append, or fold on the step that fills the log) for every tile."""
+    rc = load_library().dl_decode_step(ctypes.byref(pool.c_dims), ctypes.byref(pool.c_pool),
+                                       ctypes.byref(io), _stream(stream))
+    _check(rc, "dl_decode_step")
+
+
+def dl_merge(pool: DeltaLogPool, min_fill: int = 1, stream=None) -> None:
+    """Fold the log of every tile holding >= min_fill entries into its base."""
+    rc = load_library().dl_merge(ctypes.byref(pool.c_dims), ctypes.byref(pool.c_pool), int(min_fill),
+                                 _stream(stream))
+    _check(rc, "dl_merge")
+
+
+def dl_eager_step(variant: int, state: torch.Tensor, io: StepIO, stream=None) -> None:
+    """Eager comparator: read `state` [B][H][dk][dv], update it in place, write io.out."""
+    if state.dtype != torch.float32 or state.dim() != 4 or not state.is_contiguous() or not state.is_cuda:
+        raise ValueError("state must be a contiguous fp32 cuda tensor [B][H][dk][dv]")
+    B, H, dk, dv = state.shape
+    dims = Dims(int(variant), B, H, dk, dv, 1)
+    rc = load_library().dl_eager_step(ctypes.byref(dims), state.data_ptr(), ctypes.byref(io), _stream(stream))
+    _check(rc, "dl_eager_step")

@@ -1,0 +1,144 @@
+"""The C ABI library: it loads, exports what the header declares, and rejects bad
+arguments on the host before touching the GPU (CPU only: no kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "deltalog.h")
+LIB = os.path.join(ROOT, "linear_attention_recurrent_amd", "libdeltalog.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(dl_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libdeltalog.so is not built: run `python -m linear_attention_recurrent_amd.build`")
+    from linear_attention_recurrent_amd import deltalog
+    return deltalog.load_library()
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("dl_init_state", "dl_decode_step", "dl_merge", "dl_eager_step", "dl_status_string"):
+        assert n in names
+    assert len(names) == 5, names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {LIB}").read()
+    exported = set(re.findall(r"\sT\s+(dl_\w+)$", out, flags=re.M))
+    assert exported == set(declared_functions()), exported
+
+
+def test_status_strings(lib):
+    from linear_attention_recurrent_amd import deltalog as dl
+    for code, tag in [(dl.DL_OK, "DL_OK"), (dl.DL_EINVAL, "DL_EINVAL"), (dl.DL_EUNSUPPORTED, "DL_EUNSUPPORTED"),
+                      (dl.DL_EALIGN, "DL_EALIGN"), (dl.DL_EHIP, "DL_EHIP")]:
+        assert dl.status_string(code).startswith(tag)
+    assert "unknown" in dl.status_string(12345)
+
+
+# Fake device addresses: the host checks reject these calls before any HIP call,
+# so nothing is dereferenced.
+A = 0x10000      # 16-byte aligned
+M = 0x10004      # misaligned
+
+
+def _dims(dl, variant=0, batch=2, heads=2, dk=128, dv=128, L=16):
+    return dl.Dims(variant, batch, heads, dk, dv, L)
+
+
+def _pool(dl, base=A):
+    return dl.Pool(base, A, A, A, A)
+
+
+def _io(dl, variant=0, **kw):
+    f = dict(q=A, k=A, v=A, decay=A, beta=A if variant != 2 else None,
+             bonus=A if variant == 2 else None, out=A)
+    f.update(kw)
+    return dl.StepIO(f["q"], f["k"], f["v"], f["decay"], f["beta"], f["bonus"], f["out"])
+
+
+def _decode(lib, dims, pool, io):
+    return lib.dl_decode_step(ctypes.byref(dims), ctypes.byref(pool), ctypes.byref(io), None)
+
+
+def test_dims_errors(lib):
+    from linear_attention_recurrent_amd import deltalog as dl
+    bad = [(dict(variant=3), dl.DL_EINVAL), (dict(variant=-1), dl.DL_EINVAL), (dict(batch=-1), dl.DL_EINVAL),
+           (dict(heads=0), dl.DL_EINVAL), (dict(L=0), dl.DL_EINVAL), (dict(L=129), dl.DL_EINVAL),
+           (dict(dk=96), dl.DL_EUNSUPPORTED), (dict(dv=256), dl.DL_EUNSUPPORTED),
+           (dict(batch=1 << 20, heads=1 << 12), dl.DL_EINVAL)]
+    for kw, code in bad:
+        assert _decode(lib, _dims(dl, **kw), _pool(dl), _io(dl)) == code, kw
+    assert lib.dl_decode_step(None, ctypes.byref(_pool(dl)), ctypes.byref(_io(dl)), None) == dl.DL_EINVAL
+
+
+def test_pool_and_io_errors(lib):
+    from linear_attention_recurrent_amd import deltalog as dl
+    d = _dims(dl)
+    assert _decode(lib, d, dl.Pool(A, None, A, A, A), _io(dl)) == dl.DL_EINVAL
+    assert _decode(lib, d, _pool(dl, base=M), _io(dl)) == dl.DL_EALIGN
+    assert _decode(lib, d, _pool(dl), _io(dl, out=None)) == dl.DL_EINVAL
+    assert _decode(lib, d, _pool(dl), _io(dl, q=M)) == dl.DL_EALIGN
+    # one-scalar-per-tile arrays need only 4-byte alignment, but not less
+    assert _decode(lib, d, _pool(dl), _io(dl, decay=A + 2)) == dl.DL_EALIGN
+    assert _decode(lib, d, _pool(dl), _io(dl, out=A + 2)) == dl.DL_EALIGN
+    assert _decode(lib, d, dl.Pool(A, A, A, A, A + 2), _io(dl)) == dl.DL_EALIGN
+    d1 = _dims(dl, variant=1)
+    assert _decode(lib, d1, _pool(dl), _io(dl, variant=1, decay=M)) == dl.DL_EALIGN
+    assert _decode(lib, d1, dl.Pool(A, A, A, M, A), _io(dl, variant=1)) == dl.DL_EALIGN
+    # variant / pointer mismatches
+    assert _decode(lib, d, _pool(dl), _io(dl, beta=None)) == dl.DL_EUNSUPPORTED
+    assert _decode(lib, d, _pool(dl), _io(dl, bonus=A)) == dl.DL_EUNSUPPORTED
+    d2 = _dims(dl, variant=2, dk=64, dv=64, L=32)
+    assert _decode(lib, d2, _pool(dl), _io(dl, variant=2, beta=A)) == dl.DL_EUNSUPPORTED
+    assert _decode(lib, d2, _pool(dl), _io(dl, variant=2, bonus=None)) == dl.DL_EUNSUPPORTED
+    assert lib.dl_decode_step(ctypes.byref(d), ctypes.byref(_pool(dl)), None, None) == dl.DL_EINVAL
+
+
+def test_merge_init_eager_errors(lib):
+    from linear_attention_recurrent_amd import deltalog as dl
+    d = _dims(dl, L=16)
+    p = _pool(dl)
+    assert lib.dl_merge(ctypes.byref(d), ctypes.byref(p), 0, None) == dl.DL_EINVAL
+    assert lib.dl_merge(ctypes.byref(d), ctypes.byref(p), 17, None) == dl.DL_EINVAL
+    assert lib.dl_merge(ctypes.byref(d), None, 1, None) == dl.DL_EINVAL
+    fills = (ctypes.c_int32 * 2)(0, 16)
+    assert lib.dl_init_state(ctypes.byref(d), ctypes.byref(p), None, fills, None) == dl.DL_EINVAL
+    fills = (ctypes.c_int32 * 2)(-1, 0)
+    assert lib.dl_init_state(ctypes.byref(d), ctypes.byref(p), None, fills, None) == dl.DL_EINVAL
+    assert lib.dl_init_state(ctypes.byref(d), ctypes.byref(p), M, None, None) == dl.DL_EALIGN
+    assert lib.dl_eager_step(ctypes.byref(d), None, ctypes.byref(_io(dl)), None) == dl.DL_EINVAL
+    assert lib.dl_eager_step(ctypes.byref(d), M, ctypes.byref(_io(dl)), None) == dl.DL_EALIGN
+
+
+def test_batch_zero_returns_ok_without_looking_at_pointers(lib):
+    from linear_attention_recurrent_amd import deltalog as dl
+    d = _dims(dl, batch=0)
+    empty = dl.Pool(None, None, None, None, None)
+    noio = dl.StepIO(None, None, None, None, None, None, None)
+    assert lib.dl_decode_step(ctypes.byref(d), ctypes.byref(empty), ctypes.byref(noio), None) == dl.DL_OK
+    assert lib.dl_merge(ctypes.byref(d), ctypes.byref(empty), 1, None) == dl.DL_OK
+    assert lib.dl_init_state(ctypes.byref(d), ctypes.byref(empty), None, None, None) == dl.DL_OK
+    assert lib.dl_eager_step(ctypes.byref(d), None, ctypes.byref(noio), None) == dl.DL_OK
+
+
+def test_product_path_does_not_use_the_oracle():
+    pkg = os.path.join(ROOT, "linear_attention_recurrent_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert not re.search(r"(^|[^A-Za-z])_work/", text), f
