@@ -110,44 +110,56 @@ def read_counter_profile(workload_name: str):
 
 
 # ----------------------------------------------------------- CPU baseline ---
-def _cpu_worker(args):
-    workload, tiles, steps = args
+_CPU_JOB = {}
+
+
+def _cpu_worker(i, barrier, queue):
     import oracle  # the fp64 oracle, timed as it stands
-    inp = make_inputs(workload, steps, pool=steps, batch=WORKLOADS[workload]["batch"])
-    sel = tiles
+    job = _CPU_JOB
+    barrier.wait()
     t0 = time.perf_counter()
-    oracle.run_eager(inp, steps, sel=sel, keep_outputs=False)
-    return time.perf_counter() - t0, len(sel) * steps
+    oracle.run_eager(job["inp"], job["steps"], sel=job["chunks"][i], keep_outputs=False)
+    queue.put((i, time.perf_counter() - t0, len(job["chunks"][i]) * job["steps"]))
 
 
 def cpu_baseline(workload: int, target_s: float = 12.0) -> dict:
-    """Time the fp64 eager oracle on the host cores over a bounded sample of the workload."""
+    """Time the fp64 eager oracle on the host cores over a bounded sample of the workload.
+
+    The inputs are drawn once in this process; forked workers (one per core, at
+    most 16) each run the oracle on a contiguous share of the tiles, starting
+    together at a barrier.  Throughput = all tile-steps / the slowest worker's time.
+    """
     import multiprocessing as mp
 
     import oracle
     w = WORKLOADS[workload]
     B, H = w["batch"], w["heads"]
     cores = min(len(os.sched_getaffinity(0)), 16)
-    # calibrate on one core: seconds per tile-step
-    inp = make_inputs(workload, 2, pool=2, batch=1, heads=min(H, 8))
-    sel = [(0, h) for h in range(inp.heads)]
+    probe = make_inputs(workload, 2, pool=2, batch=1, heads=min(H, 8))
+    sel = [(0, h) for h in range(probe.heads)]
     t0 = time.perf_counter()
-    oracle.run_eager(inp, 2, sel=sel, keep_outputs=False)
-    per = (time.perf_counter() - t0) / (2 * len(sel))
+    oracle.run_eager(probe, 2, sel=sel, keep_outputs=False)
+    per = (time.perf_counter() - t0) / (2 * len(sel))          # seconds per tile-step, one core
     all_tiles = [(b, h) for b in range(B) for h in range(H)]
-    steps = max(2, int(target_s / (per * len(all_tiles) / cores)))
-    steps = min(steps, 64)
-    chunks = [all_tiles[i::cores] for i in range(cores)]
-    # the sample: `steps` steps on the workload's full batch, tiles split over the cores
+    steps = int(min(64, max(2, target_s * cores / (per * len(all_tiles)))))
+    per_core = (len(all_tiles) + cores - 1) // cores
+    _CPU_JOB.update(inp=make_inputs(workload, steps, pool=steps), steps=steps,
+                    chunks=[all_tiles[i * per_core:(i + 1) * per_core] for i in range(cores)])
     ctx = mp.get_context("fork")
-    t0 = time.perf_counter()
-    with ctx.Pool(cores) as p:
-        res = p.map(_cpu_worker, [(workload, c, steps) for c in chunks])
-    wall = time.perf_counter() - t0
-    work = sum(r[1] for r in res)
+    barrier, queue = ctx.Barrier(cores), ctx.Queue()
+    procs = [ctx.Process(target=_cpu_worker, args=(i, barrier, queue)) for i in range(cores)]
+    for p in procs:
+        p.start()
+    res = [queue.get() for _ in procs]
+    for p in procs:
+        p.join()
+    wall = max(r[1] for r in res)
+    work = sum(r[2] for r in res)
+    _CPU_JOB.clear()
     return {"value": work / wall, "unit": "state-steps/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 NumPy eager oracle, {steps} steps x {B}x{H} tiles of the same workload "
-                      f"split over {cores} forked workers, {wall:.1f} s wall (incl. input generation)"}
+            "sample": f"fp64 NumPy eager oracle on the same workload: {steps} steps x all {B}x{H} tiles, "
+                      f"tiles split over {cores} forked single-threaded workers, {wall:.1f} s "
+                      f"(slowest worker; input drawing not timed)"}
 
 
 # -------------------------------------------------------------- GPU legs ----
