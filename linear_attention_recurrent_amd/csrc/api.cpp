@@ -6,7 +6,7 @@
 
 #include <vector>
 
-#include "../../include/deltalog.h"
+#include "deltalog.h"
 #include "launch.hpp"
 
 namespace {

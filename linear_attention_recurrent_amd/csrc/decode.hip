@@ -8,7 +8,7 @@
 // appends on most steps, periodic merges into the base).
 //
 // Decode step, per (sequence, head) tile, n = entries in the log:
-//   reads   r_k = B^T (2^c_t . k_t)  and  r_q = B^T (2^c_t . q_t)   one pass over B
+//   reads   r_k = B^T (2^c_t . k_t)  and  r_q = B^T (2^c_t . q_t)   one streamed pass over B
 //           sigma^k_j = sum_i k_j[i] 2^(c_t[i]-c_j[i]) k_t[i]  (and sigma^q_j with q_t)
 //   GDN/KDA u_t = beta (v_t - r_k - sum_j sigma^k_j u_j)     the delta-rule residual write
 //           o_t = r_q + sum_j sigma^q_j u_j + (k_t . q_t) u_t  output of the updated state
@@ -16,9 +16,9 @@
 //           (sigma^r_j with c_{t-1}: the readout sees the state before the write)
 //   append  (k_t, u_t, c_t) to slot n, unless n + 1 == L: then fold all L
 //           updates into B (B <- diag(2^c_t) B + sum_j diag(2^(c_t-c_j)) k_j u_j^T)
-//           and reset the fill to 0.
-// The base is read once and written only by folding steps; a non-folding step
-// writes the output, one log entry and the fill.
+//           in a second streamed pass over B, and reset the fill to 0.
+// A non-folding step reads the base once and writes only the output, one log
+// entry and the fill.
 #include <type_traits>
 
 #include "dl_device.hpp"
@@ -26,112 +26,56 @@
 
 namespace dl {
 
-// Fold log entries [0, nlog) of a tile, plus the current step's update when
-// has_cur, into the base rows held in registers.  s_cnow is the cumulative
-// log2-decay to fold at (LDS, 1 or DK floats), s_kcur / s_ucur the current
-// update's key and factor (LDS).  s_w / s_uu are LDS staging areas of MC*DK and
-// MC*DV floats.  Must be called by every thread of the workgroup.
-template <int VAR, int DK, int DV, int RPT>
-__device__ __forceinline__ void fold_into(float4 (&B)[RPT], const PoolArgs& p, int tile,
-                                          int nlog, const float* s_cnow, bool has_cur,
-                                          const float* s_kcur, const float* s_ucur, float* s_w,
-                                          float* s_uu) {
-  using G = Geo<DK, DV>;
-  static_assert(RPT == G::RPT, "register tile");
-  const int tid = threadIdx.x;
-  const int rg = tid / G::CG, cg = tid % G::CG;
-  const size_t lbase = (size_t)tile * p.L;
-
-  if constexpr (VAR == DL_GDN) {
-    const float g = exp2f(s_cnow[0]);
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) B[r] = f4_mul(B[r], g);
-  } else {
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) B[r] = f4_mul(B[r], exp2f(s_cnow[rg * RPT + r]));
-  }
-
-  const int total = nlog + (has_cur ? 1 : 0);
-  for (int m0 = 0; m0 < total; m0 += G::MC) {
-    for (int idx = tid; idx < G::MC * DK; idx += G::NT) {
-      const int m = idx / DK, i = idx % DK, e = m0 + m;
-      float w = 0.f;
-      if (e < nlog) {
-        const float kj = bf16_to_f32(p.log_k[(lbase + e) * DK + i]);
-        const float dc = (VAR == DL_GDN) ? (s_cnow[0] - p.log_c[lbase + e])
-                                         : (s_cnow[i] - p.log_c[(lbase + e) * DK + i]);
-        w = exp2f(dc) * kj;
-      } else if (e == nlog && has_cur) {
-        w = s_kcur[i];
-      }
-      s_w[m * DK + i] = w;
-    }
-    for (int idx = tid; idx < G::MC * DV; idx += G::NT) {
-      const int m = idx / DV, j = idx % DV, e = m0 + m;
-      float u = 0.f;
-      if (e < nlog) {
-        if constexpr (VAR == DL_RWKV6)
-          u = bf16_to_f32(static_cast<const uint16_t*>(p.log_u)[(lbase + e) * DV + j]);
-        else
-          u = static_cast<const float*>(p.log_u)[(lbase + e) * DV + j];
-      } else if (e == nlog && has_cur) {
-        u = s_ucur[j];
-      }
-      s_uu[m * DV + j] = u;
-    }
-    __syncthreads();
-    const int mcount = min(G::MC, total - m0);
-    for (int m = 0; m < mcount; ++m) {
-      const float4 u4 = *reinterpret_cast<const float4*>(s_uu + m * DV + cg * 4);
-      const float* wr = s_w + m * DK + rg * RPT;
-#pragma unroll
-      for (int r = 0; r < RPT; r += 4) {
-        const float4 w4 = *reinterpret_cast<const float4*>(wr + r);
-        B[r + 0] = f4_fma(w4.x, u4, B[r + 0]);
-        B[r + 1] = f4_fma(w4.y, u4, B[r + 1]);
-        B[r + 2] = f4_fma(w4.z, u4, B[r + 2]);
-        B[r + 3] = f4_fma(w4.w, u4, B[r + 3]);
-      }
-    }
-    __syncthreads();
-  }
-}
-
 // Read coefficients of one log entry j, computed by a group of LPE lanes that
 // each hold 8 key channels:
 //   GDN    sigma^k_j = 2^(c_t - c_j) (k_j . k_t),   sigma^q_j = 2^(c_t - c_j) (k_j . q_t)
 //   KDA    sigma^k_j = sum_i k_j[i] 2^(c_t[i] - c_j[i]) k_t[i]   (sigma^q_j with q_t)
 //   RWKV6  sigma^r_j = sum_i k_j[i] 2^(c_{t-1}[i] - c_j[i]) r_t[i]
-// Lane 0 of the group stores them to s_sig[0][j] and s_sig[1][j].
-template <int VAR, int LPE, int CWN>
+// Lane 0 of the group stores them to s_sig[0][j] and s_sig[1][j].  When
+// `stage` is set, the group also stores the entry's fold weights
+// w_j[i] = 2^(c_t[i] - c_j[i]) k_j[i] to s_w (rows permuted).
+template <int VAR, int DK, int DV, int CWN>
 __device__ __forceinline__ void log_coefs(const uint4 kj8, const float (&cj)[CWN], const float (&kt)[8],
                                           const float (&qt)[8], const float (&ct)[CWN],
                                           const float (&cprev)[CWN], float (*s_sig)[DL_MAX_LOG_LEN],
-                                          int j, int ch) {
+                                          int j, int ch, bool stage, float* s_w) {
+  using G = SGeo<DK, DV>;
   float kj[8];
   unpack8(kj8, kj);
   float a = 0.f, b = 0.f;
+  float e[8];  // 2^(c_t - c_j) per channel (GDN: one value)
   if constexpr (VAR == DL_GDN) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       a = fmaf(kj[i], kt[i], a);
       b = fmaf(kj[i], qt[i], b);
     }
+    const float sc = exp2f(ct[0] - cj[0]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = sc;
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float e = kj[i] * exp2f((VAR == DL_RWKV6 ? cprev[i] : ct[i]) - cj[i]);
-      a = fmaf(e, VAR == DL_RWKV6 ? qt[i] : kt[i], a);
-      if constexpr (VAR == DL_KDA) b = fmaf(e, qt[i], b);
+      e[i] = exp2f(ct[i] - cj[i]);
+      if constexpr (VAR == DL_RWKV6) {
+        a = fmaf(kj[i] * exp2f(cprev[i] - cj[i]), qt[i], a);
+      } else {
+        const float w = kj[i] * e[i];
+        a = fmaf(w, kt[i], a);
+        b = fmaf(w, qt[i], b);
+      }
     }
   }
-  a = group_sum<LPE>(a);
-  if constexpr (VAR != DL_RWKV6) b = group_sum<LPE>(b);
+  if (stage) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s_w[j * DK + G::perm(ch * 8 + i)] = e[i] * kj[i];
+  }
+  a = group_sum<G::LPE>(a);
+  if constexpr (VAR != DL_RWKV6) b = group_sum<G::LPE>(b);
   if (ch == 0) {
     if constexpr (VAR == DL_GDN) {
-      const float sc = exp2f(ct[0] - cj[0]);
-      s_sig[0][j] = sc * a;
-      s_sig[1][j] = sc * b;
+      s_sig[0][j] = e[0] * a;
+      s_sig[1][j] = e[0] * b;
     } else {
       s_sig[0][j] = a;
       s_sig[1][j] = b;
@@ -139,116 +83,231 @@ __device__ __forceinline__ void log_coefs(const uint4 kj8, const float (&cj)[CWN
   }
 }
 
+// Stage fold entries [e0, e0 + cnt) of a tile into s_w / s_uu for a fold at
+// cumulative decay s_cnow (LDS, natural channel order).  Entries below nlog
+// come from the log: s_w[m][perm(i)] = 2^(c_now[i] - c_e[i]) k_e[i] and
+// s_uu[m][j] = u_e[j]; entry nlog, when asked for, is the current update
+// (s_kcur, already permuted, and s_ucur).  Every thread takes part.
+template <int VAR, int DK, int DV, bool HAS_CUR>
+__device__ __forceinline__ void stage_entries(const PoolArgs& p, int tile, int e0, int cnt, int nlog,
+                                              const float* s_cnow, const float* s_kcur,
+                                              const float* s_ucur, float* s_w, float* s_uu) {
+  using G = SGeo<DK, DV>;
+  const size_t lbase = (size_t)tile * p.L;
+  for (int idx = threadIdx.x; idx < cnt * DK; idx += G::NT) {
+    const int m = idx / DK, i = idx % DK, e = e0 + m;
+    if (!HAS_CUR || e < nlog) {
+      const float kj = bf16_to_f32(p.log_k[(lbase + e) * DK + i]);
+      const float dc = (VAR == DL_GDN) ? (s_cnow[0] - p.log_c[lbase + e])
+                                       : (s_cnow[i] - p.log_c[(lbase + e) * DK + i]);
+      s_w[m * DK + G::perm(i)] = exp2f(dc) * kj;
+    } else {
+      if constexpr (HAS_CUR) s_w[m * DK + i] = s_kcur[i];  // both permuted: a plain copy
+    }
+  }
+  for (int idx = threadIdx.x; idx < cnt * DV; idx += G::NT) {
+    const int m = idx / DV, j = idx % DV, e = e0 + m;
+    float u = 0.f;
+    if (!HAS_CUR || e < nlog) {
+      if constexpr (VAR == DL_RWKV6)
+        u = bf16_to_f32(static_cast<const uint16_t*>(p.log_u)[(lbase + e) * DV + j]);
+      else
+        u = static_cast<const float*>(p.log_u)[(lbase + e) * DV + j];
+    } else {
+      if constexpr (HAS_CUR) u = s_ucur[j];
+    }
+    s_uu[m * DV + j] = u;
+  }
+}
+
+// One streamed fold pass over a tile's base:
+//   B[row][cols] <- g[row] B[row][cols] + sum_{m < nent} s_w[m][perm(row)] s_uu[m][cols]
+// with g = 2^c (s_g, rows permuted; one value for GDN) when `scale`, else 1.
 template <int VAR, int DK, int DV>
-__global__ void __launch_bounds__((Geo<DK, DV>::NT)) decode_kernel(PoolArgs p, StepArgs s) {
-  using G = Geo<DK, DV>;
+__device__ __forceinline__ void fold_pass(float* tile_base, int nent, bool scale, const float* s_g,
+                                          const float* s_w, const float* s_uu) {
+  using G = SGeo<DK, DV>;
+  constexpr int RPC = G::RPC;
+  const int tid = threadIdx.x;
+  const int rg = tid / G::CG, cg = tid % G::CG;
+  float4* bp = reinterpret_cast<float4*>(tile_base) + cg;
+  float4 buf[G::NB][RPC];
+#pragma unroll
+  for (int c = 0; c < G::NB; ++c)
+#pragma unroll
+    for (int rr = 0; rr < RPC; ++rr) buf[c][rr] = bp[(size_t)((c * RPC + rr) * G::RG + rg) * (DV / 4)];
+#pragma unroll
+  for (int c = 0; c < G::NC; ++c) {
+    float g[RPC];
+    if constexpr (VAR == DL_GDN) {
+#pragma unroll
+      for (int rr = 0; rr < RPC; ++rr) g[rr] = scale ? s_g[0] : 1.f;
+    } else {
+      const float4 g4 = scale ? *reinterpret_cast<const float4*>(s_g + rg * G::RPT + c * RPC)
+                              : make_float4(1.f, 1.f, 1.f, 1.f);
+      g[0] = g4.x; g[1] = g4.y; g[2] = g4.z; g[3] = g4.w;
+    }
+    float4 x[RPC];
+#pragma unroll
+    for (int rr = 0; rr < RPC; ++rr) x[rr] = f4_mul(buf[c % G::NB][rr], g[rr]);
+    if (c + G::NB < G::NC) {
+#pragma unroll
+      for (int rr = 0; rr < RPC; ++rr)
+        buf[c % G::NB][rr] = bp[(size_t)(((c + G::NB) * RPC + rr) * G::RG + rg) * (DV / 4)];
+    }
+    for (int m = 0; m < nent; ++m) {
+      const float4 u4 = *reinterpret_cast<const float4*>(s_uu + m * DV + cg * 4);
+      const float4 w4 = *reinterpret_cast<const float4*>(s_w + m * DK + rg * G::RPT + c * RPC);
+      x[0] = f4_fma(w4.x, u4, x[0]);
+      x[1] = f4_fma(w4.y, u4, x[1]);
+      x[2] = f4_fma(w4.z, u4, x[2]);
+      x[3] = f4_fma(w4.w, u4, x[3]);
+    }
+#pragma unroll
+    for (int rr = 0; rr < RPC; ++rr) bp[(size_t)((c * RPC + rr) * G::RG + rg) * (DV / 4)] = x[rr];
+  }
+}
+
+// Fold a tile's nlog logged entries, plus the current update when HAS_CUR,
+// into its base, in stages of MC entries loaded from the log (used when the
+// fold's entries are not already staged).  Each stage streams the base once;
+// a thread re-reads only what it wrote itself in the previous stage.
+template <int VAR, int DK, int DV, bool HAS_CUR>
+__device__ __forceinline__ void fold_staged(const PoolArgs& p, int tile, int nlog,
+                                            const float* s_ct, const float* s_g, const float* s_kcur,
+                                            const float* s_ucur, float* s_w, float* s_uu) {
+  using G = SGeo<DK, DV>;
+  float* tb = p.base + (size_t)tile * DK * DV;
+  const int total = nlog + (HAS_CUR ? 1 : 0);
+  for (int e0 = 0; e0 < total; e0 += G::MC) {
+    const int cnt = min(G::MC, total - e0);
+    __syncthreads();  // the previous stage's LDS reads are done
+    stage_entries<VAR, DK, DV, HAS_CUR>(p, tile, e0, cnt, nlog, s_ct, s_kcur, s_ucur, s_w, s_uu);
+    __syncthreads();
+    fold_pass<VAR, DK, DV>(tb, cnt, e0 == 0, s_g, s_w, s_uu);
+  }
+}
+
+template <int VAR, int DK, int DV>
+__global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, StepArgs s) {
+  using G = SGeo<DK, DV>;
   constexpr bool VEC = VAR != DL_GDN;  // per-key-channel decay
   constexpr int CW = VEC ? DK : 1;     // floats per log_c entry
-  constexpr int RPT = G::RPT;
+  constexpr int RPC = G::RPC;
   using UT = std::conditional_t<VAR == DL_RWKV6, uint16_t, float>;
+  using URaw = std::conditional_t<VAR == DL_RWKV6, uint2, float4>;  // 4 log factors, raw
 
   const int tid = threadIdx.x;
   const int tile = blockIdx.x;
   const int L = p.L;
   const int n = p.fill[tile];  // same for the whole workgroup
   const bool due = (n + 1 == L);
+  const bool reg_stage = due && L <= G::MC;  // the fold's entries come from this pass's registers
   const size_t lbase = (size_t)tile * L;
   const UT* log_u = static_cast<const UT*>(p.log_u);
 
-  __shared__ float s_kt[DK];                   // k_t
-  __shared__ float s_yk[DK];                   // 2^c_t . k_t   (RWKV6: 2^c_{t-1} . r_t)
-  __shared__ float s_yq[DK];                   // 2^c_t . q_t   (GDN/KDA)
-  __shared__ float s_ct[CW];                   // c_t
-  __shared__ float s_sig[2][DL_MAX_LOG_LEN];   // sigma^k_j, sigma^q_j (RWKV6: sigma^r_j)
-  __shared__ float s_dot;                      // k_t . q_t  (RWKV6: sum r bonus k)
-  __shared__ float s_red[G::NW][2][DV];        // per-wave column partial sums
-  __shared__ float s_u[DV];                    // u_t (RWKV6: v_t)
-  __shared__ __attribute__((aligned(16))) float s_w[G::MC * DK];
-  __shared__ __attribute__((aligned(16))) float s_uu[G::MC * DV];
+  __shared__ __attribute__((aligned(16))) float s_yk[DK];  // 2^c_t . k_t (RWKV6: 2^c_{t-1} . r_t), permuted
+  __shared__ __attribute__((aligned(16))) float s_yq[DK];  // 2^c_t . q_t (GDN/KDA), permuted
+  __shared__ __attribute__((aligned(16))) float s_g[CW];   // 2^c_t, permuted (fold scale)
+  __shared__ __attribute__((aligned(16))) float s_ct[CW];  // c_t, natural order
+  __shared__ float s_kcur[DK];                             // k_t, permuted (long-log fold)
+  __shared__ float s_ucur[DV];                             // u_t (long-log fold)
+  __shared__ float s_sig[2][DL_MAX_LOG_LEN];               // sigma^k_j, sigma^q_j (RWKV6: sigma^r_j)
+  __shared__ float s_dot;                                  // k_t . q_t  (RWKV6: sum r bonus k)
+  __shared__ float s_red[G::NW][2][DV];                    // per-wave column partial sums
+  __shared__ __attribute__((aligned(16))) float s_w[G::MC * DK];   // fold weights, permuted rows
+  __shared__ __attribute__((aligned(16))) float s_uu[G::MC * DV];  // fold factors
 
-  // ---- 1. small loads first: they are consumed while the base is in flight.
-  // All of them are unconditional (slot indices are clamped into [0, L), which
-  // init_state zeroed), so no branch forces a wait before the base loads issue;
-  // entries beyond the fill are masked out where they are used.
-  // "Entry lanes": group eg of LPE lanes works on log entry eg (+NG, ...), lane ch on
-  // channels [8ch, 8ch+8).
+  // ---- 1. small loads first: they are consumed while the base streams in.
+  // Log slots at or past the fill are read through buffer resources with an
+  // out-of-range offset: they return zeros without touching memory, and no
+  // branch stands between these loads and the base loads below.
+  // "Entry lanes": group eg of LPE lanes works on log entry eg (+NG, ...), lane ch
+  // on channels [8ch, 8ch+8).
   const int eg = tid / G::LPE, ch = tid % G::LPE;
   const size_t in_off = (size_t)tile * DK + ch * 8;
+  const auto rk = make_rsrc(p.log_k + lbase * DK, (uint32_t)(L * DK * 2));
+  const auto ru = make_rsrc(log_u + lbase * DV, (uint32_t)(L * DV * sizeof(UT)));
+  const auto rc = make_rsrc(p.log_c + lbase * CW, (uint32_t)(L * CW * 4));
   const uint4 kt8 = *reinterpret_cast<const uint4*>(s.k + in_off);
   const uint4 qt8 = *reinterpret_cast<const uint4*>(s.q + in_off);
-  const int prev = n > 0 ? n - 1 : 0;     // slot of the newest entry (read only if n > 0)
-  const int e0 = eg < L ? eg : L - 1;     // first-pass entry slot of this lane group
+  // c of the newest entry (zeros when the log is empty)
+  const uint32_t prev_off = n > 0 ? (uint32_t)(((n - 1) * CW + (VEC ? ch * 8 : 0)) * 4) : kOutOfRange;
+  // the first-pass entry of this lane group (zeros past the fill)
+  const bool has_e = eg < n;
+  const uint32_t ek_off = has_e ? (uint32_t)((eg * DK + ch * 8) * 2) : kOutOfRange;
+  const uint32_t ec_off = has_e ? (uint32_t)((eg * CW + (VEC ? ch * 8 : 0)) * 4) : kOutOfRange;
   float dec[VEC ? 8 : 1], cprev[VEC ? 8 : 1], cj[VEC ? 8 : 1];
   float bonus[VAR == DL_RWKV6 ? 8 : 1];
   if constexpr (VEC) {
     load8(s.decay + in_off, dec);
-    load8(p.log_c + (lbase + prev) * DK + ch * 8, cprev);
-    load8(p.log_c + (lbase + e0) * DK + ch * 8, cj);
+    bload8f(rc, prev_off, cprev);
+    bload8f(rc, ec_off, cj);
   } else {
     dec[0] = s.decay[tile];
-    cprev[0] = p.log_c[lbase + prev];
-    cj[0] = p.log_c[lbase + e0];
+    cprev[0] = bload4f(rc, prev_off);
+    cj[0] = bload4f(rc, ec_off);
   }
   if constexpr (VAR == DL_RWKV6) load8(s.bonus + (size_t)(tile % p.heads) * DK + ch * 8, bonus);
-  const uint4 kj8 = *reinterpret_cast<const uint4*>(p.log_k + (lbase + e0) * DK + ch * 8);
-  // "Tile lanes": thread (rg, cg) owns rows [rg*RPT, +RPT) x columns [4cg, 4cg+4).
+  const uint4 kj8 = bload16(rk, ek_off);
+  // "Tile lanes": thread (rg, cg) owns columns [4cg, 4cg+4) of rows (c*RPC + rr)*RG + rg.
   const int rg = tid / G::CG, cg = tid % G::CG;
-  using URaw = std::conditional_t<VAR == DL_RWKV6, uint2, float4>;  // 4 factors, raw
-  URaw up[G::UPF];
+  float4 up[G::UPF];  // factors u_j[4cg..4cg+4) of entries j = rg + RG*e (zeros past the fill)
 #pragma unroll
   for (int e = 0; e < G::UPF; ++e) {
-    const int j = min(rg + G::RG * e, L - 1);
-    up[e] = *reinterpret_cast<const URaw*>(log_u + (lbase + j) * DV + cg * 4);
+    const int j = rg + G::RG * e;
+    up[e] = bload_factor4(ru, j < n ? (uint32_t)((j * DV + cg * 4) * sizeof(UT)) : kOutOfRange, UT{});
   }
-  // column lanes: v_t and beta
-  const uint16_t vbits = s.v[(size_t)tile * DV + (tid % DV)];
+  const uint16_t vbits = s.v[(size_t)tile * DV + (tid % DV)];  // column lanes: v_t
   float beta = 0.f;
   if constexpr (VAR != DL_RWKV6) beta = s.beta[tile];
   uint4 v8 = make_uint4(0, 0, 0, 0);  // RWKV6 appends v_t's bf16 bits
   if constexpr (VAR == DL_RWKV6)
     v8 = *reinterpret_cast<const uint4*>(s.v + (size_t)tile * DV + (tid % (DV / 8)) * 8);
 
-  // ---- 2. the base tile: RPT float4 loads per thread, all in flight at once.
-  float4 B[RPT];
-  {
-    const float4* bp = reinterpret_cast<const float4*>(p.base + ((size_t)tile * DK + rg * RPT) * DV) + cg;
+  // Keep the small loads ahead of the base loads in the issue order: a load that
+  // is waited for first must not sit behind the base chunks in the queue.
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 2. the first NB chunks of the base.
+  const float4* bp = reinterpret_cast<const float4*>(p.base + (size_t)tile * DK * DV) + cg;
+  float4 buf[G::NB][RPC];
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) B[r] = bp[(size_t)r * (DV / 4)];
-  }
+  for (int c = 0; c < G::NB; ++c)
+#pragma unroll
+    for (int rr = 0; rr < RPC; ++rr) buf[c][rr] = bp[(size_t)((c * RPC + rr) * G::RG + rg) * (DV / 4)];
 
   // ---- 3. decay bookkeeping, scaled read vectors and log coefficients (entry lanes).
-  float kt[8], qt[8];
-  unpack8(kt8, kt);
-  unpack8(qt8, qt);
-  float ct[VEC ? 8 : 1];
-  float gsc[8];  // 2^c_t per channel (RWKV6: 2^c_{t-1})
-#pragma unroll
-  for (int i = 0; i < (VEC ? 8 : 1); ++i) cprev[i] = n > 0 ? cprev[i] : 0.f;
-  if constexpr (VEC) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ct[i] = cprev[i] + step_log2_decay(dec[i]);
-      gsc[i] = exp2f(VAR == DL_RWKV6 ? cprev[i] : ct[i]);
-    }
-  } else {
-    ct[0] = cprev[0] + step_log2_decay(dec[0]);
-    const float g = exp2f(ct[0]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) gsc[i] = g;
-  }
-  if (eg == 0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      s_kt[ch * 8 + i] = kt[i];
-      s_yk[ch * 8 + i] = gsc[i] * (VAR == DL_RWKV6 ? qt[i] : kt[i]);
-      if constexpr (VAR != DL_RWKV6) s_yq[ch * 8 + i] = gsc[i] * qt[i];
-      if constexpr (VEC) s_ct[ch * 8 + i] = ct[i];
-    }
-    if constexpr (!VEC) {
-      if (ch == 0) s_ct[0] = ct[0];
-    }
-  }
   {
+    float kt[8], qt[8];
+    unpack8(kt8, kt);
+    unpack8(qt8, qt);
+    float ct[VEC ? 8 : 1];
+#pragma unroll
+    for (int i = 0; i < (VEC ? 8 : 1); ++i) ct[i] = cprev[i] + step_log2_decay(dec[i]);
+    if (eg == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int pi = G::perm(ch * 8 + i);
+        const float g = exp2f(ct[VEC ? i : 0]);  // 2^c_t
+        if constexpr (VAR == DL_RWKV6) {
+          s_yk[pi] = exp2f(cprev[i]) * qt[i];
+        } else {
+          s_yk[pi] = g * kt[i];
+          s_yq[pi] = g * qt[i];
+        }
+        s_kcur[pi] = kt[i];
+        if constexpr (VEC) {
+          s_g[pi] = g;
+          s_ct[ch * 8 + i] = ct[i];
+        } else if (ch == 0 && i == 0) {
+          s_g[0] = g;
+          s_ct[0] = ct[0];
+        }
+        // the current update's fold weight is k_t itself (no decay after it)
+        if (reg_stage) s_w[n * DK + pi] = kt[i];
+      }
+    }
     float d = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -257,53 +316,58 @@ __global__ void __launch_bounds__((Geo<DK, DV>::NT)) decode_kernel(PoolArgs p, S
     }
     d = group_sum<G::LPE>(d);
     if (tid == 0) s_dot = d;
-  }
-  // first pass: entry eg, from the registers loaded above
-  if (eg < n) log_coefs<VAR, G::LPE>(kj8, cj, kt, qt, ct, cprev, s_sig, eg, ch);
-  // later passes, only when L > NG + 1
-  for (int j = eg + G::NG; j < n; j += G::NG) {
-    float cjj[VEC ? 8 : 1];
-    if constexpr (VEC) load8(p.log_c + (lbase + j) * DK + ch * 8, cjj);
-    else cjj[0] = p.log_c[lbase + j];
-    const uint4 kjj = *reinterpret_cast<const uint4*>(p.log_k + (lbase + j) * DK + ch * 8);
-    log_coefs<VAR, G::LPE>(kjj, cjj, kt, qt, ct, cprev, s_sig, j, ch);
+    // first pass: entry eg, from the registers loaded above
+    if (eg < n) log_coefs<VAR, DK, DV>(kj8, cj, kt, qt, ct, cprev, s_sig, eg, ch, reg_stage, s_w);
+    // later passes, only when L > NG + 1
+    for (int j = eg + G::NG; j < n; j += G::NG) {
+      float cjj[VEC ? 8 : 1];
+      if constexpr (VEC) load8(p.log_c + (lbase + j) * DK + ch * 8, cjj);
+      else cjj[0] = p.log_c[lbase + j];
+      const uint4 kjj = *reinterpret_cast<const uint4*>(p.log_k + (lbase + j) * DK + ch * 8);
+      log_coefs<VAR, DK, DV>(kjj, cjj, kt, qt, ct, cprev, s_sig, j, ch, false, s_w);
+    }
   }
   __syncthreads();
 
-  // ---- 4. column sums: log part, then the base matvec (tile lanes).
+  // ---- 4. column sums: the streamed base matvec, then the log part (tile lanes).
   float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), aq = ak;
+#pragma unroll
+  for (int c = 0; c < G::NC; ++c) {
+    float4 x[RPC];
+#pragma unroll
+    for (int rr = 0; rr < RPC; ++rr) x[rr] = buf[c % G::NB][rr];
+    if (c + G::NB < G::NC) {
+#pragma unroll
+      for (int rr = 0; rr < RPC; ++rr)
+        buf[c % G::NB][rr] = bp[(size_t)(((c + G::NB) * RPC + rr) * G::RG + rg) * (DV / 4)];
+    }
+    const float4 k4 = *reinterpret_cast<const float4*>(s_yk + rg * G::RPT + c * RPC);
+    ak = f4_fma(k4.x, x[0], ak);
+    ak = f4_fma(k4.y, x[1], ak);
+    ak = f4_fma(k4.z, x[2], ak);
+    ak = f4_fma(k4.w, x[3], ak);
+    if constexpr (VAR != DL_RWKV6) {
+      const float4 q4 = *reinterpret_cast<const float4*>(s_yq + rg * G::RPT + c * RPC);
+      aq = f4_fma(q4.x, x[0], aq);
+      aq = f4_fma(q4.y, x[1], aq);
+      aq = f4_fma(q4.z, x[2], aq);
+      aq = f4_fma(q4.w, x[3], aq);
+    }
+  }
 #pragma unroll
   for (int e = 0; e < G::UPF; ++e) {
     const int j = rg + G::RG * e;
     if (j < n) {
-      const float4 uj = widen4(up[e]);
+      const float4 uj = up[e];
       ak = f4_fma(s_sig[0][j], uj, ak);
       if constexpr (VAR != DL_RWKV6) aq = f4_fma(s_sig[1][j], uj, aq);
+      if (reg_stage) *reinterpret_cast<float4*>(s_uu + j * DV + cg * 4) = uj;  // the fold's factors
     }
   }
   for (int j = rg + G::RG * G::UPF; j < n; j += G::RG) {  // only when L > RG*UPF + 1
     const float4 uj = widen4(*reinterpret_cast<const URaw*>(log_u + (lbase + j) * DV + cg * 4));
     ak = f4_fma(s_sig[0][j], uj, ak);
     if constexpr (VAR != DL_RWKV6) aq = f4_fma(s_sig[1][j], uj, aq);
-  }
-  {
-    const float* yk = s_yk + rg * RPT;
-    const float* yq = s_yq + rg * RPT;
-#pragma unroll
-    for (int r = 0; r < RPT; r += 4) {
-      const float4 k4 = *reinterpret_cast<const float4*>(yk + r);
-      ak = f4_fma(k4.x, B[r + 0], ak);
-      ak = f4_fma(k4.y, B[r + 1], ak);
-      ak = f4_fma(k4.z, B[r + 2], ak);
-      ak = f4_fma(k4.w, B[r + 3], ak);
-      if constexpr (VAR != DL_RWKV6) {
-        const float4 q4 = *reinterpret_cast<const float4*>(yq + r);
-        aq = f4_fma(q4.x, B[r + 0], aq);
-        aq = f4_fma(q4.y, B[r + 1], aq);
-        aq = f4_fma(q4.z, B[r + 2], aq);
-        aq = f4_fma(q4.w, B[r + 3], aq);
-      }
-    }
   }
   // reduce over the row groups of this wave, then across waves through LDS
   ak.x = colgroup_sum<G::CG>(ak.x);
@@ -342,17 +406,18 @@ __global__ void __launch_bounds__((Geo<DK, DV>::NT)) decode_kernel(PoolArgs p, S
       if (!due) static_cast<float*>(p.log_u)[(lbase + n) * DV + tid] = u;
     }
     s.out[(size_t)tile * DV + tid] = o;
-    s_u[tid] = u;
+    if (reg_stage) s_uu[n * DV + tid] = u;  // the current update's fold factor
+    s_ucur[tid] = u;
   }
   if (!due) {
     if (eg == 0) {
       *reinterpret_cast<uint4*>(p.log_k + (lbase + n) * DK + ch * 8) = kt8;
       if constexpr (VEC) {
         float4* cp = reinterpret_cast<float4*>(p.log_c + (lbase + n) * DK + ch * 8);
-        cp[0] = make_float4(ct[0], ct[1], ct[2], ct[3]);
-        cp[1] = make_float4(ct[4], ct[5], ct[6], ct[7]);
+        cp[0] = *reinterpret_cast<const float4*>(s_ct + ch * 8);
+        cp[1] = *reinterpret_cast<const float4*>(s_ct + ch * 8 + 4);
       } else {
-        if (ch == 0) p.log_c[lbase + n] = ct[0];
+        if (ch == 0) p.log_c[lbase + n] = s_ct[0];
       }
     }
     if constexpr (VAR == DL_RWKV6) {
@@ -363,45 +428,39 @@ __global__ void __launch_bounds__((Geo<DK, DV>::NT)) decode_kernel(PoolArgs p, S
     return;
   }
 
-  // ---- 6. folding step: B <- diag(2^c_t) B + sum_j diag(2^(c_t-c_j)) k_j u_j^T + k_t u_t^T.
+  // ---- 6. folding step: B <- diag(2^c_t) B + sum_j diag(2^(c_t-c_j)) k_j u_j^T + k_t u_t^T,
+  // streamed over the base once more.
   __syncthreads();
-  fold_into<VAR, DK, DV, RPT>(B, p, tile, n, s_ct, true, s_kt, s_u, s_w, s_uu);
-  {
-    float4* bp = reinterpret_cast<float4*>(p.base + ((size_t)tile * DK + rg * RPT) * DV) + cg;
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) bp[(size_t)r * (DV / 4)] = B[r];
-  }
+  if (reg_stage)
+    fold_pass<VAR, DK, DV>(p.base + (size_t)tile * DK * DV, n + 1, true, s_g, s_w, s_uu);
+  else
+    fold_staged<VAR, DK, DV, true>(p, tile, n, s_ct, s_g, s_kcur, s_ucur, s_w, s_uu);
   if (tid == 0) p.fill[tile] = 0;
 }
 
 // dl_merge: fold the logs of tiles holding at least min_fill entries.
 template <int VAR, int DK, int DV>
-__global__ void __launch_bounds__((Geo<DK, DV>::NT)) merge_kernel(PoolArgs p, int min_fill) {
-  using G = Geo<DK, DV>;
+__global__ void __launch_bounds__((SGeo<DK, DV>::NT)) merge_kernel(PoolArgs p, int min_fill) {
+  using G = SGeo<DK, DV>;
   constexpr bool VEC = VAR != DL_GDN;
   constexpr int CW = VEC ? DK : 1;
-  constexpr int RPT = G::RPT;
   const int tid = threadIdx.x;
   const int tile = blockIdx.x;
   const int n = p.fill[tile];
   if (n < min_fill || n == 0) return;  // uniform: the whole workgroup leaves
   const size_t lbase = (size_t)tile * p.L;
 
-  __shared__ float s_c[CW];
+  __shared__ __attribute__((aligned(16))) float s_c[CW];  // c of the newest entry, natural order
+  __shared__ __attribute__((aligned(16))) float s_g[CW];  // 2^c, permuted
   __shared__ __attribute__((aligned(16))) float s_w[G::MC * DK];
   __shared__ __attribute__((aligned(16))) float s_uu[G::MC * DV];
 
-  const int rg = tid / G::CG, cg = tid % G::CG;
-  float4 B[RPT];
-  const float4* bp = reinterpret_cast<const float4*>(p.base + ((size_t)tile * DK + rg * RPT) * DV) + cg;
-#pragma unroll
-  for (int r = 0; r < RPT; ++r) B[r] = bp[(size_t)r * (DV / 4)];
-  for (int i = tid; i < CW; i += G::NT) s_c[i] = p.log_c[(lbase + n - 1) * CW + i];
-  __syncthreads();
-  fold_into<VAR, DK, DV, RPT>(B, p, tile, n, s_c, false, nullptr, nullptr, s_w, s_uu);
-  float4* wp = reinterpret_cast<float4*>(p.base + ((size_t)tile * DK + rg * RPT) * DV) + cg;
-#pragma unroll
-  for (int r = 0; r < RPT; ++r) wp[(size_t)r * (DV / 4)] = B[r];
+  for (int i = tid; i < CW; i += G::NT) {
+    const float c = p.log_c[(lbase + n - 1) * CW + i];
+    s_c[i] = c;
+    s_g[VEC ? G::perm(i) : 0] = exp2f(c);
+  }
+  fold_staged<VAR, DK, DV, false>(p, tile, n, s_c, s_g, s_w, s_uu, s_w, s_uu);
   if (tid == 0) p.fill[tile] = 0;
 }
 
@@ -452,7 +511,7 @@ hipError_t launch_decode(int variant, int dk, int dv, int tiles, const PoolArgs&
   void* args[] = {&pa, &sa};
 #define CALL_DECODE(V, K, D)                                                                    \
   err = hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<V, K, D>), dim3(tiles),    \
-                        dim3(Geo<K, D>::NT), args, 0, stream)
+                        dim3(SGeo<K, D>::NT), args, 0, stream)
   DL_VARIANTS(variant, dk, dv, CALL_DECODE);
 #undef CALL_DECODE
   return err;
@@ -466,7 +525,7 @@ hipError_t launch_merge(int variant, int dk, int dv, int tiles, const PoolArgs& 
   void* args[] = {&pa, &mf};
 #define CALL_MERGE(V, K, D)                                                                    \
   err = hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<V, K, D>), dim3(tiles),    \
-                        dim3(Geo<K, D>::NT), args, 0, stream)
+                        dim3(SGeo<K, D>::NT), args, 0, stream)
   DL_VARIANTS(variant, dk, dv, CALL_MERGE);
 #undef CALL_MERGE
   return err;

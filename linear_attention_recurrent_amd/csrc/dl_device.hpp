@@ -1,21 +1,21 @@
 // Device-side building blocks shared by the DeltaLog kernels (gfx950, wave64).
 //
-// Tile geometry.  One workgroup owns one (sequence, head) tile: the dk x dv
-// fp32 state block (64 KiB at 128 x 128), its log entries and its fill
-// counter, so every tile has exactly one reader/writer and no atomics are
-// needed.  Thread (rg, cg) holds rows [rg*RPT, rg*RPT + RPT) of the four
-// columns [4cg, 4cg + 4) in registers as RPT float4 values.  A half wave (32
-// lanes at dv = 128) therefore reads one 512-byte state row per load
-// instruction: four whole 128-byte lines, fully coalesced.
+// One workgroup owns one (sequence, head) tile: the dk x dv fp32 state block
+// (64 KiB at 128 x 128), its log entries and its fill counter, so every tile
+// has exactly one reader/writer and no atomics are needed.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/deltalog.h"
+#include "deltalog.h"
 
 namespace dl {
 
+// Register-resident tile geometry (eager kernel): thread (rg, cg) holds rows
+// [rg*RPT, rg*RPT + RPT) of the four columns [4cg, 4cg + 4) as RPT float4
+// values, read once and written once.  A half wave (32 lanes at dv = 128)
+// reads one 512-byte state row per load instruction: four whole 128-byte lines.
 template <int DK, int DV>
 struct Geo {
   static constexpr int CG = DV / 4;                 // float4 column groups
@@ -23,13 +23,37 @@ struct Geo {
   static constexpr int RG = DK / RPT;               // row groups
   static constexpr int NT = CG * RG;                // threads per workgroup
   static constexpr int NW = NT / 64;                // waves per workgroup
-  static constexpr int RG_PER_WAVE = 64 / CG;       // row groups sharing one wave
-  static constexpr int LPE = DK / 8;                // lanes per log entry (8 channels each)
-  static constexpr int NG = NT / LPE;               // log entries per pass
-  static constexpr int UPF = 2;                     // log factors prefetched per thread
-  static constexpr int MC = 16;                     // log entries staged per merge chunk
+  static constexpr int LPE = DK / 8;                // lanes per 8-channel group
   static_assert(NT % 64 == 0 && NT >= DK && NT >= DV, "tile geometry");
   static_assert(DK % RPT == 0 && RPT % 4 == 0, "tile geometry");
+};
+
+// Streaming tile geometry (decode and fold).  Thread (rg, cg) handles columns
+// [4cg, 4cg + 4) of rows (c*RPC + rr)*RG + rg for chunks c < NC and rr < RPC:
+// each load instruction of a wave covers 64/CG consecutive whole rows.  Only
+// NB chunks (NB*RPC float4 per thread) are in registers at a time, so many
+// more tiles fit on a CU than when the whole tile is register-resident.
+// In LDS, per-row vectors are stored permuted by perm(i) = (i % RG)*RPT + i/RG,
+// which makes the RPC rows of one chunk of one thread four consecutive floats.
+template <int DK, int DV>
+struct SGeo {
+  static constexpr int NT = (DK * DV >= 8192) ? 256 : 128;  // threads per workgroup
+  static constexpr int CG = DV / 4;                          // float4 column groups
+  static constexpr int RG = NT / CG;                         // row groups
+  static constexpr int RPT = DK / RG;                        // rows per thread
+  static constexpr int RPC = 4;                              // rows per chunk
+  static constexpr int NC = RPT / RPC;                       // chunks per thread
+  static constexpr int NB = NC < 2 ? NC : 2;                 // chunks in flight
+  static constexpr int NW = NT / 64;                         // waves per workgroup
+  static constexpr int LPE = DK / 8;                         // lanes per log entry (8 channels each)
+  static constexpr int NG = NT / LPE;                        // log entries per pass
+  static constexpr int UPF = 2;                              // log factors prefetched per thread
+  static constexpr int MC = 16;                              // log entries per fold stage
+  static_assert(NT % 64 == 0 && NT >= DK && NT >= DV && 64 % CG == 0, "tile geometry");
+  static_assert(RPT % RPC == 0 && NC >= 1, "tile geometry");
+  // Logs of up to MC entries are folded from what the read pass already holds.
+  static_assert(NG >= MC - 1 && RG * UPF >= MC - 1, "register staging of a full log");
+  __device__ static constexpr int perm(int i) { return (i % RG) * RPT + i / RG; }
 };
 
 // Lowest per-step log2 decay: 2^-126 is the smallest normal float, so a zero
@@ -62,6 +86,38 @@ __device__ __forceinline__ float4 widen4(const float4 x) { return x; }
 __device__ __forceinline__ float4 widen4(const uint2 w) {
   return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
                      __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw, stride 0).  A load whose
+// offset lies beyond the range returns zeros and makes no memory access, which
+// masks log slots past the fill without branches (a branch around a load
+// makes the compiler wait for it before the base loads can issue).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void bload8f(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&f)[8]) {
+  const uint4 a = bload16(r, off), b = bload16(r, off + 16);
+  f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y); f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
+  f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y); f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
+}
+__device__ __forceinline__ float4 bload_factor4(__amdgpu_buffer_rsrc_t r, uint32_t off, float) {
+  const uint4 v = bload16(r, off);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+__device__ __forceinline__ float4 bload_factor4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint16_t) {
+  return widen4(bload8(r, off));
 }
 
 __device__ __forceinline__ float step_log2_decay(float d) {
