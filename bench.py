@@ -122,7 +122,7 @@ def _cpu_worker(i, barrier, queue):
     queue.put((i, time.perf_counter() - t0, len(job["chunks"][i]) * job["steps"]))
 
 
-def cpu_baseline(workload: int, target_s: float = 12.0) -> dict:
+def cpu_baseline(workload: int, target_s: float = 15.0) -> dict:
     """Time the fp64 eager oracle on the host cores over a bounded sample of the workload.
 
     The inputs are drawn once in this process; forked workers (one per core, at
@@ -141,9 +141,9 @@ def cpu_baseline(workload: int, target_s: float = 12.0) -> dict:
     oracle.run_eager(probe, 2, sel=sel, keep_outputs=False)
     per = (time.perf_counter() - t0) / (2 * len(sel))          # seconds per tile-step, one core
     all_tiles = [(b, h) for b in range(B) for h in range(H)]
-    steps = int(min(64, max(2, target_s * cores / (per * len(all_tiles)))))
+    steps = int(min(4096, max(2, target_s * cores / (per * len(all_tiles)))))
     per_core = (len(all_tiles) + cores - 1) // cores
-    _CPU_JOB.update(inp=make_inputs(workload, steps, pool=steps), steps=steps,
+    _CPU_JOB.update(inp=make_inputs(workload, steps, pool=min(steps, 64)), steps=steps,
                     chunks=[all_tiles[i * per_core:(i + 1) * per_core] for i in range(cores)])
     ctx = mp.get_context("fork")
     barrier, queue = ctx.Barrier(cores), ctx.Queue()
@@ -157,9 +157,9 @@ def cpu_baseline(workload: int, target_s: float = 12.0) -> dict:
     work = sum(r[2] for r in res)
     _CPU_JOB.clear()
     return {"value": work / wall, "unit": "state-steps/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 NumPy eager oracle on the same workload: {steps} steps x all {B}x{H} tiles, "
-                      f"tiles split over {cores} forked single-threaded workers, {wall:.1f} s "
-                      f"(slowest worker; input drawing not timed)"}
+            "sample": f"fp64 NumPy eager oracle on the same workload: {steps} steps (inputs cycling "
+                      f"over 64 drawn steps) x all {B}x{H} tiles, tiles split over {cores} forked "
+                      f"single-threaded workers, {wall:.1f} s (slowest worker; input drawing not timed)"}
 
 
 # -------------------------------------------------------------- GPU legs ----
