@@ -188,35 +188,42 @@ __device__ __forceinline__ void fold_staged(const PoolArgs& p, int tile, int nlo
   }
 }
 
-template <int VAR, int DK, int DV>
-__global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, StepArgs s) {
+// LDS of one decode workgroup.  Per-row vectors are stored with rows permuted
+// (SGeo::perm) so that the RPC rows of one chunk of one thread are adjacent.
+template <int DK, int DV, int CW, int NW, int MC>
+struct DecodeLds {
+  __attribute__((aligned(16))) float yk[DK];    // 2^c_t . k_t (RWKV6: 2^c_{t-1} . r_t), permuted
+  __attribute__((aligned(16))) float yq[DK];    // 2^c_t . q_t (GDN/KDA), permuted
+  __attribute__((aligned(16))) float g[CW];     // 2^c_t, permuted (fold scale)
+  __attribute__((aligned(16))) float ct[CW];    // c_t, natural order
+  __attribute__((aligned(16))) float kcur[DK];  // k_t, permuted (staged folds)
+  __attribute__((aligned(16))) float ucur[DV];  // u_t (staged folds)
+  float sig[2][DL_MAX_LOG_LEN];                 // sigma^k_j, sigma^q_j (RWKV6: sigma^r_j)
+  float dot;                                    // k_t . q_t  (RWKV6: sum r bonus k)
+  __attribute__((aligned(16))) float red[NW][2][DV];  // per-wave column partial sums
+  __attribute__((aligned(16))) float w[MC * DK];      // fold weights, permuted rows
+  __attribute__((aligned(16))) float uu[MC * DV];     // fold factors
+};
+
+// One decode step of one tile.  FOLD is the step whose update fills the log:
+// it keeps the whole base tile in registers (one read), folds every update
+// into it and writes it back once.  Otherwise the base is streamed in chunks
+// and only the output, one log entry and the fill are written.
+template <int VAR, int DK, int DV, bool FOLD, typename Lds>
+__device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s, int tile, int n, Lds& sh) {
   using G = SGeo<DK, DV>;
   constexpr bool VEC = VAR != DL_GDN;  // per-key-channel decay
   constexpr int CW = VEC ? DK : 1;     // floats per log_c entry
   constexpr int RPC = G::RPC;
+  constexpr int NBUF = FOLD ? G::NC : G::NB;  // base chunks held in registers
   using UT = std::conditional_t<VAR == DL_RWKV6, uint16_t, float>;
   using URaw = std::conditional_t<VAR == DL_RWKV6, uint2, float4>;  // 4 log factors, raw
 
   const int tid = threadIdx.x;
-  const int tile = blockIdx.x;
   const int L = p.L;
-  const int n = p.fill[tile];  // same for the whole workgroup
-  const bool due = (n + 1 == L);
-  const bool reg_stage = due && L <= G::MC;  // the fold's entries come from this pass's registers
+  const bool reg_stage = FOLD && L <= G::MC;  // the fold's entries come from this pass's registers
   const size_t lbase = (size_t)tile * L;
   const UT* log_u = static_cast<const UT*>(p.log_u);
-
-  __shared__ __attribute__((aligned(16))) float s_yk[DK];  // 2^c_t . k_t (RWKV6: 2^c_{t-1} . r_t), permuted
-  __shared__ __attribute__((aligned(16))) float s_yq[DK];  // 2^c_t . q_t (GDN/KDA), permuted
-  __shared__ __attribute__((aligned(16))) float s_g[CW];   // 2^c_t, permuted (fold scale)
-  __shared__ __attribute__((aligned(16))) float s_ct[CW];  // c_t, natural order
-  __shared__ float s_kcur[DK];                             // k_t, permuted (long-log fold)
-  __shared__ float s_ucur[DV];                             // u_t (long-log fold)
-  __shared__ float s_sig[2][DL_MAX_LOG_LEN];               // sigma^k_j, sigma^q_j (RWKV6: sigma^r_j)
-  __shared__ float s_dot;                                  // k_t . q_t  (RWKV6: sum r bonus k)
-  __shared__ float s_red[G::NW][2][DV];                    // per-wave column partial sums
-  __shared__ __attribute__((aligned(16))) float s_w[G::MC * DK];   // fold weights, permuted rows
-  __shared__ __attribute__((aligned(16))) float s_uu[G::MC * DV];  // fold factors
 
   // ---- 1. small loads first: they are consumed while the base streams in.
   // Log slots at or past the fill are read through buffer resources with an
@@ -233,23 +240,28 @@ __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, 
   const uint4 qt8 = *reinterpret_cast<const uint4*>(s.q + in_off);
   // c of the newest entry (zeros when the log is empty)
   const uint32_t prev_off = n > 0 ? (uint32_t)(((n - 1) * CW + (VEC ? ch * 8 : 0)) * 4) : kOutOfRange;
-  // the first-pass entry of this lane group (zeros past the fill)
-  const bool has_e = eg < n;
-  const uint32_t ek_off = has_e ? (uint32_t)((eg * DK + ch * 8) * 2) : kOutOfRange;
-  const uint32_t ec_off = has_e ? (uint32_t)((eg * CW + (VEC ? ch * 8 : 0)) * 4) : kOutOfRange;
-  float dec[VEC ? 8 : 1], cprev[VEC ? 8 : 1], cj[VEC ? 8 : 1];
+  float dec[VEC ? 8 : 1], cprev[VEC ? 8 : 1];
   float bonus[VAR == DL_RWKV6 ? 8 : 1];
   if constexpr (VEC) {
     load8(s.decay + in_off, dec);
     bload8f(rc, prev_off, cprev);
-    bload8f(rc, ec_off, cj);
   } else {
     dec[0] = s.decay[tile];
     cprev[0] = bload4f(rc, prev_off);
-    cj[0] = bload4f(rc, ec_off);
   }
   if constexpr (VAR == DL_RWKV6) load8(s.bonus + (size_t)(tile % p.heads) * DK + ch * 8, bonus);
-  const uint4 kj8 = bload16(rk, ek_off);
+  // the first EPF entry passes of this lane group: entries eg + NG*e (zeros past the fill)
+  uint4 kj8[G::EPF];
+  float cj[G::EPF][VEC ? 8 : 1];
+#pragma unroll
+  for (int e = 0; e < G::EPF; ++e) {
+    const int j = eg + G::NG * e;
+    const bool has = j < n;
+    kj8[e] = bload16(rk, has ? (uint32_t)((j * DK + ch * 8) * 2) : kOutOfRange);
+    const uint32_t coff = has ? (uint32_t)((j * CW + (VEC ? ch * 8 : 0)) * 4) : kOutOfRange;
+    if constexpr (VEC) bload8f(rc, coff, cj[e]);
+    else cj[e][0] = bload4f(rc, coff);
+  }
   // "Tile lanes": thread (rg, cg) owns columns [4cg, 4cg+4) of rows (c*RPC + rr)*RG + rg.
   const int rg = tid / G::CG, cg = tid % G::CG;
   float4 up[G::UPF];  // factors u_j[4cg..4cg+4) of entries j = rg + RG*e (zeros past the fill)
@@ -262,20 +274,23 @@ __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, 
   float beta = 0.f;
   if constexpr (VAR != DL_RWKV6) beta = s.beta[tile];
   uint4 v8 = make_uint4(0, 0, 0, 0);  // RWKV6 appends v_t's bf16 bits
-  if constexpr (VAR == DL_RWKV6)
+  if constexpr (VAR == DL_RWKV6 && !FOLD)
     v8 = *reinterpret_cast<const uint4*>(s.v + (size_t)tile * DV + (tid % (DV / 8)) * 8);
-
   // Keep the small loads ahead of the base loads in the issue order: a load that
   // is waited for first must not sit behind the base chunks in the queue.
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- 2. the first NB chunks of the base.
-  const float4* bp = reinterpret_cast<const float4*>(p.base + (size_t)tile * DK * DV) + cg;
-  float4 buf[G::NB][RPC];
+  // ---- 2. the base: the first NB chunks on an appending step.  A folding step
+  // loads the whole tile after step 3, so the tile and step 3's registers are
+  // not live together.
+  float4* bp = reinterpret_cast<float4*>(p.base + (size_t)tile * DK * DV) + cg;
+  float4 buf[NBUF][RPC];
+  if constexpr (!FOLD) {
 #pragma unroll
-  for (int c = 0; c < G::NB; ++c)
+    for (int c = 0; c < NBUF; ++c)
 #pragma unroll
-    for (int rr = 0; rr < RPC; ++rr) buf[c][rr] = bp[(size_t)((c * RPC + rr) * G::RG + rg) * (DV / 4)];
+      for (int rr = 0; rr < RPC; ++rr) buf[c][rr] = bp[(size_t)((c * RPC + rr) * G::RG + rg) * (DV / 4)];
+  }
 
   // ---- 3. decay bookkeeping, scaled read vectors and log coefficients (entry lanes).
   {
@@ -291,21 +306,21 @@ __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, 
         const int pi = G::perm(ch * 8 + i);
         const float g = exp2f(ct[VEC ? i : 0]);  // 2^c_t
         if constexpr (VAR == DL_RWKV6) {
-          s_yk[pi] = exp2f(cprev[i]) * qt[i];
+          sh.yk[pi] = exp2f(cprev[i]) * qt[i];
         } else {
-          s_yk[pi] = g * kt[i];
-          s_yq[pi] = g * qt[i];
+          sh.yk[pi] = g * kt[i];
+          sh.yq[pi] = g * qt[i];
         }
-        s_kcur[pi] = kt[i];
+        if constexpr (FOLD) sh.kcur[pi] = kt[i];
         if constexpr (VEC) {
-          s_g[pi] = g;
-          s_ct[ch * 8 + i] = ct[i];
+          sh.g[pi] = g;
+          sh.ct[ch * 8 + i] = ct[i];
         } else if (ch == 0 && i == 0) {
-          s_g[0] = g;
-          s_ct[0] = ct[0];
+          sh.g[0] = g;
+          sh.ct[0] = ct[0];
         }
         // the current update's fold weight is k_t itself (no decay after it)
-        if (reg_stage) s_w[n * DK + pi] = kt[i];
+        if (reg_stage) sh.w[n * DK + pi] = kt[i];
       }
     }
     float d = 0.f;
@@ -315,39 +330,50 @@ __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, 
       else d = fmaf(kt[i], qt[i], d);
     }
     d = group_sum<G::LPE>(d);
-    if (tid == 0) s_dot = d;
-    // first pass: entry eg, from the registers loaded above
-    if (eg < n) log_coefs<VAR, DK, DV>(kj8, cj, kt, qt, ct, cprev, s_sig, eg, ch, reg_stage, s_w);
-    // later passes, only when L > NG + 1
-    for (int j = eg + G::NG; j < n; j += G::NG) {
+    if (tid == 0) sh.dot = d;
+    // the prefetched passes: entries eg + NG*e, from the registers loaded above
+#pragma unroll
+    for (int e = 0; e < G::EPF; ++e) {
+      const int j = eg + G::NG * e;
+      if (j < n) log_coefs<VAR, DK, DV>(kj8[e], cj[e], kt, qt, ct, cprev, sh.sig, j, ch, reg_stage, sh.w);
+    }
+    // later passes, only when L > NG*EPF + 1
+    for (int j = eg + G::NG * G::EPF; j < n; j += G::NG) {
       float cjj[VEC ? 8 : 1];
       if constexpr (VEC) load8(p.log_c + (lbase + j) * DK + ch * 8, cjj);
       else cjj[0] = p.log_c[lbase + j];
       const uint4 kjj = *reinterpret_cast<const uint4*>(p.log_k + (lbase + j) * DK + ch * 8);
-      log_coefs<VAR, DK, DV>(kjj, cjj, kt, qt, ct, cprev, s_sig, j, ch, false, s_w);
+      log_coefs<VAR, DK, DV>(kjj, cjj, kt, qt, ct, cprev, sh.sig, j, ch, false, sh.w);
     }
+  }
+  if constexpr (FOLD) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < NBUF; ++c)
+#pragma unroll
+      for (int rr = 0; rr < RPC; ++rr) buf[c][rr] = bp[(size_t)((c * RPC + rr) * G::RG + rg) * (DV / 4)];
   }
   __syncthreads();
 
-  // ---- 4. column sums: the streamed base matvec, then the log part (tile lanes).
+  // ---- 4. column sums: the base matvec (streamed, or from the resident tile), then the log part.
   float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), aq = ak;
 #pragma unroll
   for (int c = 0; c < G::NC; ++c) {
     float4 x[RPC];
 #pragma unroll
-    for (int rr = 0; rr < RPC; ++rr) x[rr] = buf[c % G::NB][rr];
-    if (c + G::NB < G::NC) {
+    for (int rr = 0; rr < RPC; ++rr) x[rr] = buf[c % NBUF][rr];
+    if (!FOLD && c + G::NB < G::NC) {
 #pragma unroll
       for (int rr = 0; rr < RPC; ++rr)
-        buf[c % G::NB][rr] = bp[(size_t)(((c + G::NB) * RPC + rr) * G::RG + rg) * (DV / 4)];
+        buf[c % NBUF][rr] = bp[(size_t)(((c + G::NB) * RPC + rr) * G::RG + rg) * (DV / 4)];
     }
-    const float4 k4 = *reinterpret_cast<const float4*>(s_yk + rg * G::RPT + c * RPC);
+    const float4 k4 = *reinterpret_cast<const float4*>(sh.yk + rg * G::RPT + c * RPC);
     ak = f4_fma(k4.x, x[0], ak);
     ak = f4_fma(k4.y, x[1], ak);
     ak = f4_fma(k4.z, x[2], ak);
     ak = f4_fma(k4.w, x[3], ak);
     if constexpr (VAR != DL_RWKV6) {
-      const float4 q4 = *reinterpret_cast<const float4*>(s_yq + rg * G::RPT + c * RPC);
+      const float4 q4 = *reinterpret_cast<const float4*>(sh.yq + rg * G::RPT + c * RPC);
       aq = f4_fma(q4.x, x[0], aq);
       aq = f4_fma(q4.y, x[1], aq);
       aq = f4_fma(q4.z, x[2], aq);
@@ -359,15 +385,15 @@ __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, 
     const int j = rg + G::RG * e;
     if (j < n) {
       const float4 uj = up[e];
-      ak = f4_fma(s_sig[0][j], uj, ak);
-      if constexpr (VAR != DL_RWKV6) aq = f4_fma(s_sig[1][j], uj, aq);
-      if (reg_stage) *reinterpret_cast<float4*>(s_uu + j * DV + cg * 4) = uj;  // the fold's factors
+      ak = f4_fma(sh.sig[0][j], uj, ak);
+      if constexpr (VAR != DL_RWKV6) aq = f4_fma(sh.sig[1][j], uj, aq);
+      if (reg_stage) *reinterpret_cast<float4*>(sh.uu + j * DV + cg * 4) = uj;  // the fold's factors
     }
   }
   for (int j = rg + G::RG * G::UPF; j < n; j += G::RG) {  // only when L > RG*UPF + 1
     const float4 uj = widen4(*reinterpret_cast<const URaw*>(log_u + (lbase + j) * DV + cg * 4));
-    ak = f4_fma(s_sig[0][j], uj, ak);
-    if constexpr (VAR != DL_RWKV6) aq = f4_fma(s_sig[1][j], uj, aq);
+    ak = f4_fma(sh.sig[0][j], uj, ak);
+    if constexpr (VAR != DL_RWKV6) aq = f4_fma(sh.sig[1][j], uj, aq);
   }
   // reduce over the row groups of this wave, then across waves through LDS
   ak.x = colgroup_sum<G::CG>(ak.x);
@@ -382,8 +408,8 @@ __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, 
   }
   const int wave = tid / 64, lane = tid % 64;
   if (lane < G::CG) {
-    *reinterpret_cast<float4*>(&s_red[wave][0][cg * 4]) = ak;
-    if constexpr (VAR != DL_RWKV6) *reinterpret_cast<float4*>(&s_red[wave][1][cg * 4]) = aq;
+    *reinterpret_cast<float4*>(&sh.red[wave][0][cg * 4]) = ak;
+    if constexpr (VAR != DL_RWKV6) *reinterpret_cast<float4*>(&sh.red[wave][1][cg * 4]) = aq;
   }
   __syncthreads();
 
@@ -393,31 +419,33 @@ __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, 
     float pk = 0.f, oq = 0.f;
 #pragma unroll
     for (int w = 0; w < G::NW; ++w) {
-      pk += s_red[w][0][tid];
-      if constexpr (VAR != DL_RWKV6) oq += s_red[w][1][tid];
+      pk += sh.red[w][0][tid];
+      if constexpr (VAR != DL_RWKV6) oq += sh.red[w][1][tid];
     }
     float o, u;
     if constexpr (VAR == DL_RWKV6) {
       u = vcol;
-      o = fmaf(s_dot, vcol, pk);
+      o = fmaf(sh.dot, vcol, pk);
     } else {
       u = beta * (vcol - pk);
-      o = fmaf(s_dot, u, oq);
-      if (!due) static_cast<float*>(p.log_u)[(lbase + n) * DV + tid] = u;
+      o = fmaf(sh.dot, u, oq);
+      if constexpr (!FOLD) static_cast<float*>(p.log_u)[(lbase + n) * DV + tid] = u;
     }
     s.out[(size_t)tile * DV + tid] = o;
-    if (reg_stage) s_uu[n * DV + tid] = u;  // the current update's fold factor
-    s_ucur[tid] = u;
+    if constexpr (FOLD) {
+      if (reg_stage) sh.uu[n * DV + tid] = u;  // the current update's fold factor
+      else sh.ucur[tid] = u;
+    }
   }
-  if (!due) {
+  if constexpr (!FOLD) {
     if (eg == 0) {
       *reinterpret_cast<uint4*>(p.log_k + (lbase + n) * DK + ch * 8) = kt8;
       if constexpr (VEC) {
         float4* cp = reinterpret_cast<float4*>(p.log_c + (lbase + n) * DK + ch * 8);
-        cp[0] = *reinterpret_cast<const float4*>(s_ct + ch * 8);
-        cp[1] = *reinterpret_cast<const float4*>(s_ct + ch * 8 + 4);
+        cp[0] = *reinterpret_cast<const float4*>(sh.ct + ch * 8);
+        cp[1] = *reinterpret_cast<const float4*>(sh.ct + ch * 8 + 4);
       } else {
-        if (ch == 0) p.log_c[lbase + n] = s_ct[0];
+        if (ch == 0) p.log_c[lbase + n] = sh.ct[0];
       }
     }
     if constexpr (VAR == DL_RWKV6) {
@@ -425,17 +453,60 @@ __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, 
         *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.log_u) + (lbase + n) * DV + tid * 8) = v8;
     }
     if (tid == 0) p.fill[tile] = n + 1;
-    return;
+  } else {
+    // ---- 6. folding step, on the resident tile:
+    //   B <- diag(2^c_t) B + sum_{j<n} diag(2^(c_t-c_j)) k_j u_j^T + k_t u_t^T
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c) {
+      float g[RPC];
+      if constexpr (VEC) {
+        const float4 g4 = *reinterpret_cast<const float4*>(sh.g + rg * G::RPT + c * RPC);
+        g[0] = g4.x; g[1] = g4.y; g[2] = g4.z; g[3] = g4.w;
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < RPC; ++rr) g[rr] = sh.g[0];
+      }
+#pragma unroll
+      for (int rr = 0; rr < RPC; ++rr) buf[c][rr] = f4_mul(buf[c][rr], g[rr]);
+    }
+    const int total = n + 1;
+    for (int e0 = 0; e0 < total; e0 += G::MC) {
+      const int cnt = min(G::MC, total - e0);
+      if (!reg_stage) {
+        __syncthreads();  // the previous stage's LDS reads are done
+        stage_entries<VAR, DK, DV, true>(p, tile, e0, cnt, n, sh.ct, sh.kcur, sh.ucur, sh.w, sh.uu);
+      }
+      __syncthreads();
+      for (int m = 0; m < cnt; ++m) {
+        const float4 u4 = *reinterpret_cast<const float4*>(sh.uu + m * DV + cg * 4);
+#pragma unroll
+        for (int c = 0; c < G::NC; ++c) {
+          const float4 w4 = *reinterpret_cast<const float4*>(sh.w + m * DK + rg * G::RPT + c * RPC);
+          buf[c][0] = f4_fma(w4.x, u4, buf[c][0]);
+          buf[c][1] = f4_fma(w4.y, u4, buf[c][1]);
+          buf[c][2] = f4_fma(w4.z, u4, buf[c][2]);
+          buf[c][3] = f4_fma(w4.w, u4, buf[c][3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < G::NC; ++c)
+#pragma unroll
+      for (int rr = 0; rr < RPC; ++rr) bp[(size_t)((c * RPC + rr) * G::RG + rg) * (DV / 4)] = buf[c][rr];
+    if (tid == 0) p.fill[tile] = 0;
   }
+}
 
-  // ---- 6. folding step: B <- diag(2^c_t) B + sum_j diag(2^(c_t-c_j)) k_j u_j^T + k_t u_t^T,
-  // streamed over the base once more.
-  __syncthreads();
-  if (reg_stage)
-    fold_pass<VAR, DK, DV>(p.base + (size_t)tile * DK * DV, n + 1, true, s_g, s_w, s_uu);
+template <int VAR, int DK, int DV>
+__global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, StepArgs s) {
+  using G = SGeo<DK, DV>;
+  __shared__ DecodeLds<DK, DV, (VAR == DL_GDN ? 1 : DK), G::NW, G::MC> sh;
+  const int tile = blockIdx.x;
+  const int n = p.fill[tile];  // same for the whole workgroup
+  if (n + 1 == p.L)
+    decode_tile<VAR, DK, DV, true>(p, s, tile, n, sh);
   else
-    fold_staged<VAR, DK, DV, true>(p, tile, n, s_ct, s_g, s_kcur, s_ucur, s_w, s_uu);
-  if (tid == 0) p.fill[tile] = 0;
+    decode_tile<VAR, DK, DV, false>(p, s, tile, n, sh);
 }
 
 // dl_merge: fold the logs of tiles holding at least min_fill entries.

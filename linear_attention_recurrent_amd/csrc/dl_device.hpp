@@ -47,12 +47,16 @@ struct SGeo {
   static constexpr int NW = NT / 64;                         // waves per workgroup
   static constexpr int LPE = DK / 8;                         // lanes per log entry (8 channels each)
   static constexpr int NG = NT / LPE;                        // log entries per pass
-  static constexpr int UPF = 2;                              // log factors prefetched per thread
-  static constexpr int MC = 16;                              // log entries per fold stage
+  static constexpr int MCT = (DK * DV >= 16384) ? 16 : 32;  // fold stage size aimed at
+  static constexpr int EPF = (MCT + NG - 1) / NG;            // entry passes prefetched
+  static constexpr int UPF = (MCT + RG - 1) / RG;            // log factors prefetched per thread
+  // Log entries per fold stage.  A log of up to MC entries is folded from what
+  // the read pass already holds: the prefetched entry passes cover NG*EPF
+  // entries and the factor prefetch RG*UPF entries.
+  static constexpr int MC = NG * EPF < RG * UPF ? NG * EPF : RG * UPF;
   static_assert(NT % 64 == 0 && NT >= DK && NT >= DV && 64 % CG == 0, "tile geometry");
   static_assert(RPT % RPC == 0 && NC >= 1, "tile geometry");
-  // Logs of up to MC entries are folded from what the read pass already holds.
-  static_assert(NG >= MC - 1 && RG * UPF >= MC - 1, "register staging of a full log");
+  static_assert(MC >= 16 && MC <= 32, "fold stage size");
   __device__ static constexpr int perm(int i) { return (i % RG) * RPT + i / RG; }
 };
 
