@@ -176,9 +176,11 @@ def gpu_setup(workload, pool_slots, log_len=None):
              bonus=None if inp.bonus is None else torch.from_numpy(inp.bonus).to(dev),
              s0=torch.from_numpy(inp.s0).to(dev),
              out=torch.empty((inp.batch, inp.heads, inp.dv), dtype=torch.float32, device=dev))
+    T["eta"] = None if inp.eta is None else torch.from_numpy(inp.eta).to(dev)
     ios = [dl.make_step_io(inp.variant, inp.batch, inp.heads, inp.dk, inp.dv, dev, T["q"][p], T["k"][p],
                            T["v"][p], T["decay"][p], None if T["beta"] is None else T["beta"][p],
-                           T["bonus"], T["out"]) for p in range(pool_slots)]
+                           T["bonus"], T["out"], None if T["eta"] is None else T["eta"][p], inp.eps)
+           for p in range(pool_slots)]
     return inp, T, ios, w
 
 
@@ -216,7 +218,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 6])
     ap.add_argument("--log-len", type=int, default=None)
     ap.add_argument("--pool-slots", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -318,7 +320,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{VARIANT_NAMES[var]} decode B={B} H={H} dk={dk} dv={dv} L={L}",
+        "config": {"workload": f"{w['name']}: {VARIANT_NAMES[var]} decode B={B} H={H} dk={dk} dv={dv} L={L}"
+                               + (" (Kaczmarz step size)" if inp.eta is not None else ""),
                    "variant": VARIANT_NAMES[var], "batch": B, "heads": H, "dk": dk, "dv": dv,
                    "log_len": L, "initial_fill": "0 for every sequence" if not np.any(inp.fill0) else "ragged",
                    "input_pool_steps": P, "hip_graph": bool(chunk)},

@@ -99,9 +99,13 @@ typedef struct {
   const uint16_t *v;   /* bf16 [batch][heads][dv]  value                                        */
   const float *decay;  /* GDN: fp32 [batch][heads] alpha; KDA/RWKV6: fp32 [batch][heads][dk];
                           values in (0, 1]                                                      */
-  const float *beta;   /* GDN/KDA: fp32 [batch][heads]; RWKV6: must be NULL                     */
+  const float *beta;   /* GDN/KDA: fp32 [batch][heads] step size; RWKV6: must be NULL           */
   const float *bonus;  /* RWKV6: fp32 [heads][dk]; GDN/KDA: must be NULL                        */
   float *out;          /* fp32 [batch][heads][dv]  this step's output (written)                 */
+  const float *eta;    /* GDN/KDA, instead of beta: fp32 [batch][heads]; the step size is then
+                          the Kaczmarz one, beta = eta / (||k||^2 + eps) with k as passed
+                          (Kaczmarz Linear Attention abstract).  RWKV6: must be NULL.           */
+  float eps;           /* the eps above, >= 0 (ignored when eta is NULL)                        */
 } dl_step_io;
 
 /* Start a pool (DeltaLog Abstract: the dense base plus an initially empty or
@@ -121,7 +125,8 @@ int dl_init_state(const dl_dims *dims, const dl_pool *pool, const float *init_ba
  * update; a step that fills the log merges it into the base).  Reads the base
  * but never writes it except on merging steps; writes io->out, one log entry
  * per tile, and the fills.  Errors: DL_EINVAL for null q/k/v/decay/out or pool
- * arrays; DL_EUNSUPPORTED if beta/bonus presence does not match the variant. */
+ * arrays, or eps < 0 with eta set; DL_EUNSUPPORTED if beta/eta/bonus presence does
+ * not match the variant (GDN/KDA: exactly one of beta and eta; RWKV6: bonus only). */
 int dl_decode_step(const dl_dims *dims, const dl_pool *pool, const dl_step_io *io, void *stream);
 
 /* Fold the log of every tile whose fill is >= min_fill (1 <= min_fill <= L)

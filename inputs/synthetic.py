@@ -46,6 +46,11 @@ WORKLOADS = {
     5: dict(name="gdn-serve-48l-b512-h32-d128", variant=GDN, batch=512, heads=32, dk=128,
             dv=128, log_len=16, steps=4096, decay="uniform09", q_norm=False, ragged=True,
             layers=48),
+    # Kaczmarz step size (beta = eta / (||k||^2 + eps)) on the GDN B=64 shape; keys are not
+    # normalised here, so the key norm actually sets the step.
+    6: dict(name="gdn-kla-b64-h32-d128", variant=GDN, batch=64, heads=32, dk=128, dv=128,
+            log_len=16, steps=1024, decay="uniform09", q_norm=False, k_norm=False, ragged=False,
+            kla=True, eps=1e-6),
 }
 
 
@@ -74,6 +79,8 @@ class DecodeInputs:
     beta:  fp32 [P][B][H] (GDN, KDA) or None (RWKV6)
     bonus: fp32 [H][dk] (RWKV6) or None
     fill0: int32 [B] initial log fills, each in [0, log_len)
+    eta:   fp32 [P][B][H] or None: when set (GDN/KDA), beta is None and the step
+           size is the Kaczmarz one, eta / (||k||^2 + eps)
     """
     variant: int
     batch: int
@@ -90,6 +97,8 @@ class DecodeInputs:
     beta: Optional[np.ndarray]
     bonus: Optional[np.ndarray]
     fill0: np.ndarray
+    eta: Optional[np.ndarray] = None
+    eps: float = 0.0
 
     @property
     def pool(self) -> int:
@@ -103,7 +112,8 @@ class DecodeInputs:
         """The inputs of step t as a dict of arrays [B][H][...]."""
         p = self.slot(t)
         return dict(q=self.q[p], k=self.k[p], v=self.v[p], decay=self.decay[p],
-                    beta=None if self.beta is None else self.beta[p])
+                    beta=None if self.beta is None else self.beta[p],
+                    eta=None if self.eta is None else self.eta[p])
 
 
 def _rng(*key: int) -> np.random.Generator:
@@ -142,7 +152,7 @@ def make_inputs(workload: int, steps: Optional[int] = None, *, batch: Optional[i
                 heads: Optional[int] = None, log_len: Optional[int] = None,
                 pool: Optional[int] = None, seed: Optional[int] = None,
                 fill0: Optional[np.ndarray] = None, layer: int = 0, dk: Optional[int] = None,
-                dv: Optional[int] = None) -> DecodeInputs:
+                dv: Optional[int] = None, kla: Optional[bool] = None) -> DecodeInputs:
     """Draw the inputs of a decode workload (see WORKLOADS).
 
     steps:   number of decode steps the run will take (default: the workload's).
@@ -154,6 +164,7 @@ def make_inputs(workload: int, steps: Optional[int] = None, *, batch: Optional[i
              sequence for ragged workloads.
     layer:   layer index for multi-layer workloads (separate streams per layer).
     dk, dv:  override the head sizes (edge-case shapes; distributions unchanged).
+    kla:     GDN/KDA only: draw eta ~ sigmoid(N(0,1)) in place of beta (Kaczmarz step size).
     """
     w = WORKLOADS[workload]
     variant = w["variant"]
@@ -166,6 +177,10 @@ def make_inputs(workload: int, steps: Optional[int] = None, *, batch: Optional[i
     P = min(T, 256) if pool is None else int(pool)
     P = max(P, 1)
     seed = workload if seed is None else int(seed)
+    kla = bool(w.get("kla", False)) if kla is None else bool(kla)
+    if kla and variant == RWKV6:
+        raise ValueError("the Kaczmarz step size applies to GDN and KDA")
+    k_norm = w.get("k_norm", variant != RWKV6)
 
     s0 = np.empty((B, H, dk, dv), np.float32)
     for b in range(B):
@@ -184,10 +199,10 @@ def make_inputs(workload: int, steps: Optional[int] = None, *, batch: Optional[i
             qq = g.standard_normal((H, dk))
             kk = g.standard_normal((H, dk))
             vv = g.standard_normal((H, dv))
-            if variant != RWKV6:
+            if k_norm:
                 kk = _l2n(kk)
-                if w["q_norm"]:
-                    qq = _l2n(qq)
+            if w["q_norm"]:
+                qq = _l2n(qq)
             q[p, b] = f32_to_bf16_bits(qq.astype(np.float32))
             k[p, b] = f32_to_bf16_bits(kk.astype(np.float32))
             v[p, b] = f32_to_bf16_bits(vv.astype(np.float32))
@@ -207,7 +222,12 @@ def make_inputs(workload: int, steps: Optional[int] = None, *, batch: Optional[i
     fill0 = np.ascontiguousarray(fill0, dtype=np.int32)
     assert fill0.shape == (B,)
 
-    return DecodeInputs(variant, B, H, dk, dv, L, T, s0, q, k, v, decay, beta, bonus, fill0)
+    eta = None
+    if kla:
+        # eta takes beta's draw (sigmoid of a standard normal) and beta goes away
+        eta, beta = beta, None
+    return DecodeInputs(variant, B, H, dk, dv, L, T, s0, q, k, v, decay, beta, bonus, fill0, eta,
+                        float(w.get("eps", 1e-6)) if kla else 0.0)
 
 
 def tile_inputs(inp: DecodeInputs, b: int, h: int) -> DecodeInputs:
@@ -217,4 +237,4 @@ def tile_inputs(inp: DecodeInputs, b: int, h: int) -> DecodeInputs:
                         np.ascontiguousarray(inp.s0[b:b + 1, h:h + 1]),
                         sl(inp.q), sl(inp.k), sl(inp.v), sl(inp.decay), sl(inp.beta),
                         None if inp.bonus is None else np.ascontiguousarray(inp.bonus[h:h + 1]),
-                        np.ascontiguousarray(inp.fill0[b:b + 1]))
+                        np.ascontiguousarray(inp.fill0[b:b + 1]), sl(inp.eta), inp.eps)

@@ -40,11 +40,14 @@ int check_io(const dl_dims* d, const dl_step_io* io) {
   if (io == nullptr) return DL_EINVAL;
   if (!io->q || !io->k || !io->v || !io->decay || !io->out) return DL_EINVAL;
   const bool rwkv = d->variant == DL_RWKV6;
-  if (rwkv && (io->beta != nullptr || io->bonus == nullptr)) return DL_EUNSUPPORTED;
-  if (!rwkv && (io->beta == nullptr || io->bonus != nullptr)) return DL_EUNSUPPORTED;
+  if (rwkv && (io->beta != nullptr || io->eta != nullptr || io->bonus == nullptr)) return DL_EUNSUPPORTED;
+  // GDN/KDA: exactly one of beta (given step size) and eta (Kaczmarz step size)
+  if (!rwkv && ((io->beta == nullptr) == (io->eta == nullptr) || io->bonus != nullptr)) return DL_EUNSUPPORTED;
+  if (io->eta != nullptr && !(io->eps >= 0.f)) return DL_EINVAL;
   if (misaligned(io->q) || misaligned(io->k) || misaligned(io->v) ||
       misaligned(io->decay, rwkv || d->variant == DL_KDA ? 16 : 4) || misaligned(io->out, 4) ||
-      (io->beta && misaligned(io->beta, 4)) || (io->bonus && misaligned(io->bonus)))
+      (io->beta && misaligned(io->beta, 4)) || (io->eta && misaligned(io->eta, 4)) ||
+      (io->bonus && misaligned(io->bonus)))
     return DL_EALIGN;
   return DL_OK;
 }
@@ -54,7 +57,7 @@ dl::PoolArgs pool_args(const dl_dims* d, const dl_pool* p) {
 }
 
 dl::StepArgs step_args(const dl_step_io* io) {
-  return dl::StepArgs{io->q, io->k, io->v, io->decay, io->beta, io->bonus, io->out};
+  return dl::StepArgs{io->q, io->k, io->v, io->decay, io->beta, io->bonus, io->out, io->eta, io->eps};
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DL_OK : DL_EHIP; }

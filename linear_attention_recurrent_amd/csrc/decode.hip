@@ -200,6 +200,7 @@ struct DecodeLds {
   __attribute__((aligned(16))) float ucur[DV];  // u_t (staged folds)
   float sig[2][DL_MAX_LOG_LEN];                 // sigma^k_j, sigma^q_j (RWKV6: sigma^r_j)
   float dot;                                    // k_t . q_t  (RWKV6: sum r bonus k)
+  float kk;                                     // ||k_t||^2 (Kaczmarz step size)
   __attribute__((aligned(16))) float red[NW][2][DV];  // per-wave column partial sums
   __attribute__((aligned(16))) float w[MC * DK];      // fold weights, permuted rows
   __attribute__((aligned(16))) float uu[MC * DV];     // fold factors
@@ -271,8 +272,8 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
     up[e] = bload_factor4(ru, j < n ? (uint32_t)((j * DV + cg * 4) * sizeof(UT)) : kOutOfRange, UT{});
   }
   const uint16_t vbits = s.v[(size_t)tile * DV + (tid % DV)];  // column lanes: v_t
-  float beta = 0.f;
-  if constexpr (VAR != DL_RWKV6) beta = s.beta[tile];
+  float beta = 0.f;  // the given step size, or eta for the Kaczmarz one
+  if constexpr (VAR != DL_RWKV6) beta = s.eta ? s.eta[tile] : s.beta[tile];
   uint4 v8 = make_uint4(0, 0, 0, 0);  // RWKV6 appends v_t's bf16 bits
   if constexpr (VAR == DL_RWKV6 && !FOLD)
     v8 = *reinterpret_cast<const uint4*>(s.v + (size_t)tile * DV + (tid % (DV / 8)) * 8);
@@ -323,14 +324,22 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
         if (reg_stage) sh.w[n * DK + pi] = kt[i];
       }
     }
-    float d = 0.f;
+    float d = 0.f, kk = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if constexpr (VAR == DL_RWKV6) d = fmaf(qt[i] * bonus[i], kt[i], d);
-      else d = fmaf(kt[i], qt[i], d);
+      if constexpr (VAR == DL_RWKV6) {
+        d = fmaf(qt[i] * bonus[i], kt[i], d);
+      } else {
+        d = fmaf(kt[i], qt[i], d);
+        kk = fmaf(kt[i], kt[i], kk);
+      }
     }
     d = group_sum<G::LPE>(d);
-    if (tid == 0) sh.dot = d;
+    if constexpr (VAR != DL_RWKV6) kk = group_sum<G::LPE>(kk);
+    if (tid == 0) {
+      sh.dot = d;
+      sh.kk = kk;
+    }
     // the prefetched passes: entries eg + NG*e, from the registers loaded above
 #pragma unroll
     for (int e = 0; e < G::EPF; ++e) {
@@ -427,7 +436,9 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
       u = vcol;
       o = fmaf(sh.dot, vcol, pk);
     } else {
-      u = beta * (vcol - pk);
+      // Kaczmarz step size (Kaczmarz Linear Attention abstract): beta = eta / (||k||^2 + eps)
+      const float b = s.eta ? beta / (sh.kk + s.eps) : beta;
+      u = b * (vcol - pk);
       o = fmaf(sh.dot, u, oq);
       if constexpr (!FOLD) static_cast<float*>(p.log_u)[(lbase + n) * DV + tid] = u;
     }

@@ -171,6 +171,8 @@ struct StepArgs {
   const float* beta;
   const float* bonus;
   float* out;
+  const float* eta;  // Kaczmarz step size: beta = eta / (||k||^2 + eps) when set
+  float eps;
 };
 
 }  // namespace dl

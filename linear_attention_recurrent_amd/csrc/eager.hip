@@ -28,6 +28,7 @@ __global__ void __launch_bounds__((Geo<DK, DV>::NT)) eager_kernel(float* state, 
   __shared__ __attribute__((aligned(16))) float s_yk[DK];  // d . k   (RWKV6: unused)
   __shared__ __attribute__((aligned(16))) float s_yq[DK];  // d . q   (RWKV6: r)
   __shared__ float s_dot;
+  __shared__ float s_kk;  // ||k||^2 (Kaczmarz step size)
   __shared__ float s_red[G::NW][2][DV];
   __shared__ __attribute__((aligned(16))) float s_u[DV];
 
@@ -55,8 +56,8 @@ __global__ void __launch_bounds__((Geo<DK, DV>::NT)) eager_kernel(float* state, 
   }
   float vcol = 0.f;
   if (tid < DV) vcol = bf16_to_f32(s.v[(size_t)tile * DV + tid]);
-  float beta = 0.f;
-  if constexpr (VAR != DL_RWKV6) beta = s.beta[tile];
+  float beta = 0.f;  // the given step size, or eta for the Kaczmarz one
+  if constexpr (VAR != DL_RWKV6) beta = s.eta ? s.eta[tile] : s.beta[tile];
 
   const int rg = tid / G::CG, cg = tid % G::CG;
   float4 B[RPT];
@@ -68,7 +69,7 @@ __global__ void __launch_bounds__((Geo<DK, DV>::NT)) eager_kernel(float* state, 
     float kt[8], qt[8];
     unpack8(kt8, kt);
     unpack8(qt8, qt);
-    float d = 0.f;
+    float d = 0.f, kk = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       s_d[ch * 8 + i] = dec[i];
@@ -80,10 +81,15 @@ __global__ void __launch_bounds__((Geo<DK, DV>::NT)) eager_kernel(float* state, 
         s_yk[ch * 8 + i] = dec[i] * kt[i];
         s_yq[ch * 8 + i] = dec[i] * qt[i];
         d = fmaf(kt[i], qt[i], d);
+        kk = fmaf(kt[i], kt[i], kk);
       }
     }
     d = group_sum<G::LPE>(d);
-    if (tid == 0) s_dot = d;
+    kk = group_sum<G::LPE>(kk);
+    if (tid == 0) {
+      s_dot = d;
+      s_kk = kk;
+    }
   }
   __syncthreads();
 
@@ -135,7 +141,9 @@ __global__ void __launch_bounds__((Geo<DK, DV>::NT)) eager_kernel(float* state, 
       u = vcol;
       o = fmaf(s_dot, vcol, oq);
     } else {
-      u = beta * (vcol - pk);
+      // Kaczmarz step size (Kaczmarz Linear Attention abstract): beta = eta / (||k||^2 + eps)
+      const float b = s.eta ? beta / (s_kk + s.eps) : beta;
+      u = b * (vcol - pk);
       o = fmaf(s_dot, u, oq);
     }
     s.out[(size_t)tile * DV + tid] = o;

@@ -35,7 +35,7 @@ class Pool(ctypes.Structure):
 class StepIO(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("decay", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("bonus", ctypes.c_void_p),
-                ("out", ctypes.c_void_p)]
+                ("out", ctypes.c_void_p), ("eta", ctypes.c_void_p), ("eps", ctypes.c_float)]
 
 
 class DeltaLogError(RuntimeError):
@@ -137,13 +137,16 @@ class DeltaLogPool:
             getattr(other, name).copy_(t)
         return other
 
-    def step_io(self, q, k, v, decay, beta, bonus, out) -> StepIO:
+    def step_io(self, q, k, v, decay, beta, bonus, out, eta=None, eps=0.0) -> StepIO:
         """Check the step tensors against this pool's shape and pack them into a StepIO."""
         return make_step_io(self.variant, self.batch, self.heads, self.dk, self.dv, self.device,
-                            q, k, v, decay, beta, bonus, out)
+                            q, k, v, decay, beta, bonus, out, eta, eps)
 
 
-def make_step_io(variant, batch, heads, dk, dv, device, q, k, v, decay, beta, bonus, out) -> StepIO:
+def make_step_io(variant, batch, heads, dk, dv, device, q, k, v, decay, beta, bonus, out,
+                 eta=None, eps=0.0) -> StepIO:
+    """Pack one step's tensors.  GDN/KDA take either beta (the given step size) or eta
+    (the Kaczmarz step size beta = eta / (||k||^2 + eps), computed in the kernel)."""
     B, H = batch, heads
     _need(q, "q", (B, H, dk), torch.bfloat16, device)
     _need(k, "k", (B, H, dk), torch.bfloat16, device)
@@ -151,14 +154,17 @@ def make_step_io(variant, batch, heads, dk, dv, device, q, k, v, decay, beta, bo
     _need(decay, "decay", (B, H) if variant == GDN else (B, H, dk), torch.float32, device)
     if variant == RWKV6:
         _need(bonus, "bonus", (H, dk), torch.float32, device)
-        if beta is not None:
-            raise ValueError("beta must be None for RWKV6")
+        if beta is not None or eta is not None:
+            raise ValueError("beta and eta must be None for RWKV6")
     else:
-        _need(beta, "beta", (B, H), torch.float32, device)
+        if (beta is None) == (eta is None):
+            raise ValueError("GDN/KDA take exactly one of beta and eta")
+        _need(beta if eta is None else eta, "beta" if eta is None else "eta", (B, H), torch.float32, device)
         if bonus is not None:
             raise ValueError("bonus must be None for GDN/KDA")
     _need(out, "out", (B, H, dv), torch.float32, device)
-    return StepIO(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta), _ptr(bonus), _ptr(out))
+    return StepIO(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta), _ptr(bonus), _ptr(out), _ptr(eta),
+                  float(eps))
 
 
 # ------------------------------------------------------------- the C calls --

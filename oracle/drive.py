@@ -14,7 +14,7 @@ import numpy as np
 from inputs import bf16_bits_to_f32
 
 from .deferred import DeferredTile
-from .recurrences import eager_step
+from .recurrences import eager_step, kaczmarz_beta
 
 
 def step_arrays(inp, t: int, sel: Optional[Sequence] = None) -> dict:
@@ -30,7 +30,12 @@ def step_arrays(inp, t: int, sel: Optional[Sequence] = None) -> dict:
         out[name] = a if sel is None else np.stack([a[b, h] for b, h in sel])
     d = x["decay"].astype(np.float64)
     out["decay"] = d if sel is None else np.stack([d[b, h] for b, h in sel])
-    if x["beta"] is None:
+    if getattr(inp, "eta", None) is not None:
+        # Kaczmarz step size from eta and the (bf16) key actually used
+        et = inp.eta[inp.slot(t)].astype(np.float64)
+        et = et if sel is None else np.array([et[b, h] for b, h in sel])
+        out["beta"] = kaczmarz_beta(et, out["k"], inp.eps)
+    elif x["beta"] is None:
         out["beta"] = None
     else:
         bt = x["beta"].astype(np.float64)

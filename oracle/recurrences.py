@@ -75,6 +75,15 @@ def rwkv6_step(S, r, k, v, w, bonus):
     return S_new, o
 
 
+def kaczmarz_beta(eta, k, eps):
+    """Kaczmarz step size beta = eta / (||k||^2 + eps) (Kaczmarz Linear Attention abstract).
+
+    eta: [...] per state; k: [..., dk]; eps >= 0.  With eta = 1 and eps = 0 the
+    delta-rule write projects the state so that S'^T k = v exactly.
+    """
+    return np.asarray(eta, np.float64) / (np.sum(np.asarray(k, np.float64) ** 2, axis=-1) + eps)
+
+
 def eager_step(variant: int, S, q, k, v, decay, beta=None, bonus=None):
     """Dispatch on the variant code (0 = GDN, 1 = KDA, 2 = RWKV6)."""
     if variant == 0:

@@ -31,13 +31,15 @@ class Uploaded:
         self.v = to_bf16(inp.v, d)
         self.decay = torch.from_numpy(inp.decay).to(d)
         self.beta = None if inp.beta is None else torch.from_numpy(inp.beta).to(d)
+        self.eta = None if inp.eta is None else torch.from_numpy(inp.eta).to(d)
         self.bonus = None if inp.bonus is None else torch.from_numpy(inp.bonus).to(d)
         self.s0 = torch.from_numpy(inp.s0).to(d)
         self.out = out if out is not None else torch.empty((inp.batch, inp.heads, inp.dv), dtype=torch.float32,
                                                            device=d)
         self.ios = [dl.make_step_io(inp.variant, inp.batch, inp.heads, inp.dk, inp.dv, d,
                                     self.q[p], self.k[p], self.v[p], self.decay[p],
-                                    None if self.beta is None else self.beta[p], self.bonus, self.out)
+                                    None if self.beta is None else self.beta[p], self.bonus, self.out,
+                                    None if self.eta is None else self.eta[p], inp.eps)
                     for p in range(inp.pool)]
 
     def io(self, t: int):

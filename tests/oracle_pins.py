@@ -215,3 +215,25 @@ def pin_deferred_equals_eager(tile_cls, step, log_lens=(1, 2, 3, 8, 16, 64), T=1
                         assert tile.merges == merges and np.array_equal(tile.base, base), (variant, L, n0, t)
                     base = tile.base.copy()
                     merges = tile.merges
+
+
+# ------------------------------------------------------------ Kaczmarz ----
+def pin_kaczmarz_step_size(step, kbeta):
+    """Kaczmarz step size (Kaczmarz Linear Attention abstract), beta = eta / (||k||^2 + eps):
+    the delta write then moves S^T k from the decayed read D^T k towards v by the
+    fraction rho = eta ||k||^2 / (||k||^2 + eps); eta = 1, eps = 0 lands on v exactly."""
+    for variant in (0, 1):
+        S0, steps, _ = _random_run(variant, 800 + variant, unit_k=False)
+        S = S0.copy()
+        for i, st in enumerate(steps):
+            eta = 1.0 if i % 2 == 0 else 0.3 + 0.05 * i
+            eps = 0.0 if i % 3 == 0 else 0.25
+            k = st["k"] * (1.0 + i)  # norms far from 1
+            d = st["decay"]
+            read_before = ((np.eye(S.shape[0]) * d if variant == 0 else np.diag(d)) @ S).T @ k
+            beta = kbeta(np.asarray(eta), k, eps)
+            S, _ = step(variant, S, st["q"], k, st["v"], d, beta, None)
+            kk = float(np.dot(k, k))
+            rho = eta * kk / (kk + eps)
+            np.testing.assert_allclose(S.T @ k, (1 - rho) * read_before + rho * st["v"],
+                                       rtol=0, atol=1e-10 * max(1.0, kk))

@@ -242,3 +242,70 @@ def test_bad_fill_is_rejected_before_any_work():
     with pytest.raises(dl.DeltaLogError) as ei:
         dl.dl_merge(pool, 0)
     assert ei.value.status == dl.DL_EINVAL
+
+
+# ------------------------------------------------- Kaczmarz step size (KLA) --
+@pytest.mark.parametrize("w,kla", [(6, None), (3, True)])
+def test_kaczmarz_step_size(w, kla):
+    inp = make_inputs(w, 2048, batch=2, heads=4, pool=2048, kla=kla)
+    assert inp.eta is not None and inp.beta is None
+    pool, outs = run_deltalog(inp, 2048)
+    _compare(inp, 2048, pool, outs)
+    S, eo = run_eager_gpu(inp, 512)
+    ref_S, ref_o = oracle.run_eager(inp, 512)
+    _close("eager outputs", eo, ref_o, (-1,))
+    _close("eager state", S, ref_S, (-2, -1))
+
+
+def test_kaczmarz_projection_on_gpu():
+    """eta = 1, eps = 0, decay 1: after each step the state maps k_t onto v_t."""
+    inp = make_inputs(6, 24, batch=2, heads=2, pool=24)
+    inp.eta[:] = 1.0
+    inp.eps = 0.0
+    inp.decay[:] = 1.0
+    up = Uploaded(inp)
+    pool = new_pool(inp, up=up)
+    kf = oracle.step_arrays  # reuse only to widen the bf16 inputs exactly
+    for t in range(24):
+        dl.dl_decode_step(pool, up.io(t))
+        S = materialized_state(pool).astype(np.float64)
+        a = kf(inp, t)
+        got = np.einsum("bhij,bhi->bhj", S, a["k"])
+        np.testing.assert_allclose(got, a["v"], rtol=0, atol=2e-4 * np.abs(a["v"]).max())
+
+
+# ------------------------------------------------------------- HIP graphs ----
+def test_hip_graph_replays_match_direct_launches():
+    """Capture one fold period of decode steps in a HIP graph and replay it several
+    times, with other work and synchronisation in between; every replay must give
+    bit-identical outputs and pool to the same steps launched directly."""
+    inp = make_inputs(2, 16, batch=4, heads=4, pool=16, fill0=np.array([0, 3, 9, 15], np.int32))
+    up = Uploaded(inp)
+    ref_pool = new_pool(inp, up=up)
+    ref = []
+    for t in range(48):
+        dl.dl_decode_step(ref_pool, up.io(t % 16))
+        ref.append(up.out.clone())
+    torch.cuda.synchronize()
+
+    pool = new_pool(inp, up=up)
+    outbuf = torch.empty((16,) + tuple(up.out.shape), dtype=torch.float32, device=dev())
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for t in range(16):
+                dl.dl_decode_step(pool, up.io(t))
+                outbuf[t].copy_(up.out)
+    torch.cuda.synchronize()
+    # capture recorded the launches without running them: start from the same pool state
+    dl.dl_init_state(pool, up.s0, inp.fill0)
+    for r in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (torch.ones(1 << 20, device=dev()) * 2).sum().item()  # unrelated work between replays
+        for t in range(16):
+            assert torch.equal(outbuf[t], ref[16 * r + t]), (r, t)
+    for name, tnsr in pool.tensors().items():
+        assert torch.equal(tnsr, ref_pool.tensors()[name]), name

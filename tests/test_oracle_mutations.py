@@ -157,3 +157,13 @@ def test_deferred_mutant_is_caught(cls):
         except Exception:
             failed = True
     assert failed, cls.__name__
+
+
+@pytest.mark.parametrize("kbeta", [
+    lambda eta, k, eps: np.asarray(eta) / (np.sqrt(np.sum(k * k, axis=-1)) + eps),   # norm, not its square
+    lambda eta, k, eps: np.asarray(eta) / np.sum(k * k, axis=-1),                     # eps dropped
+    lambda eta, k, eps: np.asarray(eta) * np.sum(k * k, axis=-1) / (1.0 + eps),       # inverted
+])
+def test_kaczmarz_mutant_is_caught(kbeta):
+    with pytest.raises(AssertionError):
+        P.pin_kaczmarz_step_size(oracle.eager_step, kbeta)

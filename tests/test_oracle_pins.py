@@ -33,3 +33,7 @@ def test_kda_reduces_to_gdn():
 
 def test_deferred_equals_eager():
     P.pin_deferred_equals_eager(oracle.DeferredTile, oracle.eager_step)
+
+
+def test_kaczmarz_step_size():
+    P.pin_kaczmarz_step_size(oracle.eager_step, oracle.kaczmarz_beta)
