@@ -12,5 +12,5 @@ Modules:
   drive        loops over a seeded workload, and the relative-error measure
 """
 from .recurrences import eager_step, gdn_step, kaczmarz_beta, kda_step, rwkv6_step  # noqa: F401
-from .deferred import DeferredTile  # noqa: F401
+from .deferred import DeferredTile, round_to_bf16  # noqa: F401
 from .drive import deferred_tiles, rel_err, run_deferred, run_eager, step_arrays  # noqa: F401

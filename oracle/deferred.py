@@ -11,7 +11,8 @@ so the model observes the same dense state as eager decoding.  The AI Summary
 of the same page says the appends replace full write-backs.
 
 Representation used here (written for clarity, not speed, and independent of
-the GPU code, which keeps cumulative log2-decays instead):
+the GPU code, which keeps cumulative log2-decays instead).  With a low-bit base
+the base is rounded to bf16 wherever it is written (start and merges):
 
 * base: float64 [dk, dv], the state as of the last merge.
 * log entry j: (k_j, u_j, d_j) where u_j is the rank-1 write of its step
@@ -36,15 +37,35 @@ from __future__ import annotations
 import numpy as np
 
 
+def round_to_bf16(x) -> np.ndarray:
+    """Round to the nearest bfloat16 value (8 significant bits, ties to even), in float64.
+
+    For the low-bit base (LeapQuant abstract, on the card page titled "A
+    Persistent-State Dataflow Accelerator for Memory-Bound Linear Attention
+    Decode on FPGA": outputs come from a fixed low-bit state plus high-precision
+    buffered updates, and the state is quantised once per window).  Written from
+    the format's definition: x = m 2^e with m in [0.5, 1); keep m to 2^-8.
+    Exact for the normal range (bf16 shares float32's exponent range); values
+    below 2^-126 keep 8 significant bits here, where bf16 would flush them
+    towards subnormals.
+    """
+    x = np.asarray(x, np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)  # np.rint rounds half to even
+
+
 class DeferredTile:
     """One (sequence, head) state in base + log form, float64."""
 
     def __init__(self, variant: int, s0: np.ndarray, log_len: int, fill0: int = 0,
-                 bonus: np.ndarray | None = None):
+                 bonus: np.ndarray | None = None, low_bit_base: bool = False):
         if log_len < 1 or not (0 <= fill0 < log_len):
             raise ValueError("need log_len >= 1 and 0 <= fill0 < log_len")
         self.variant = variant
+        self.low_bit_base = low_bit_base  # base kept in bf16: rounded wherever it is written
         self.base = np.array(s0, dtype=np.float64)
+        if low_bit_base:
+            self.base = round_to_bf16(self.base)
         self.log_len = log_len
         dk, dv = self.base.shape
         g = 1 if variant == 0 else dk
@@ -84,6 +105,8 @@ class DeferredTile:
     def merge(self) -> None:
         """Fold every log entry into the base and empty the log."""
         self.base = self.materialize()
+        if self.low_bit_base:
+            self.base = round_to_bf16(self.base)
         self.ks, self.us, self.ds = [], [], []
         self.merges += 1
 

@@ -74,24 +74,24 @@ def run_eager(inp, steps: int, sel: Optional[Sequence] = None, keep_outputs: boo
     return res + (snaps,) if check_every is not None else res
 
 
-def deferred_tiles(inp, sel: Sequence, log_len: Optional[int] = None):
+def deferred_tiles(inp, sel: Sequence, log_len: Optional[int] = None, low_bit_base: bool = False):
     """Build one DeferredTile per (b, h) in `sel`, started at the workload's fills."""
     L = inp.log_len if log_len is None else log_len
     tiles = []
     for b, h in sel:
         bonus = None if inp.bonus is None else inp.bonus[h]
-        tiles.append(DeferredTile(inp.variant, inp.s0[b, h], L, int(inp.fill0[b]), bonus))
+        tiles.append(DeferredTile(inp.variant, inp.s0[b, h], L, int(inp.fill0[b]), bonus, low_bit_base))
     return tiles
 
 
-def run_deferred(inp, steps: int, sel: Sequence, log_len: Optional[int] = None):
+def run_deferred(inp, steps: int, sel: Sequence, log_len: Optional[int] = None, low_bit_base: bool = False):
     """Deferred fp64 model over `steps` steps for tiles `sel`.
 
     Returns (tiles, outputs [steps][len(sel)][dv], fills [steps][len(sel)],
     slots [steps][len(sel)]) where fills are the log fills after each step and
     slots the slot each step appended to.
     """
-    tiles = deferred_tiles(inp, sel, log_len)
+    tiles = deferred_tiles(inp, sel, log_len, low_bit_base)
     outs, fills, slots = [], [], []
     for t in range(steps):
         a = step_arrays(inp, t, sel)
