@@ -13,6 +13,7 @@ last-level cache), and the fp64 CPU oracle on the host cores.
 
   python bench.py [--gpus 1] [--steps 1024] [--warmup 32] [--workload 2]
                   [--no-cpu-baseline] [--graph] [--only deltalog|eager|copy]
+                  [--base-dtype f32|bf16]
 """
 from __future__ import annotations
 
@@ -58,10 +59,11 @@ def input_bytes(variant: int, dk: int, dv: int, batch: int) -> float:
     return b
 
 
-def deltalog_bytes_per_state_step(variant, dk, dv, L, batch) -> dict:
-    """Algorithmic HBM bytes per (sequence, head, token), averaged over a period of L steps."""
+def deltalog_bytes_per_state_step(variant, dk, dv, L, batch, base_bytes=4) -> dict:
+    """Algorithmic HBM bytes per (sequence, head, token), averaged over a period of L steps.
+    base_bytes: 4 for the fp32 base, 2 for the bf16 base."""
     E = entry_bytes(variant, dk, dv)
-    state = 4 * dk * dv
+    state = base_bytes * dk * dv
     parts = dict(
         base_read=state,
         inputs=input_bytes(variant, dk, dv, batch),
@@ -92,10 +94,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_counter_profile(workload_name: str):
+def counter_profile_name(workload_name: str, bf16_base: bool) -> str:
+    return f"decode_{workload_name}{'_bf16base' if bf16_base else ''}_counters.txt"
+
+
+def read_counter_profile(workload_name: str, bf16_base: bool = False):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source (else None)."""
-    path = os.path.join(PROFILE_DIR, f"decode_{workload_name}_counters.txt")
+    path = os.path.join(PROFILE_DIR, counter_profile_name(workload_name, bf16_base))
     if not os.path.exists(path):
         return None
     vals = {}
@@ -225,6 +231,9 @@ def main():
     ap.add_argument("--graph", action="store_true", help="replay the step loop as a HIP graph")
     ap.add_argument("--only", choices=["deltalog", "eager", "copy"], default=None,
                     help="run one leg only (for profiling runs)")
+    ap.add_argument("--base-dtype", choices=["f32", "bf16"], default="f32",
+                    help="storage of the dense base: fp32 (exact path) or bf16 (low-bit base, "
+                         "rounded at each fold; log and arithmetic stay fp32)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -266,9 +275,11 @@ def main():
         chunk = L * max(1, 64 // L)
         K = max(chunk, (K // chunk) * chunk)
 
+    bf16_base = args.base_dtype == "bf16"
+    base_dt = dl.BASE_BF16 if bf16_base else dl.BASE_F32
     result = {}
     if args.only in (None, "deltalog"):
-        pool = dl.DeltaLogPool(var, B, H, dk, dv, L, dev)
+        pool = dl.DeltaLogPool(var, B, H, dk, dv, L, dev, base_dt)
         dl.dl_init_state(pool, T["s0"], inp.fill0)
         # W warmup steps, then K timed steps; both start the timed window at the same phase
         W_al = ((W + L - 1) // L) * L
@@ -283,7 +294,7 @@ def main():
         return
 
     # cache-cold variant: three independent pools used in turn
-    pools = [dl.DeltaLogPool(var, B, H, dk, dv, L, dev) for _ in range(3)]
+    pools = [dl.DeltaLogPool(var, B, H, dk, dv, L, dev, base_dt) for _ in range(3)]
     for p_ in pools:
         dl.dl_init_state(p_, T["s0"], inp.fill0)
     W_al = ((W + 3 * L - 1) // (3 * L)) * (3 * L)
@@ -291,21 +302,21 @@ def main():
     secs_c = time_loop(lambda t: dl.dl_decode_step(pools[t % 3], ios[t % P]), Kc, W_al)
     del pools
 
-    mdl = deltalog_bytes_per_state_step(var, dk, dv, L, B)
+    mdl = deltalog_bytes_per_state_step(var, dk, dv, L, B, 2 if bf16_base else 4)
     eag = eager_bytes_per_state_step(var, dk, dv, B)
     t_step = result["deltalog"] / K
     t_eager = result["eager"] / K
     t_cold = secs_c / Kc
     value = tiles / t_step
     achieved = mdl["total"] * tiles / t_step / 1e9
-    prof = read_counter_profile(w["name"])
+    prof = read_counter_profile(w["name"], bf16_base)
     traffic = None
     counter_write = None
     if prof is not None:
         traffic = float(prof["fetch_bytes_per_launch"]) + float(prof["write_bytes_per_launch"])
         counter_write = {"deltalog": float(prof["write_bytes_per_launch"]) / tiles,
                          "eager": float(prof.get("eager_write_bytes_per_launch", "nan")) / tiles,
-                         "source": f"profiles/decode_{w['name']}_counters.txt"}
+                         "source": f"profiles/{counter_profile_name(w['name'], bf16_base)}"}
 
     line = {
         "metric": "decode state-steps/s (B×H per s)",
@@ -321,7 +332,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{w['name']}: {VARIANT_NAMES[var]} decode B={B} H={H} dk={dk} dv={dv} L={L}"
-                               + (" (Kaczmarz step size)" if inp.eta is not None else ""),
+                               + (" (Kaczmarz step size)" if inp.eta is not None else "")
+                               + (", bf16 base" if bf16_base else ""),
+                   "base": "bf16, rounded at each fold" if bf16_base else "f32",
                    "variant": VARIANT_NAMES[var], "batch": B, "heads": H, "dk": dk, "dv": dv,
                    "log_len": L, "initial_fill": "0 for every sequence" if not np.any(inp.fill0) else "ragged",
                    "input_pool_steps": P, "hip_graph": bool(chunk)},

@@ -62,13 +62,17 @@ typedef enum { DL_GDN = 0, DL_KDA = 1, DL_RWKV6 = 2 } dl_variant;
 
 enum {
   DL_OK = 0,
-  DL_EINVAL = -1,       /* null required pointer, bad dims, L outside [1,128], fill outside [0,L) */
+  DL_EINVAL = -1,       /* null required pointer, bad dims, L outside [1,128], fill outside [0,L),
+                           unknown base_dtype */
   DL_EUNSUPPORTED = -2, /* dk or dv not 64/128, or a pointer given/missing for this variant */
   DL_EALIGN = -3,       /* a device pointer is not aligned as required (16 or 4 bytes) */
   DL_EHIP = -4          /* the HIP runtime reported an error when enqueuing */
 };
 
 #define DL_MAX_LOG_LEN 128
+
+/* Storage type of the base state. */
+enum { DL_BASE_F32 = 0, DL_BASE_BF16 = 1 };
 
 /* Shape of one pool.  batch >= 0 (0: every call returns DL_OK at once, after
  * checking only the other dims, and no pointer is looked at), heads >= 1,
@@ -80,11 +84,16 @@ typedef struct {
   int32_t dk;
   int32_t dv;
   int32_t log_len;
+  int32_t base_dtype; /* DL_BASE_F32, or DL_BASE_BF16: a low-bit base.  The log and all
+                         arithmetic stay fp32; the base is rounded to bf16 (to nearest,
+                         ties to even) only where it is written: at init and at folds.
+                         Outputs then see the fixed low-bit base plus fp32 buffered
+                         updates (LeapQuant abstract, on the FPGA-titled card page). */
 } dl_dims;
 
 /* The per-layer state pool (all device, caller-owned).  G = 1 for GDN, dk otherwise. */
 typedef struct {
-  float *base;     /* fp32 [batch][heads][dk][dv]  base state B (rows = key channels)          */
+  void *base;      /* fp32 (or bf16) [batch][heads][dk][dv]  base state B (rows = key channels) */
   uint16_t *log_k; /* bf16 [batch][heads][L][dk]   keys of the logged updates                  */
   void *log_u;     /* GDN/KDA: fp32 [batch][heads][L][dv] factors u_j;
                       RWKV6:   bf16 [batch][heads][L][dv] values v_j                          */
@@ -140,7 +149,8 @@ int dl_merge(const dl_dims *dims, const dl_pool *pool, int32_t min_fill, void *s
 /* The eager comparator (DeltaLog Abstract: materialize and write back the
  * full recurrent state after every generated token): reads `state` (device,
  * fp32 [batch][heads][dk][dv]), writes the updated state in place and io->out.
- * dims->log_len is ignored (may be any value in [1, 128]). */
+ * dims->log_len is ignored (may be any value in [1, 128]); base_dtype must be
+ * DL_BASE_F32 (else DL_EUNSUPPORTED). */
 int dl_eager_step(const dl_dims *dims, float *state, const dl_step_io *io, void *stream);
 
 /* A static, human-readable name for a status code (never NULL). */

@@ -24,6 +24,7 @@ int check_dims(const dl_dims* d) {
   if (d->log_len < 1 || d->log_len > DL_MAX_LOG_LEN) return DL_EINVAL;
   if (static_cast<int64_t>(d->batch) * d->heads > INT32_MAX) return DL_EINVAL;
   if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128)) return DL_EUNSUPPORTED;
+  if (d->base_dtype != DL_BASE_F32 && d->base_dtype != DL_BASE_BF16) return DL_EINVAL;
   return DL_OK;
 }
 
@@ -56,6 +57,9 @@ dl::PoolArgs pool_args(const dl_dims* d, const dl_pool* p) {
   return dl::PoolArgs{p->base, p->log_k, p->log_u, p->log_c, p->fill, d->heads, d->log_len};
 }
 
+bool bf16_base(const dl_dims* d) { return d->base_dtype == DL_BASE_BF16;
+}
+
 dl::StepArgs step_args(const dl_step_io* io) {
   return dl::StepArgs{io->q, io->k, io->v, io->decay, io->beta, io->bonus, io->out, io->eta, io->eps};
 }
@@ -84,7 +88,8 @@ int dl_init_state(const dl_dims* dims, const dl_pool* pool, const float* init_ba
   hipError_t e = hipMemcpyAsync(pool->fill, fills.data(), fills.size() * sizeof(int32_t),
                                 hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return DL_EHIP;
-  e = dl::launch_init(dims->variant, dims->dk, dims->dv, batch * heads, pool_args(dims, pool), init_base, st);
+  e = dl::launch_init(dims->variant, bf16_base(dims), dims->dk, dims->dv, batch * heads, pool_args(dims, pool),
+                      init_base, st);
   if (e != hipSuccess) return DL_EHIP;
   return hip_status(hipStreamSynchronize(st));
 }
@@ -94,7 +99,7 @@ int dl_decode_step(const dl_dims* dims, const dl_pool* pool, const dl_step_io* i
   if (rc != DL_OK || dims->batch == 0) return rc;
   if ((rc = check_pool(pool, dims->variant)) != DL_OK) return rc;
   if ((rc = check_io(dims, io)) != DL_OK) return rc;
-  return hip_status(dl::launch_decode(dims->variant, dims->dk, dims->dv, dims->batch * dims->heads,
+  return hip_status(dl::launch_decode(dims->variant, bf16_base(dims), dims->dk, dims->dv, dims->batch * dims->heads,
                                       pool_args(dims, pool), step_args(io),
                                       static_cast<hipStream_t>(stream)));
 }
@@ -105,13 +110,14 @@ int dl_merge(const dl_dims* dims, const dl_pool* pool, int32_t min_fill, void* s
   if (min_fill < 1 || min_fill > dims->log_len) return DL_EINVAL;
   if (dims->batch == 0) return DL_OK;
   if ((rc = check_pool(pool, dims->variant)) != DL_OK) return rc;
-  return hip_status(dl::launch_merge(dims->variant, dims->dk, dims->dv, dims->batch * dims->heads,
+  return hip_status(dl::launch_merge(dims->variant, bf16_base(dims), dims->dk, dims->dv, dims->batch * dims->heads,
                                      pool_args(dims, pool), min_fill, static_cast<hipStream_t>(stream)));
 }
 
 int dl_eager_step(const dl_dims* dims, float* state, const dl_step_io* io, void* stream) {
   int rc = check_dims(dims);
   if (rc != DL_OK || dims->batch == 0) return rc;
+  if (dims->base_dtype != DL_BASE_F32) return DL_EUNSUPPORTED;  // the eager state is fp32
   if ((rc = check_io(dims, io)) != DL_OK) return rc;
   if (state == nullptr) return DL_EINVAL;
   if (misaligned(state)) return DL_EALIGN;

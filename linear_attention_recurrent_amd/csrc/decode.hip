@@ -123,19 +123,20 @@ __device__ __forceinline__ void stage_entries(const PoolArgs& p, int tile, int e
 // One streamed fold pass over a tile's base:
 //   B[row][cols] <- g[row] B[row][cols] + sum_{m < nent} s_w[m][perm(row)] s_uu[m][cols]
 // with g = 2^c (s_g, rows permuted; one value for GDN) when `scale`, else 1.
-template <int VAR, int DK, int DV>
-__device__ __forceinline__ void fold_pass(float* tile_base, int nent, bool scale, const float* s_g,
+template <int VAR, int DK, int DV, bool BF>
+__device__ __forceinline__ void fold_pass(typename BaseIO<BF>::T* tb, int nent, bool scale, const float* s_g,
                                           const float* s_w, const float* s_uu) {
   using G = SGeo<DK, DV>;
+  using BIO = BaseIO<BF>;
   constexpr int RPC = G::RPC;
   const int tid = threadIdx.x;
   const int rg = tid / G::CG, cg = tid % G::CG;
-  float4* bp = reinterpret_cast<float4*>(tile_base) + cg;
+  auto gidx = [&](int c, int rr) { return (size_t)((c * RPC + rr) * G::RG + rg) * (DV / 4) + cg; };
   float4 buf[G::NB][RPC];
 #pragma unroll
   for (int c = 0; c < G::NB; ++c)
 #pragma unroll
-    for (int rr = 0; rr < RPC; ++rr) buf[c][rr] = bp[(size_t)((c * RPC + rr) * G::RG + rg) * (DV / 4)];
+    for (int rr = 0; rr < RPC; ++rr) buf[c][rr] = BIO::load(tb, gidx(c, rr));
 #pragma unroll
   for (int c = 0; c < G::NC; ++c) {
     float g[RPC];
@@ -152,8 +153,7 @@ __device__ __forceinline__ void fold_pass(float* tile_base, int nent, bool scale
     for (int rr = 0; rr < RPC; ++rr) x[rr] = f4_mul(buf[c % G::NB][rr], g[rr]);
     if (c + G::NB < G::NC) {
 #pragma unroll
-      for (int rr = 0; rr < RPC; ++rr)
-        buf[c % G::NB][rr] = bp[(size_t)(((c + G::NB) * RPC + rr) * G::RG + rg) * (DV / 4)];
+      for (int rr = 0; rr < RPC; ++rr) buf[c % G::NB][rr] = BIO::load(tb, gidx(c + G::NB, rr));
     }
     for (int m = 0; m < nent; ++m) {
       const float4 u4 = *reinterpret_cast<const float4*>(s_uu + m * DV + cg * 4);
@@ -164,7 +164,7 @@ __device__ __forceinline__ void fold_pass(float* tile_base, int nent, bool scale
       x[3] = f4_fma(w4.w, u4, x[3]);
     }
 #pragma unroll
-    for (int rr = 0; rr < RPC; ++rr) bp[(size_t)((c * RPC + rr) * G::RG + rg) * (DV / 4)] = x[rr];
+    for (int rr = 0; rr < RPC; ++rr) BIO::store(tb, gidx(c, rr), x[rr]);
   }
 }
 
@@ -172,19 +172,19 @@ __device__ __forceinline__ void fold_pass(float* tile_base, int nent, bool scale
 // into its base, in stages of MC entries loaded from the log (used when the
 // fold's entries are not already staged).  Each stage streams the base once;
 // a thread re-reads only what it wrote itself in the previous stage.
-template <int VAR, int DK, int DV, bool HAS_CUR>
+template <int VAR, int DK, int DV, bool BF, bool HAS_CUR>
 __device__ __forceinline__ void fold_staged(const PoolArgs& p, int tile, int nlog,
                                             const float* s_ct, const float* s_g, const float* s_kcur,
                                             const float* s_ucur, float* s_w, float* s_uu) {
   using G = SGeo<DK, DV>;
-  float* tb = p.base + (size_t)tile * DK * DV;
+  auto* tb = BaseIO<BF>::tile(p.base, (size_t)tile * DK * DV);
   const int total = nlog + (HAS_CUR ? 1 : 0);
   for (int e0 = 0; e0 < total; e0 += G::MC) {
     const int cnt = min(G::MC, total - e0);
     __syncthreads();  // the previous stage's LDS reads are done
     stage_entries<VAR, DK, DV, HAS_CUR>(p, tile, e0, cnt, nlog, s_ct, s_kcur, s_ucur, s_w, s_uu);
     __syncthreads();
-    fold_pass<VAR, DK, DV>(tb, cnt, e0 == 0, s_g, s_w, s_uu);
+    fold_pass<VAR, DK, DV, BF>(tb, cnt, e0 == 0, s_g, s_w, s_uu);
   }
 }
 
@@ -210,9 +210,10 @@ struct DecodeLds {
 // it keeps the whole base tile in registers (one read), folds every update
 // into it and writes it back once.  Otherwise the base is streamed in chunks
 // and only the output, one log entry and the fill are written.
-template <int VAR, int DK, int DV, bool FOLD, typename Lds>
+template <int VAR, int DK, int DV, bool BF, bool FOLD, typename Lds>
 __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s, int tile, int n, Lds& sh) {
   using G = SGeo<DK, DV>;
+  using BIO = BaseIO<BF>;
   constexpr bool VEC = VAR != DL_GDN;  // per-key-channel decay
   constexpr int CW = VEC ? DK : 1;     // floats per log_c entry
   constexpr int RPC = G::RPC;
@@ -284,13 +285,14 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
   // ---- 2. the base: the first NB chunks on an appending step.  A folding step
   // loads the whole tile after step 3, so the tile and step 3's registers are
   // not live together.
-  float4* bp = reinterpret_cast<float4*>(p.base + (size_t)tile * DK * DV) + cg;
+  auto* tb = BIO::tile(p.base, (size_t)tile * DK * DV);
+  auto gidx = [&](int c, int rr) { return (size_t)((c * RPC + rr) * G::RG + rg) * (DV / 4) + cg; };
   float4 buf[NBUF][RPC];
   if constexpr (!FOLD) {
 #pragma unroll
     for (int c = 0; c < NBUF; ++c)
 #pragma unroll
-      for (int rr = 0; rr < RPC; ++rr) buf[c][rr] = bp[(size_t)((c * RPC + rr) * G::RG + rg) * (DV / 4)];
+      for (int rr = 0; rr < RPC; ++rr) buf[c][rr] = BIO::load(tb, gidx(c, rr));
   }
 
   // ---- 3. decay bookkeeping, scaled read vectors and log coefficients (entry lanes).
@@ -360,7 +362,7 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
 #pragma unroll
     for (int c = 0; c < NBUF; ++c)
 #pragma unroll
-      for (int rr = 0; rr < RPC; ++rr) buf[c][rr] = bp[(size_t)((c * RPC + rr) * G::RG + rg) * (DV / 4)];
+      for (int rr = 0; rr < RPC; ++rr) buf[c][rr] = BIO::load(tb, gidx(c, rr));
   }
   __syncthreads();
 
@@ -373,8 +375,7 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
     for (int rr = 0; rr < RPC; ++rr) x[rr] = buf[c % NBUF][rr];
     if (!FOLD && c + G::NB < G::NC) {
 #pragma unroll
-      for (int rr = 0; rr < RPC; ++rr)
-        buf[c % NBUF][rr] = bp[(size_t)(((c + G::NB) * RPC + rr) * G::RG + rg) * (DV / 4)];
+      for (int rr = 0; rr < RPC; ++rr) buf[c % NBUF][rr] = BIO::load(tb, gidx(c + G::NB, rr));
     }
     const float4 k4 = *reinterpret_cast<const float4*>(sh.yk + rg * G::RPT + c * RPC);
     ak = f4_fma(k4.x, x[0], ak);
@@ -503,25 +504,25 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
 #pragma unroll
     for (int c = 0; c < G::NC; ++c)
 #pragma unroll
-      for (int rr = 0; rr < RPC; ++rr) bp[(size_t)((c * RPC + rr) * G::RG + rg) * (DV / 4)] = buf[c][rr];
+      for (int rr = 0; rr < RPC; ++rr) BIO::store(tb, gidx(c, rr), buf[c][rr]);
     if (tid == 0) p.fill[tile] = 0;
   }
 }
 
-template <int VAR, int DK, int DV>
+template <int VAR, int DK, int DV, bool BF>
 __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, StepArgs s) {
   using G = SGeo<DK, DV>;
   __shared__ DecodeLds<DK, DV, (VAR == DL_GDN ? 1 : DK), G::NW, G::MC> sh;
   const int tile = blockIdx.x;
   const int n = p.fill[tile];  // same for the whole workgroup
   if (n + 1 == p.L)
-    decode_tile<VAR, DK, DV, true>(p, s, tile, n, sh);
+    decode_tile<VAR, DK, DV, BF, true>(p, s, tile, n, sh);
   else
-    decode_tile<VAR, DK, DV, false>(p, s, tile, n, sh);
+    decode_tile<VAR, DK, DV, BF, false>(p, s, tile, n, sh);
 }
 
 // dl_merge: fold the logs of tiles holding at least min_fill entries.
-template <int VAR, int DK, int DV>
+template <int VAR, int DK, int DV, bool BF>
 __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) merge_kernel(PoolArgs p, int min_fill) {
   using G = SGeo<DK, DV>;
   constexpr bool VEC = VAR != DL_GDN;
@@ -542,23 +543,24 @@ __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) merge_kernel(PoolArgs p, i
     s_c[i] = c;
     s_g[VEC ? G::perm(i) : 0] = exp2f(c);
   }
-  fold_staged<VAR, DK, DV, false>(p, tile, n, s_c, s_g, s_w, s_uu, s_w, s_uu);
+  fold_staged<VAR, DK, DV, BF, false>(p, tile, n, s_c, s_g, s_w, s_uu, s_w, s_uu);
   if (tid == 0) p.fill[tile] = 0;
 }
 
-// dl_init_state: copy or zero the base and zero every log slot of each tile.
-template <int VAR, int DK, int DV>
+// dl_init_state: copy (fp32 -> base type) or zero the base and zero every log slot of each tile.
+template <int VAR, int DK, int DV, bool BF>
 __global__ void __launch_bounds__(256) init_kernel(PoolArgs p, const float* init_base) {
+  using BIO = BaseIO<BF>;
   constexpr int CW = (VAR == DL_GDN) ? 1 : DK;
   constexpr int USZ = (VAR == DL_RWKV6) ? 2 : 4;
   const int tid = threadIdx.x;
   const size_t tile = blockIdx.x;
   const size_t L = p.L;
-  float4* dst = reinterpret_cast<float4*>(p.base + tile * DK * DV);
+  auto* dst = BIO::tile(p.base, tile * DK * DV);
   const float4* src = init_base ? reinterpret_cast<const float4*>(init_base + tile * DK * DV) : nullptr;
-  if (src != dst) {
+  if (init_base == nullptr || static_cast<const void*>(init_base) != p.base) {
     for (int i = tid; i < DK * DV / 4; i += 256)
-      dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      BIO::store(dst, i, src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f));
   }
   const uint4 z = make_uint4(0, 0, 0, 0);
   uint4* lk = reinterpret_cast<uint4*>(p.log_k + tile * L * DK);
@@ -570,59 +572,65 @@ __global__ void __launch_bounds__(256) init_kernel(PoolArgs p, const float* init
 }
 
 // ------------------------------------------------------------------ launchers
-#define DL_DISPATCH(VAR_, DK_, DV_, CALL)                                  \
+#define DL_DISPATCH(VAR_, BF_, DK_, DV_, CALL)                             \
   do {                                                                     \
-    if ((DK_) == 128 && (DV_) == 128) { CALL(VAR_, 128, 128); }            \
-    else if ((DK_) == 64 && (DV_) == 64) { CALL(VAR_, 64, 64); }           \
-    else if ((DK_) == 128 && (DV_) == 64) { CALL(VAR_, 128, 64); }         \
-    else { CALL(VAR_, 64, 128); }                                          \
+    if ((DK_) == 128 && (DV_) == 128) { CALL(VAR_, BF_, 128, 128); }       \
+    else if ((DK_) == 64 && (DV_) == 64) { CALL(VAR_, BF_, 64, 64); }      \
+    else if ((DK_) == 128 && (DV_) == 64) { CALL(VAR_, BF_, 128, 64); }    \
+    else { CALL(VAR_, BF_, 64, 128); }                                     \
   } while (0)
 
-#define DL_VARIANTS(VARI, DK_, DV_, CALL)                                  \
+#define DL_BASES(VAR_, BFI, DK_, DV_, CALL)                                \
   do {                                                                     \
-    if ((VARI) == DL_GDN) DL_DISPATCH(DL_GDN, DK_, DV_, CALL);             \
-    else if ((VARI) == DL_KDA) DL_DISPATCH(DL_KDA, DK_, DV_, CALL);        \
-    else DL_DISPATCH(DL_RWKV6, DK_, DV_, CALL);                            \
+    if (BFI) DL_DISPATCH(VAR_, true, DK_, DV_, CALL);                      \
+    else DL_DISPATCH(VAR_, false, DK_, DV_, CALL);                         \
   } while (0)
 
-hipError_t launch_decode(int variant, int dk, int dv, int tiles, const PoolArgs& p, const StepArgs& s,
-                         hipStream_t stream) {
+#define DL_VARIANTS(VARI, BFI, DK_, DV_, CALL)                             \
+  do {                                                                     \
+    if ((VARI) == DL_GDN) DL_BASES(DL_GDN, BFI, DK_, DV_, CALL);           \
+    else if ((VARI) == DL_KDA) DL_BASES(DL_KDA, BFI, DK_, DV_, CALL);      \
+    else DL_BASES(DL_RWKV6, BFI, DK_, DV_, CALL);                          \
+  } while (0)
+
+hipError_t launch_decode(int variant, bool bf16_base, int dk, int dv, int tiles, const PoolArgs& p,
+                         const StepArgs& s, hipStream_t stream) {
   hipError_t err = hipSuccess;
   PoolArgs pa = p;
   StepArgs sa = s;
   void* args[] = {&pa, &sa};
-#define CALL_DECODE(V, K, D)                                                                    \
-  err = hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<V, K, D>), dim3(tiles),    \
+#define CALL_DECODE(V, B, K, D)                                                                    \
+  err = hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<V, K, D, B>), dim3(tiles),    \
                         dim3(SGeo<K, D>::NT), args, 0, stream)
-  DL_VARIANTS(variant, dk, dv, CALL_DECODE);
+  DL_VARIANTS(variant, bf16_base, dk, dv, CALL_DECODE);
 #undef CALL_DECODE
   return err;
 }
 
-hipError_t launch_merge(int variant, int dk, int dv, int tiles, const PoolArgs& p, int min_fill,
-                        hipStream_t stream) {
+hipError_t launch_merge(int variant, bool bf16_base, int dk, int dv, int tiles, const PoolArgs& p,
+                        int min_fill, hipStream_t stream) {
   hipError_t err = hipSuccess;
   PoolArgs pa = p;
   int mf = min_fill;
   void* args[] = {&pa, &mf};
-#define CALL_MERGE(V, K, D)                                                                    \
-  err = hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<V, K, D>), dim3(tiles),    \
+#define CALL_MERGE(V, B, K, D)                                                                    \
+  err = hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<V, K, D, B>), dim3(tiles),    \
                         dim3(SGeo<K, D>::NT), args, 0, stream)
-  DL_VARIANTS(variant, dk, dv, CALL_MERGE);
+  DL_VARIANTS(variant, bf16_base, dk, dv, CALL_MERGE);
 #undef CALL_MERGE
   return err;
 }
 
-hipError_t launch_init(int variant, int dk, int dv, int tiles, const PoolArgs& p, const float* init_base,
-                       hipStream_t stream) {
+hipError_t launch_init(int variant, bool bf16_base, int dk, int dv, int tiles, const PoolArgs& p,
+                       const float* init_base, hipStream_t stream) {
   hipError_t err = hipSuccess;
   PoolArgs pa = p;
   const float* ib = init_base;
   void* args[] = {&pa, &ib};
-#define CALL_INIT(V, K, D)                                                                     \
-  err = hipLaunchKernel(reinterpret_cast<const void*>(&init_kernel<V, K, D>), dim3(tiles),     \
+#define CALL_INIT(V, B, K, D)                                                                     \
+  err = hipLaunchKernel(reinterpret_cast<const void*>(&init_kernel<V, K, D, B>), dim3(tiles),     \
                         dim3(256), args, 0, stream)
-  DL_VARIANTS(variant, dk, dv, CALL_INIT);
+  DL_VARIANTS(variant, bf16_base, dk, dv, CALL_INIT);
 #undef CALL_INIT
   return err;
 }

@@ -124,6 +124,34 @@ __device__ __forceinline__ float4 bload_factor4(__amdgpu_buffer_rsrc_t r, uint32
   return widen4(bload8(r, off));
 }
 
+// fp32 -> bf16 bits, round to nearest, ties to even (finite values).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// Access to the base in groups of four consecutive elements of a row: fp32, or
+// bf16 (the low-bit base, rounded to nearest even when written).
+template <bool BF>
+struct BaseIO;
+template <>
+struct BaseIO<false> {
+  using T = float;
+  __device__ static T* tile(void* base, size_t elem) { return static_cast<T*>(base) + elem; }
+  __device__ static float4 load(const T* t, size_t g) { return reinterpret_cast<const float4*>(t)[g]; }
+  __device__ static void store(T* t, size_t g, float4 x) { reinterpret_cast<float4*>(t)[g] = x; }
+};
+template <>
+struct BaseIO<true> {
+  using T = uint16_t;
+  __device__ static T* tile(void* base, size_t elem) { return static_cast<T*>(base) + elem; }
+  __device__ static float4 load(const T* t, size_t g) { return widen4(reinterpret_cast<const uint2*>(t)[g]); }
+  __device__ static void store(T* t, size_t g, float4 x) {
+    reinterpret_cast<uint2*>(t)[g] = make_uint2(f32_to_bf16_rne(x.x) | (f32_to_bf16_rne(x.y) << 16),
+                                                f32_to_bf16_rne(x.z) | (f32_to_bf16_rne(x.w) << 16));
+  }
+};
+
 __device__ __forceinline__ float step_log2_decay(float d) {
   return fmaxf(log2f(d), kMinLog2Decay);
 }
@@ -154,7 +182,7 @@ __device__ __forceinline__ float4 f4_mul(const float4 a, float s) {
 
 // Arguments of the decode and merge kernels.
 struct PoolArgs {
-  float* base;
+  void* base;  // fp32 or bf16 [tiles][dk][dv] (BaseIO)
   uint16_t* log_k;
   void* log_u;
   float* log_c;

@@ -8,12 +8,12 @@
 
 namespace dl {
 
-hipError_t launch_decode(int variant, int dk, int dv, int tiles, const PoolArgs& p, const StepArgs& s,
-                         hipStream_t stream);
-hipError_t launch_merge(int variant, int dk, int dv, int tiles, const PoolArgs& p, int min_fill,
-                        hipStream_t stream);
-hipError_t launch_init(int variant, int dk, int dv, int tiles, const PoolArgs& p, const float* init_base,
-                       hipStream_t stream);
+hipError_t launch_decode(int variant, bool bf16_base, int dk, int dv, int tiles, const PoolArgs& p,
+                         const StepArgs& s, hipStream_t stream);
+hipError_t launch_merge(int variant, bool bf16_base, int dk, int dv, int tiles, const PoolArgs& p,
+                        int min_fill, hipStream_t stream);
+hipError_t launch_init(int variant, bool bf16_base, int dk, int dv, int tiles, const PoolArgs& p,
+                       const float* init_base, hipStream_t stream);
 hipError_t launch_eager(int variant, int dk, int dv, int tiles, int heads, float* state, const StepArgs& s,
                         hipStream_t stream);
 

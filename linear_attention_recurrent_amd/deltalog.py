@@ -19,12 +19,14 @@ LIB_PATH = os.path.join(_HERE, "libdeltalog.so")
 
 GDN, KDA, RWKV6 = 0, 1, 2
 DL_OK, DL_EINVAL, DL_EUNSUPPORTED, DL_EALIGN, DL_EHIP = 0, -1, -2, -3, -4
+BASE_F32, BASE_BF16 = 0, 1
 MAX_LOG_LEN = 128
 
 
 class Dims(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("batch", ctypes.c_int32), ("heads", ctypes.c_int32),
-                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("log_len", ctypes.c_int32)]
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("log_len", ctypes.c_int32),
+                ("base_dtype", ctypes.c_int32)]
 
 
 class Pool(ctypes.Structure):
@@ -103,13 +105,13 @@ def _need(t: torch.Tensor, name: str, shape: tuple, dtype: torch.dtype, device) 
 class DeltaLogPool:
     """One layer's state pool: the device tensors of dl_pool plus its dims.
 
-    base  fp32 [B][H][dk][dv]; log_k bf16 [B][H][L][dk];
+    base  fp32 (base_dtype BASE_F32) or bf16 (BASE_BF16) [B][H][dk][dv]; log_k bf16 [B][H][L][dk];
     log_u fp32 (GDN/KDA) or bf16 (RWKV6) [B][H][L][dv];
     log_c fp32 [B][H][L][1 or dk]; fill int32 [B][H].
     """
 
     def __init__(self, variant: int, batch: int, heads: int, dk: int, dv: int, log_len: int,
-                 device="cuda"):
+                 device="cuda", base_dtype: int = BASE_F32):
         self.device = torch.device(device)
         if self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
@@ -118,13 +120,15 @@ class DeltaLogPool:
         B, H, L = self.batch, self.heads, self.log_len
         g = 1 if variant == GDN else dk
         kw = dict(device=self.device)
-        self.base = torch.empty((B, H, dk, dv), dtype=torch.float32, **kw)
+        self.base_dtype = int(base_dtype)
+        self.base = torch.empty((B, H, dk, dv), dtype=torch.bfloat16 if self.base_dtype == BASE_BF16
+                                else torch.float32, **kw)
         self.log_k = torch.empty((B, H, L, dk), dtype=torch.bfloat16, **kw)
         self.log_u = torch.empty((B, H, L, dv), dtype=torch.bfloat16 if variant == RWKV6 else torch.float32,
                                  **kw)
         self.log_c = torch.empty((B, H, L, g), dtype=torch.float32, **kw)
         self.fill = torch.empty((B, H), dtype=torch.int32, **kw)
-        self.c_dims = Dims(self.variant, B, H, self.dk, self.dv, L)
+        self.c_dims = Dims(self.variant, B, H, self.dk, self.dv, L, self.base_dtype)
         self.c_pool = Pool(self.base.data_ptr(), self.log_k.data_ptr(), self.log_u.data_ptr(),
                            self.log_c.data_ptr(), self.fill.data_ptr())
 
@@ -132,7 +136,8 @@ class DeltaLogPool:
         return dict(base=self.base, log_k=self.log_k, log_u=self.log_u, log_c=self.log_c, fill=self.fill)
 
     def clone(self) -> "DeltaLogPool":
-        other = DeltaLogPool(self.variant, self.batch, self.heads, self.dk, self.dv, self.log_len, self.device)
+        other = DeltaLogPool(self.variant, self.batch, self.heads, self.dk, self.dv, self.log_len, self.device,
+                             self.base_dtype)
         for name, t in self.tensors().items():
             getattr(other, name).copy_(t)
         return other
@@ -172,7 +177,7 @@ def dl_init_state(pool: DeltaLogPool, init_base: Optional[torch.Tensor] = None,
                   init_fill=None, stream=None) -> None:
     """Start the pool from `init_base` (or zeros) with per-sequence log fills `init_fill`."""
     if init_base is not None:
-        _need(init_base, "init_base", tuple(pool.base.shape), torch.float32, pool.device)
+        _need(init_base, "init_base", tuple(pool.base.shape), torch.float32, pool.device)  # always fp32
     fill_arr = None
     if init_fill is not None:
         vals = [int(x) for x in init_fill]
@@ -203,6 +208,6 @@ def dl_eager_step(variant: int, state: torch.Tensor, io: StepIO, stream=None) ->
     if state.dtype != torch.float32 or state.dim() != 4 or not state.is_contiguous() or not state.is_cuda:
         raise ValueError("state must be a contiguous fp32 cuda tensor [B][H][dk][dv]")
     B, H, dk, dv = state.shape
-    dims = Dims(int(variant), B, H, dk, dv, 1)
+    dims = Dims(int(variant), B, H, dk, dv, 1, BASE_F32)
     rc = load_library().dl_eager_step(ctypes.byref(dims), state.data_ptr(), ctypes.byref(io), _stream(stream))
     _check(rc, "dl_eager_step")

@@ -46,20 +46,21 @@ class Uploaded:
         return self.ios[t % self.inp.pool]
 
 
-def new_pool(inp, log_len=None, fill0=None, up: Uploaded = None):
+def new_pool(inp, log_len=None, fill0=None, up: Uploaded = None, base_dtype=dl.BASE_F32):
     L = inp.log_len if log_len is None else log_len
-    pool = dl.DeltaLogPool(inp.variant, inp.batch, inp.heads, inp.dk, inp.dv, L, dev())
+    pool = dl.DeltaLogPool(inp.variant, inp.batch, inp.heads, inp.dk, inp.dv, L, dev(), base_dtype)
     dl.dl_init_state(pool, up.s0 if up is not None else torch.from_numpy(inp.s0).to(dev()),
                      inp.fill0 if fill0 is None else fill0)
     return pool
 
 
-def run_deltalog(inp, steps, log_len=None, sel=None, up: Uploaded = None, every_step=None):
+def run_deltalog(inp, steps, log_len=None, sel=None, up: Uploaded = None, every_step=None,
+                 base_dtype=dl.BASE_F32):
     """Run `steps` decode steps; return (pool, outputs) with outputs float32 numpy
     [steps][tiles][dv] for the tiles in `sel` (list of (b, h)), or all tiles if None.
     every_step(t, pool) is called after each step when given."""
     up = up or Uploaded(inp)
-    pool = new_pool(inp, log_len, up=up)
+    pool = new_pool(inp, log_len, up=up, base_dtype=base_dtype)
     if sel is None:
         idx = None
         outs = torch.empty((steps, inp.batch * inp.heads, inp.dv), dtype=torch.float32, device=dev())
@@ -99,4 +100,4 @@ def materialized_state(pool) -> np.ndarray:
     dl.dl_merge(c, 1)
     torch.cuda.synchronize()
     assert int(c.fill.max().item()) == 0
-    return c.base.cpu().numpy()
+    return c.base.float().cpu().numpy()

@@ -54,8 +54,8 @@ A = 0x10000      # 16-byte aligned
 M = 0x10004      # misaligned
 
 
-def _dims(dl, variant=0, batch=2, heads=2, dk=128, dv=128, L=16):
-    return dl.Dims(variant, batch, heads, dk, dv, L)
+def _dims(dl, variant=0, batch=2, heads=2, dk=128, dv=128, L=16, base_dtype=0):
+    return dl.Dims(variant, batch, heads, dk, dv, L, base_dtype)
 
 
 def _pool(dl, base=A):
@@ -78,7 +78,8 @@ def test_dims_errors(lib):
     bad = [(dict(variant=3), dl.DL_EINVAL), (dict(variant=-1), dl.DL_EINVAL), (dict(batch=-1), dl.DL_EINVAL),
            (dict(heads=0), dl.DL_EINVAL), (dict(L=0), dl.DL_EINVAL), (dict(L=129), dl.DL_EINVAL),
            (dict(dk=96), dl.DL_EUNSUPPORTED), (dict(dv=256), dl.DL_EUNSUPPORTED),
-           (dict(batch=1 << 20, heads=1 << 12), dl.DL_EINVAL)]
+           (dict(batch=1 << 20, heads=1 << 12), dl.DL_EINVAL),
+           (dict(base_dtype=2), dl.DL_EINVAL), (dict(base_dtype=-1), dl.DL_EINVAL)]
     for kw, code in bad:
         assert _decode(lib, _dims(dl, **kw), _pool(dl), _io(dl)) == code, kw
     assert lib.dl_decode_step(None, ctypes.byref(_pool(dl)), ctypes.byref(_io(dl)), None) == dl.DL_EINVAL
@@ -121,6 +122,9 @@ def test_merge_init_eager_errors(lib):
     assert lib.dl_init_state(ctypes.byref(d), ctypes.byref(p), M, None, None) == dl.DL_EALIGN
     assert lib.dl_eager_step(ctypes.byref(d), None, ctypes.byref(_io(dl)), None) == dl.DL_EINVAL
     assert lib.dl_eager_step(ctypes.byref(d), M, ctypes.byref(_io(dl)), None) == dl.DL_EALIGN
+    # the eager comparator keeps an fp32 state only
+    dbf = _dims(dl, base_dtype=dl.BASE_BF16)
+    assert lib.dl_eager_step(ctypes.byref(dbf), A, ctypes.byref(_io(dl)), None) == dl.DL_EUNSUPPORTED
 
 
 def test_batch_zero_returns_ok_without_looking_at_pointers(lib):
