@@ -94,14 +94,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_profile_name(workload_name: str, bf16_base: bool) -> str:
-    return f"decode_{workload_name}{'_bf16base' if bf16_base else ''}_counters.txt"
+def counter_profile_name(workload_name: str, bf16_base: bool, log_len=None) -> str:
+    tag = "" if log_len is None else f"_L{log_len}"
+    return f"decode_{workload_name}{tag}{'_bf16base' if bf16_base else ''}_counters.txt"
 
 
-def read_counter_profile(workload_name: str, bf16_base: bool = False):
+def read_counter_profile(workload_name: str, bf16_base: bool = False, log_len=None):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source (else None)."""
-    path = os.path.join(PROFILE_DIR, counter_profile_name(workload_name, bf16_base))
+    path = os.path.join(PROFILE_DIR, counter_profile_name(workload_name, bf16_base, log_len))
     if not os.path.exists(path):
         return None
     vals = {}
@@ -219,12 +220,93 @@ def time_loop(fn, steps, warmup, graph_chunk=0):
     return start.elapsed_time(end) / 1e3
 
 
+def serving_leg(args, cpu) -> dict:
+    """The 48-layer serving pool: one pool per layer (B = 512, H = 32, 128/128, ragged
+    start fills shared by a sequence's layers), one step = one dl_decode_step per layer.
+    A pool of drawn step inputs is reused across steps and layers (values do not change
+    the traffic).  The eager comparator keeps one fp32 state per layer."""
+    import torch
+
+    from linear_attention_recurrent_amd import deltalog as dl
+    w = WORKLOADS[5]
+    layers = w["layers"]
+    P = min(args.pool_slots, 16)
+    inp, T, ios, _ = gpu_setup(5, P, args.log_len)
+    B, H, dk, dv, L, var = inp.batch, inp.heads, inp.dk, inp.dv, inp.log_len, inp.variant
+    tiles = B * H
+    dev = torch.device("cuda", 0)
+    bf16_base = args.base_dtype == "bf16"
+    base_dt = dl.BASE_BF16 if bf16_base else dl.BASE_F32
+    pools = [dl.DeltaLogPool(var, B, H, dk, dv, L, dev, base_dt) for _ in range(layers)]
+    for p_ in pools:
+        dl.dl_init_state(p_, T["s0"], inp.fill0)
+    K, W = args.steps, args.warmup
+
+    def step(t):
+        io = ios[t % P]
+        for p_ in pools:
+            dl.dl_decode_step(p_, io)
+    secs = time_loop(step, K, W)
+    del pools
+    torch.cuda.empty_cache()
+    Ke = max(1, K // 4)
+    states = [T["s0"].clone() for _ in range(layers)]
+
+    def eager(t):
+        io = ios[t % P]
+        for st in states:
+            dl.dl_eager_step(var, st, io)
+    secs_e = time_loop(eager, Ke, min(W, 4))
+    del states
+
+    mdl = deltalog_bytes_per_state_step(var, dk, dv, L, B, 2 if bf16_base else 4)
+    eag = eager_bytes_per_state_step(var, dk, dv, B)
+    t_step, t_eager = secs / K, secs_e / Ke
+    work = tiles * layers
+    achieved = mdl["total"] * tiles / (t_step / layers) / 1e9
+    prof = read_counter_profile(w["name"], bf16_base, L)
+    traffic = None
+    if prof is not None:
+        traffic = float(prof["fetch_bytes_per_launch"]) + float(prof["write_bytes_per_launch"])
+    return {
+        "metric": "decode state-steps/s (B×H×layers per s)",
+        "value": work / t_step,
+        "unit": "state-steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{w['name']}: GDN decode, {layers} layers, B={B} H={H} dk={dk} dv={dv} "
+                               f"L={L}, ragged start fills U{{0..L-1}} per sequence"
+                               + (", bf16 base" if bf16_base else ""),
+                   "base": "bf16, rounded at each fold" if bf16_base else "f32",
+                   "variant": VARIANT_NAMES[var], "layers": layers, "batch": B, "heads": H, "dk": dk,
+                   "dv": dv, "log_len": L, "input_pool_steps": P},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+        "cpu_baseline": cpu,
+        "bytes_per_state_step_model": {"deltalog": mdl["total"], "eager": eag["total"]},
+        "state_write_bytes_per_state_step": {
+            "deltalog_model": mdl["state_writes"], "eager_model": eag["state_writes"],
+            "cut_model": eag["state_writes"] / mdl["state_writes"]},
+        "eager": {"value": work / t_eager, "ms_per_step": t_eager * 1e3, "steps": Ke,
+                  "hbm_gbs_algorithmic": eag["total"] * work / t_eager / 1e9,
+                  "deltalog_speedup": t_eager / t_step},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 6])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6],
+                    help="5 = the 48-layer serving pool (B=512, ragged fills); --log-len picks its L")
     ap.add_argument("--log-len", type=int, default=None)
     ap.add_argument("--pool-slots", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -263,6 +345,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_each_way": n, "launches": 5}))
+        return
+
+    if args.workload == 5:
+        print(json.dumps(serving_leg(args, cpu)))
         return
 
     inp, T, ios, w = gpu_setup(args.workload, args.pool_slots, args.log_len)
