@@ -153,6 +153,37 @@ int dl_merge(const dl_dims *dims, const dl_pool *pool, int32_t min_fill, void *s
  * DL_BASE_F32 (else DL_EUNSUPPORTED). */
 int dl_eager_step(const dl_dims *dims, float *state, const dl_step_io *io, void *stream);
 
+/* A prompt's inputs and outputs for dl_prefill (all device).  T = tokens >= 0;
+ * row t of a sequence is its t-th prompt token. */
+typedef struct {
+  const uint16_t *q;   /* bf16 [batch][T][heads][dk]                                           */
+  const uint16_t *k;   /* bf16 [batch][T][heads][dk]                                           */
+  const uint16_t *v;   /* bf16 [batch][T][heads][dv]                                           */
+  const float *decay;  /* GDN: fp32 [batch][T][heads] alpha, in (0, 1]                          */
+  const float *beta;   /* GDN: fp32 [batch][T][heads]; or NULL with eta                         */
+  float *out;          /* fp32 [batch][T][heads][dv]  every token's output (written)            */
+  const float *eta;    /* GDN, instead of beta: fp32 [batch][T][heads], the Kaczmarz step size
+                          beta = eta / (||k||^2 + eps) (Kaczmarz Linear Attention abstract)    */
+  float eps;           /* >= 0 (ignored when eta is NULL)                                       */
+  int32_t tokens;      /* T                                                                     */
+} dl_prefill_io;
+
+/* Prefill: run the recurrence over T prompt tokens for every (sequence, head),
+ * starting from the dense state the pool stands for, and leave the state after
+ * the last token in the base with an empty log, ready for dl_decode_step.  Every
+ * token's output is written.  The result equals T eager steps; it is computed
+ * chunk by chunk in the chunkwise-parallel form that the Q-Delta, Kaczmarz
+ * Linear Attention and Gated DeltaNet-2 abstracts (card pages) name for
+ * delta-rule models: within a chunk, the delta-rule writes come from a
+ * triangular solve (the WY form) and every product with the state is a matrix
+ * product.  Any non-empty log is folded into the base first, as dl_merge with
+ * min_fill = 1 would.  With a bf16 base the final state is rounded once.
+ * GDN only (dims->variant must be DL_GDN, else DL_EUNSUPPORTED).  Errors:
+ * DL_EINVAL for tokens < 0, null q/k/v/decay/out, or eps < 0 with eta set;
+ * DL_EUNSUPPORTED unless exactly one of beta and eta is given.  tokens == 0
+ * only folds the logs and looks at no prompt pointer. */
+int dl_prefill(const dl_dims *dims, const dl_pool *pool, const dl_prefill_io *io, void *stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char *dl_status_string(int status);
 

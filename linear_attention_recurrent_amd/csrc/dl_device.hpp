@@ -191,6 +191,20 @@ struct PoolArgs {
   int L;
 };
 
+// Arguments of the prefill kernel: a prompt of `tokens` rows per sequence,
+// [batch][tokens][heads][d] for q, k, v, out and [batch][tokens][heads] for decay, beta, eta.
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* decay;
+  const float* beta;
+  const float* eta;
+  float* out;
+  float eps;
+  int tokens;
+};
+
 struct StepArgs {
   const uint16_t* q;
   const uint16_t* k;

@@ -1,7 +1,7 @@
 """Python binding of libdeltalog.so: argument marshalling only.
 
-The four calls have the C names and meanings declared in include/deltalog.h
-(dl_init_state, dl_decode_step, dl_merge, dl_eager_step).  PyTorch supplies
+The calls have the C names and meanings declared in include/deltalog.h
+(dl_init_state, dl_decode_step, dl_merge, dl_eager_step, dl_prefill).  PyTorch supplies
 device memory and the stream; every step of the decode path runs in the HIP
 kernels of libdeltalog.so.  There is no CPU fallback: if the library is not
 built, or no GPU is present, these calls raise.
@@ -40,6 +40,12 @@ class StepIO(ctypes.Structure):
                 ("out", ctypes.c_void_p), ("eta", ctypes.c_void_p), ("eps", ctypes.c_float)]
 
 
+class PrefillIO(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("decay", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("eta", ctypes.c_void_p), ("eps", ctypes.c_float), ("tokens", ctypes.c_int32)]
+
+
 class DeltaLogError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__(f"{what}: {status_string(status)} ({status})")
@@ -64,9 +70,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dl_decode_step.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Pool), ctypes.POINTER(StepIO), vp]
     lib.dl_merge.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Pool), ctypes.c_int32, vp]
     lib.dl_eager_step.argtypes = [ctypes.POINTER(Dims), vp, ctypes.POINTER(StepIO), vp]
+    lib.dl_prefill.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Pool), ctypes.POINTER(PrefillIO), vp]
     lib.dl_status_string.argtypes = [ctypes.c_int]
     lib.dl_status_string.restype = ctypes.c_char_p
-    for f in (lib.dl_init_state, lib.dl_decode_step, lib.dl_merge, lib.dl_eager_step):
+    for f in (lib.dl_init_state, lib.dl_decode_step, lib.dl_merge, lib.dl_eager_step, lib.dl_prefill):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -211,3 +218,28 @@ def dl_eager_step(variant: int, state: torch.Tensor, io: StepIO, stream=None) ->
     dims = Dims(int(variant), B, H, dk, dv, 1, BASE_F32)
     rc = load_library().dl_eager_step(ctypes.byref(dims), state.data_ptr(), ctypes.byref(io), _stream(stream))
     _check(rc, "dl_eager_step")
+
+
+def make_prefill_io(pool: DeltaLogPool, q, k, v, decay, beta, out, eta=None, eps=0.0) -> PrefillIO:
+    """Check a prompt's tensors ([batch][T][heads][...], see dl_prefill_io) against the pool."""
+    B, H, dk, dv = pool.batch, pool.heads, pool.dk, pool.dv
+    if k is None or k.dim() != 4:
+        raise ValueError("k must be a [batch][T][heads][dk] tensor")
+    T = int(k.shape[1])
+    dev = pool.device
+    _need(q, "q", (B, T, H, dk), torch.bfloat16, dev)
+    _need(k, "k", (B, T, H, dk), torch.bfloat16, dev)
+    _need(v, "v", (B, T, H, dv), torch.bfloat16, dev)
+    _need(decay, "decay", (B, T, H), torch.float32, dev)
+    if (beta is None) == (eta is None):
+        raise ValueError("give exactly one of beta and eta")
+    _need(beta if eta is None else eta, "beta" if eta is None else "eta", (B, T, H), torch.float32, dev)
+    _need(out, "out", (B, T, H, dv), torch.float32, dev)
+    return PrefillIO(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta), _ptr(out), _ptr(eta), float(eps), T)
+
+
+def dl_prefill(pool: DeltaLogPool, io: PrefillIO, stream=None) -> None:
+    """Run a prompt through every tile (chunkwise) and leave the state in the base, log empty."""
+    rc = load_library().dl_prefill(ctypes.byref(pool.c_dims), ctypes.byref(pool.c_pool), ctypes.byref(io),
+                                   _stream(stream))
+    _check(rc, "dl_prefill")

@@ -25,11 +25,11 @@ def lib():
     return deltalog.load_library()
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_the_calls():
     names = declared_functions()
-    for n in ("dl_init_state", "dl_decode_step", "dl_merge", "dl_eager_step", "dl_status_string"):
+    for n in ("dl_init_state", "dl_decode_step", "dl_merge", "dl_eager_step", "dl_prefill", "dl_status_string"):
         assert n in names
-    assert len(names) == 5, names
+    assert len(names) == 6, names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -146,3 +146,37 @@ def test_product_path_does_not_use_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert not re.search(r"(^|[^A-Za-z])_work/", text), f
+
+
+def _pio(dl, T=8, **kw):
+    f = dict(q=A, k=A, v=A, decay=A, beta=A, out=A, eta=None, eps=0.0)
+    f.update(kw)
+    return dl.PrefillIO(f["q"], f["k"], f["v"], f["decay"], f["beta"], f["out"], f["eta"], f["eps"], T)
+
+
+def _prefill(lib, dims, pool, io):
+    return lib.dl_prefill(ctypes.byref(dims), ctypes.byref(pool), ctypes.byref(io), None)
+
+
+def test_prefill_errors(lib):
+    from linear_attention_recurrent_amd import deltalog as dl
+    d = _dims(dl)
+    p = _pool(dl)
+    assert _prefill(lib, d, p, _pio(dl, T=-1)) == dl.DL_EINVAL
+    assert lib.dl_prefill(ctypes.byref(d), ctypes.byref(p), None, None) == dl.DL_EINVAL
+    assert _prefill(lib, _dims(dl, variant=1), p, _pio(dl)) == dl.DL_EUNSUPPORTED  # GDN only
+    assert _prefill(lib, _dims(dl, variant=2, dk=64, dv=64), p, _pio(dl)) == dl.DL_EUNSUPPORTED
+    assert _prefill(lib, d, p, _pio(dl, q=None)) == dl.DL_EINVAL
+    assert _prefill(lib, d, p, _pio(dl, out=None)) == dl.DL_EINVAL
+    assert _prefill(lib, d, p, _pio(dl, beta=None)) == dl.DL_EUNSUPPORTED       # neither beta nor eta
+    assert _prefill(lib, d, p, _pio(dl, eta=A)) == dl.DL_EUNSUPPORTED           # both
+    assert _prefill(lib, d, p, _pio(dl, beta=None, eta=A, eps=-1.0)) == dl.DL_EINVAL
+    assert _prefill(lib, d, p, _pio(dl, k=M)) == dl.DL_EALIGN
+    assert _prefill(lib, d, p, _pio(dl, decay=A + 2)) == dl.DL_EALIGN
+    assert _prefill(lib, d, _pool(dl, base=M), _pio(dl)) == dl.DL_EALIGN
+    assert _prefill(lib, d, dl.Pool(A, None, A, A, A), _pio(dl)) == dl.DL_EINVAL
+    # an empty prompt needs no prompt pointers (it only folds): checked up to the pool
+    assert _prefill(lib, d, dl.Pool(A, None, A, A, A), _pio(dl, T=0, q=None, k=None, v=None, out=None)) == dl.DL_EINVAL
+    # batch 0: nothing is looked at
+    empty = dl.Pool(None, None, None, None, None)
+    assert _prefill(lib, _dims(dl, batch=0), empty, _pio(dl, q=None, k=None, v=None, out=None)) == dl.DL_OK

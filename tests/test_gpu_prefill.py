@@ -1,0 +1,162 @@
+"""dl_prefill (chunkwise GDN prefill on MFMA) against the fp64 eager oracle (GPU).
+
+A prompt of T tokens is the workload's first T drawn steps; the oracle runs the
+same T eager steps.  Outputs (one per token) and the final state (the base,
+log empty) must be within 1e-4 per tensor.  Chunks are 32 tokens, so T covers
+a single token, one token short of and past a chunk, several chunks and a long
+prompt.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_harness import Uploaded, dev, materialized_state, new_pool
+from inputs import make_inputs
+from linear_attention_recurrent_amd import deltalog as dl
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU is required for the gpu-marked tests")
+    dl.load_library()
+
+
+def _close(what, got, ref, axes, tol=TOL):
+    err = oracle.rel_err(got, ref, axes)
+    print(f"{what}: max per-tensor rel err {err:.3e}", flush=True)
+    assert err <= tol, (what, err)
+    return err
+
+
+def prompt(up: Uploaded, t0: int, T: int):
+    """Steps t0 .. t0+T-1 of an uploaded workload as [batch][T][heads][...] prompt tensors."""
+    sl = slice(t0, t0 + T)
+    tm = lambda x: None if x is None else x[sl].transpose(0, 1).contiguous()
+    return dict(q=tm(up.q), k=tm(up.k), v=tm(up.v), decay=tm(up.decay), beta=tm(up.beta), eta=tm(up.eta))
+
+
+def run_prefill(pool, up, t0, T, eps=0.0):
+    p = prompt(up, t0, T)
+    inp = up.inp
+    out = torch.full((inp.batch, T, inp.heads, inp.dv), float("nan"), dtype=torch.float32, device=dev())
+    io = dl.make_prefill_io(pool, p["q"], p["k"], p["v"], p["decay"], p["beta"], out, p["eta"], eps)
+    dl.dl_prefill(pool, io)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().transpose(1, 0, 2, 3)  # [T][batch][heads][dv]
+
+
+def check_prefill(inp, T, base_dtype=dl.BASE_F32):
+    up = Uploaded(inp)
+    pool = new_pool(inp, up=up, base_dtype=base_dtype)
+    outs = run_prefill(pool, up, 0, T, inp.eps)
+    assert int(pool.fill.max().item()) == 0
+    ref_S, ref_o = oracle.run_eager(inp, T)
+    _close(f"outputs T={T}", outs, ref_o, (-1,))
+    _close(f"state T={T}", pool.base.float().cpu().numpy(), ref_S, (-2, -1))
+    return pool, up
+
+
+@pytest.mark.parametrize("T", [1, 31, 32, 33, 100, 4096])
+def test_gdn_prefill_lengths(T):
+    inp = make_inputs(2, T, batch=2, heads=4, pool=T)
+    check_prefill(inp, T)
+
+
+def test_gdn_smoke_shape():
+    inp = make_inputs(1, 64, pool=64)
+    check_prefill(inp, 64)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
+def test_head_size_combinations(dk, dv):
+    inp = make_inputs(2, 97, batch=2, heads=3, pool=97, dk=dk, dv=dv)
+    check_prefill(inp, 97)
+
+
+def test_kaczmarz_step_size():
+    inp = make_inputs(6, 300, batch=2, heads=4, pool=300)
+    assert inp.eta is not None
+    check_prefill(inp, 300)
+
+
+def test_zero_and_unit_decay_tokens():
+    inp = make_inputs(2, 70, batch=2, heads=2, pool=70)
+    inp.decay[5] = 0.0          # a token that resets every state
+    inp.decay[40:45] = 1.0      # no decay
+    inp.beta[50:52] = 0.0       # no write
+    check_prefill(inp, 70)
+
+
+def test_decode_continues_after_prefill():
+    """Prefill 100 tokens, then 40 decode steps (two folds at L = 16): same as 140 eager steps."""
+    inp = make_inputs(2, 140, batch=2, heads=4, pool=140)
+    up = Uploaded(inp)
+    pool = new_pool(inp, up=up)
+    run_prefill(pool, up, 0, 100)
+    outs = []
+    for t in range(100, 140):
+        dl.dl_decode_step(pool, up.io(t))
+        outs.append(up.out.cpu().numpy())
+    ref_S, ref_o = oracle.run_eager(inp, 140)
+    _close("decode outputs after prefill", np.stack(outs), ref_o[100:], (-1,))
+    _close("state after prefill + decode", materialized_state(pool), ref_S, (-2, -1))
+
+
+def test_prefill_folds_a_pending_log_first():
+    """Decode steps from ragged fills leave logs non-empty; prefill folds them, then runs the prompt."""
+    inp = make_inputs(2, 90, batch=3, heads=2, pool=90, log_len=16, fill0=np.array([0, 5, 11], np.int32))
+    up = Uploaded(inp)
+    pool = new_pool(inp, up=up)
+    for t in range(10):
+        dl.dl_decode_step(pool, up.io(t))
+    assert int(pool.fill.max().item()) > 0
+    outs = run_prefill(pool, up, 10, 80)
+    assert int(pool.fill.max().item()) == 0
+    ref_S, ref_o = oracle.run_eager(inp, 90)
+    _close("prompt outputs after decode", outs, ref_o[10:], (-1,))
+    _close("state", pool.base.cpu().numpy(), ref_S, (-2, -1))
+    # an empty prompt only folds
+    for t in range(10):
+        dl.dl_decode_step(pool, up.io(t))
+    want = materialized_state(pool)
+    out = torch.empty((inp.batch, 0, inp.heads, inp.dv), dtype=torch.float32, device=dev())
+    p = prompt(up, 0, 0)
+    dl.dl_prefill(pool, dl.make_prefill_io(pool, p["q"], p["k"], p["v"], p["decay"], p["beta"], out))
+    torch.cuda.synchronize()
+    assert int(pool.fill.max().item()) == 0
+    assert np.array_equal(pool.base.cpu().numpy(), want)
+
+
+def test_bf16_base_prefill():
+    """With a bf16 base the prompt starts from the rounded state and the final state is rounded once."""
+    T = 200
+    inp = make_inputs(2, T, batch=2, heads=4, pool=T)
+    up = Uploaded(inp)
+    pool = new_pool(inp, up=up, base_dtype=dl.BASE_BF16)
+    outs = run_prefill(pool, up, 0, T)
+    s0 = oracle.round_to_bf16(inp.s0.astype(np.float64))
+    ref_S, ref_o = oracle.run_eager(inp, T, s0=s0)
+    _close("outputs, bf16 base", outs, ref_o, (-1,))
+    got = pool.base.float().cpu().numpy().astype(np.float64)
+    ref = oracle.round_to_bf16(ref_S)
+    same = float(np.mean(got == ref))
+    print(f"final base: {same:.4%} bit-equal to the rounded oracle state", flush=True)
+    assert same >= 0.99
+    _, e = np.frexp(np.maximum(np.abs(got), np.abs(ref)))
+    slack = 1e-5 * np.max(np.abs(ref), axis=(-2, -1), keepdims=True)
+    assert np.all(np.abs(got - ref) <= np.ldexp(1.0, e - 8) + slack)
+
+
+def test_reruns_are_bit_identical():
+    inp = make_inputs(2, 77, batch=2, heads=2, pool=77)
+    up = Uploaded(inp)
+    res = []
+    for _ in range(2):
+        pool = new_pool(inp, up=up)
+        res.append((run_prefill(pool, up, 0, 77), pool.base.cpu().numpy()))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
