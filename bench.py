@@ -220,6 +220,63 @@ def time_loop(fn, steps, warmup, graph_chunk=0):
     return start.elapsed_time(end) / 1e3
 
 
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD's published figure
+PREFILL_CHUNK = 32
+
+
+def prefill_model(dk: int, dv: int, C: int = PREFILL_CHUNK) -> dict:
+    """Per (sequence, head, prompt token): HBM bytes, the chunkwise method's flops, and the
+    bf16 MFMA flops the kernel issues (fp32 operands split in two: 2 or 3 products each)."""
+    byts = 2 * dk * 2 + 2 * dv + 4 + 4 + 4 * dv  # q, k, v bf16; decay, beta; fp32 output
+    method = 2 * C * C * dk * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 3  # per chunk
+    # issued per chunk: K K^T, Q K^T lower blocks (3 of 4 each), W (x2), U~ (x2), W S (x3),
+    # Q S (x2), (M o Q K^T) U (x3), K^T U (x2)
+    issued = (2 * 3 * 16 * 16 * dk * 2 + 2 * C * C * dk * 2 + 2 * C * C * dv * 2
+              + 2 * C * dk * dv * 3 + 2 * C * dk * dv * 2 + 2 * C * C * dv * 3 + 2 * C * dk * dv * 2)
+    return {"bytes": byts, "method_flops": method / C, "issued_flops": issued / C}
+
+
+def prefill_leg(args, inp, Tn, base_dt, reps: int = 5) -> dict:
+    """Time dl_prefill of a prompt of --prefill-tokens tokens on every tile of the workload
+    (prompt rows cycle over the drawn steps already on the device)."""
+    import torch
+
+    from linear_attention_recurrent_amd import deltalog as dl
+    B, H, dk, dv, L = inp.batch, inp.heads, inp.dk, inp.dv, inp.log_len
+    Tp = args.prefill_tokens
+    dev = torch.device("cuda", 0)
+    P = Tn["q"].shape[0]
+    idx = torch.arange(Tp, device=dev) % P
+    tm = lambda x: None if x is None else x.index_select(0, idx).transpose(0, 1).contiguous()
+    q, k, v, decay, beta, eta = (tm(Tn[n]) for n in ("q", "k", "v", "decay", "beta", "eta"))
+    out = torch.empty((B, Tp, H, dv), dtype=torch.float32, device=dev)
+    pool = dl.DeltaLogPool(inp.variant, B, H, dk, dv, L, dev, base_dt)
+    dl.dl_init_state(pool, Tn["s0"], None)
+    io = dl.make_prefill_io(pool, q, k, v, decay, beta, out, eta, inp.eps)
+    for _ in range(2):
+        dl.dl_prefill(pool, io)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(reps):
+        dl.dl_prefill(pool, io)
+    end.record(stream)
+    torch.cuda.synchronize()
+    secs = start.elapsed_time(end) / 1e3 / reps
+    m = prefill_model(dk, dv)
+    units = B * H * Tp
+    gbs = m["bytes"] * units / secs / 1e9
+    tf_issued = m["issued_flops"] * units / secs / 1e12
+    return {"value": units / secs, "unit": "state-steps/s (B x H x prompt tokens per s)",
+            "ms_per_prefill": secs * 1e3, "tokens": Tp, "reps": reps,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+            "mfma": {"issued_tflops": tf_issued, "peak": BF16_MFMA_PEAK_TFLOPS, "frac": tf_issued / BF16_MFMA_PEAK_TFLOPS,
+                     "method_tflops": m["method_flops"] * units / secs / 1e12},
+            "bytes_per_state_step": m["bytes"], "issued_flops_per_state_step": m["issued_flops"]}
+
+
 def serving_leg(args, cpu) -> dict:
     """The 48-layer serving pool: one pool per layer (B = 512, H = 32, 128/128, ragged
     start fills shared by a sequence's layers), one step = one dl_decode_step per layer.
@@ -311,8 +368,10 @@ def main():
     ap.add_argument("--pool-slots", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step loop as a HIP graph")
-    ap.add_argument("--only", choices=["deltalog", "eager", "copy"], default=None,
+    ap.add_argument("--only", choices=["deltalog", "eager", "copy", "prefill"], default=None,
                     help="run one leg only (for profiling runs)")
+    ap.add_argument("--prefill-tokens", type=int, default=4096,
+                    help="prompt length of the prefill leg (GDN workloads)")
     ap.add_argument("--base-dtype", choices=["f32", "bf16"], default="f32",
                     help="storage of the dense base: fp32 (exact path) or bf16 (low-bit base, "
                          "rounded at each fold; log and arithmetic stay fp32)")
@@ -375,8 +434,13 @@ def main():
         state = T["s0"].clone()
         secs_e = time_loop(lambda t: dl.dl_eager_step(var, state, ios[t % P]), K, W, chunk)
         result["eager"] = secs_e
+    if args.only == "prefill" or (args.only is None and var == 0):
+        result["prefill"] = prefill_leg(args, inp, T, base_dt)
     if args.only is not None:
-        print(json.dumps({k: v / K * 1e3 for k, v in result.items()} | {"unit": "ms per step"}))
+        if args.only == "prefill":
+            print(json.dumps(result["prefill"]))
+        else:
+            print(json.dumps({k: v / K * 1e3 for k, v in result.items()} | {"unit": "ms per step"}))
         return
 
     # cache-cold variant: three independent pools used in turn
@@ -438,6 +502,7 @@ def main():
         "cold_three_pools": {"value": tiles / t_cold, "ms_per_step": t_cold * 1e3,
                              "hbm_gbs_algorithmic": mdl["total"] * tiles / t_cold / 1e9,
                              "frac": mdl["total"] * tiles / t_cold / 1e9 / HBM_PEAK_GBS},
+        "prefill": result.get("prefill"),
     }
     print(json.dumps(line))
 

@@ -29,6 +29,8 @@
 // B[8g + s][n] for s < 8; the result holds D[4g + r][n] for r < 4.  Sums over k
 // may pair any k order consistently between A and B; the state and U feed the
 // B operand straight from accumulator registers with k = {4g + r} u {16 + 4g + r}.
+// K and V are also kept token-major in LDS so that every operand is read with
+// 8- or 16-byte LDS loads.
 #include "launch.hpp"
 
 namespace dl {
@@ -62,27 +64,6 @@ __device__ __forceinline__ bf16x8 ld_2x64(const uint16_t* p0, const uint16_t* p1
   return pack8(a.x, a.y, b.x, b.y);
 }
 
-// Eight bf16 at a stride (a column of a row-major LDS array).
-__device__ __forceinline__ bf16x8 ld_col8(const uint16_t* p, int stride) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = uint32_t(p[(2 * i) * stride]) | (uint32_t(p[(2 * i + 1) * stride]) << 16);
-  return pack8(w[0], w[1], w[2], w[3]);
-}
-
-// Column `n` of a row-major LDS array at the paired token order {4g + s} u {16 + 4g + s}.
-__device__ __forceinline__ bf16x8 ld_col_paired(const uint16_t* col, int stride, int g) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint16_t* a = col + (4 * g + 2 * i) * stride;
-    const uint16_t* b = col + (16 + 4 * g + 2 * i) * stride;
-    w[i] = uint32_t(a[0]) | (uint32_t(a[stride]) << 16);
-    w[2 + i] = uint32_t(b[0]) | (uint32_t(b[stride]) << 16);
-  }
-  return pack8(w[0], w[1], w[2], w[3]);
-}
-
 // fp32 -> bf16 hi + lo (bit patterns).
 __device__ __forceinline__ void split(float x, uint32_t& hi, uint32_t& lo) {
   hi = f32_to_bf16_rne(x);
@@ -101,50 +82,72 @@ __device__ __forceinline__ void split_pair(const float (&x0)[4], const float (&x
   lo = pack8(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
 }
 
+// One state element of a tile through a buffer resource over that tile: the
+// per-lane part of the offset is one VGPR and the rest an immediate, so the 64
+// addresses of a lane's state elements are never materialised as registers.
 template <bool BF>
-__device__ __forceinline__ float ld_base(const void* base, size_t i) {
-  if constexpr (BF) return bf16_to_f32(static_cast<const uint16_t*>(base)[i]);
-  else return static_cast<const float*>(base)[i];
+__device__ __forceinline__ float ld_base(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  if constexpr (BF) return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
+  else return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
 template <bool BF>
-__device__ __forceinline__ void st_base(void* base, size_t i, float x) {
-  if constexpr (BF) static_cast<uint16_t*>(base)[i] = static_cast<uint16_t>(f32_to_bf16_rne(x));
-  else static_cast<float*>(base)[i] = x;
+__device__ __forceinline__ void st_base(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, float x) {
+  if constexpr (BF)
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(f32_to_bf16_rne(x)), r, voff, soff, 0);
+  else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
 }
+
+// Token-major copies of K and V (one row per channel, tokens along the row) are
+// stored with the token index XORed by 8 ((channel / 8) mod 4): a group of 8 (or
+// 4) consecutive tokens stays contiguous, and the transposing 2-byte stores of
+// the 16 lanes that share a token spread over the LDS banks.
+__device__ __forceinline__ int tswz(int ch, int tok) { return tok ^ (((ch >> 3) & 3) << 3); }
 
 template <int DK, int DV>
 struct PrefillLds {
   static constexpr int C = kChunk;
   static constexpr int KS = DK + 8;  // bf16 row stride of the K, Q and W arrays (16-byte pad)
-  static constexpr int VS = DV + 8;  // bf16 row stride of V
+  static constexpr int TS = C + 8;   // bf16 row stride of the token-major K and V
   static constexpr int MS = C + 1;   // fp32 row stride of the C x C matrices
   static constexpr int BS = C + 8;   // bf16 row stride of the split C x C matrices
-  uint16_t k[C * KS];
-  uint16_t q[C * KS];
-  uint16_t v[C * VS];
-  uint16_t wh[C * KS], wl[C * KS];  // W = T diag(b g) K, split
-  float g[C * MS];                   // K K^T, then A (strictly lower part)
-  float p[C * MS];                   // Q K^T; later 16 x 17 scratch for the off-diagonal block of T
-  float t[C * MS];                   // T = (I + A)^-1
-  uint16_t t1h[C * BS], t1l[C * BS];  // T diag(b)
+  // Arrays read or written with lane-dependent addresses on every chunk come first so
+  // that they lie within the 64 KiB reach of an LDS instruction's immediate offset.
+  float c[C];      // cumulative log2 decay within the chunk
+  float gam[C];    // 2^c
+  float beta[C];   // step size (0 for tokens past the end)
+  float braw[C];   // beta or eta as given
+  float knorm[C];  // ||k||^2 (Kaczmarz step size)
+  float g[C * MS];  // K K^T, then A (strictly lower part)
+  union {
+    float p[C * MS];  // Q K^T
+    float t[C * MS];  // then T = (I + A)^-1
+  };
+  union {
+    uint16_t t1h[C * BS];  // T diag(b) (hi part)
+    float xs[16 * 17];     // before it: scratch for the off-diagonal block of T
+  };
+  uint16_t t1l[C * BS];
   uint16_t t2h[C * BS], t2l[C * BS];  // T diag(b g)
   uint16_t pmh[C * BS], pml[C * BS];  // M o Q K^T
-  float c[C];                         // cumulative log2 decay within the chunk
-  float gam[C];                       // 2^c
-  float beta[C];                      // step size (0 for tokens past the end)
-  float braw[C];                      // beta or eta as given
-  float knorm[C];                     // ||k||^2 (Kaczmarz step size)
+  union {
+    uint16_t k[C * KS];   // K, token rows: read by K K^T and Q K^T
+    uint16_t wh[C * KS];  // then W = T diag(b g) K (hi part), token rows
+  };
+  uint16_t q[C * KS];
+  uint16_t kt[DK * TS];  // K token-major
+  uint16_t wl[C * KS];   // W (lo part)
+  uint16_t vt[DV * TS];  // V token-major
 };
 
 template <int DK, int DV, bool BF>
-__global__ void __launch_bounds__(kThreads) prefill_kernel(PoolArgs pa, PrefillArgs a) {
+__global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, PrefillArgs a) {
   constexpr int C = kChunk;
   constexpr int CW = DV / 4;    // value columns per wave
   constexpr int NCB = CW / 16;  // 16-column blocks per wave
   constexpr int NKB = DK / 16;  // 16-channel blocks
   constexpr int NKP = DK / 32;  // pairs of channel blocks (one MFMA k-step each)
   using Lds = PrefillLds<DK, DV>;
-  constexpr int KS = Lds::KS, VS = Lds::VS, MS = Lds::MS, BS = Lds::BS;
+  constexpr int KS = Lds::KS, TS = Lds::TS, MS = Lds::MS, BS = Lds::BS;
   static_assert(NCB >= 1 && NKP >= 1, "head sizes 64 or 128");
   __shared__ __align__(16) Lds sh;
 
@@ -154,40 +157,75 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PoolArgs pa, PrefillA
   const int H = pa.heads, T = a.tokens;
   const size_t bseq = static_cast<size_t>(tile / H), h = static_cast<size_t>(tile % H);
   const int col0 = wave * CW;
+  // Token columns of this lane's reads of the token-major K and V (see tswz): channel
+  // 16 b + ln has swizzle ((ln / 8) + 2 b) mod 4, i.e. sw0 for even b and sw0 ^ 16 for odd b.
+  const int sw0 = (ln >> 3) << 3;
+  const int colw = (8 * lg) ^ sw0;  // the 8-token group 8 lg
+  const int colp = (4 * lg) ^ sw0;  // the 4-token group 4 lg (the group 16 + 4 lg: ^ 16)
 
   // The state columns of this wave: S[kb][cb][r] = S(16 kb + 4 lg + r, col0 + 16 cb + ln).
   float S[NKB][NCB][4];
-  const size_t tbase = static_cast<size_t>(tile) * DK * DV;
+  constexpr int EB = BF ? 2 : 4;  // bytes per base element
+  const auto brsrc = make_rsrc(static_cast<const char*>(pa.base) + static_cast<size_t>(tile) * DK * DV * EB,
+                               DK * DV * EB);
+  const uint32_t bvoff = static_cast<uint32_t>((4 * lg * DV + col0 + ln) * EB);
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        S[kb][cb][r] = ld_base<BF>(pa.base, tbase + size_t(16 * kb + 4 * lg + r) * DV + col0 + 16 * cb + ln);
+      for (int r = 0; r < 4; ++r) S[kb][cb][r] = ld_base<BF>(brsrc, bvoff, ((16 * kb + r) * DV + 16 * cb) * EB);
 
   const bool kla = a.eta != nullptr;
+  // Inputs of the next chunk are loaded into registers while this chunk is computed.
+  constexpr int NLK = C * DK / 8 / kThreads, NLV = C * DV / 8 / kThreads;
+  uint4 nk[NLK], nq[NLK], nv[NLV];
+  float ndec = 1.f, nbt = 0.f;
+  auto row_ptr = [&](const uint16_t* x, int t, int d) { return x + ((bseq * T + t) * H + h) * d; };
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < NLK; ++i) {
+      const int pc = tid + i * kThreads, row = pc / (DK / 8), seg = pc % (DK / 8);
+      nk[i] = nq[i] = make_uint4(0, 0, 0, 0);
+      if (t0 + row < T) {
+        nk[i] = reinterpret_cast<const uint4*>(row_ptr(a.k, t0 + row, DK))[seg];
+        nq[i] = reinterpret_cast<const uint4*>(row_ptr(a.q, t0 + row, DK))[seg];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NLV; ++i) {
+      const int pc = tid + i * kThreads, row = pc / (DV / 8), seg = pc % (DV / 8);
+      nv[i] = make_uint4(0, 0, 0, 0);
+      if (t0 + row < T) nv[i] = reinterpret_cast<const uint4*>(row_ptr(a.v, t0 + row, DV))[seg];
+    }
+    if (wave == 3) {
+      const int t = t0 + lane;
+      const bool ok = lane < C && t < T;
+      const size_t si = (bseq * T + (ok ? t : 0)) * H + h;
+      ndec = ok ? a.decay[si] : 1.f;
+      nbt = ok ? (kla ? a.eta[si] : a.beta[si]) : 0.f;
+    }
+  };
+  fetch(0);
+
   for (int t0 = 0; t0 < T; t0 += C) {
     __syncthreads();  // every wave is done with the previous chunk's LDS arrays
 
-    // ---- 1. this chunk's rows of K, Q, V (zeros past the end); ||k||^2; decays
-    auto row_ptr = [&](const uint16_t* x, int t, int d) {
-      return x + ((bseq * T + t) * H + h) * d;
-    };
+    // ---- 1. this chunk's rows of K, Q, V (zeros past the end) into LDS; ||k||^2; decays
 #pragma unroll
-    for (int i = 0; i < C * DK / 8 / kThreads; ++i) {
+    for (int i = 0; i < NLK; ++i) {
       const int pc = tid + i * kThreads, row = pc / (DK / 8), seg = pc % (DK / 8);
-      const bool ok = t0 + row < T;
-      uint4 kw = make_uint4(0, 0, 0, 0), qw = kw;
-      if (ok) {
-        kw = reinterpret_cast<const uint4*>(row_ptr(a.k, t0 + row, DK))[seg];
-        qw = reinterpret_cast<const uint4*>(row_ptr(a.q, t0 + row, DK))[seg];
+      *reinterpret_cast<uint4*>(&sh.k[row * KS + seg * 8]) = nk[i];
+      *reinterpret_cast<uint4*>(&sh.q[row * KS + seg * 8]) = nq[i];
+      const uint32_t kw[4] = {nk[i].x, nk[i].y, nk[i].z, nk[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ch = seg * 8 + e;
+        sh.kt[ch * TS + tswz(ch, row)] = static_cast<uint16_t>(kw[e / 2] >> (16 * (e % 2)));
       }
-      *reinterpret_cast<uint4*>(&sh.k[row * KS + seg * 8]) = kw;
-      *reinterpret_cast<uint4*>(&sh.q[row * KS + seg * 8]) = qw;
       if (kla) {
         float f[8];
-        unpack8(kw, f);
+        unpack8(nk[i], f);
         float ss = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
@@ -196,19 +234,18 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PoolArgs pa, PrefillA
       }
     }
 #pragma unroll
-    for (int i = 0; i < C * DV / 8 / kThreads; ++i) {
+    for (int i = 0; i < NLV; ++i) {
       const int pc = tid + i * kThreads, row = pc / (DV / 8), seg = pc % (DV / 8);
-      uint4 vw = make_uint4(0, 0, 0, 0);
-      if (t0 + row < T) vw = reinterpret_cast<const uint4*>(row_ptr(a.v, t0 + row, DV))[seg];
-      *reinterpret_cast<uint4*>(&sh.v[row * VS + seg * 8]) = vw;
+      const uint32_t vw[4] = {nv[i].x, nv[i].y, nv[i].z, nv[i].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ch = seg * 8 + e;
+        sh.vt[ch * TS + tswz(ch, row)] = static_cast<uint16_t>(vw[e / 2] >> (16 * (e % 2)));
+      }
     }
     if (wave == 3) {
       // lanes 0..31: one token each; inclusive prefix sum of the clamped log2 decays
-      const int t = t0 + lane;
-      const bool ok = lane < C && t < T;
-      const size_t si = (bseq * T + (ok ? t : 0)) * H + h;
-      float l2 = ok ? step_log2_decay(a.decay[si]) : 0.f;
-      const float bt = ok ? (kla ? a.eta[si] : a.beta[si]) : 0.f;
+      float l2 = (lane < C && t0 + lane < T) ? step_log2_decay(ndec) : 0.f;
 #pragma unroll
       for (int off = 1; off < 32; off <<= 1) {
         const float y = __shfl_up(l2, off, 64);
@@ -217,9 +254,10 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PoolArgs pa, PrefillA
       if (lane < C) {
         sh.c[lane] = l2;
         sh.gam[lane] = exp2f(l2);
-        sh.braw[lane] = bt;
+        sh.braw[lane] = nbt;
       }
     }
+    if (t0 + C < T) fetch(t0 + C);
     __syncthreads();
 
     // ---- 2. G = K K^T and P = Q K^T on the lower blocks (waves 0..2); step sizes (wave 3)
@@ -246,36 +284,45 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PoolArgs pa, PrefillA
     __syncthreads();
 
     // ---- 3. A = strictly lower b_i 2^(c_i - c_j) G_ij (in place); M o P split; T's upper block = 0
-    for (int e = tid; e < C * C; e += kThreads) {
-      const int i = e / C, j = e % C;
-      if (j < i) sh.g[i * MS + j] *= sh.beta[i] * exp2f(sh.c[i] - sh.c[j]);
-      const float pm = j <= i ? exp2f(sh.c[i] - sh.c[j]) * sh.p[i * MS + j] : 0.f;
-      uint32_t hi, lo;
-      split(pm, hi, lo);
-      sh.pmh[i * BS + j] = static_cast<uint16_t>(hi);
-      sh.pml[i * BS + j] = static_cast<uint16_t>(lo);
-      if (i < 16 && j >= 16) sh.t[i * MS + j] = 0.f;
+    {
+      const int j = tid % C;
+      const float cj = sh.c[j];
+#pragma unroll
+      for (int e = 0; e < C * C / kThreads; ++e) {
+        const int i = tid / C + e * (kThreads / C);
+        const float dij = exp2f(fminf(sh.c[i] - cj, 0.f));  // used only where j <= i
+        if (j < i) sh.g[i * MS + j] *= sh.beta[i] * dij;
+        const float pm = j <= i ? dij * sh.p[i * MS + j] : 0.f;
+        uint32_t hi, lo;
+        split(pm, hi, lo);
+        sh.pmh[i * BS + j] = static_cast<uint16_t>(hi);
+        sh.pml[i * BS + j] = static_cast<uint16_t>(lo);
+      }
     }
     __syncthreads();
+    // T (aliasing P from here on): zero its upper-right block
+    for (int e = tid; e < 16 * 16; e += kThreads) sh.t[(e / 16) * MS + 16 + e % 16] = 0.f;
 
     // ---- 4. diagonal 16 x 16 blocks of T by forward substitution (lane j: column j)
     if (wave < 2 && lane < 16) {
       const int o = 16 * wave;
+      int col = lane;
+      asm volatile("" : "+v"(col));  // keeps the 16 (m == col) selects inside the chunk loop
       float x[16];
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
-        float s = m == lane ? 1.f : 0.f;
+        float s[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums shorten the dependent chain
 #pragma unroll
-        for (int pp = 0; pp < m; ++pp) s = fmaf(-sh.g[(o + m) * MS + o + pp], x[pp], s);
-        x[m] = s;
+        for (int pp = 0; pp < m; ++pp) s[pp % 4] = fmaf(sh.g[(o + m) * MS + o + pp], x[pp], s[pp % 4]);
+        x[m] = (m == col ? 1.f : 0.f) - ((s[0] + s[1]) + (s[2] + s[3]));
       }
 #pragma unroll
-      for (int m = 0; m < 16; ++m) sh.t[(o + m) * MS + o + lane] = x[m];
+      for (int m = 0; m < 16; ++m) sh.t[(o + m) * MS + o + col] = x[m];
     }
     __syncthreads();
 
     // ---- 5. off-diagonal block: T_10 = -T_11 (A_10 T_00)
-    float* xs = sh.p;  // P is no longer needed
+    float* xs = sh.xs;
     {
       const int i = tid >> 4, j = tid & 15;
       float s = 0.f;
@@ -291,40 +338,47 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PoolArgs pa, PrefillA
     __syncthreads();
 
     // ---- 6. T diag(b) and T diag(b g), split
-    for (int e = tid; e < C * C; e += kThreads) {
-      const int i = e / C, j = e % C;
-      const float t1 = sh.t[i * MS + j] * sh.beta[j];
-      uint32_t hi, lo;
-      split(t1, hi, lo);
-      sh.t1h[i * BS + j] = static_cast<uint16_t>(hi);
-      sh.t1l[i * BS + j] = static_cast<uint16_t>(lo);
-      split(t1 * sh.gam[j], hi, lo);
-      sh.t2h[i * BS + j] = static_cast<uint16_t>(hi);
-      sh.t2l[i * BS + j] = static_cast<uint16_t>(lo);
+    {
+      const int j = tid % C;
+      const float bj = sh.beta[j], bgj = bj * sh.gam[j];
+      float tv[C * C / kThreads];
+#pragma unroll
+      for (int e = 0; e < C * C / kThreads; ++e) tv[e] = sh.t[(tid / C + e * (kThreads / C)) * MS + j];
+#pragma unroll
+      for (int e = 0; e < C * C / kThreads; ++e) {
+        const int i = tid / C + e * (kThreads / C);
+        uint32_t hi, lo;
+        split(tv[e] * bj, hi, lo);
+        sh.t1h[i * BS + j] = static_cast<uint16_t>(hi);
+        sh.t1l[i * BS + j] = static_cast<uint16_t>(lo);
+        split(tv[e] * bgj, hi, lo);
+        sh.t2h[i * BS + j] = static_cast<uint16_t>(hi);
+        sh.t2l[i * BS + j] = static_cast<uint16_t>(lo);
+      }
     }
     __syncthreads();
 
     // ---- 7. W = T diag(b g) K into LDS (blocks shared out over the waves); this wave's T diag(b) V
 #pragma unroll
+    // W^T = K^T (T diag(b g))^T: the result holds 4 consecutive channels of one token per lane
     for (int e = 0; e < NKB / 2; ++e) {
       const int blk = wave + 4 * e;  // 2 * NKB blocks: (ib, cb) = (blk / NKB, blk % NKB)
       const int ib = blk / NKB, cb = blk % NKB;
-      const bf16x8 kb8 = ld_col8(&sh.k[(8 * lg) * KS + 16 * cb + ln], KS);
+      const bf16x8 ka = ld_b128(&sh.kt[(16 * cb + ln) * TS + (colw ^ ((cb & 1) << 4))]);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mma(ld_b128(&sh.t2h[(16 * ib + ln) * BS + 8 * lg]), kb8, acc);
-      acc = mma(ld_b128(&sh.t2l[(16 * ib + ln) * BS + 8 * lg]), kb8, acc);
+      acc = mma(ka, ld_b128(&sh.t2h[(16 * ib + ln) * BS + 8 * lg]), acc);
+      acc = mma(ka, ld_b128(&sh.t2l[(16 * ib + ln) * BS + 8 * lg]), acc);
+      uint32_t hi[4], lo[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        uint32_t hi, lo;
-        split(acc[r], hi, lo);
-        sh.wh[(16 * ib + 4 * lg + r) * KS + 16 * cb + ln] = static_cast<uint16_t>(hi);
-        sh.wl[(16 * ib + 4 * lg + r) * KS + 16 * cb + ln] = static_cast<uint16_t>(lo);
-      }
+      for (int r = 0; r < 4; ++r) split(acc[r], hi[r], lo[r]);
+      const int wo = (16 * ib + ln) * KS + 16 * cb + 4 * lg;
+      *reinterpret_cast<uint2*>(&sh.wh[wo]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+      *reinterpret_cast<uint2*>(&sh.wl[wo]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
     }
     float U[2][NCB][4];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      const bf16x8 vb8 = ld_col8(&sh.v[(8 * lg) * VS + col0 + 16 * cb + ln], VS);
+      const bf16x8 vb8 = ld_b128(&sh.vt[(col0 + 16 * cb + ln) * TS + (colw ^ ((((col0 >> 4) + cb) & 1) << 4))]);
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -336,43 +390,47 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PoolArgs pa, PrefillA
     }
     __syncthreads();
 
-    // ---- 8. U = T diag(b) V - W S, and diag(g) Q S, with S split once
-    bf16x8 shi[NKP][NCB], slo[NKP][NCB];
-#pragma unroll
-    for (int kp = 0; kp < NKP; ++kp)
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) split_pair(S[2 * kp][cb], S[2 * kp + 1][cb], shi[kp][cb], slo[kp][cb]);
+    // ---- 8. U = T diag(b) V - W S, and diag(g) Q S (S split one channel-block pair at a time)
     float O[2][NCB][4];
+    {
+      f32x4 ws[2][NCB], qs[2][NCB];
 #pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      f32x4 ws[NCB], qs[NCB];
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        ws[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        qs[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int kp = 0; kp < NKP; ++kp) {
-        const int rowk = (16 * ib + ln) * KS + 32 * kp + 4 * lg;
-        const bf16x8 wah = ld_2x64(&sh.wh[rowk], &sh.wh[rowk + 16]);
-        const bf16x8 wal = ld_2x64(&sh.wl[rowk], &sh.wl[rowk + 16]);
-        const bf16x8 qa = ld_2x64(&sh.q[rowk], &sh.q[rowk + 16]);
+      for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          ws[cb] = mma(wah, shi[kp][cb], ws[cb]);
-          ws[cb] = mma(wah, slo[kp][cb], ws[cb]);
-          ws[cb] = mma(wal, shi[kp][cb], ws[cb]);
-          qs[cb] = mma(qa, shi[kp][cb], qs[cb]);
-          qs[cb] = mma(qa, slo[kp][cb], qs[cb]);
+          ws[ib][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          qs[ib][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int kp = 0; kp < NKP; ++kp) {
+        bf16x8 shi[NCB], slo[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) split_pair(S[2 * kp][cb], S[2 * kp + 1][cb], shi[cb], slo[cb]);
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+          const int rowk = (16 * ib + ln) * KS + 32 * kp + 4 * lg;
+          const bf16x8 wah = ld_2x64(&sh.wh[rowk], &sh.wh[rowk + 16]);
+          const bf16x8 wal = ld_2x64(&sh.wl[rowk], &sh.wl[rowk + 16]);
+          const bf16x8 qa = ld_2x64(&sh.q[rowk], &sh.q[rowk + 16]);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            ws[ib][cb] = mma(wah, shi[cb], ws[ib][cb]);
+            ws[ib][cb] = mma(wah, slo[cb], ws[ib][cb]);
+            ws[ib][cb] = mma(wal, shi[cb], ws[ib][cb]);
+            qs[ib][cb] = mma(qa, shi[cb], qs[ib][cb]);
+            qs[ib][cb] = mma(qa, slo[cb], qs[ib][cb]);
+          }
         }
       }
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
+      for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          U[ib][cb][r] -= ws[cb][r];
-          O[ib][cb][r] = sh.gam[16 * ib + 4 * lg + r] * qs[cb][r];
-        }
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            U[ib][cb][r] -= ws[ib][cb][r];
+            O[ib][cb][r] = sh.gam[16 * ib + 4 * lg + r] * qs[ib][cb][r];
+          }
     }
 
     // ---- 9. O += (M o Q K^T) U; write the outputs
@@ -412,7 +470,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PoolArgs pa, PrefillA
     for (int cb = 0; cb < NCB; ++cb) split_pair(U[0][cb], U[1][cb], u2hi[cb], u2lo[cb]);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const bf16x8 ka = ld_col_paired(&sh.k[16 * kb + ln], KS, lg);
+      const uint16_t* kr = &sh.kt[(16 * kb + ln) * TS];
+      const bf16x8 ka = ld_2x64(kr + (colp ^ ((kb & 1) << 4)), kr + (colp ^ ((~kb & 1) << 4)));
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         f32x4 acc = {gC * S[kb][cb][0], gC * S[kb][cb][1], gC * S[kb][cb][2], gC * S[kb][cb][3]};
@@ -429,8 +488,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kernel(PoolArgs pa, PrefillA
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        st_base<BF>(pa.base, tbase + size_t(16 * kb + 4 * lg + r) * DV + col0 + 16 * cb + ln, S[kb][cb][r]);
+      for (int r = 0; r < 4; ++r) st_base<BF>(brsrc, bvoff, ((16 * kb + r) * DV + 16 * cb) * EB, S[kb][cb][r]);
 }
 
 }  // namespace
