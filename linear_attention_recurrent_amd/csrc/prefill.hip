@@ -39,6 +39,7 @@ namespace {
 using bf16x8 = __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16;
 using f32x4 = __attribute__((__vector_size__(4 * sizeof(float)))) float;
 using u32x4 = __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t;
+using bf16x2 = __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16;
 
 constexpr int kChunk = 32;  // tokens per chunk
 constexpr int kThreads = 256;
@@ -64,22 +65,28 @@ __device__ __forceinline__ bf16x8 ld_2x64(const uint16_t* p0, const uint16_t* p1
   return pack8(a.x, a.y, b.x, b.y);
 }
 
-// fp32 -> bf16 hi + lo (bit patterns).
-__device__ __forceinline__ void split(float x, uint32_t& hi, uint32_t& lo) {
-  hi = f32_to_bf16_rne(x);
-  lo = f32_to_bf16_rne(x - bf16_to_f32(hi));
+// Two fp32 values rounded to bf16 (to nearest, ties to even; one v_cvt_pk_bf16_f32)
+// and packed, a in the low half.
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// fp32 -> bf16 hi + lo for two values at once (packed pairs): x - hi is exact in fp32.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = cvt2(a, b);
+  lo = cvt2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
 // Two accumulator blocks (4 values each, k = 4g + r and 16 + 4g + r) as split B operands.
 __device__ __forceinline__ void split_pair(const float (&x0)[4], const float (&x1)[4], bf16x8& hi, bf16x8& lo) {
-  uint32_t h[8], l[8];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    split(x0[r], h[r], l[r]);
-    split(x1[r], h[4 + r], l[4 + r]);
-  }
-  hi = pack8(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
-  lo = pack8(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+  uint32_t h[4], l[4];
+  split2(x0[0], x0[1], h[0], l[0]);
+  split2(x0[2], x0[3], h[1], l[1]);
+  split2(x1[0], x1[1], h[2], l[2]);
+  split2(x1[2], x1[3], h[3], l[3]);
+  hi = pack8(h[0], h[1], h[2], h[3]);
+  lo = pack8(l[0], l[1], l[2], l[3]);
 }
 
 // One state element of a tile through a buffer resource over that tile: the
@@ -283,20 +290,27 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     }
     __syncthreads();
 
-    // ---- 3. A = strictly lower b_i 2^(c_i - c_j) G_ij (in place); M o P split; T's upper block = 0
+    // ---- 3. A = strictly lower b_i 2^(c_i - c_j) G_ij (in place); M o P split
     {
       const int j = tid % C;
       const float cj = sh.c[j];
+      float pm[C * C / kThreads];
 #pragma unroll
       for (int e = 0; e < C * C / kThreads; ++e) {
         const int i = tid / C + e * (kThreads / C);
         const float dij = exp2f(fminf(sh.c[i] - cj, 0.f));  // used only where j <= i
         if (j < i) sh.g[i * MS + j] *= sh.beta[i] * dij;
-        const float pm = j <= i ? dij * sh.p[i * MS + j] : 0.f;
+        pm[e] = j <= i ? dij * sh.p[i * MS + j] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < C * C / kThreads; e += 2) {
+        const int i0 = tid / C + e * (kThreads / C), i1 = i0 + kThreads / C;
         uint32_t hi, lo;
-        split(pm, hi, lo);
-        sh.pmh[i * BS + j] = static_cast<uint16_t>(hi);
-        sh.pml[i * BS + j] = static_cast<uint16_t>(lo);
+        split2(pm[e], pm[e + 1], hi, lo);
+        sh.pmh[i0 * BS + j] = static_cast<uint16_t>(hi);
+        sh.pmh[i1 * BS + j] = static_cast<uint16_t>(hi >> 16);
+        sh.pml[i0 * BS + j] = static_cast<uint16_t>(lo);
+        sh.pml[i1 * BS + j] = static_cast<uint16_t>(lo >> 16);
       }
     }
     __syncthreads();
@@ -345,22 +359,26 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
 #pragma unroll
       for (int e = 0; e < C * C / kThreads; ++e) tv[e] = sh.t[(tid / C + e * (kThreads / C)) * MS + j];
 #pragma unroll
-      for (int e = 0; e < C * C / kThreads; ++e) {
-        const int i = tid / C + e * (kThreads / C);
+      for (int e = 0; e < C * C / kThreads; e += 2) {
+        const int i0 = tid / C + e * (kThreads / C), i1 = i0 + kThreads / C;
         uint32_t hi, lo;
-        split(tv[e] * bj, hi, lo);
-        sh.t1h[i * BS + j] = static_cast<uint16_t>(hi);
-        sh.t1l[i * BS + j] = static_cast<uint16_t>(lo);
-        split(tv[e] * bgj, hi, lo);
-        sh.t2h[i * BS + j] = static_cast<uint16_t>(hi);
-        sh.t2l[i * BS + j] = static_cast<uint16_t>(lo);
+        split2(tv[e] * bj, tv[e + 1] * bj, hi, lo);
+        sh.t1h[i0 * BS + j] = static_cast<uint16_t>(hi);
+        sh.t1h[i1 * BS + j] = static_cast<uint16_t>(hi >> 16);
+        sh.t1l[i0 * BS + j] = static_cast<uint16_t>(lo);
+        sh.t1l[i1 * BS + j] = static_cast<uint16_t>(lo >> 16);
+        split2(tv[e] * bgj, tv[e + 1] * bgj, hi, lo);
+        sh.t2h[i0 * BS + j] = static_cast<uint16_t>(hi);
+        sh.t2h[i1 * BS + j] = static_cast<uint16_t>(hi >> 16);
+        sh.t2l[i0 * BS + j] = static_cast<uint16_t>(lo);
+        sh.t2l[i1 * BS + j] = static_cast<uint16_t>(lo >> 16);
       }
     }
     __syncthreads();
 
     // ---- 7. W = T diag(b g) K into LDS (blocks shared out over the waves); this wave's T diag(b) V
-#pragma unroll
     // W^T = K^T (T diag(b g))^T: the result holds 4 consecutive channels of one token per lane
+#pragma unroll
     for (int e = 0; e < NKB / 2; ++e) {
       const int blk = wave + 4 * e;  // 2 * NKB blocks: (ib, cb) = (blk / NKB, blk % NKB)
       const int ib = blk / NKB, cb = blk % NKB;
@@ -368,12 +386,12 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       acc = mma(ka, ld_b128(&sh.t2h[(16 * ib + ln) * BS + 8 * lg]), acc);
       acc = mma(ka, ld_b128(&sh.t2l[(16 * ib + ln) * BS + 8 * lg]), acc);
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) split(acc[r], hi[r], lo[r]);
+      uint32_t h01, l01, h23, l23;
+      split2(acc[0], acc[1], h01, l01);
+      split2(acc[2], acc[3], h23, l23);
       const int wo = (16 * ib + ln) * KS + 16 * cb + 4 * lg;
-      *reinterpret_cast<uint2*>(&sh.wh[wo]) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-      *reinterpret_cast<uint2*>(&sh.wl[wo]) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+      *reinterpret_cast<uint2*>(&sh.wh[wo]) = make_uint2(h01, h23);
+      *reinterpret_cast<uint2*>(&sh.wl[wo]) = make_uint2(l01, l23);
     }
     float U[2][NCB][4];
 #pragma unroll
