@@ -185,25 +185,36 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
 
   const bool kla = a.eta != nullptr;
   // Inputs of the next chunk are loaded into registers while this chunk is computed.
-  constexpr int NLK = C * DK / 8 / kThreads, NLV = C * DV / 8 / kThreads;
-  uint4 nk[NLK], nq[NLK], nv[NLV];
+  // Each thread takes one 16-byte piece (8 channels) of two consecutive tokens, so the
+  // token-major copies are written two tokens per 4-byte LDS store.
+  constexpr int KP = DK / 8, VP = DV / 8;                         // pieces per row
+  constexpr int NPK = C / 2 * KP, NPV = C / 2 * VP;               // (token pair, piece) jobs
+  constexpr int LK = (NPK + kThreads - 1) / kThreads, LV = (NPV + kThreads - 1) / kThreads;
+  uint4 nk[LK][2], nq[LK][2], nv[LV][2];
   float ndec = 1.f, nbt = 0.f;
   auto row_ptr = [&](const uint16_t* x, int t, int d) { return x + ((bseq * T + t) * H + h) * d; };
   auto fetch = [&](int t0) {
 #pragma unroll
-    for (int i = 0; i < NLK; ++i) {
-      const int pc = tid + i * kThreads, row = pc / (DK / 8), seg = pc % (DK / 8);
-      nk[i] = nq[i] = make_uint4(0, 0, 0, 0);
-      if (t0 + row < T) {
-        nk[i] = reinterpret_cast<const uint4*>(row_ptr(a.k, t0 + row, DK))[seg];
-        nq[i] = reinterpret_cast<const uint4*>(row_ptr(a.q, t0 + row, DK))[seg];
+    for (int i = 0; i < LK; ++i) {
+      const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        nk[i][s2] = nq[i][s2] = make_uint4(0, 0, 0, 0);
+        if (pc < NPK && t0 + tok + s2 < T) {
+          nk[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.k, t0 + tok + s2, DK))[seg];
+          nq[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.q, t0 + tok + s2, DK))[seg];
+        }
       }
     }
 #pragma unroll
-    for (int i = 0; i < NLV; ++i) {
-      const int pc = tid + i * kThreads, row = pc / (DV / 8), seg = pc % (DV / 8);
-      nv[i] = make_uint4(0, 0, 0, 0);
-      if (t0 + row < T) nv[i] = reinterpret_cast<const uint4*>(row_ptr(a.v, t0 + row, DV))[seg];
+    for (int i = 0; i < LV; ++i) {
+      const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        nv[i][s2] = make_uint4(0, 0, 0, 0);
+        if (pc < NPV && t0 + tok + s2 < T)
+          nv[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.v, t0 + tok + s2, DV))[seg];
+      }
     }
     if (wave == 3) {
       const int t = t0 + lane;
@@ -213,6 +224,15 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
       nbt = ok ? (kla ? a.eta[si] : a.beta[si]) : 0.f;
     }
   };
+  // Two tokens' words w0, w1 (8 channels each) as 4 (channel e: tok0 | tok1 << 16) pairs per half.
+  auto interleave = [](const uint4 w0, const uint4 w1, uint32_t (&o)[8]) {
+    const uint32_t a0[4] = {w0.x, w0.y, w0.z, w0.w}, a1[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[2 * e] = (a0[e] & 0xffffu) | (a1[e] << 16);
+      o[2 * e + 1] = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
+    }
+  };
   fetch(0);
 
   for (int t0 = 0; t0 < T; t0 += C) {
@@ -220,34 +240,46 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
 
     // ---- 1. this chunk's rows of K, Q, V (zeros past the end) into LDS; ||k||^2; decays
 #pragma unroll
-    for (int i = 0; i < NLK; ++i) {
-      const int pc = tid + i * kThreads, row = pc / (DK / 8), seg = pc % (DK / 8);
-      *reinterpret_cast<uint4*>(&sh.k[row * KS + seg * 8]) = nk[i];
-      *reinterpret_cast<uint4*>(&sh.q[row * KS + seg * 8]) = nq[i];
-      const uint32_t kw[4] = {nk[i].x, nk[i].y, nk[i].z, nk[i].w};
+    for (int i = 0; i < LK; ++i) {
+      const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
+      if (pc < NPK) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ch = seg * 8 + e;
-        sh.kt[ch * TS + tswz(ch, row)] = static_cast<uint16_t>(kw[e / 2] >> (16 * (e % 2)));
-      }
-      if (kla) {
-        float f[8];
-        unpack8(nk[i], f);
-        float ss = 0.f;
+        for (int s2 = 0; s2 < 2; ++s2) {
+          *reinterpret_cast<uint4*>(&sh.k[(tok + s2) * KS + seg * 8]) = nk[i][s2];
+          *reinterpret_cast<uint4*>(&sh.q[(tok + s2) * KS + seg * 8]) = nq[i][s2];
+        }
+        uint32_t kw[8];
+        interleave(nk[i][0], nk[i][1], kw);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
-        ss = group_sum<DK / 8>(ss);
-        if (seg == 0) sh.knorm[row] = ss;
+        for (int e = 0; e < 8; ++e) {
+          const int ch = seg * 8 + e;
+          *reinterpret_cast<uint32_t*>(&sh.kt[ch * TS + tswz(ch, tok)]) = kw[e];
+        }
+        if (kla) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            float f[8];
+            unpack8(nk[i][s2], f);
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+            ss = group_sum<KP>(ss);
+            if (seg == 0) sh.knorm[tok + s2] = ss;
+          }
+        }
       }
     }
 #pragma unroll
-    for (int i = 0; i < NLV; ++i) {
-      const int pc = tid + i * kThreads, row = pc / (DV / 8), seg = pc % (DV / 8);
-      const uint32_t vw[4] = {nv[i].x, nv[i].y, nv[i].z, nv[i].w};
+    for (int i = 0; i < LV; ++i) {
+      const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
+      if (pc < NPV) {
+        uint32_t vw[8];
+        interleave(nv[i][0], nv[i][1], vw);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ch = seg * 8 + e;
-        sh.vt[ch * TS + tswz(ch, row)] = static_cast<uint16_t>(vw[e / 2] >> (16 * (e % 2)));
+        for (int e = 0; e < 8; ++e) {
+          const int ch = seg * 8 + e;
+          *reinterpret_cast<uint32_t*>(&sh.vt[ch * TS + tswz(ch, tok)]) = vw[e];
+        }
       }
     }
     if (wave == 3) {
