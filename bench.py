@@ -99,6 +99,38 @@ def counter_profile_name(workload_name: str, bf16_base: bool, log_len=None) -> s
     return f"decode_{workload_name}{tag}{'_bf16base' if bf16_base else ''}_counters.txt"
 
 
+PREFILL_SOURCES = ["linear_attention_recurrent_amd/csrc/prefill.hip",
+                   "linear_attention_recurrent_amd/csrc/dl_device.hpp"]
+
+
+def prefill_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in PREFILL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _read_kv(path):
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    return vals
+
+
+def read_prefill_counters(workload_name: str, tokens: int):
+    """HBM bytes per prefill launch from the committed counter summary, if it was taken on
+    the current kernel source at this prompt length (else None)."""
+    path = os.path.join(PROFILE_DIR, f"prefill_{workload_name}_T{tokens}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = _read_kv(path)
+    return vals if vals.get("kernel_source_sha256") == prefill_source_hash() else None
+
+
 def read_counter_profile(workload_name: str, bf16_base: bool = False, log_len=None):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source (else None)."""
@@ -268,10 +300,13 @@ def prefill_leg(args, inp, Tn, base_dt, reps: int = 5) -> dict:
     units = B * H * Tp
     gbs = m["bytes"] * units / secs / 1e9
     tf_issued = m["issued_flops"] * units / secs / 1e12
+    prof = read_prefill_counters(WORKLOADS[args.workload]["name"], Tp) if base_dt == dl.BASE_F32 else None
+    traffic = None if prof is None else (float(prof["fetch_bytes_per_launch"])
+                                         + float(prof["write_bytes_per_launch"]))
     return {"value": units / secs, "unit": "state-steps/s (B x H x prompt tokens per s)",
             "ms_per_prefill": secs * 1e3, "tokens": Tp, "reps": reps,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": traffic},
             "mfma": {"issued_tflops": tf_issued, "peak": BF16_MFMA_PEAK_TFLOPS, "frac": tf_issued / BF16_MFMA_PEAK_TFLOPS,
                      "method_tflops": m["method_flops"] * units / secs / 1e12},
             "bytes_per_state_step": m["bytes"], "issued_flops_per_state_step": m["issued_flops"]}
