@@ -161,7 +161,7 @@ def _cpu_worker(i, barrier, queue):
     queue.put((i, time.perf_counter() - t0, len(job["chunks"][i]) * job["steps"]))
 
 
-def cpu_baseline(workload: int, target_s: float = 15.0) -> dict:
+def cpu_baseline(workload: int, target_s: float = 25.0) -> dict:
     """Time the fp64 eager oracle on the host cores over a bounded sample of the workload.
 
     The inputs are drawn once in this process; forked workers (one per core, at
