@@ -256,15 +256,20 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD's published
 PREFILL_CHUNK = 32
 
 
-def prefill_model(dk: int, dv: int, C: int = PREFILL_CHUNK) -> dict:
+def prefill_model(dk: int, dv: int, C: int = PREFILL_CHUNK, variant: int = 0) -> dict:
     """Per (sequence, head, prompt token): HBM bytes, the chunkwise method's flops, and the
-    bf16 MFMA flops the kernel issues (fp32 operands split in two: 2 or 3 products each)."""
-    byts = 2 * dk * 2 + 2 * dv + 4 + 4 + 4 * dv  # q, k, v bf16; decay, beta; fp32 output
+    bf16 MFMA flops the kernel issues (fp32 operands split in two: 2 or 3 products each).
+    KDA: the decay is a dk-vector per token, the decay-weighted K K^T and Q K^T are formed
+    on the vector units (not counted as MFMA work), and W, (Q o G) S and the state update
+    take three products each because their key/query operand carries the decay."""
+    byts = 2 * dk * 2 + 2 * dv + 4 * (dk if variant == 1 else 1) + 4 + 4 * dv
     method = 2 * C * C * dk * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 3  # per chunk
-    # issued per chunk: K K^T, Q K^T lower blocks (3 of 4 each), W (x2), U~ (x2), W S (x3),
-    # Q S (x2), (M o Q K^T) U (x3), K^T U (x2)
-    issued = (2 * 3 * 16 * 16 * dk * 2 + 2 * C * C * dk * 2 + 2 * C * C * dv * 2
-              + 2 * C * dk * dv * 3 + 2 * C * dk * dv * 2 + 2 * C * C * dv * 3 + 2 * C * dk * dv * 2)
+    if variant == 1:
+        issued = (2 * C * C * dk * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 3 + 2 * C * dk * dv * 3
+                  + 2 * C * C * dv * 3 + 2 * C * dk * dv * 3)
+    else:  # K K^T, Q K^T lower blocks (3 of 4 each), W (x2), U~ (x2), W S (x3), Q S (x2), P U (x3), K^T U (x2)
+        issued = (2 * 3 * 16 * 16 * dk * 2 + 2 * C * C * dk * 2 + 2 * C * C * dv * 2
+                  + 2 * C * dk * dv * 3 + 2 * C * dk * dv * 2 + 2 * C * C * dv * 3 + 2 * C * dk * dv * 2)
     return {"bytes": byts, "method_flops": method / C, "issued_flops": issued / C}
 
 
@@ -296,7 +301,7 @@ def prefill_leg(args, inp, Tn, base_dt, reps: int = 5) -> dict:
     end.record(stream)
     torch.cuda.synchronize()
     secs = start.elapsed_time(end) / 1e3 / reps
-    m = prefill_model(dk, dv)
+    m = prefill_model(dk, dv, variant=inp.variant)
     units = B * H * Tp
     gbs = m["bytes"] * units / secs / 1e9
     tf_issued = m["issued_flops"] * units / secs / 1e12
@@ -469,7 +474,7 @@ def main():
         state = T["s0"].clone()
         secs_e = time_loop(lambda t: dl.dl_eager_step(var, state, ios[t % P]), K, W, chunk)
         result["eager"] = secs_e
-    if args.only == "prefill" or (args.only is None and var == 0):
+    if args.only == "prefill" or (args.only is None and var in (0, 1)):
         result["prefill"] = prefill_leg(args, inp, T, base_dt)
     if args.only is not None:
         if args.only == "prefill":

@@ -159,10 +159,11 @@ typedef struct {
   const uint16_t *q;   /* bf16 [batch][T][heads][dk]                                           */
   const uint16_t *k;   /* bf16 [batch][T][heads][dk]                                           */
   const uint16_t *v;   /* bf16 [batch][T][heads][dv]                                           */
-  const float *decay;  /* GDN: fp32 [batch][T][heads] alpha, in (0, 1]                          */
-  const float *beta;   /* GDN: fp32 [batch][T][heads]; or NULL with eta                         */
+  const float *decay;  /* GDN: fp32 [batch][T][heads] alpha; KDA: fp32 [batch][T][heads][dk];
+                          values in (0, 1]                                                      */
+  const float *beta;   /* fp32 [batch][T][heads]; or NULL with eta                              */
   float *out;          /* fp32 [batch][T][heads][dv]  every token's output (written)            */
-  const float *eta;    /* GDN, instead of beta: fp32 [batch][T][heads], the Kaczmarz step size
+  const float *eta;    /* instead of beta: fp32 [batch][T][heads], the Kaczmarz step size
                           beta = eta / (||k||^2 + eps) (Kaczmarz Linear Attention abstract)    */
   float eps;           /* >= 0 (ignored when eta is NULL)                                       */
   int32_t tokens;      /* T                                                                     */
@@ -178,7 +179,8 @@ typedef struct {
  * triangular solve (the WY form) and every product with the state is a matrix
  * product.  Any non-empty log is folded into the base first, as dl_merge with
  * min_fill = 1 would.  With a bf16 base the final state is rounded once.
- * GDN only (dims->variant must be DL_GDN, else DL_EUNSUPPORTED).  Errors:
+ * GDN and KDA (RWKV6: DL_EUNSUPPORTED); for KDA the decay-weighted products
+ * inside a chunk are formed channel by channel, the others on matrix units.  Errors:
  * DL_EINVAL for tokens < 0, null q/k/v/decay/out, or eps < 0 with eta set;
  * DL_EUNSUPPORTED unless exactly one of beta and eta is given.  tokens == 0
  * only folds the logs and looks at no prompt pointer. */

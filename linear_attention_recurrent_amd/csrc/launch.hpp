@@ -14,8 +14,8 @@ hipError_t launch_merge(int variant, bool bf16_base, int dk, int dv, int tiles, 
                         int min_fill, hipStream_t stream);
 hipError_t launch_init(int variant, bool bf16_base, int dk, int dv, int tiles, const PoolArgs& p,
                        const float* init_base, hipStream_t stream);
-hipError_t launch_prefill(bool bf16_base, int dk, int dv, int tiles, const PoolArgs& p, const PrefillArgs& a,
-                          hipStream_t stream);
+hipError_t launch_prefill(int variant, bool bf16_base, int dk, int dv, int tiles, const PoolArgs& p,
+                          const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_eager(int variant, int dk, int dv, int tiles, int heads, float* state, const StepArgs& s,
                         hipStream_t stream);
 

@@ -110,6 +110,44 @@ __device__ __forceinline__ void st_base(__amdgpu_buffer_rsrc_t r, uint32_t voff,
 // the 16 lanes that share a token spread over the LDS banks.
 __device__ __forceinline__ int tswz(int ch, int tok) { return tok ^ (((ch >> 3) & 3) << 3); }
 
+// T = (I + A)^-1 for a 32 x 32 strictly lower A (fp32 in LDS, row stride MS), by
+// blocks of 16: the two diagonal blocks by forward substitution (waves 0 and 1,
+// lane j: column j, four partial sums per row to shorten the dependent chain),
+// then T_10 = -T_11 (A_10 T_00) with every thread computing one entry.  T's upper
+// right block must already be zero.  xs: 16 x 17 floats of scratch.  Called by
+// the whole workgroup (it synchronises); returns after a barrier.
+template <int MS>
+__device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, float* xs, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  if (wave < 2 && lane < 16) {
+    const int o = 16 * wave;
+    int col = lane;
+    asm volatile("" : "+v"(col));  // keeps the 16 (m == col) selects inside the caller's loop
+    float x[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int pp = 0; pp < m; ++pp) s[pp % 4] = fmaf(g[(o + m) * MS + o + pp], x[pp], s[pp % 4]);
+      x[m] = (m == col ? 1.f : 0.f) - ((s[0] + s[1]) + (s[2] + s[3]));
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) t[(o + m) * MS + o + col] = x[m];
+  }
+  __syncthreads();
+  const int i = tid >> 4, j = tid & 15;
+  float s = 0.f;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) s = fmaf(g[(16 + i) * MS + m], t[m * MS + j], s);
+  xs[i * 17 + j] = s;
+  __syncthreads();
+  float y = 0.f;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) y = fmaf(t[(16 + i) * MS + 16 + m], xs[m * 17 + j], y);
+  t[(16 + i) * MS + j] = -y;
+  __syncthreads();
+}
+
 template <int DK, int DV>
 struct PrefillLds {
   static constexpr int C = kChunk;
@@ -349,39 +387,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     // T (aliasing P from here on): zero its upper-right block
     for (int e = tid; e < 16 * 16; e += kThreads) sh.t[(e / 16) * MS + 16 + e % 16] = 0.f;
 
-    // ---- 4. diagonal 16 x 16 blocks of T by forward substitution (lane j: column j)
-    if (wave < 2 && lane < 16) {
-      const int o = 16 * wave;
-      int col = lane;
-      asm volatile("" : "+v"(col));  // keeps the 16 (m == col) selects inside the chunk loop
-      float x[16];
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        float s[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums shorten the dependent chain
-#pragma unroll
-        for (int pp = 0; pp < m; ++pp) s[pp % 4] = fmaf(sh.g[(o + m) * MS + o + pp], x[pp], s[pp % 4]);
-        x[m] = (m == col ? 1.f : 0.f) - ((s[0] + s[1]) + (s[2] + s[3]));
-      }
-#pragma unroll
-      for (int m = 0; m < 16; ++m) sh.t[(o + m) * MS + o + col] = x[m];
-    }
-    __syncthreads();
-
-    // ---- 5. off-diagonal block: T_10 = -T_11 (A_10 T_00)
-    float* xs = sh.xs;
-    {
-      const int i = tid >> 4, j = tid & 15;
-      float s = 0.f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) s = fmaf(sh.g[(16 + i) * MS + m], sh.t[m * MS + j], s);
-      xs[i * 17 + j] = s;
-      __syncthreads();
-      float y = 0.f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) y = fmaf(sh.t[(16 + i) * MS + 16 + m], xs[m * 17 + j], y);
-      sh.t[(16 + i) * MS + j] = -y;
-    }
-    __syncthreads();
+    // ---- 4, 5. T = (I + A)^-1
+    invert_unit_lower32<MS>(sh.g, sh.t, sh.xs, tid);
 
     // ---- 6. T diag(b) and T diag(b g), split
     {
@@ -541,12 +548,468 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
       for (int r = 0; r < 4; ++r) st_base<BF>(brsrc, bvoff, ((16 * kb + r) * DV + 16 * cb) * EB, S[kb][cb][r]);
 }
 
+
+// ------------------------------------------------------------------ KDA prefill
+// KDA decays each key channel on its own: with G_i = a_1 ... a_i (a dk-vector,
+// cumulative within the chunk, kept as log2 in cc) the chunk form becomes
+//   A_ij = b_i sum_c k_i[c] k_j[c] G_i[c] / G_j[c]  (j < i),   T = (I + A)^-1
+//   U    = T diag(b) V - T diag(b) (K o G) S
+//   O    = (Q o G) S + P U,   P_ij = sum_c q_i[c] k_j[c] G_i[c] / G_j[c]  (j <= i)
+//   S'   = diag(G_C) S + (K o G_C / G)^T U
+// (the same unrolling of u_i as for GDN, with diag(G) in place of the scalar g).
+// The decay-weighted products A and P are formed directly, one 2^(c_i - c_j) per
+// channel and pair, so any decay down to the -126 clamp stays exact; every other
+// product runs on MFMA with the decay folded into a split operand.
+template <int DK, int DV>
+struct PrefillKdaLds {
+  static constexpr int C = kChunk;
+  static constexpr int KS = DK + 8;  // bf16 row stride of K, Q, W and Q o G
+  static constexpr int TS = C + 8;   // bf16 row stride of the token-major arrays
+  static constexpr int MS = C + 1;   // fp32 row stride of the C x C matrices
+  static constexpr int BS = C + 8;   // bf16 row stride of the split C x C matrices
+  static constexpr int CS = DK + 4;  // fp32 row stride of the per-channel decays
+  float beta[C];
+  float braw[C];
+  float knorm[C];
+  float g[C * MS];  // A (strictly lower part)
+  float t[C * MS];  // T = (I + A)^-1
+  union {
+    uint16_t t1h[C * BS];  // T diag(b) (hi part)
+    float xs[16 * 17];     // before it: scratch of the inverse
+  };
+  uint16_t t1l[C * BS];
+  uint16_t pmh[C * BS], pml[C * BS];  // P (lower triangle, split)
+  union {
+    uint16_t k[C * KS];  // K, token rows
+    uint16_t wh[C * KS];  // then W (hi part)
+  };
+  union {
+    uint16_t q[C * KS];  // Q, token rows
+    uint16_t wl[C * KS];  // then W (lo part)
+  };
+  uint16_t qgh[C * KS], qgl[C * KS];  // Q o G, token rows, split
+  uint16_t vt[DV * TS];               // V token-major
+  uint16_t kgh[DK * TS], kgl[DK * TS];  // K o G, token-major, split
+  uint16_t kdh[DK * TS], kdl[DK * TS];  // K o G_C / G, token-major, split
+  float cc[C * CS];                     // log2 decays, then their prefix sums over the chunk
+};
+
+template <int DK, int DV, bool BF>
+__global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, PrefillArgs a) {
+  constexpr int C = kChunk;
+  constexpr int CW = DV / 4;
+  constexpr int NCB = CW / 16;
+  constexpr int NKB = DK / 16;
+  constexpr int NKP = DK / 32;
+  using Lds = PrefillKdaLds<DK, DV>;
+  constexpr int KS = Lds::KS, TS = Lds::TS, MS = Lds::MS, BS = Lds::BS, CS = Lds::CS;
+  __shared__ __align__(16) Lds sh;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 15, lg = lane >> 4;
+  const int tile = blockIdx.x;
+  const int H = pa.heads, T = a.tokens;
+  const size_t bseq = static_cast<size_t>(tile / H), h = static_cast<size_t>(tile % H);
+  const int col0 = wave * CW;
+  const int sw0 = (ln >> 3) << 3;
+  const int colw = (8 * lg) ^ sw0;
+  const int colp = (4 * lg) ^ sw0;
+
+  float S[NKB][NCB][4];
+  constexpr int EB = BF ? 2 : 4;
+  const auto brsrc = make_rsrc(static_cast<const char*>(pa.base) + static_cast<size_t>(tile) * DK * DV * EB,
+                               DK * DV * EB);
+  const uint32_t bvoff = static_cast<uint32_t>((4 * lg * DV + col0 + ln) * EB);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[kb][cb][r] = ld_base<BF>(brsrc, bvoff, ((16 * kb + r) * DV + 16 * cb) * EB);
+
+  const bool kla = a.eta != nullptr;
+  constexpr int KP = DK / 8, VP = DV / 8;
+  constexpr int NPK = C / 2 * KP, NPV = C / 2 * VP;
+  constexpr int LK = (NPK + kThreads - 1) / kThreads, LV = (NPV + kThreads - 1) / kThreads;
+  constexpr int ND = C * DK / 4 / kThreads;  // float4 decay pieces per thread
+  uint4 nk[LK][2], nq[LK][2], nv[LV][2];
+  float4 nd[ND];
+  float nbt = 0.f;
+  auto row_ptr = [&](const uint16_t* x, int t, int d) { return x + ((bseq * T + t) * H + h) * d; };
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+      const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        nk[i][s2] = nq[i][s2] = make_uint4(0, 0, 0, 0);
+        if (pc < NPK && t0 + tok + s2 < T) {
+          nk[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.k, t0 + tok + s2, DK))[seg];
+          nq[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.q, t0 + tok + s2, DK))[seg];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        nv[i][s2] = make_uint4(0, 0, 0, 0);
+        if (pc < NPV && t0 + tok + s2 < T)
+          nv[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.v, t0 + tok + s2, DV))[seg];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      const int pc = tid + i * kThreads, tok = pc / (DK / 4), seg = pc % (DK / 4);
+      nd[i] = make_float4(1.f, 1.f, 1.f, 1.f);
+      if (t0 + tok < T)
+        nd[i] = reinterpret_cast<const float4*>(a.decay + ((bseq * T + t0 + tok) * H + h) * DK)[seg];
+    }
+    if (wave == 3) {
+      const int t = t0 + lane;
+      const bool ok = lane < C && t < T;
+      const size_t si = (bseq * T + (ok ? t : 0)) * H + h;
+      nbt = ok ? (kla ? a.eta[si] : a.beta[si]) : 0.f;
+    }
+  };
+  auto interleave = [](const uint4 w0, const uint4 w1, uint32_t (&o)[8]) {
+    const uint32_t a0[4] = {w0.x, w0.y, w0.z, w0.w}, a1[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[2 * e] = (a0[e] & 0xffffu) | (a1[e] << 16);
+      o[2 * e + 1] = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
+    }
+  };
+  fetch(0);
+
+  for (int t0 = 0; t0 < T; t0 += C) {
+    __syncthreads();
+
+    // ---- 1. K, Q rows; V token-major; clamped log2 decays; ||k||^2; step sizes
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+      const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
+      if (pc < NPK) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          *reinterpret_cast<uint4*>(&sh.k[(tok + s2) * KS + seg * 8]) = nk[i][s2];
+          *reinterpret_cast<uint4*>(&sh.q[(tok + s2) * KS + seg * 8]) = nq[i][s2];
+        }
+        if (kla) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            float f[8];
+            unpack8(nk[i][s2], f);
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+            ss = group_sum<KP>(ss);
+            if (seg == 0) sh.knorm[tok + s2] = ss;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
+      if (pc < NPV) {
+        uint32_t vw[8];
+        interleave(nv[i][0], nv[i][1], vw);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ch = seg * 8 + e;
+          *reinterpret_cast<uint32_t*>(&sh.vt[ch * TS + tswz(ch, tok)]) = vw[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      const int pc = tid + i * kThreads, tok = pc / (DK / 4), seg = pc % (DK / 4);
+      *reinterpret_cast<float4*>(&sh.cc[tok * CS + seg * 4]) =
+          make_float4(step_log2_decay(nd[i].x), step_log2_decay(nd[i].y), step_log2_decay(nd[i].z),
+                      step_log2_decay(nd[i].w));
+    }
+    if (wave == 3 && lane < C) sh.braw[lane] = nbt;
+    if (t0 + C < T) fetch(t0 + C);
+    __syncthreads();
+
+    // ---- 2. prefix sums of the log2 decays over the chunk's tokens (one channel per
+    //         32-lane half wave); step sizes; zero the upper triangle of P and T's upper block
+#pragma unroll
+    for (int it = 0; it < DK / 8; ++it) {
+      const int ch = wave * (DK / 4) + 2 * it + (lane >> 5), tok = lane & 31;
+      float x = sh.cc[tok * CS + ch];
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        const float y = __shfl_up(x, off, 32);
+        if (tok >= off) x += y;
+      }
+      sh.cc[tok * CS + ch] = x;
+    }
+    if (tid < C) {
+      const bool ok = t0 + tid < T;
+      sh.beta[tid] = !ok ? 0.f : kla ? sh.braw[tid] / (sh.knorm[tid] + a.eps) : sh.braw[tid];
+    }
+    for (int e = tid; e < C * C; e += kThreads) {
+      const int i = e / C, j = e % C;
+      if (j > i) {
+        sh.pmh[i * BS + j] = 0;
+        sh.pml[i * BS + j] = 0;
+      }
+      if (i < 16 && j >= 16) sh.t[i * MS + j] = 0.f;
+    }
+    __syncthreads();
+
+    // ---- 3. decay-folded operands: Q o G (rows), K o G and K o G_C / G (token-major), split
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+      const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
+      if (pc < NPK) {
+        float kf[2][8], qf[2][8], cf[2][8], cl[8];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          unpack8(*reinterpret_cast<const uint4*>(&sh.k[(tok + s2) * KS + seg * 8]), kf[s2]);
+          unpack8(*reinterpret_cast<const uint4*>(&sh.q[(tok + s2) * KS + seg * 8]), qf[s2]);
+          load8(&sh.cc[(tok + s2) * CS + seg * 8], cf[s2]);
+        }
+        load8(&sh.cc[(C - 1) * CS + seg * 8], cl);
+        uint32_t qh[2][4], ql[2][4], kgh2[8], kgl2[8], kdh2[8], kdl2[8];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+            split2(qf[s2][e] * exp2f(cf[s2][e]), qf[s2][e + 1] * exp2f(cf[s2][e + 1]), qh[s2][e / 2], ql[s2][e / 2]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {  // channel seg*8 + e: tokens tok, tok + 1 packed
+          split2(kf[0][e] * exp2f(cf[0][e]), kf[1][e] * exp2f(cf[1][e]), kgh2[e], kgl2[e]);
+          split2(kf[0][e] * exp2f(cl[e] - cf[0][e]), kf[1][e] * exp2f(cl[e] - cf[1][e]), kdh2[e], kdl2[e]);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          *reinterpret_cast<uint4*>(&sh.qgh[(tok + s2) * KS + seg * 8]) =
+              make_uint4(qh[s2][0], qh[s2][1], qh[s2][2], qh[s2][3]);
+          *reinterpret_cast<uint4*>(&sh.qgl[(tok + s2) * KS + seg * 8]) =
+              make_uint4(ql[s2][0], ql[s2][1], ql[s2][2], ql[s2][3]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ch = seg * 8 + e, o = ch * TS + tswz(ch, tok);
+          *reinterpret_cast<uint32_t*>(&sh.kgh[o]) = kgh2[e];
+          *reinterpret_cast<uint32_t*>(&sh.kgl[o]) = kgl2[e];
+          *reinterpret_cast<uint32_t*>(&sh.kdh[o]) = kdh2[e];
+          *reinterpret_cast<uint32_t*>(&sh.kdl[o]) = kdl2[e];
+        }
+      }
+    }
+
+    // ---- 4. A and P directly: thread (row pair ip, ip' = 31 - ip; channel slice sl)
+    {
+      constexpr int SL = DK / 16;  // channels per slice
+      const int ip = tid >> 4, sl = tid & 15;
+      float kr[2][SL], qr[2][SL], cr[2][SL];
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const int r = w == 0 ? ip : C - 1 - ip;
+#pragma unroll
+        for (int e = 0; e < SL; ++e) {
+          kr[w][e] = bf16_to_f32(sh.k[r * KS + sl * SL + e]);
+          qr[w][e] = bf16_to_f32(sh.q[r * KS + sl * SL + e]);
+          cr[w][e] = sh.cc[r * CS + sl * SL + e];
+        }
+      }
+      for (int n = 0; n <= C; ++n) {  // row ip takes j = 0..ip, row 31 - ip takes j = 0..31 - ip
+        const bool first = n <= ip;
+        const int r = first ? ip : C - 1 - ip, j = first ? n : n - ip - 1;
+        float av = 0.f, pv = 0.f;
+#pragma unroll
+        for (int e = 0; e < SL; ++e) {
+          const float u = bf16_to_f32(sh.k[j * KS + sl * SL + e]) *
+                          exp2f((first ? cr[0][e] : cr[1][e]) - sh.cc[j * CS + sl * SL + e]);
+          av = fmaf(first ? kr[0][e] : kr[1][e], u, av);
+          pv = fmaf(first ? qr[0][e] : qr[1][e], u, pv);
+        }
+        av = group_sum<16>(av);
+        pv = group_sum<16>(pv);
+        if (sl == 0) {
+          if (j < r) sh.g[r * MS + j] = sh.beta[r] * av;
+          uint32_t hi, lo;
+          split2(pv, 0.f, hi, lo);
+          sh.pmh[r * BS + j] = static_cast<uint16_t>(hi);
+          sh.pml[r * BS + j] = static_cast<uint16_t>(lo);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- 5. T = (I + A)^-1
+    invert_unit_lower32<MS>(sh.g, sh.t, sh.xs, tid);
+
+    // ---- 6. T diag(b), split
+    {
+      const int j = tid % C;
+      const float bj = sh.beta[j];
+      float tv[C * C / kThreads];
+#pragma unroll
+      for (int e = 0; e < C * C / kThreads; ++e) tv[e] = sh.t[(tid / C + e * (kThreads / C)) * MS + j];
+#pragma unroll
+      for (int e = 0; e < C * C / kThreads; e += 2) {
+        const int i0 = tid / C + e * (kThreads / C), i1 = i0 + kThreads / C;
+        uint32_t hi, lo;
+        split2(tv[e] * bj, tv[e + 1] * bj, hi, lo);
+        sh.t1h[i0 * BS + j] = static_cast<uint16_t>(hi);
+        sh.t1h[i1 * BS + j] = static_cast<uint16_t>(hi >> 16);
+        sh.t1l[i0 * BS + j] = static_cast<uint16_t>(lo);
+        sh.t1l[i1 * BS + j] = static_cast<uint16_t>(lo >> 16);
+      }
+    }
+    __syncthreads();
+
+    // ---- 7. W = T diag(b) (K o G) via its transpose (to LDS, split); this wave's T diag(b) V
+#pragma unroll
+    for (int e = 0; e < NKB / 2; ++e) {
+      const int blk = wave + 4 * e;
+      const int ib = blk / NKB, cb = blk % NKB;
+      const int o = (16 * cb + ln) * TS + (colw ^ ((cb & 1) << 4));
+      const bf16x8 kah = ld_b128(&sh.kgh[o]), kal = ld_b128(&sh.kgl[o]);
+      const bf16x8 tbh = ld_b128(&sh.t1h[(16 * ib + ln) * BS + 8 * lg]);
+      const bf16x8 tbl = ld_b128(&sh.t1l[(16 * ib + ln) * BS + 8 * lg]);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mma(kah, tbh, acc);
+      acc = mma(kah, tbl, acc);
+      acc = mma(kal, tbh, acc);
+      uint32_t h01, l01, h23, l23;
+      split2(acc[0], acc[1], h01, l01);
+      split2(acc[2], acc[3], h23, l23);
+      const int wo = (16 * ib + ln) * KS + 16 * cb + 4 * lg;
+      *reinterpret_cast<uint2*>(&sh.wh[wo]) = make_uint2(h01, h23);
+      *reinterpret_cast<uint2*>(&sh.wl[wo]) = make_uint2(l01, l23);
+    }
+    float U[2][NCB][4];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const bf16x8 vb8 = ld_b128(&sh.vt[(col0 + 16 * cb + ln) * TS + (colw ^ ((((col0 >> 4) + cb) & 1) << 4))]);
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma(ld_b128(&sh.t1h[(16 * ib + ln) * BS + 8 * lg]), vb8, acc);
+        acc = mma(ld_b128(&sh.t1l[(16 * ib + ln) * BS + 8 * lg]), vb8, acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) U[ib][cb][r] = acc[r];
+      }
+    }
+    __syncthreads();
+
+    // ---- 8. U = T diag(b) V - W S and (Q o G) S
+    float O[2][NCB][4];
+    {
+      f32x4 ws[2][NCB], qs[2][NCB];
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          ws[ib][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          qs[ib][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int kp = 0; kp < NKP; ++kp) {
+        bf16x8 shi[NCB], slo[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) split_pair(S[2 * kp][cb], S[2 * kp + 1][cb], shi[cb], slo[cb]);
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+          const int rowk = (16 * ib + ln) * KS + 32 * kp + 4 * lg;
+          const bf16x8 wah = ld_2x64(&sh.wh[rowk], &sh.wh[rowk + 16]);
+          const bf16x8 wal = ld_2x64(&sh.wl[rowk], &sh.wl[rowk + 16]);
+          const bf16x8 qah = ld_2x64(&sh.qgh[rowk], &sh.qgh[rowk + 16]);
+          const bf16x8 qal = ld_2x64(&sh.qgl[rowk], &sh.qgl[rowk + 16]);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            ws[ib][cb] = mma(wah, shi[cb], ws[ib][cb]);
+            ws[ib][cb] = mma(wah, slo[cb], ws[ib][cb]);
+            ws[ib][cb] = mma(wal, shi[cb], ws[ib][cb]);
+            qs[ib][cb] = mma(qah, shi[cb], qs[ib][cb]);
+            qs[ib][cb] = mma(qah, slo[cb], qs[ib][cb]);
+            qs[ib][cb] = mma(qal, shi[cb], qs[ib][cb]);
+          }
+        }
+      }
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            U[ib][cb][r] -= ws[ib][cb][r];
+            O[ib][cb][r] = qs[ib][cb][r];
+          }
+    }
+
+    // ---- 9. O += P U; outputs
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      bf16x8 uhi, ulo;
+      split_pair(U[0][cb], U[1][cb], uhi, ulo);
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+        const int rowp = (16 * ib + ln) * BS + 4 * lg;
+        const bf16x8 pah = ld_2x64(&sh.pmh[rowp], &sh.pmh[rowp + 16]);
+        const bf16x8 pal = ld_2x64(&sh.pml[rowp], &sh.pml[rowp + 16]);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma(pah, uhi, acc);
+        acc = mma(pah, ulo, acc);
+        acc = mma(pal, uhi, acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + 16 * ib + 4 * lg + r;
+          if (t < T) a.out[((bseq * T + t) * H + h) * DV + col0 + 16 * cb + ln] = O[ib][cb][r] + acc[r];
+        }
+      }
+    }
+
+    // ---- 10. S = diag(G_C) S + (K o G_C / G)^T U
+    bf16x8 u2hi[NCB], u2lo[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) split_pair(U[0][cb], U[1][cb], u2hi[cb], u2lo[cb]);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int ro = (16 * kb + ln) * TS;
+      const int c0 = colp ^ ((kb & 1) << 4), c1 = colp ^ ((~kb & 1) << 4);
+      const bf16x8 kah = ld_2x64(&sh.kdh[ro + c0], &sh.kdh[ro + c1]);
+      const bf16x8 kal = ld_2x64(&sh.kdl[ro + c0], &sh.kdl[ro + c1]);
+      float gl[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gl[r] = exp2f(sh.cc[(C - 1) * CS + 16 * kb + 4 * lg + r]);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        f32x4 acc = {gl[0] * S[kb][cb][0], gl[1] * S[kb][cb][1], gl[2] * S[kb][cb][2], gl[3] * S[kb][cb][3]};
+        acc = mma(kah, u2hi[cb], acc);
+        acc = mma(kah, u2lo[cb], acc);
+        acc = mma(kal, u2hi[cb], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[kb][cb][r] = acc[r];
+      }
+    }
+  }
+
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st_base<BF>(brsrc, bvoff, ((16 * kb + r) * DV + 16 * cb) * EB, S[kb][cb][r]);
+}
+
 }  // namespace
 
-hipError_t launch_prefill(bool bf16_base, int dk, int dv, int tiles, const PoolArgs& p, const PrefillArgs& a,
-                          hipStream_t stream) {
-#define DL_PREFILL(BF_, DK_, DV_) \
-  prefill_kernel<DK_, DV_, BF_><<<tiles, kThreads, 0, stream>>>(p, a)
+hipError_t launch_prefill(int variant, bool bf16_base, int dk, int dv, int tiles, const PoolArgs& p,
+                          const PrefillArgs& a, hipStream_t stream) {
+#define DL_PREFILL(BF_, DK_, DV_)                                                   \
+  do {                                                                              \
+    if (variant == DL_KDA) prefill_kda_kernel<DK_, DV_, BF_><<<tiles, kThreads, 0, stream>>>(p, a); \
+    else prefill_kernel<DK_, DV_, BF_><<<tiles, kThreads, 0, stream>>>(p, a);        \
+  } while (0)
 #define DL_PREFILL_SHAPES(BF_)                                  \
   do {                                                          \
     if (dk == 128 && dv == 128) DL_PREFILL(BF_, 128, 128);      \

@@ -230,7 +230,7 @@ def make_prefill_io(pool: DeltaLogPool, q, k, v, decay, beta, out, eta=None, eps
     _need(q, "q", (B, T, H, dk), torch.bfloat16, dev)
     _need(k, "k", (B, T, H, dk), torch.bfloat16, dev)
     _need(v, "v", (B, T, H, dv), torch.bfloat16, dev)
-    _need(decay, "decay", (B, T, H), torch.float32, dev)
+    _need(decay, "decay", (B, T, H) if pool.variant == GDN else (B, T, H, dk), torch.float32, dev)
     if (beta is None) == (eta is None):
         raise ValueError("give exactly one of beta and eta")
     _need(beta if eta is None else eta, "beta" if eta is None else "eta", (B, T, H), torch.float32, dev)

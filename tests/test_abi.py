@@ -164,7 +164,7 @@ def test_prefill_errors(lib):
     p = _pool(dl)
     assert _prefill(lib, d, p, _pio(dl, T=-1)) == dl.DL_EINVAL
     assert lib.dl_prefill(ctypes.byref(d), ctypes.byref(p), None, None) == dl.DL_EINVAL
-    assert _prefill(lib, _dims(dl, variant=1), p, _pio(dl)) == dl.DL_EUNSUPPORTED  # GDN only
+    assert _prefill(lib, _dims(dl, variant=1), p, _pio(dl, decay=A + 4)) == dl.DL_EALIGN  # KDA decay rows: 16 B
     assert _prefill(lib, _dims(dl, variant=2, dk=64, dv=64), p, _pio(dl)) == dl.DL_EUNSUPPORTED
     assert _prefill(lib, d, p, _pio(dl, q=None)) == dl.DL_EINVAL
     assert _prefill(lib, d, p, _pio(dl, out=None)) == dl.DL_EINVAL

@@ -1,4 +1,4 @@
-"""dl_prefill (chunkwise GDN prefill on MFMA) against the fp64 eager oracle (GPU).
+"""dl_prefill (chunkwise GDN and KDA prefill on MFMA) against the fp64 eager oracle (GPU).
 
 A prompt of T tokens is the workload's first T drawn steps; the oracle runs the
 same T eager steps.  Outputs (one per token) and the final state (the base,
@@ -160,3 +160,74 @@ def test_reruns_are_bit_identical():
         pool = new_pool(inp, up=up)
         res.append((run_prefill(pool, up, 0, 77), pool.base.cpu().numpy()))
     assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+
+
+# --------------------------------------------------------------------- KDA --
+@pytest.mark.parametrize("T", [1, 31, 33, 100, 4096])
+def test_kda_prefill_lengths(T):
+    inp = make_inputs(3, T, batch=2, heads=4, pool=T)
+    check_prefill(inp, T)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
+def test_kda_head_size_combinations(dk, dv):
+    inp = make_inputs(3, 97, batch=2, heads=3, pool=97, dk=dk, dv=dv)
+    check_prefill(inp, 97)
+
+
+def test_kda_kaczmarz_step_size():
+    inp = make_inputs(3, 200, batch=2, heads=4, pool=200, kla=True)
+    assert inp.eta is not None
+    check_prefill(inp, 200)
+
+
+def test_kda_strong_zero_and_unit_channel_decays():
+    """Per-channel extremes inside one chunk: some channels decay to zero, some by 2^-40
+    per token (far below what a factorised 2^(c_i - r) 2^(r - c_j) could hold), some not
+    at all; the decay-weighted products are formed pair by pair, so all stay exact."""
+    inp = make_inputs(3, 70, batch=2, heads=2, pool=70)
+    inp.decay[5, :, :, :16] = 0.0
+    inp.decay[10:30, :, :, 16:32] = 2.0 ** -40
+    inp.decay[40:45, :, :, 32:] = 1.0
+    inp.beta[50:52] = 0.0
+    check_prefill(inp, 70)
+
+
+def test_kda_decode_continues_after_prefill():
+    inp = make_inputs(3, 140, batch=2, heads=4, pool=140)
+    up = Uploaded(inp)
+    pool = new_pool(inp, up=up)
+    run_prefill(pool, up, 0, 100)
+    outs = []
+    for t in range(100, 140):
+        dl.dl_decode_step(pool, up.io(t))
+        outs.append(up.out.cpu().numpy())
+    ref_S, ref_o = oracle.run_eager(inp, 140)
+    _close("decode outputs after prefill", np.stack(outs), ref_o[100:], (-1,))
+    _close("state after prefill + decode", materialized_state(pool), ref_S, (-2, -1))
+
+
+def test_kda_bf16_base_prefill():
+    T = 120
+    inp = make_inputs(3, T, batch=2, heads=4, pool=T)
+    up = Uploaded(inp)
+    pool = new_pool(inp, up=up, base_dtype=dl.BASE_BF16)
+    outs = run_prefill(pool, up, 0, T)
+    s0 = oracle.round_to_bf16(inp.s0.astype(np.float64))
+    ref_S, ref_o = oracle.run_eager(inp, T, s0=s0)
+    _close("outputs, bf16 base", outs, ref_o, (-1,))
+    got = pool.base.float().cpu().numpy().astype(np.float64)
+    ref = oracle.round_to_bf16(ref_S)
+    assert float(np.mean(got == ref)) >= 0.99
+
+
+def test_rwkv6_prefill_is_rejected():
+    inp = make_inputs(4, 8, batch=1, heads=2, pool=8)
+    up = Uploaded(inp)
+    pool = new_pool(inp, up=up)
+    out = torch.empty((1, 8, 2, inp.dv), dtype=torch.float32, device=dev())
+    io = dl.PrefillIO(up.q.data_ptr(), up.k.data_ptr(), up.v.data_ptr(), up.decay.data_ptr(), None,
+                      out.data_ptr(), None, 0.0, 8)
+    with pytest.raises(dl.DeltaLogError) as ei:
+        dl.dl_prefill(pool, io)
+    assert ei.value.status == dl.DL_EUNSUPPORTED
