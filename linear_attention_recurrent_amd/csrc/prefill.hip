@@ -804,8 +804,77 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
       }
     }
 
-    // ---- 4. A and P directly: thread (row pair ip, ip' = 31 - ip; channel slice sl)
+    // ---- 4. A and P.  G_i / G_j = (G_i / G_R)(G_R / G_j) splits the decay of a pair
+    //        around a reference token R: R = start of the chunk for the block of
+    //        rows and columns 0..15, R = token 15 for the blocks of rows 16..31.
+    //        Row factors are then <= 1 and column factors at most the decay over 16
+    //        tokens, so when no channel decays by more than 2^-60 over either half of
+    //        the chunk the products run on MFMA with split operands (three waves, one
+    //        16 x 16 block each).  Otherwise every pair is formed directly.
+    bool direct;
     {
+      bool big = false;
+      for (int ch = tid; ch < DK; ch += kThreads)
+        big = big || -sh.cc[15 * CS + ch] > 60.f || sh.cc[15 * CS + ch] - sh.cc[(C - 1) * CS + ch] > 60.f;
+      direct = __syncthreads_or(big);
+    }
+    if (!direct) {
+      if (wave < 3) {
+        const int ib = wave == 0 ? 0 : 1, jb = wave == 2 ? 1 : 0;
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+          const int ch0 = 32 * kk + 8 * lg;
+          float cr[8], cj[8], ref[8], kr[8], qr[8], kc[8];
+          load8(&sh.cc[(16 * ib + ln) * CS + ch0], cr);
+          load8(&sh.cc[(16 * jb + ln) * CS + ch0], cj);
+          if (ib == 1) load8(&sh.cc[15 * CS + ch0], ref);
+          else
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ref[e] = 0.f;
+          unpack8(*reinterpret_cast<const uint4*>(&sh.k[(16 * ib + ln) * KS + ch0]), kr);
+          unpack8(*reinterpret_cast<const uint4*>(&sh.q[(16 * ib + ln) * KS + ch0]), qr);
+          unpack8(*reinterpret_cast<const uint4*>(&sh.k[(16 * jb + ln) * KS + ch0]), kc);
+          uint32_t ah[4], al[4], qh[4], ql[4], bh[4], bl[4];
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float r0 = exp2f(cr[e] - ref[e]), r1 = exp2f(cr[e + 1] - ref[e + 1]);
+            const float c0 = exp2f(ref[e] - cj[e]), c1 = exp2f(ref[e + 1] - cj[e + 1]);
+            split2(kr[e] * r0, kr[e + 1] * r1, ah[e / 2], al[e / 2]);
+            split2(qr[e] * r0, qr[e + 1] * r1, qh[e / 2], ql[e / 2]);
+            split2(kc[e] * c0, kc[e + 1] * c1, bh[e / 2], bl[e / 2]);
+          }
+          const bf16x8 Ah = pack8(ah[0], ah[1], ah[2], ah[3]), Al = pack8(al[0], al[1], al[2], al[3]);
+          const bf16x8 Qh = pack8(qh[0], qh[1], qh[2], qh[3]), Ql = pack8(ql[0], ql[1], ql[2], ql[3]);
+          const bf16x8 Bh = pack8(bh[0], bh[1], bh[2], bh[3]), Bl = pack8(bl[0], bl[1], bl[2], bl[3]);
+          accA = mma(Ah, Bh, accA);
+          accA = mma(Ah, Bl, accA);
+          accA = mma(Al, Bh, accA);
+          accP = mma(Qh, Bh, accP);
+          accP = mma(Qh, Bl, accP);
+          accP = mma(Ql, Bh, accP);
+        }
+        const int j = 16 * jb + ln;
+        float pm[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * ib + 4 * lg + r;
+          sh.g[i * MS + j] = j < i ? sh.beta[i] * accA[r] : 0.f;
+          pm[r] = j <= i ? accP[r] : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; r += 2) {
+          const int i = 16 * ib + 4 * lg + r;
+          uint32_t hi, lo;
+          split2(pm[r], pm[r + 1], hi, lo);
+          sh.pmh[i * BS + j] = static_cast<uint16_t>(hi);
+          sh.pmh[(i + 1) * BS + j] = static_cast<uint16_t>(hi >> 16);
+          sh.pml[i * BS + j] = static_cast<uint16_t>(lo);
+          sh.pml[(i + 1) * BS + j] = static_cast<uint16_t>(lo >> 16);
+        }
+      }
+    } else {
+      // pairwise: thread (row pair ip, ip' = 31 - ip; channel slice sl)
       constexpr int SL = DK / 16;  // channels per slice
       const int ip = tid >> 4, sl = tid & 15;
       float kr[2][SL], qr[2][SL], cr[2][SL];

@@ -193,6 +193,14 @@ def test_kda_strong_zero_and_unit_channel_decays():
     check_prefill(inp, 70)
 
 
+def test_kda_strong_decays_within_the_matrix_path():
+    """Channels decaying by 2^-3 per token: 2^-48 over half a chunk, inside the range where
+    the decay-weighted products run on MFMA with column factors up to 2^48."""
+    inp = make_inputs(3, 96, batch=2, heads=2, pool=96)
+    inp.decay[:, :, :, :40] = 2.0 ** -3
+    check_prefill(inp, 96)
+
+
 def test_kda_decode_continues_after_prefill():
     inp = make_inputs(3, 140, batch=2, heads=4, pool=140)
     up = Uploaded(inp)
