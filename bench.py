@@ -262,9 +262,12 @@ def prefill_model(dk: int, dv: int, C: int = PREFILL_CHUNK, variant: int = 0) ->
     KDA: the decay is a dk-vector per token, the decay-weighted K K^T and Q K^T are formed
     on the vector units (not counted as MFMA work), and W, (Q o G) S and the state update
     take three products each because their key/query operand carries the decay."""
-    byts = 2 * dk * 2 + 2 * dv + 4 * (dk if variant == 1 else 1) + 4 + 4 * dv
+    byts = 2 * dk * 2 + 2 * dv + 4 * (1 if variant == 0 else dk) + (4 if variant != 2 else 0) + 4 * dv
     method = 2 * C * C * dk * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 3  # per chunk
-    if variant == 1:
+    if variant == 2:  # P (3 lower blocks, x3), (R o G) S (x3), P V (x2), state update (x2)
+        method = 2 * C * C * dk + 2 * C * dk * dv + 2 * C * C * dv + 2 * C * dk * dv
+        issued = (3 * 2 * 16 * 16 * dk * 3 + 2 * C * dk * dv * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 2)
+    elif variant == 1:
         issued = (2 * C * C * dk * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 3 + 2 * C * dk * dv * 3
                   + 2 * C * C * dv * 3 + 2 * C * dk * dv * 3)
     else:  # K K^T, Q K^T lower blocks (3 of 4 each), W (x2), U~ (x2), W S (x3), Q S (x2), P U (x3), K^T U (x2)
@@ -289,7 +292,7 @@ def prefill_leg(args, inp, Tn, base_dt, reps: int = 5) -> dict:
     out = torch.empty((B, Tp, H, dv), dtype=torch.float32, device=dev)
     pool = dl.DeltaLogPool(inp.variant, B, H, dk, dv, L, dev, base_dt)
     dl.dl_init_state(pool, Tn["s0"], None)
-    io = dl.make_prefill_io(pool, q, k, v, decay, beta, out, eta, inp.eps)
+    io = dl.make_prefill_io(pool, q, k, v, decay, beta, out, eta, inp.eps, bonus=Tn["bonus"])
     for _ in range(2):
         dl.dl_prefill(pool, io)
     torch.cuda.synchronize()
@@ -474,7 +477,7 @@ def main():
         state = T["s0"].clone()
         secs_e = time_loop(lambda t: dl.dl_eager_step(var, state, ios[t % P]), K, W, chunk)
         result["eager"] = secs_e
-    if args.only == "prefill" or (args.only is None and var in (0, 1)):
+    if args.only == "prefill" or args.only is None:
         result["prefill"] = prefill_leg(args, inp, T, base_dt)
     if args.only is not None:
         if args.only == "prefill":

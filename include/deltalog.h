@@ -156,15 +156,16 @@ int dl_eager_step(const dl_dims *dims, float *state, const dl_step_io *io, void 
 /* A prompt's inputs and outputs for dl_prefill (all device).  T = tokens >= 0;
  * row t of a sequence is its t-th prompt token. */
 typedef struct {
-  const uint16_t *q;   /* bf16 [batch][T][heads][dk]                                           */
+  const uint16_t *q;   /* bf16 [batch][T][heads][dk]  (RWKV6: receptance r)                    */
   const uint16_t *k;   /* bf16 [batch][T][heads][dk]                                           */
   const uint16_t *v;   /* bf16 [batch][T][heads][dv]                                           */
-  const float *decay;  /* GDN: fp32 [batch][T][heads] alpha; KDA: fp32 [batch][T][heads][dk];
+  const float *decay;  /* GDN: fp32 [batch][T][heads] alpha; KDA/RWKV6: fp32 [batch][T][heads][dk];
                           values in (0, 1]                                                      */
-  const float *beta;   /* fp32 [batch][T][heads]; or NULL with eta                              */
+  const float *beta;   /* GDN/KDA: fp32 [batch][T][heads], or NULL with eta; RWKV6: NULL        */
+  const float *bonus;  /* RWKV6: fp32 [heads][dk]; GDN/KDA: NULL                                */
   float *out;          /* fp32 [batch][T][heads][dv]  every token's output (written)            */
-  const float *eta;    /* instead of beta: fp32 [batch][T][heads], the Kaczmarz step size
-                          beta = eta / (||k||^2 + eps) (Kaczmarz Linear Attention abstract)    */
+  const float *eta;    /* GDN/KDA instead of beta: fp32 [batch][T][heads], the Kaczmarz step
+                          size beta = eta / (||k||^2 + eps) (Kaczmarz Linear Attention abstract) */
   float eps;           /* >= 0 (ignored when eta is NULL)                                       */
   int32_t tokens;      /* T                                                                     */
 } dl_prefill_io;
@@ -179,11 +180,14 @@ typedef struct {
  * triangular solve (the WY form) and every product with the state is a matrix
  * product.  Any non-empty log is folded into the base first, as dl_merge with
  * min_fill = 1 would.  With a bf16 base the final state is rounded once.
- * GDN and KDA (RWKV6: DL_EUNSUPPORTED); for KDA the decay-weighted products
- * inside a chunk are formed channel by channel, the others on matrix units.  Errors:
+ * All three variants; for KDA and RWKV6 (a decay per key channel) the
+ * decay-weighted products inside a chunk are split around a reference token
+ * per half chunk and run on matrix units when no channel decays by more than
+ * 2^-60 over half a chunk, else they are formed pair by pair.  Errors:
  * DL_EINVAL for tokens < 0, null q/k/v/decay/out, or eps < 0 with eta set;
- * DL_EUNSUPPORTED unless exactly one of beta and eta is given.  tokens == 0
- * only folds the logs and looks at no prompt pointer. */
+ * DL_EUNSUPPORTED if beta/eta/bonus do not match the variant (GDN/KDA: exactly
+ * one of beta and eta, no bonus; RWKV6: bonus only).  tokens == 0 only folds
+ * the logs and looks at no prompt pointer. */
 int dl_prefill(const dl_dims *dims, const dl_pool *pool, const dl_prefill_io *io, void *stream);
 
 /* A static, human-readable name for a status code (never NULL). */

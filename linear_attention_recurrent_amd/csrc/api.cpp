@@ -130,14 +130,15 @@ int dl_prefill(const dl_dims* dims, const dl_pool* pool, const dl_prefill_io* io
   if (rc != DL_OK) return rc;
   if (io == nullptr || io->tokens < 0) return DL_EINVAL;
   if (dims->batch == 0) return DL_OK;
-  if (dims->variant == DL_RWKV6) return DL_EUNSUPPORTED;
   if ((rc = check_pool(pool, dims->variant)) != DL_OK) return rc;
   if (io->tokens > 0) {  // an empty prompt only folds: its pointers are not looked at
     if (!io->q || !io->k || !io->v || !io->decay || !io->out) return DL_EINVAL;
-    if ((io->beta == nullptr) == (io->eta == nullptr)) return DL_EUNSUPPORTED;
+    const bool rwkv = dims->variant == DL_RWKV6;
+    if (rwkv && (io->beta != nullptr || io->eta != nullptr || io->bonus == nullptr)) return DL_EUNSUPPORTED;
+    if (!rwkv && ((io->beta == nullptr) == (io->eta == nullptr) || io->bonus != nullptr)) return DL_EUNSUPPORTED;
     if (io->eta != nullptr && !(io->eps >= 0.f)) return DL_EINVAL;
     if (misaligned(io->q) || misaligned(io->k) || misaligned(io->v) ||
-        misaligned(io->decay, dims->variant == DL_KDA ? 16 : 4) ||
+        misaligned(io->decay, dims->variant == DL_GDN ? 4 : 16) || (io->bonus && misaligned(io->bonus)) ||
         misaligned(io->out, 4) || (io->beta && misaligned(io->beta, 4)) || (io->eta && misaligned(io->eta, 4)))
       return DL_EALIGN;
   }
@@ -147,7 +148,7 @@ int dl_prefill(const dl_dims* dims, const dl_pool* pool, const dl_prefill_io* io
   hipError_t e = dl::launch_merge(dims->variant, bf16_base(dims), dims->dk, dims->dv, tiles,
                                   pool_args(dims, pool), 1, st);
   if (e != hipSuccess || io->tokens == 0) return hip_status(e);
-  const dl::PrefillArgs a{io->q, io->k, io->v, io->decay, io->beta, io->eta, io->out, io->eps, io->tokens};
+  const dl::PrefillArgs a{io->q, io->k, io->v, io->decay, io->beta, io->eta, io->bonus, io->out, io->eps, io->tokens};
   return hip_status(dl::launch_prefill(dims->variant, bf16_base(dims), dims->dk, dims->dv, tiles,
                                        pool_args(dims, pool), a, st));
 }

@@ -191,8 +191,9 @@ struct PoolArgs {
   int L;
 };
 
-// Arguments of the prefill kernel: a prompt of `tokens` rows per sequence,
-// [batch][tokens][heads][d] for q, k, v, out and [batch][tokens][heads] for decay, beta, eta.
+// Arguments of the prefill kernels: a prompt of `tokens` rows per sequence,
+// [batch][tokens][heads][d] for q, k, v, out (and KDA/RWKV6 decay) and
+// [batch][tokens][heads] for beta, eta (and GDN decay).
 struct PrefillArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -200,6 +201,7 @@ struct PrefillArgs {
   const float* decay;
   const float* beta;
   const float* eta;
+  const float* bonus;  // RWKV6: [heads][dk]
   float* out;
   float eps;
   int tokens;

@@ -1,6 +1,7 @@
-// Chunkwise prefill for the GDN delta rule (and its Kaczmarz step size) on gfx950.
+// Chunkwise prefill on gfx950: the GDN delta rule (and its Kaczmarz step size)
+// below, KDA and RWKV6 further down.
 //
-// dl_prefill runs T prompt tokens of the recurrence
+// For GDN, dl_prefill runs T prompt tokens of the recurrence
 //   S_i = a_i S_{i-1} + k_i u_i^T,   u_i = b_i (v_i - (a_i S_{i-1})^T k_i),   o_i = S_i^T q_i
 // for every (sequence, head) tile and leaves S_T in the base.  The Q-Delta,
 // Kaczmarz Linear Attention and Gated DeltaNet-2 abstracts (card pages) name
@@ -1070,6 +1071,410 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
       for (int r = 0; r < 4; ++r) st_base<BF>(brsrc, bvoff, ((16 * kb + r) * DV + 16 * cb) * EB, S[kb][cb][r]);
 }
 
+
+// ---------------------------------------------------------------- RWKV6 prefill
+// RWKV6 reads the state before each token's write and adds a bonus term:
+//   o_i = S_{i-1}^T r_i + (sum_c r_i[c] u[c] k_i[c]) v_i,   S_i = diag(w_i) S_{i-1} + k_i v_i^T.
+// With G_i = w_1 ... w_i within the chunk (G_-1 = 1; log2 in cc):
+//   O  = (R o G_prev) S + P V,   P_ij = sum_c r_i[c] k_j[c] G_{i-1}[c] / G_j[c]  (j < i),
+//                                P_ii = sum_c r_i[c] u[c] k_i[c]
+//   S' = diag(G_C) S + (K o G_C / G)^T V
+// There is no delta-rule solve; V enters every product as an exact bf16 operand.
+// P's decay-weighted part uses the same reference-token split (and pairwise
+// fallback) as KDA, with the row decay taken one token earlier.
+template <int DK, int DV>
+struct PrefillRwkvLds {
+  static constexpr int C = kChunk;
+  static constexpr int KS = DK + 8;
+  static constexpr int TS = C + 8;
+  static constexpr int BS = C + 8;
+  static constexpr int CS = DK + 4;
+  float bonus[DK];
+  float pd[C];                        // the bonus diagonal of P
+  uint16_t pmh[C * BS], pml[C * BS];  // P, split
+  uint16_t k[C * KS];                 // K, token rows
+  uint16_t q[C * KS];                 // R, token rows
+  uint16_t rgh[C * KS], rgl[C * KS];  // R o G_prev, token rows, split
+  uint16_t vt[DV * TS];               // V token-major
+  uint16_t kdh[DK * TS], kdl[DK * TS];  // K o G_C / G, token-major, split
+  float cc[C * CS];                     // log2 decays, then their prefix sums
+};
+
+template <int DK, int DV, bool BF>
+__global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, PrefillArgs a) {
+  constexpr int C = kChunk;
+  constexpr int CW = DV / 4;
+  constexpr int NCB = CW / 16;
+  constexpr int NKB = DK / 16;
+  constexpr int NKP = DK / 32;
+  using Lds = PrefillRwkvLds<DK, DV>;
+  constexpr int KS = Lds::KS, TS = Lds::TS, BS = Lds::BS, CS = Lds::CS;
+  __shared__ __align__(16) Lds sh;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 15, lg = lane >> 4;
+  const int tile = blockIdx.x;
+  const int H = pa.heads, T = a.tokens;
+  const size_t bseq = static_cast<size_t>(tile / H), h = static_cast<size_t>(tile % H);
+  const int col0 = wave * CW;
+  const int sw0 = (ln >> 3) << 3;
+  const int colw = (8 * lg) ^ sw0;
+
+  float S[NKB][NCB][4];
+  constexpr int EB = BF ? 2 : 4;
+  const auto brsrc = make_rsrc(static_cast<const char*>(pa.base) + static_cast<size_t>(tile) * DK * DV * EB,
+                               DK * DV * EB);
+  const uint32_t bvoff = static_cast<uint32_t>((4 * lg * DV + col0 + ln) * EB);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[kb][cb][r] = ld_base<BF>(brsrc, bvoff, ((16 * kb + r) * DV + 16 * cb) * EB);
+  for (int ch = tid; ch < DK; ch += kThreads) sh.bonus[ch] = a.bonus[h * DK + ch];
+
+  constexpr int KP = DK / 8, VP = DV / 8;
+  constexpr int NPK = C / 2 * KP, NPV = C / 2 * VP;
+  constexpr int LK = (NPK + kThreads - 1) / kThreads, LV = (NPV + kThreads - 1) / kThreads;
+  constexpr int ND = C * DK / 4 / kThreads;
+  uint4 nk[LK][2], nq[LK][2], nv[LV][2];
+  float4 nd[ND];
+  auto row_ptr = [&](const uint16_t* x, int t, int d) { return x + ((bseq * T + t) * H + h) * d; };
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+      const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        nk[i][s2] = nq[i][s2] = make_uint4(0, 0, 0, 0);
+        if (pc < NPK && t0 + tok + s2 < T) {
+          nk[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.k, t0 + tok + s2, DK))[seg];
+          nq[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.q, t0 + tok + s2, DK))[seg];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        nv[i][s2] = make_uint4(0, 0, 0, 0);
+        if (pc < NPV && t0 + tok + s2 < T)
+          nv[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.v, t0 + tok + s2, DV))[seg];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      const int pc = tid + i * kThreads, tok = pc / (DK / 4), seg = pc % (DK / 4);
+      nd[i] = make_float4(1.f, 1.f, 1.f, 1.f);
+      if (t0 + tok < T)
+        nd[i] = reinterpret_cast<const float4*>(a.decay + ((bseq * T + t0 + tok) * H + h) * DK)[seg];
+    }
+  };
+  auto interleave = [](const uint4 w0, const uint4 w1, uint32_t (&o)[8]) {
+    const uint32_t a0[4] = {w0.x, w0.y, w0.z, w0.w}, a1[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o[2 * e] = (a0[e] & 0xffffu) | (a1[e] << 16);
+      o[2 * e + 1] = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
+    }
+  };
+  fetch(0);
+
+  for (int t0 = 0; t0 < T; t0 += C) {
+    __syncthreads();
+
+    // ---- 1. K, R rows; V token-major; clamped log2 decays
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+      const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
+      if (pc < NPK) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          *reinterpret_cast<uint4*>(&sh.k[(tok + s2) * KS + seg * 8]) = nk[i][s2];
+          *reinterpret_cast<uint4*>(&sh.q[(tok + s2) * KS + seg * 8]) = nq[i][s2];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
+      if (pc < NPV) {
+        uint32_t vw[8];
+        interleave(nv[i][0], nv[i][1], vw);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ch = seg * 8 + e;
+          *reinterpret_cast<uint32_t*>(&sh.vt[ch * TS + tswz(ch, tok)]) = vw[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+      const int pc = tid + i * kThreads, tok = pc / (DK / 4), seg = pc % (DK / 4);
+      *reinterpret_cast<float4*>(&sh.cc[tok * CS + seg * 4]) =
+          make_float4(step_log2_decay(nd[i].x), step_log2_decay(nd[i].y), step_log2_decay(nd[i].z),
+                      step_log2_decay(nd[i].w));
+    }
+    if (t0 + C < T) fetch(t0 + C);
+    __syncthreads();
+
+    // ---- 2. prefix sums of the log2 decays over the chunk's tokens
+#pragma unroll
+    for (int it = 0; it < DK / 8; ++it) {
+      const int ch = wave * (DK / 4) + 2 * it + (lane >> 5), tok = lane & 31;
+      float x = sh.cc[tok * CS + ch];
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        const float y = __shfl_up(x, off, 32);
+        if (tok >= off) x += y;
+      }
+      sh.cc[tok * CS + ch] = x;
+    }
+    __syncthreads();
+
+    // ---- 3. R o G_prev (rows) and K o G_C / G (token-major), split; the bonus diagonal
+#pragma unroll
+    for (int i = 0; i < LK; ++i) {
+      const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
+      if (pc < NPK) {
+        float kf[2][8], rf[2][8], cf[2][8], cp[8], cl[8];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          unpack8(*reinterpret_cast<const uint4*>(&sh.k[(tok + s2) * KS + seg * 8]), kf[s2]);
+          unpack8(*reinterpret_cast<const uint4*>(&sh.q[(tok + s2) * KS + seg * 8]), rf[s2]);
+          load8(&sh.cc[(tok + s2) * CS + seg * 8], cf[s2]);
+        }
+        if (tok > 0) load8(&sh.cc[(tok - 1) * CS + seg * 8], cp);  // G_prev of token tok
+        else
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cp[e] = 0.f;
+        load8(&sh.cc[(C - 1) * CS + seg * 8], cl);
+        uint32_t rh[2][4], rl[2][4], kdh2[8], kdl2[8];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          // token tok reads G_{tok-1}, token tok + 1 reads G_tok
+          split2(rf[0][e] * exp2f(cp[e]), rf[0][e + 1] * exp2f(cp[e + 1]), rh[0][e / 2], rl[0][e / 2]);
+          split2(rf[1][e] * exp2f(cf[0][e]), rf[1][e + 1] * exp2f(cf[0][e + 1]), rh[1][e / 2], rl[1][e / 2]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          split2(kf[0][e] * exp2f(cl[e] - cf[0][e]), kf[1][e] * exp2f(cl[e] - cf[1][e]), kdh2[e], kdl2[e]);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          *reinterpret_cast<uint4*>(&sh.rgh[(tok + s2) * KS + seg * 8]) =
+              make_uint4(rh[s2][0], rh[s2][1], rh[s2][2], rh[s2][3]);
+          *reinterpret_cast<uint4*>(&sh.rgl[(tok + s2) * KS + seg * 8]) =
+              make_uint4(rl[s2][0], rl[s2][1], rl[s2][2], rl[s2][3]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ch = seg * 8 + e, o = ch * TS + tswz(ch, tok);
+          *reinterpret_cast<uint32_t*>(&sh.kdh[o]) = kdh2[e];
+          *reinterpret_cast<uint32_t*>(&sh.kdl[o]) = kdl2[e];
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) d = fmaf(rf[s2][e] * sh.bonus[seg * 8 + e], kf[s2][e], d);
+          d = group_sum<KP>(d);
+          if (seg == 0) sh.pd[tok + s2] = d;
+        }
+      }
+    }
+
+    // ---- 4. P (see the KDA kernel for the reference-token split; rows use G_{i-1})
+    bool direct;
+    {
+      bool big = false;
+      for (int ch = tid; ch < DK; ch += kThreads)
+        big = big || -sh.cc[15 * CS + ch] > 60.f || sh.cc[15 * CS + ch] - sh.cc[(C - 1) * CS + ch] > 60.f;
+      direct = __syncthreads_or(big);  // also orders step 3's stores before the reads below
+    }
+    if (!direct) {
+      if (wave < 3) {
+        const int ib = wave == 0 ? 0 : 1, jb = wave == 2 ? 1 : 0;
+        f32x4 accP = {0.f, 0.f, 0.f, 0.f};
+        const int ri = 16 * ib + ln;  // this lane's row of the A operand
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+          const int ch0 = 32 * kk + 8 * lg;
+          float cr[8], cj[8], ref[8], rr[8], kc[8];
+          if (ri > 0) load8(&sh.cc[(ri - 1) * CS + ch0], cr);
+          else
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cr[e] = 0.f;
+          load8(&sh.cc[(16 * jb + ln) * CS + ch0], cj);
+          if (ib == 1) load8(&sh.cc[15 * CS + ch0], ref);
+          else
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ref[e] = 0.f;
+          unpack8(*reinterpret_cast<const uint4*>(&sh.q[ri * KS + ch0]), rr);
+          unpack8(*reinterpret_cast<const uint4*>(&sh.k[(16 * jb + ln) * KS + ch0]), kc);
+          uint32_t ah[4], al[4], bh[4], bl[4];
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            split2(rr[e] * exp2f(cr[e] - ref[e]), rr[e + 1] * exp2f(cr[e + 1] - ref[e + 1]), ah[e / 2], al[e / 2]);
+            split2(kc[e] * exp2f(ref[e] - cj[e]), kc[e + 1] * exp2f(ref[e + 1] - cj[e + 1]), bh[e / 2], bl[e / 2]);
+          }
+          const bf16x8 Ah = pack8(ah[0], ah[1], ah[2], ah[3]), Al = pack8(al[0], al[1], al[2], al[3]);
+          const bf16x8 Bh = pack8(bh[0], bh[1], bh[2], bh[3]), Bl = pack8(bl[0], bl[1], bl[2], bl[3]);
+          accP = mma(Ah, Bh, accP);
+          accP = mma(Ah, Bl, accP);
+          accP = mma(Al, Bh, accP);
+        }
+        const int j = 16 * jb + ln;
+        float pm[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * ib + 4 * lg + r;
+          pm[r] = j < i ? accP[r] : j == i ? sh.pd[i] : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; r += 2) {
+          const int i = 16 * ib + 4 * lg + r;
+          uint32_t hi, lo;
+          split2(pm[r], pm[r + 1], hi, lo);
+          sh.pmh[i * BS + j] = static_cast<uint16_t>(hi);
+          sh.pmh[(i + 1) * BS + j] = static_cast<uint16_t>(hi >> 16);
+          sh.pml[i * BS + j] = static_cast<uint16_t>(lo);
+          sh.pml[(i + 1) * BS + j] = static_cast<uint16_t>(lo >> 16);
+        }
+      } else {
+        // the upper right block of P is zero
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = (lane >> 4) + 4 * e, j = 16 + ln;
+          sh.pmh[i * BS + j] = 0;
+          sh.pml[i * BS + j] = 0;
+        }
+      }
+    } else {
+      // pairwise: thread (row pair ip, 31 - ip; channel slice sl); j < row, plus the diagonal
+      constexpr int SL = DK / 16;
+      const int ip = tid >> 4, sl = tid & 15;
+      for (int e = tid; e < C * C; e += kThreads) {
+        const int i = e / C, jj = e % C;
+        if (jj >= i) {
+          uint32_t hi, lo;
+          split2(jj == i ? sh.pd[i] : 0.f, 0.f, hi, lo);
+          sh.pmh[i * BS + jj] = static_cast<uint16_t>(hi);
+          sh.pml[i * BS + jj] = static_cast<uint16_t>(lo);
+        }
+      }
+      float rr[2][SL], cr[2][SL];
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const int r = w == 0 ? ip : C - 1 - ip;
+#pragma unroll
+        for (int e = 0; e < SL; ++e) {
+          rr[w][e] = bf16_to_f32(sh.q[r * KS + sl * SL + e]);
+          cr[w][e] = r > 0 ? sh.cc[(r - 1) * CS + sl * SL + e] : 0.f;
+        }
+      }
+      for (int n = 0; n < C - 1; ++n) {  // row ip takes j = 0..ip-1, row 31 - ip takes j = 0..30 - ip
+        const bool first = n < ip;
+        const int r = first ? ip : C - 1 - ip, j = first ? n : n - ip;
+        float pv = 0.f;
+#pragma unroll
+        for (int e = 0; e < SL; ++e) {
+          const float u = bf16_to_f32(sh.k[j * KS + sl * SL + e]) *
+                          exp2f((first ? cr[0][e] : cr[1][e]) - sh.cc[j * CS + sl * SL + e]);
+          pv = fmaf(first ? rr[0][e] : rr[1][e], u, pv);
+        }
+        pv = group_sum<16>(pv);
+        if (sl == 0) {
+          uint32_t hi, lo;
+          split2(pv, 0.f, hi, lo);
+          sh.pmh[r * BS + j] = static_cast<uint16_t>(hi);
+          sh.pml[r * BS + j] = static_cast<uint16_t>(lo);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- 5. O = (R o G_prev) S + P V; outputs
+    float O[2][NCB][4];
+    {
+      f32x4 qs[2][NCB];
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) qs[ib][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kp = 0; kp < NKP; ++kp) {
+        bf16x8 shi[NCB], slo[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) split_pair(S[2 * kp][cb], S[2 * kp + 1][cb], shi[cb], slo[cb]);
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+          const int rowk = (16 * ib + ln) * KS + 32 * kp + 4 * lg;
+          const bf16x8 rah = ld_2x64(&sh.rgh[rowk], &sh.rgh[rowk + 16]);
+          const bf16x8 ral = ld_2x64(&sh.rgl[rowk], &sh.rgl[rowk + 16]);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            qs[ib][cb] = mma(rah, shi[cb], qs[ib][cb]);
+            qs[ib][cb] = mma(rah, slo[cb], qs[ib][cb]);
+            qs[ib][cb] = mma(ral, shi[cb], qs[ib][cb]);
+          }
+        }
+      }
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) O[ib][cb][r] = qs[ib][cb][r];
+    }
+    bf16x8 vb[NCB];  // V[token 8 lg + s][this lane's column], the B operand of P V and of the update
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      vb[cb] = ld_b128(&sh.vt[(col0 + 16 * cb + ln) * TS + (colw ^ ((((col0 >> 4) + cb) & 1) << 4))]);
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      const bf16x8 pah = ld_b128(&sh.pmh[(16 * ib + ln) * BS + 8 * lg]);
+      const bf16x8 pal = ld_b128(&sh.pml[(16 * ib + ln) * BS + 8 * lg]);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mma(pah, vb[cb], acc);
+        acc = mma(pal, vb[cb], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + 16 * ib + 4 * lg + r;
+          if (t < T) a.out[((bseq * T + t) * H + h) * DV + col0 + 16 * cb + ln] = O[ib][cb][r] + acc[r];
+        }
+      }
+    }
+
+    // ---- 6. S = diag(G_C) S + (K o G_C / G)^T V
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const int o = (16 * kb + ln) * TS + (colw ^ ((kb & 1) << 4));
+      const bf16x8 kah = ld_b128(&sh.kdh[o]), kal = ld_b128(&sh.kdl[o]);
+      float gl[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gl[r] = exp2f(sh.cc[(C - 1) * CS + 16 * kb + 4 * lg + r]);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        f32x4 acc = {gl[0] * S[kb][cb][0], gl[1] * S[kb][cb][1], gl[2] * S[kb][cb][2], gl[3] * S[kb][cb][3]};
+        acc = mma(kah, vb[cb], acc);
+        acc = mma(kal, vb[cb], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[kb][cb][r] = acc[r];
+      }
+    }
+  }
+
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st_base<BF>(brsrc, bvoff, ((16 * kb + r) * DV + 16 * cb) * EB, S[kb][cb][r]);
+}
+
 }  // namespace
 
 hipError_t launch_prefill(int variant, bool bf16_base, int dk, int dv, int tiles, const PoolArgs& p,
@@ -1077,6 +1482,7 @@ hipError_t launch_prefill(int variant, bool bf16_base, int dk, int dv, int tiles
 #define DL_PREFILL(BF_, DK_, DV_)                                                   \
   do {                                                                              \
     if (variant == DL_KDA) prefill_kda_kernel<DK_, DV_, BF_><<<tiles, kThreads, 0, stream>>>(p, a); \
+    else if (variant == DL_RWKV6) prefill_rwkv_kernel<DK_, DV_, BF_><<<tiles, kThreads, 0, stream>>>(p, a); \
     else prefill_kernel<DK_, DV_, BF_><<<tiles, kThreads, 0, stream>>>(p, a);        \
   } while (0)
 #define DL_PREFILL_SHAPES(BF_)                                  \

@@ -42,8 +42,9 @@ class StepIO(ctypes.Structure):
 
 class PrefillIO(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
-                ("decay", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("out", ctypes.c_void_p),
-                ("eta", ctypes.c_void_p), ("eps", ctypes.c_float), ("tokens", ctypes.c_int32)]
+                ("decay", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("bonus", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("eta", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("tokens", ctypes.c_int32)]
 
 
 class DeltaLogError(RuntimeError):
@@ -220,7 +221,7 @@ def dl_eager_step(variant: int, state: torch.Tensor, io: StepIO, stream=None) ->
     _check(rc, "dl_eager_step")
 
 
-def make_prefill_io(pool: DeltaLogPool, q, k, v, decay, beta, out, eta=None, eps=0.0) -> PrefillIO:
+def make_prefill_io(pool: DeltaLogPool, q, k, v, decay, beta, out, eta=None, eps=0.0, bonus=None) -> PrefillIO:
     """Check a prompt's tensors ([batch][T][heads][...], see dl_prefill_io) against the pool."""
     B, H, dk, dv = pool.batch, pool.heads, pool.dk, pool.dv
     if k is None or k.dim() != 4:
@@ -231,11 +232,19 @@ def make_prefill_io(pool: DeltaLogPool, q, k, v, decay, beta, out, eta=None, eps
     _need(k, "k", (B, T, H, dk), torch.bfloat16, dev)
     _need(v, "v", (B, T, H, dv), torch.bfloat16, dev)
     _need(decay, "decay", (B, T, H) if pool.variant == GDN else (B, T, H, dk), torch.float32, dev)
-    if (beta is None) == (eta is None):
-        raise ValueError("give exactly one of beta and eta")
-    _need(beta if eta is None else eta, "beta" if eta is None else "eta", (B, T, H), torch.float32, dev)
+    if pool.variant == RWKV6:
+        _need(bonus, "bonus", (H, dk), torch.float32, dev)
+        if beta is not None or eta is not None:
+            raise ValueError("beta and eta must be None for RWKV6")
+    else:
+        if (beta is None) == (eta is None):
+            raise ValueError("give exactly one of beta and eta")
+        _need(beta if eta is None else eta, "beta" if eta is None else "eta", (B, T, H), torch.float32, dev)
+        if bonus is not None:
+            raise ValueError("bonus must be None for GDN/KDA")
     _need(out, "out", (B, T, H, dv), torch.float32, dev)
-    return PrefillIO(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta), _ptr(out), _ptr(eta), float(eps), T)
+    return PrefillIO(_ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta), _ptr(bonus), _ptr(out), _ptr(eta),
+                     float(eps), T)
 
 
 def dl_prefill(pool: DeltaLogPool, io: PrefillIO, stream=None) -> None:

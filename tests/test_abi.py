@@ -149,9 +149,9 @@ def test_product_path_does_not_use_the_oracle():
 
 
 def _pio(dl, T=8, **kw):
-    f = dict(q=A, k=A, v=A, decay=A, beta=A, out=A, eta=None, eps=0.0)
+    f = dict(q=A, k=A, v=A, decay=A, beta=A, bonus=None, out=A, eta=None, eps=0.0)
     f.update(kw)
-    return dl.PrefillIO(f["q"], f["k"], f["v"], f["decay"], f["beta"], f["out"], f["eta"], f["eps"], T)
+    return dl.PrefillIO(f["q"], f["k"], f["v"], f["decay"], f["beta"], f["bonus"], f["out"], f["eta"], f["eps"], T)
 
 
 def _prefill(lib, dims, pool, io):
@@ -165,7 +165,11 @@ def test_prefill_errors(lib):
     assert _prefill(lib, d, p, _pio(dl, T=-1)) == dl.DL_EINVAL
     assert lib.dl_prefill(ctypes.byref(d), ctypes.byref(p), None, None) == dl.DL_EINVAL
     assert _prefill(lib, _dims(dl, variant=1), p, _pio(dl, decay=A + 4)) == dl.DL_EALIGN  # KDA decay rows: 16 B
-    assert _prefill(lib, _dims(dl, variant=2, dk=64, dv=64), p, _pio(dl)) == dl.DL_EUNSUPPORTED
+    d2 = _dims(dl, variant=2, dk=64, dv=64)
+    assert _prefill(lib, d2, p, _pio(dl)) == dl.DL_EUNSUPPORTED                       # beta given, no bonus
+    assert _prefill(lib, d2, p, _pio(dl, beta=None)) == dl.DL_EUNSUPPORTED            # no bonus
+    assert _prefill(lib, d2, p, _pio(dl, beta=None, bonus=M)) == dl.DL_EALIGN
+    assert _prefill(lib, d, p, _pio(dl, bonus=A)) == dl.DL_EUNSUPPORTED               # GDN with a bonus
     assert _prefill(lib, d, p, _pio(dl, q=None)) == dl.DL_EINVAL
     assert _prefill(lib, d, p, _pio(dl, out=None)) == dl.DL_EINVAL
     assert _prefill(lib, d, p, _pio(dl, beta=None)) == dl.DL_EUNSUPPORTED       # neither beta nor eta

@@ -1,4 +1,4 @@
-"""dl_prefill (chunkwise GDN and KDA prefill on MFMA) against the fp64 eager oracle (GPU).
+"""dl_prefill (chunkwise GDN, KDA and RWKV6 prefill on MFMA) against the fp64 eager oracle (GPU).
 
 A prompt of T tokens is the workload's first T drawn steps; the oracle runs the
 same T eager steps.  Outputs (one per token) and the final state (the base,
@@ -44,7 +44,7 @@ def run_prefill(pool, up, t0, T, eps=0.0):
     p = prompt(up, t0, T)
     inp = up.inp
     out = torch.full((inp.batch, T, inp.heads, inp.dv), float("nan"), dtype=torch.float32, device=dev())
-    io = dl.make_prefill_io(pool, p["q"], p["k"], p["v"], p["decay"], p["beta"], out, p["eta"], eps)
+    io = dl.make_prefill_io(pool, p["q"], p["k"], p["v"], p["decay"], p["beta"], out, p["eta"], eps, bonus=up.bonus)
     dl.dl_prefill(pool, io)
     torch.cuda.synchronize()
     return out.cpu().numpy().transpose(1, 0, 2, 3)  # [T][batch][heads][dv]
@@ -126,7 +126,8 @@ def test_prefill_folds_a_pending_log_first():
     want = materialized_state(pool)
     out = torch.empty((inp.batch, 0, inp.heads, inp.dv), dtype=torch.float32, device=dev())
     p = prompt(up, 0, 0)
-    dl.dl_prefill(pool, dl.make_prefill_io(pool, p["q"], p["k"], p["v"], p["decay"], p["beta"], out))
+    dl.dl_prefill(pool, dl.make_prefill_io(pool, p["q"], p["k"], p["v"], p["decay"], p["beta"], out,
+                                           bonus=up.bonus))
     torch.cuda.synchronize()
     assert int(pool.fill.max().item()) == 0
     assert np.array_equal(pool.base.cpu().numpy(), want)
@@ -229,13 +230,42 @@ def test_kda_bf16_base_prefill():
     assert float(np.mean(got == ref)) >= 0.99
 
 
-def test_rwkv6_prefill_is_rejected():
-    inp = make_inputs(4, 8, batch=1, heads=2, pool=8)
+# ------------------------------------------------------------------- RWKV6 --
+@pytest.mark.parametrize("T", [1, 31, 33, 100, 2048])
+def test_rwkv6_prefill_lengths(T):
+    inp = make_inputs(4, T, batch=2, heads=4, pool=T)
+    check_prefill(inp, T)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64)])
+def test_rwkv6_head_size_combinations(dk, dv):
+    inp = make_inputs(4, 97, batch=2, heads=3, pool=97, dk=dk, dv=dv)
+    check_prefill(inp, 97)
+
+
+def test_rwkv6_strong_and_zero_decays():
+    """Channels decaying to zero, by 2^-40 per token (pairwise path) or by 2^-3 per token
+    (matrix path), and channels that do not decay."""
+    for variant_decay in ("pairwise", "matrix"):
+        inp = make_inputs(4, 70, batch=2, heads=2, pool=70)
+        if variant_decay == "pairwise":
+            inp.decay[5, :, :, :16] = 0.0
+            inp.decay[10:30, :, :, 16:32] = 2.0 ** -40
+        else:
+            inp.decay[:, :, :, :24] = 2.0 ** -3
+        inp.decay[40:45, :, :, 40:] = 1.0
+        check_prefill(inp, 70)
+
+
+def test_rwkv6_decode_continues_after_prefill():
+    inp = make_inputs(4, 140, batch=2, heads=4, pool=140)
     up = Uploaded(inp)
     pool = new_pool(inp, up=up)
-    out = torch.empty((1, 8, 2, inp.dv), dtype=torch.float32, device=dev())
-    io = dl.PrefillIO(up.q.data_ptr(), up.k.data_ptr(), up.v.data_ptr(), up.decay.data_ptr(), None,
-                      out.data_ptr(), None, 0.0, 8)
-    with pytest.raises(dl.DeltaLogError) as ei:
-        dl.dl_prefill(pool, io)
-    assert ei.value.status == dl.DL_EUNSUPPORTED
+    run_prefill(pool, up, 0, 100)
+    outs = []
+    for t in range(100, 140):
+        dl.dl_decode_step(pool, up.io(t))
+        outs.append(up.out.cpu().numpy())
+    ref_S, ref_o = oracle.run_eager(inp, 140)
+    _close("decode outputs after prefill", np.stack(outs), ref_o[100:], (-1,))
+    _close("state after prefill + decode", materialized_state(pool), ref_S, (-2, -1))
