@@ -79,6 +79,27 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t&
   lo = cvt2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
 }
 
+// fp32 -> bf16 hi + mid + lo for two values at once: x - hi - mid - lo is below 2^-26 |x|.
+// Used for the decay-weighted key/query products, whose sums over channels cancel.
+__device__ __forceinline__ void split3(float a, float b, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = cvt2(a, b);
+  const float ra = a - __uint_as_float(hi << 16), rb = b - __uint_as_float(hi & 0xffff0000u);
+  mid = cvt2(ra, rb);
+  lo = cvt2(ra - __uint_as_float(mid << 16), rb - __uint_as_float(mid & 0xffff0000u));
+}
+
+// sum of the products of two three-way split operands, terms down to 2^-16 of the
+// leading one: hi.hi + hi.mid + mid.hi + hi.lo + mid.mid + lo.hi.
+__device__ __forceinline__ f32x4 mma3(const bf16x8 (&x)[3], const bf16x8 (&y)[3], f32x4 acc) {
+  acc = mma(x[0], y[0], acc);
+  acc = mma(x[0], y[1], acc);
+  acc = mma(x[1], y[0], acc);
+  acc = mma(x[0], y[2], acc);
+  acc = mma(x[1], y[1], acc);
+  acc = mma(x[2], y[0], acc);
+  return acc;
+}
+
 // Two accumulator blocks (4 values each, k = 4g + r and 16 + 4g + r) as split B operands.
 __device__ __forceinline__ void split_pair(const float (&x0)[4], const float (&x1)[4], bf16x8& hi, bf16x8& lo) {
   uint32_t h[4], l[4];
@@ -810,8 +831,9 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     //        rows and columns 0..15, R = token 15 for the blocks of rows 16..31.
     //        Row factors are then <= 1 and column factors at most the decay over 16
     //        tokens, so when no channel decays by more than 2^-60 over either half of
-    //        the chunk the products run on MFMA with split operands (three waves, one
-    //        16 x 16 block each).  Otherwise every pair is formed directly.
+    //        the chunk the products run on MFMA with three-way split operands (three
+    //        waves, one 16 x 16 block each; these sums over channels can cancel, so
+    //        they keep 24 bits).  Otherwise every pair is formed directly.
     bool direct;
     {
       bool big = false;
@@ -836,24 +858,24 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
           unpack8(*reinterpret_cast<const uint4*>(&sh.k[(16 * ib + ln) * KS + ch0]), kr);
           unpack8(*reinterpret_cast<const uint4*>(&sh.q[(16 * ib + ln) * KS + ch0]), qr);
           unpack8(*reinterpret_cast<const uint4*>(&sh.k[(16 * jb + ln) * KS + ch0]), kc);
-          uint32_t ah[4], al[4], qh[4], ql[4], bh[4], bl[4];
+          uint32_t ap[3][4], qp[3][4], bp[3][4];
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
             const float r0 = exp2f(cr[e] - ref[e]), r1 = exp2f(cr[e + 1] - ref[e + 1]);
             const float c0 = exp2f(ref[e] - cj[e]), c1 = exp2f(ref[e + 1] - cj[e + 1]);
-            split2(kr[e] * r0, kr[e + 1] * r1, ah[e / 2], al[e / 2]);
-            split2(qr[e] * r0, qr[e + 1] * r1, qh[e / 2], ql[e / 2]);
-            split2(kc[e] * c0, kc[e + 1] * c1, bh[e / 2], bl[e / 2]);
+            split3(kr[e] * r0, kr[e + 1] * r1, ap[0][e / 2], ap[1][e / 2], ap[2][e / 2]);
+            split3(qr[e] * r0, qr[e + 1] * r1, qp[0][e / 2], qp[1][e / 2], qp[2][e / 2]);
+            split3(kc[e] * c0, kc[e + 1] * c1, bp[0][e / 2], bp[1][e / 2], bp[2][e / 2]);
           }
-          const bf16x8 Ah = pack8(ah[0], ah[1], ah[2], ah[3]), Al = pack8(al[0], al[1], al[2], al[3]);
-          const bf16x8 Qh = pack8(qh[0], qh[1], qh[2], qh[3]), Ql = pack8(ql[0], ql[1], ql[2], ql[3]);
-          const bf16x8 Bh = pack8(bh[0], bh[1], bh[2], bh[3]), Bl = pack8(bl[0], bl[1], bl[2], bl[3]);
-          accA = mma(Ah, Bh, accA);
-          accA = mma(Ah, Bl, accA);
-          accA = mma(Al, Bh, accA);
-          accP = mma(Qh, Bh, accP);
-          accP = mma(Qh, Bl, accP);
-          accP = mma(Ql, Bh, accP);
+          bf16x8 Ax[3], Qx[3], Bx[3];
+#pragma unroll
+          for (int u = 0; u < 3; ++u) {
+            Ax[u] = pack8(ap[u][0], ap[u][1], ap[u][2], ap[u][3]);
+            Qx[u] = pack8(qp[u][0], qp[u][1], qp[u][2], qp[u][3]);
+            Bx[u] = pack8(bp[u][0], bp[u][1], bp[u][2], bp[u][3]);
+          }
+          accA = mma3(Ax, Bx, accA);
+          accP = mma3(Qx, Bx, accP);
         }
         const int j = 16 * jb + ln;
         float pm[4];
@@ -1312,17 +1334,21 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
             for (int e = 0; e < 8; ++e) ref[e] = 0.f;
           unpack8(*reinterpret_cast<const uint4*>(&sh.q[ri * KS + ch0]), rr);
           unpack8(*reinterpret_cast<const uint4*>(&sh.k[(16 * jb + ln) * KS + ch0]), kc);
-          uint32_t ah[4], al[4], bh[4], bl[4];
+          uint32_t ap[3][4], bp[3][4];
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
-            split2(rr[e] * exp2f(cr[e] - ref[e]), rr[e + 1] * exp2f(cr[e + 1] - ref[e + 1]), ah[e / 2], al[e / 2]);
-            split2(kc[e] * exp2f(ref[e] - cj[e]), kc[e + 1] * exp2f(ref[e + 1] - cj[e + 1]), bh[e / 2], bl[e / 2]);
+            split3(rr[e] * exp2f(cr[e] - ref[e]), rr[e + 1] * exp2f(cr[e + 1] - ref[e + 1]), ap[0][e / 2],
+                   ap[1][e / 2], ap[2][e / 2]);
+            split3(kc[e] * exp2f(ref[e] - cj[e]), kc[e + 1] * exp2f(ref[e + 1] - cj[e + 1]), bp[0][e / 2],
+                   bp[1][e / 2], bp[2][e / 2]);
           }
-          const bf16x8 Ah = pack8(ah[0], ah[1], ah[2], ah[3]), Al = pack8(al[0], al[1], al[2], al[3]);
-          const bf16x8 Bh = pack8(bh[0], bh[1], bh[2], bh[3]), Bl = pack8(bl[0], bl[1], bl[2], bl[3]);
-          accP = mma(Ah, Bh, accP);
-          accP = mma(Ah, Bl, accP);
-          accP = mma(Al, Bh, accP);
+          bf16x8 Ax[3], Bx[3];
+#pragma unroll
+          for (int u = 0; u < 3; ++u) {
+            Ax[u] = pack8(ap[u][0], ap[u][1], ap[u][2], ap[u][3]);
+            Bx[u] = pack8(bp[u][0], bp[u][1], bp[u][2], bp[u][3]);
+          }
+          accP = mma3(Ax, Bx, accP);
         }
         const int j = 16 * jb + ln;
         float pm[4];

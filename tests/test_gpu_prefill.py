@@ -269,3 +269,30 @@ def test_rwkv6_decode_continues_after_prefill():
     ref_S, ref_o = oracle.run_eager(inp, 140)
     _close("decode outputs after prefill", np.stack(outs), ref_o[100:], (-1,))
     _close("state after prefill + decode", materialized_state(pool), ref_S, (-2, -1))
+
+
+# ------------------------------------------- full sizes, sampled tiles ------
+@pytest.mark.parametrize("w,T", [(2, 4096), (3, 1024), (4, 2048)])
+def test_full_size_prefill_sampled_tiles(w, T):
+    """The shapes the bench times (every tile of the workload, prompt rows cycling over
+    64 drawn steps); six tiles spread over batch and heads are checked against the oracle."""
+    inp = make_inputs(w, T, pool=64)
+    B, H = inp.batch, inp.heads
+    up = Uploaded(inp)
+    pool = new_pool(inp, up=up)
+    idx = torch.arange(T, device=dev()) % inp.pool
+    tm = lambda x: None if x is None else x.index_select(0, idx).transpose(0, 1).contiguous()
+    out = torch.empty((B, T, H, inp.dv), dtype=torch.float32, device=dev())
+    io = dl.make_prefill_io(pool, tm(up.q), tm(up.k), tm(up.v), tm(up.decay), tm(up.beta), out, tm(up.eta),
+                            inp.eps, bonus=up.bonus)
+    dl.dl_prefill(pool, io)
+    torch.cuda.synchronize()
+    sel = [(0, 0), (0, H - 1), (B // 3, H // 2), (B // 2, 1), (B - 1, 0), (B - 1, H - 1)]
+    bi = torch.tensor([b for b, _ in sel], device=dev())
+    hi = torch.tensor([h for _, h in sel], device=dev())
+    got_o = out[bi, :, hi].cpu().numpy().transpose(1, 0, 2)   # [T][tiles][dv]
+    got_S = pool.base[bi, hi].cpu().numpy()
+    del out, io
+    ref_S, ref_o = oracle.run_eager(inp, T, sel=sel)
+    _close(f"outputs, workload {w}, T={T}", got_o, ref_o, (-1,))
+    _close(f"state, workload {w}, T={T}", got_S, ref_S, (-2, -1))
