@@ -495,6 +495,17 @@ def main():
     secs_c = time_loop(lambda t: dl.dl_decode_step(pools[t % 3], ios[t % P]), Kc, W_al)
     del pools
 
+    # copy ceilings on this machine: a plain device copy that fits the last-level cache
+    # (2 x 64 MiB) and one that does not (2 x 1 GiB); read + write bytes over time
+    copy = {}
+    for label, nbytes in (("fits_cache", 64 << 20), ("cold", 1 << 30)):
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        reps = 20 if nbytes < (256 << 20) else 5
+        secs_copy = time_loop(lambda t: dst.copy_(src), reps, 3)
+        copy[label] = 2 * nbytes * reps / secs_copy / 1e9
+        del src, dst
+
     mdl = deltalog_bytes_per_state_step(var, dk, dv, L, B, 2 if bf16_base else 4)
     eag = eager_bytes_per_state_step(var, dk, dv, B)
     t_step = result["deltalog"] / K
@@ -542,6 +553,8 @@ def main():
         "eager": {"value": tiles / t_eager, "ms_per_step": t_eager * 1e3,
                   "hbm_gbs_algorithmic": eag["total"] * tiles / t_eager / 1e9,
                   "deltalog_speedup": t_eager / t_step},
+        "copy_ceiling_gbs": {**copy, "decode_frac_of_fits_cache": achieved / copy["fits_cache"],
+                             "cold_decode_frac_of_cold": mdl["total"] * tiles / t_cold / 1e9 / copy["cold"]},
         "cold_three_pools": {"value": tiles / t_cold, "ms_per_step": t_cold * 1e3,
                              "hbm_gbs_algorithmic": mdl["total"] * tiles / t_cold / 1e9,
                              "frac": mdl["total"] * tiles / t_cold / 1e9 / HBM_PEAK_GBS},

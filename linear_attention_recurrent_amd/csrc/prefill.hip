@@ -170,6 +170,18 @@ __device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, fl
   __syncthreads();
 }
 
+// Output rows t0 .. t0 + C - 1 of one sequence as a buffer resource that covers only
+// the rows the prompt has: a store to a row past its end lies outside the resource
+// and is dropped, so the stores need no branch and one VGPR offset each.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rows(float* out, size_t bseq, int T, int H, int DV, int t0,
+                                                            int C) {
+  const int rows = T - t0 < C ? T - t0 : C;
+  return make_rsrc(out + (bseq * T + t0) * H * DV, rows * H * DV * 4);
+}
+__device__ __forceinline__ void st_out(__amdgpu_buffer_rsrc_t r, uint32_t off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+}
+
 template <int DK, int DV>
 struct PrefillLds {
   static constexpr int C = kChunk;
@@ -513,6 +525,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     }
 
     // ---- 9. O += (M o Q K^T) U; write the outputs
+    const auto orows = out_rows(a.out, bseq, T, H, DV, t0, C);
+    const uint32_t olane = static_cast<uint32_t>((4 * lg * H + static_cast<int>(h)) * DV + col0 + ln) * 4;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       bf16x8 uhi, ulo;
@@ -527,10 +541,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
         acc = mma(pah, ulo, acc);
         acc = mma(pal, uhi, acc);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = t0 + 16 * ib + 4 * lg + r;
-          if (t < T) a.out[((bseq * T + t) * H + h) * DV + col0 + 16 * cb + ln] = O[ib][cb][r] + acc[r];
-        }
+        for (int r = 0; r < 4; ++r)
+          st_out(orows, olane + static_cast<uint32_t>((16 * ib + r) * H * DV + 16 * cb) * 4, O[ib][cb][r] + acc[r]);
       }
     }
 
@@ -1039,6 +1051,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     }
 
     // ---- 9. O += P U; outputs
+    const auto orows = out_rows(a.out, bseq, T, H, DV, t0, C);
+    const uint32_t olane = static_cast<uint32_t>((4 * lg * H + static_cast<int>(h)) * DV + col0 + ln) * 4;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       bf16x8 uhi, ulo;
@@ -1053,10 +1067,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
         acc = mma(pah, ulo, acc);
         acc = mma(pal, uhi, acc);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = t0 + 16 * ib + 4 * lg + r;
-          if (t < T) a.out[((bseq * T + t) * H + h) * DV + col0 + 16 * cb + ln] = O[ib][cb][r] + acc[r];
-        }
+        for (int r = 0; r < 4; ++r)
+          st_out(orows, olane + static_cast<uint32_t>((16 * ib + r) * H * DV + 16 * cb) * 4, O[ib][cb][r] + acc[r]);
       }
     }
 
@@ -1453,6 +1465,8 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
 #pragma unroll
           for (int r = 0; r < 4; ++r) O[ib][cb][r] = qs[ib][cb][r];
     }
+    const auto orows = out_rows(a.out, bseq, T, H, DV, t0, C);
+    const uint32_t olane = static_cast<uint32_t>((4 * lg * H + static_cast<int>(h)) * DV + col0 + ln) * 4;
     bf16x8 vb[NCB];  // V[token 8 lg + s][this lane's column], the B operand of P V and of the update
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
@@ -1467,10 +1481,8 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
         acc = mma(pah, vb[cb], acc);
         acc = mma(pal, vb[cb], acc);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = t0 + 16 * ib + 4 * lg + r;
-          if (t < T) a.out[((bseq * T + t) * H + h) * DV + col0 + 16 * cb + ln] = O[ib][cb][r] + acc[r];
-        }
+        for (int r = 0; r < 4; ++r)
+          st_out(orows, olane + static_cast<uint32_t>((16 * ib + r) * H * DV + 16 * cb) * 4, O[ib][cb][r] + acc[r]);
       }
     }
 
