@@ -296,3 +296,46 @@ def test_full_size_prefill_sampled_tiles(w, T):
     ref_S, ref_o = oracle.run_eager(inp, T, sel=sel)
     _close(f"outputs, workload {w}, T={T}", got_o, ref_o, (-1,))
     _close(f"state, workload {w}, T={T}", got_S, ref_S, (-2, -1))
+
+
+def test_hip_graph_replays_of_prefill_and_decode():
+    """A prefill followed by decode steps, captured in a HIP graph and replayed with
+    unrelated work and synchronisation in between, gives bit-identical outputs and
+    pools to the same calls launched directly (no memset nodes are involved)."""
+    inp = make_inputs(2, 80, batch=2, heads=4, pool=80)
+    up = Uploaded(inp)
+    T = 45
+    p = prompt(up, 0, T)
+    ref_pool = new_pool(inp, up=up)
+    out_ref = torch.empty((inp.batch, T, inp.heads, inp.dv), dtype=torch.float32, device=dev())
+    dl.dl_prefill(ref_pool, dl.make_prefill_io(ref_pool, p["q"], p["k"], p["v"], p["decay"], p["beta"], out_ref))
+    dec_ref = []
+    for t in range(T, T + 20):
+        dl.dl_decode_step(ref_pool, up.io(t))
+        dec_ref.append(up.out.clone())
+    torch.cuda.synchronize()
+
+    pool = new_pool(inp, up=up)
+    out = torch.empty_like(out_ref)
+    io = dl.make_prefill_io(pool, p["q"], p["k"], p["v"], p["decay"], p["beta"], out)
+    dec = torch.empty((20,) + tuple(up.out.shape), dtype=torch.float32, device=dev())
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            dl.dl_prefill(pool, io)
+            for i, t in enumerate(range(T, T + 20)):
+                dl.dl_decode_step(pool, up.io(t))
+                dec[i].copy_(up.out)
+    torch.cuda.synchronize()
+    for r in range(3):
+        dl.dl_init_state(pool, up.s0, None)
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (torch.ones(1 << 20, device=dev()) * 3).sum().item()
+        assert torch.equal(out, out_ref), r
+        for i in range(20):
+            assert torch.equal(dec[i], dec_ref[i]), (r, i)
+        for name, tnsr in pool.tensors().items():
+            assert torch.equal(tnsr, ref_pool.tensors()[name]), (r, name)
