@@ -45,6 +45,11 @@ using bf16x2 = __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16;
 constexpr int kChunk = 32;  // tokens per chunk
 constexpr int kThreads = 256;
 
+// 2^x with the bare hardware instruction (about 1 ulp).  Every argument here is a
+// difference of cumulative log2 decays; results below 2^-126 (the normal range)
+// stand for products of decays that are negligible next to the other terms.
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ f32x4 mma(const bf16x8 a, const bf16x8 b, const f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -364,7 +369,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
       }
       if (lane < C) {
         sh.c[lane] = l2;
-        sh.gam[lane] = exp2f(l2);
+        sh.gam[lane] = fexp2(l2);
         sh.braw[lane] = nbt;
       }
     }
@@ -402,7 +407,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
 #pragma unroll
       for (int e = 0; e < C * C / kThreads; ++e) {
         const int i = tid / C + e * (kThreads / C);
-        const float dij = exp2f(fminf(sh.c[i] - cj, 0.f));  // used only where j <= i
+        const float dij = fexp2(fminf(sh.c[i] - cj, 0.f));  // used only where j <= i
         if (j < i) sh.g[i * MS + j] *= sh.beta[i] * dij;
         pm[e] = j <= i ? dij * sh.p[i * MS + j] : 0.f;
       }
@@ -552,7 +557,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float f = exp2f(cC - sh.c[16 * ib + 4 * lg + r]);
+        const float f = fexp2(cC - sh.c[16 * ib + 4 * lg + r]);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) U[ib][cb][r] *= f;
       }
@@ -583,6 +588,30 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
 }
 
 
+
+// In-place prefix sums over the 32 tokens of a chunk, for each of DK channels of a
+// [token][channel] fp32 array with row stride CS: thread (channel, half) adds up 16
+// tokens in registers and the second half adds the first half's total.  glast[ch]
+// receives 2 to the power of the last token's sum.
+template <int DK, int CS>
+__device__ __forceinline__ void prefix_over_tokens(float* cc, float* glast, int tid) {
+  const int ch = tid >> 1, hf = tid & 1;
+  if (ch < DK) {  // whole waves
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = cc[(16 * hf + i) * CS + ch];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) x[i] += x[i - 1];
+    const float first = __shfl_xor(x[15], 1, 64);  // the partner's total
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (hf == 1) x[i] += first;
+      cc[(16 * hf + i) * CS + ch] = x[i];
+    }
+    if (hf == 1) glast[ch] = fexp2(x[15]);  // 2^c of the chunk's last token
+  }
+}
+
 // ------------------------------------------------------------------ KDA prefill
 // KDA decays each key channel on its own: with G_i = a_1 ... a_i (a dk-vector,
 // cumulative within the chunk, kept as log2 in cc) the chunk form becomes
@@ -605,6 +634,7 @@ struct PrefillKdaLds {
   float beta[C];
   float braw[C];
   float knorm[C];
+  float glast[DK];  // 2^c of the chunk's last token per channel
   float g[C * MS];  // A (strictly lower part)
   float t[C * MS];  // T = (I + A)^-1
   union {
@@ -768,19 +798,9 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     if (t0 + C < T) fetch(t0 + C);
     __syncthreads();
 
-    // ---- 2. prefix sums of the log2 decays over the chunk's tokens (one channel per
-    //         32-lane half wave); step sizes; zero the upper triangle of P and T's upper block
-#pragma unroll
-    for (int it = 0; it < DK / 8; ++it) {
-      const int ch = wave * (DK / 4) + 2 * it + (lane >> 5), tok = lane & 31;
-      float x = sh.cc[tok * CS + ch];
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) {
-        const float y = __shfl_up(x, off, 32);
-        if (tok >= off) x += y;
-      }
-      sh.cc[tok * CS + ch] = x;
-    }
+    // ---- 2. prefix sums of the log2 decays over the chunk's tokens; step sizes; zero the
+    //         upper triangle of P and T's upper block
+    prefix_over_tokens<DK, CS>(sh.cc, sh.glast, tid);
     if (tid < C) {
       const bool ok = t0 + tid < T;
       sh.beta[tid] = !ok ? 0.f : kla ? sh.braw[tid] / (sh.knorm[tid] + a.eps) : sh.braw[tid];
@@ -813,12 +833,12 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
         for (int e = 0; e < 8; e += 2) {
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2)
-            split2(qf[s2][e] * exp2f(cf[s2][e]), qf[s2][e + 1] * exp2f(cf[s2][e + 1]), qh[s2][e / 2], ql[s2][e / 2]);
+            split2(qf[s2][e] * fexp2(cf[s2][e]), qf[s2][e + 1] * fexp2(cf[s2][e + 1]), qh[s2][e / 2], ql[s2][e / 2]);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {  // channel seg*8 + e: tokens tok, tok + 1 packed
-          split2(kf[0][e] * exp2f(cf[0][e]), kf[1][e] * exp2f(cf[1][e]), kgh2[e], kgl2[e]);
-          split2(kf[0][e] * exp2f(cl[e] - cf[0][e]), kf[1][e] * exp2f(cl[e] - cf[1][e]), kdh2[e], kdl2[e]);
+          split2(kf[0][e] * fexp2(cf[0][e]), kf[1][e] * fexp2(cf[1][e]), kgh2[e], kgl2[e]);
+          split2(kf[0][e] * fexp2(cl[e] - cf[0][e]), kf[1][e] * fexp2(cl[e] - cf[1][e]), kdh2[e], kdl2[e]);
         }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -873,8 +893,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
           uint32_t ap[3][4], qp[3][4], bp[3][4];
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
-            const float r0 = exp2f(cr[e] - ref[e]), r1 = exp2f(cr[e + 1] - ref[e + 1]);
-            const float c0 = exp2f(ref[e] - cj[e]), c1 = exp2f(ref[e + 1] - cj[e + 1]);
+            const float r0 = fexp2(cr[e] - ref[e]), r1 = fexp2(cr[e + 1] - ref[e + 1]);
+            const float c0 = fexp2(ref[e] - cj[e]), c1 = fexp2(ref[e + 1] - cj[e + 1]);
             split3(kr[e] * r0, kr[e + 1] * r1, ap[0][e / 2], ap[1][e / 2], ap[2][e / 2]);
             split3(qr[e] * r0, qr[e + 1] * r1, qp[0][e / 2], qp[1][e / 2], qp[2][e / 2]);
             split3(kc[e] * c0, kc[e + 1] * c1, bp[0][e / 2], bp[1][e / 2], bp[2][e / 2]);
@@ -930,7 +950,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
 #pragma unroll
         for (int e = 0; e < SL; ++e) {
           const float u = bf16_to_f32(sh.k[j * KS + sl * SL + e]) *
-                          exp2f((first ? cr[0][e] : cr[1][e]) - sh.cc[j * CS + sl * SL + e]);
+                          fexp2((first ? cr[0][e] : cr[1][e]) - sh.cc[j * CS + sl * SL + e]);
           av = fmaf(first ? kr[0][e] : kr[1][e], u, av);
           pv = fmaf(first ? qr[0][e] : qr[1][e], u, pv);
         }
@@ -1084,7 +1104,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
       const bf16x8 kal = ld_2x64(&sh.kdl[ro + c0], &sh.kdl[ro + c1]);
       float gl[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) gl[r] = exp2f(sh.cc[(C - 1) * CS + 16 * kb + 4 * lg + r]);
+      for (int r = 0; r < 4; ++r) gl[r] = sh.glast[16 * kb + 4 * lg + r];
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         f32x4 acc = {gl[0] * S[kb][cb][0], gl[1] * S[kb][cb][1], gl[2] * S[kb][cb][2], gl[3] * S[kb][cb][3]};
@@ -1124,6 +1144,7 @@ struct PrefillRwkvLds {
   static constexpr int BS = C + 8;
   static constexpr int CS = DK + 4;
   float bonus[DK];
+  float glast[DK];                    // 2^c of the chunk's last token per channel
   float pd[C];                        // the bonus diagonal of P
   uint16_t pmh[C * BS], pml[C * BS];  // P, split
   uint16_t k[C * KS];                 // K, token rows
@@ -1254,17 +1275,7 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
     __syncthreads();
 
     // ---- 2. prefix sums of the log2 decays over the chunk's tokens
-#pragma unroll
-    for (int it = 0; it < DK / 8; ++it) {
-      const int ch = wave * (DK / 4) + 2 * it + (lane >> 5), tok = lane & 31;
-      float x = sh.cc[tok * CS + ch];
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) {
-        const float y = __shfl_up(x, off, 32);
-        if (tok >= off) x += y;
-      }
-      sh.cc[tok * CS + ch] = x;
-    }
+    prefix_over_tokens<DK, CS>(sh.cc, sh.glast, tid);
     __syncthreads();
 
     // ---- 3. R o G_prev (rows) and K o G_C / G (token-major), split; the bonus diagonal
@@ -1288,12 +1299,12 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           // token tok reads G_{tok-1}, token tok + 1 reads G_tok
-          split2(rf[0][e] * exp2f(cp[e]), rf[0][e + 1] * exp2f(cp[e + 1]), rh[0][e / 2], rl[0][e / 2]);
-          split2(rf[1][e] * exp2f(cf[0][e]), rf[1][e + 1] * exp2f(cf[0][e + 1]), rh[1][e / 2], rl[1][e / 2]);
+          split2(rf[0][e] * fexp2(cp[e]), rf[0][e + 1] * fexp2(cp[e + 1]), rh[0][e / 2], rl[0][e / 2]);
+          split2(rf[1][e] * fexp2(cf[0][e]), rf[1][e + 1] * fexp2(cf[0][e + 1]), rh[1][e / 2], rl[1][e / 2]);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          split2(kf[0][e] * exp2f(cl[e] - cf[0][e]), kf[1][e] * exp2f(cl[e] - cf[1][e]), kdh2[e], kdl2[e]);
+          split2(kf[0][e] * fexp2(cl[e] - cf[0][e]), kf[1][e] * fexp2(cl[e] - cf[1][e]), kdh2[e], kdl2[e]);
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           *reinterpret_cast<uint4*>(&sh.rgh[(tok + s2) * KS + seg * 8]) =
@@ -1349,9 +1360,9 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
           uint32_t ap[3][4], bp[3][4];
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
-            split3(rr[e] * exp2f(cr[e] - ref[e]), rr[e + 1] * exp2f(cr[e + 1] - ref[e + 1]), ap[0][e / 2],
+            split3(rr[e] * fexp2(cr[e] - ref[e]), rr[e + 1] * fexp2(cr[e + 1] - ref[e + 1]), ap[0][e / 2],
                    ap[1][e / 2], ap[2][e / 2]);
-            split3(kc[e] * exp2f(ref[e] - cj[e]), kc[e + 1] * exp2f(ref[e + 1] - cj[e + 1]), bp[0][e / 2],
+            split3(kc[e] * fexp2(ref[e] - cj[e]), kc[e + 1] * fexp2(ref[e + 1] - cj[e + 1]), bp[0][e / 2],
                    bp[1][e / 2], bp[2][e / 2]);
           }
           bf16x8 Ax[3], Bx[3];
@@ -1418,7 +1429,7 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
 #pragma unroll
         for (int e = 0; e < SL; ++e) {
           const float u = bf16_to_f32(sh.k[j * KS + sl * SL + e]) *
-                          exp2f((first ? cr[0][e] : cr[1][e]) - sh.cc[j * CS + sl * SL + e]);
+                          fexp2((first ? cr[0][e] : cr[1][e]) - sh.cc[j * CS + sl * SL + e]);
           pv = fmaf(first ? rr[0][e] : rr[1][e], u, pv);
         }
         pv = group_sum<16>(pv);
@@ -1493,7 +1504,7 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
       const bf16x8 kah = ld_b128(&sh.kdh[o]), kal = ld_b128(&sh.kdl[o]);
       float gl[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) gl[r] = exp2f(sh.cc[(C - 1) * CS + 16 * kb + 4 * lg + r]);
+      for (int r = 0; r < 4; ++r) gl[r] = sh.glast[16 * kb + 4 * lg + r];
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         f32x4 acc = {gl[0] * S[kb][cb][0], gl[1] * S[kb][cb][1], gl[2] * S[kb][cb][2], gl[3] * S[kb][cb][3]};
