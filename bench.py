@@ -257,22 +257,24 @@ PREFILL_CHUNK = 32
 
 
 def prefill_model(dk: int, dv: int, C: int = PREFILL_CHUNK, variant: int = 0) -> dict:
-    """Per (sequence, head, prompt token): HBM bytes, the chunkwise method's flops, and the
-    bf16 MFMA flops the kernel issues (fp32 operands split in two: 2 or 3 products each).
-    KDA: the decay is a dk-vector per token, the decay-weighted K K^T and Q K^T are formed
-    on the vector units (not counted as MFMA work), and W, (Q o G) S and the state update
-    take three products each because their key/query operand carries the decay."""
+    """Per (sequence, head, prompt token): HBM bytes, the chunkwise method's flops (each
+    product counted once, as the kernel orders them), and the bf16 MFMA flops the kernel
+    issues: an exact bf16 operand against a two-way split one takes 2 products, two split
+    operands 3, and the decay-weighted C x C products (KDA, RWKV6; three-way splits, the
+    three lower 16 x 16 blocks) 6."""
     byts = 2 * dk * 2 + 2 * dv + 4 * (1 if variant == 0 else dk) + (4 if variant != 2 else 0) + 4 * dv
-    method = 2 * C * C * dk * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 3  # per chunk
-    if variant == 2:  # P (3 lower blocks, x3), (R o G) S (x3), P V (x2), state update (x2)
+    lower = 3 * 16 * 16 * dk * 2  # flops of one decay-weighted product over the three lower blocks
+    if variant == 2:  # P, (R o G) S, P V, state update
         method = 2 * C * C * dk + 2 * C * dk * dv + 2 * C * C * dv + 2 * C * dk * dv
-        issued = (3 * 2 * 16 * 16 * dk * 3 + 2 * C * dk * dv * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 2)
-    elif variant == 1:
-        issued = (2 * C * C * dk * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 3 + 2 * C * dk * dv * 3
+        issued = lower * 6 + 2 * C * dk * dv * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 2
+    elif variant == 1:  # A and P, W = T (K o G), T V, W S, (Q o G) S, P U, state update
+        method = 2 * C * C * dk * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 3
+        issued = (2 * lower * 6 + 2 * C * C * dk * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 3 * 2
                   + 2 * C * C * dv * 3 + 2 * C * dk * dv * 3)
-    else:  # K K^T, Q K^T lower blocks (3 of 4 each), W (x2), U~ (x2), W S (x3), Q S (x2), P U (x3), K^T U (x2)
-        issued = (2 * 3 * 16 * 16 * dk * 2 + 2 * C * C * dk * 2 + 2 * C * C * dv * 2
-                  + 2 * C * dk * dv * 3 + 2 * C * dk * dv * 2 + 2 * C * C * dv * 3 + 2 * C * dk * dv * 2)
+    else:  # K K^T, Q K^T (lower blocks), T V, X = K S, Q S, T X, P U, K^T U
+        method = 2 * C * C * dk * 2 + 2 * C * C * dv * 3 + 2 * C * dk * dv * 3
+        issued = (2 * lower + 2 * C * C * dv * 2 + 2 * C * dk * dv * 2 * 2 + 2 * C * C * dv * 3
+                  + 2 * C * C * dv * 3 + 2 * C * dk * dv * 2)
     return {"bytes": byts, "method_flops": method / C, "issued_flops": issued / C}
 
 

@@ -18,7 +18,10 @@
 // Mapping.  One workgroup (4 waves) per tile; wave w owns value columns
 // [w dv/4, (w+1) dv/4) of the state, held in MFMA accumulator layout, so the
 // dv dimension needs no communication between waves.  Chunk-shared matrices
-// (K K^T, Q K^T, T, W = T diag(b g) K) are built once per chunk in LDS.
+// (K K^T, Q K^T, T and its column-scaled copies) are built once per chunk in LDS.
+// The state enters U as T diag(b g) (K S): X = K S takes the exact bf16 keys
+// against the split state, and X then feeds T diag(b g) X from registers, so no
+// C x dk product of T with K is formed or staged.
 // Products run on v_mfma_f32_16x16x32_bf16: keys, queries and values are bf16
 // already (exact operands); an fp32 operand x is split into bf16 hi + lo with
 // x - hi - lo below 2^-17 |x|, and a product of two split operands takes the
@@ -29,9 +32,12 @@
 // MFMA 16x16x32 bf16 lane layout (lane l, n = l % 16, g = l / 16): A[n][8g + s],
 // B[8g + s][n] for s < 8; the result holds D[4g + r][n] for r < 4.  Sums over k
 // may pair any k order consistently between A and B; the state and U feed the
-// B operand straight from accumulator registers with k = {4g + r} u {16 + 4g + r}.
-// K and V are also kept token-major in LDS so that every operand is read with
-// 8- or 16-byte LDS loads.
+// B operand straight from accumulator registers with k = {4g + r} u {16 + 4g + r}
+// (so does X, over tokens).
+// Where tokens run along an operand's k index (K^T in the state update, V in T diag(b) V),
+// the GDN kernel reads the token rows through ds_read_b64_tr_b16; the KDA and RWKV6
+// kernels build decay-scaled, split copies token-major instead.  Every operand is read
+// with 8- or 16-byte LDS loads.
 #include "launch.hpp"
 
 namespace dl {
@@ -71,6 +77,40 @@ __device__ __forceinline__ bf16x8 ld_2x64(const uint16_t* p0, const uint16_t* p1
   return pack8(a.x, a.y, b.x, b.y);
 }
 
+// ds_read_b64_tr_b16: each lane names 4 consecutive bf16 (8 bytes); within each group of
+// 16 lanes, lane l receives element l % 4 of the reads of lanes l / 4 + 4 s, s = 0..3.
+// With lane j of a group reading row r0 + j / 4 at column c0 + 4 (j % 4) of a row-major
+// bf16 array, lane l gets rows r0 .. r0 + 3 of column c0 + l: a 4 x 16 block read
+// transposed, which is half of an MFMA operand whose k index runs along the rows.
+typedef short short4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 ld_tr4(const uint16_t* p) {
+  const short4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+// An operand whose k slots 0..3 and 4..7 are rows r0.. and r1.. of column c0 + (lane % 16)
+// of a row-major bf16 array with row stride rs: lane j of the group passes its own
+// row and column offsets.
+__device__ __forceinline__ bf16x8 ld_tr8(const uint16_t* base, int rs, int r0, int r1, int c0, int j) {
+  const int off = (j >> 2) * rs + c0 + 4 * (j & 3);
+  const uint2 a = ld_tr4(base + r0 * rs + off), b = ld_tr4(base + r1 * rs + off);
+  return pack8(a.x, a.y, b.x, b.y);
+}
+
+// Inclusive prefix sum over lanes 0..31 of a wave with DPP moves: shifts by 1, 2, 4 and 8
+// within each row of 16 lanes, then row 0's total (lane 15) added to row 1.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or_zero(float v) {  // lanes with no source lane get 0
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, false));
+}
+__device__ __forceinline__ float scan32(float x) {
+  x += dpp_or_zero<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_or_zero<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_or_zero<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_or_zero<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_or_zero<0x142, 0xa>(x);  // row_bcast:15, into rows 1 and 3
+  return x;
+}
+
 // Two fp32 values rounded to bf16 (to nearest, ties to even; one v_cvt_pk_bf16_f32)
 // and packed, a in the low half.
 __device__ __forceinline__ uint32_t cvt2(float a, float b) {
@@ -78,19 +118,38 @@ __device__ __forceinline__ uint32_t cvt2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// fp32 -> bf16 hi + lo for two values at once (packed pairs): x - hi is exact in fp32.
+// A packed bf16 pair held in a register.  Written as a literal, the pair (-1, 0) is
+// encoded by the compiler as the inline constant -1.0, which v_dot2c_f32_bf16 reads as
+// the pair (0, -1); the empty asm keeps the bits in an SGPR so the operand is the pair
+// as written.
+__device__ __forceinline__ bf16x2 pair_in_reg(uint32_t bits) {
+  asm("" : "+s"(bits));
+  return __builtin_bit_cast(bf16x2, bits);
+}
+
+// x - (the bf16 number in the low, or high, half of h) in one v_dot2c_f32_bf16 against
+// (-1, 0), or (0, -1): the product is exact and, when that half is x rounded to bf16,
+// so is the difference.  (Finite operands: the other half enters multiplied by 0.)
+__device__ __forceinline__ float rem_lo(uint32_t h, float x) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, h), pair_in_reg(0x0000bf80u), x, false);
+}
+__device__ __forceinline__ float rem_hi(uint32_t h, float x) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, h), pair_in_reg(0xbf800000u), x, false);
+}
+
+// fp32 -> bf16 hi + lo for two values at once (packed pairs); x - hi is exact in fp32.
 __device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
   hi = cvt2(a, b);
-  lo = cvt2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+  lo = cvt2(rem_lo(hi, a), rem_hi(hi, b));
 }
 
 // fp32 -> bf16 hi + mid + lo for two values at once: x - hi - mid - lo is below 2^-26 |x|.
 // Used for the decay-weighted key/query products, whose sums over channels cancel.
 __device__ __forceinline__ void split3(float a, float b, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
   hi = cvt2(a, b);
-  const float ra = a - __uint_as_float(hi << 16), rb = b - __uint_as_float(hi & 0xffff0000u);
+  const float ra = rem_lo(hi, a), rb = rem_hi(hi, b);
   mid = cvt2(ra, rb);
-  lo = cvt2(ra - __uint_as_float(mid << 16), rb - __uint_as_float(mid & 0xffff0000u));
+  lo = cvt2(rem_lo(mid, ra), rem_hi(mid, rb));
 }
 
 // sum of the products of two three-way split operands, terms down to 2^-16 of the
@@ -190,12 +249,11 @@ __device__ __forceinline__ void st_out(__amdgpu_buffer_rsrc_t r, uint32_t off, f
 template <int DK, int DV>
 struct PrefillLds {
   static constexpr int C = kChunk;
-  static constexpr int KS = DK + 8;  // bf16 row stride of the K, Q and W arrays (16-byte pad)
-  static constexpr int TS = C + 8;   // bf16 row stride of the token-major K and V
-  static constexpr int MS = C + 1;   // fp32 row stride of the C x C matrices
+  static constexpr int KS = DK + 8;   // bf16 row stride of the K and Q arrays (16-byte pad)
+  static constexpr int VS = DV + 16;  // bf16 row stride of V: 8 mod 32 words, so the four
+                                      // rows of a transposing read fall on distinct banks
+  static constexpr int MS = C + 1;    // fp32 row stride of the C x C matrices
   static constexpr int BS = C + 8;   // bf16 row stride of the split C x C matrices
-  // Arrays read or written with lane-dependent addresses on every chunk come first so
-  // that they lie within the 64 KiB reach of an LDS instruction's immediate offset.
   float c[C];      // cumulative log2 decay within the chunk
   float gam[C];    // 2^c
   float beta[C];   // step size (0 for tokens past the end)
@@ -213,14 +271,9 @@ struct PrefillLds {
   uint16_t t1l[C * BS];
   uint16_t t2h[C * BS], t2l[C * BS];  // T diag(b g)
   uint16_t pmh[C * BS], pml[C * BS];  // M o Q K^T
-  union {
-    uint16_t k[C * KS];   // K, token rows: read by K K^T and Q K^T
-    uint16_t wh[C * KS];  // then W = T diag(b g) K (hi part), token rows
-  };
-  uint16_t q[C * KS];
-  uint16_t kt[DK * TS];  // K token-major
-  uint16_t wl[C * KS];   // W (lo part)
-  uint16_t vt[DV * TS];  // V token-major
+  uint16_t k[C * KS];  // K, token rows
+  uint16_t q[C * KS];  // Q, token rows
+  uint16_t v[C * VS];  // V, token rows
 };
 
 template <int DK, int DV, bool BF>
@@ -231,7 +284,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
   constexpr int NKB = DK / 16;  // 16-channel blocks
   constexpr int NKP = DK / 32;  // pairs of channel blocks (one MFMA k-step each)
   using Lds = PrefillLds<DK, DV>;
-  constexpr int KS = Lds::KS, TS = Lds::TS, MS = Lds::MS, BS = Lds::BS;
+  constexpr int KS = Lds::KS, VS = Lds::VS, MS = Lds::MS, BS = Lds::BS;
   static_assert(NCB >= 1 && NKP >= 1, "head sizes 64 or 128");
   __shared__ __align__(16) Lds sh;
 
@@ -241,11 +294,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
   const int H = pa.heads, T = a.tokens;
   const size_t bseq = static_cast<size_t>(tile / H), h = static_cast<size_t>(tile % H);
   const int col0 = wave * CW;
-  // Token columns of this lane's reads of the token-major K and V (see tswz): channel
-  // 16 b + ln has swizzle ((ln / 8) + 2 b) mod 4, i.e. sw0 for even b and sw0 ^ 16 for odd b.
-  const int sw0 = (ln >> 3) << 3;
-  const int colw = (8 * lg) ^ sw0;  // the 8-token group 8 lg
-  const int colp = (4 * lg) ^ sw0;  // the 4-token group 4 lg (the group 16 + 4 lg: ^ 16)
 
   // The state columns of this wave: S[kb][cb][r] = S(16 kb + 4 lg + r, col0 + 16 cb + ln).
   float S[NKB][NCB][4];
@@ -261,9 +309,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
       for (int r = 0; r < 4; ++r) S[kb][cb][r] = ld_base<BF>(brsrc, bvoff, ((16 * kb + r) * DV + 16 * cb) * EB);
 
   const bool kla = a.eta != nullptr;
-  // Inputs of the next chunk are loaded into registers while this chunk is computed.
-  // Each thread takes one 16-byte piece (8 channels) of two consecutive tokens, so the
-  // token-major copies are written two tokens per 4-byte LDS store.
+  // Inputs of the next chunk are loaded into registers while this chunk is computed;
+  // each thread takes one 16-byte piece (8 channels) of two consecutive tokens.
   constexpr int KP = DK / 8, VP = DV / 8;                         // pieces per row
   constexpr int NPK = C / 2 * KP, NPV = C / 2 * VP;               // (token pair, piece) jobs
   constexpr int LK = (NPK + kThreads - 1) / kThreads, LV = (NPV + kThreads - 1) / kThreads;
@@ -301,15 +348,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
       nbt = ok ? (kla ? a.eta[si] : a.beta[si]) : 0.f;
     }
   };
-  // Two tokens' words w0, w1 (8 channels each) as 4 (channel e: tok0 | tok1 << 16) pairs per half.
-  auto interleave = [](const uint4 w0, const uint4 w1, uint32_t (&o)[8]) {
-    const uint32_t a0[4] = {w0.x, w0.y, w0.z, w0.w}, a1[4] = {w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o[2 * e] = (a0[e] & 0xffffu) | (a1[e] << 16);
-      o[2 * e + 1] = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
-    }
-  };
   fetch(0);
 
   for (int t0 = 0; t0 < T; t0 += C) {
@@ -324,13 +362,6 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
         for (int s2 = 0; s2 < 2; ++s2) {
           *reinterpret_cast<uint4*>(&sh.k[(tok + s2) * KS + seg * 8]) = nk[i][s2];
           *reinterpret_cast<uint4*>(&sh.q[(tok + s2) * KS + seg * 8]) = nq[i][s2];
-        }
-        uint32_t kw[8];
-        interleave(nk[i][0], nk[i][1], kw);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ch = seg * 8 + e;
-          *reinterpret_cast<uint32_t*>(&sh.kt[ch * TS + tswz(ch, tok)]) = kw[e];
         }
         if (kla) {
 #pragma unroll
@@ -350,23 +381,13 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     for (int i = 0; i < LV; ++i) {
       const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
       if (pc < NPV) {
-        uint32_t vw[8];
-        interleave(nv[i][0], nv[i][1], vw);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ch = seg * 8 + e;
-          *reinterpret_cast<uint32_t*>(&sh.vt[ch * TS + tswz(ch, tok)]) = vw[e];
-        }
+        for (int s2 = 0; s2 < 2; ++s2) *reinterpret_cast<uint4*>(&sh.v[(tok + s2) * VS + seg * 8]) = nv[i][s2];
       }
     }
     if (wave == 3) {
       // lanes 0..31: one token each; inclusive prefix sum of the clamped log2 decays
-      float l2 = (lane < C && t0 + lane < T) ? step_log2_decay(ndec) : 0.f;
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) {
-        const float y = __shfl_up(l2, off, 64);
-        if (lane >= off) l2 += y;
-      }
+      const float l2 = scan32((lane < C && t0 + lane < T) ? step_log2_decay(ndec) : 0.f);
       if (lane < C) {
         sh.c[lane] = l2;
         sh.gam[lane] = fexp2(l2);
@@ -454,27 +475,11 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     }
     __syncthreads();
 
-    // ---- 7. W = T diag(b g) K into LDS (blocks shared out over the waves); this wave's T diag(b) V
-    // W^T = K^T (T diag(b g))^T: the result holds 4 consecutive channels of one token per lane
-#pragma unroll
-    for (int e = 0; e < NKB / 2; ++e) {
-      const int blk = wave + 4 * e;  // 2 * NKB blocks: (ib, cb) = (blk / NKB, blk % NKB)
-      const int ib = blk / NKB, cb = blk % NKB;
-      const bf16x8 ka = ld_b128(&sh.kt[(16 * cb + ln) * TS + (colw ^ ((cb & 1) << 4))]);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mma(ka, ld_b128(&sh.t2h[(16 * ib + ln) * BS + 8 * lg]), acc);
-      acc = mma(ka, ld_b128(&sh.t2l[(16 * ib + ln) * BS + 8 * lg]), acc);
-      uint32_t h01, l01, h23, l23;
-      split2(acc[0], acc[1], h01, l01);
-      split2(acc[2], acc[3], h23, l23);
-      const int wo = (16 * ib + ln) * KS + 16 * cb + 4 * lg;
-      *reinterpret_cast<uint2*>(&sh.wh[wo]) = make_uint2(h01, h23);
-      *reinterpret_cast<uint2*>(&sh.wl[wo]) = make_uint2(l01, l23);
-    }
+    // ---- 7. this wave's columns of T diag(b) V
     float U[2][NCB][4];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      const bf16x8 vb8 = ld_b128(&sh.vt[(col0 + 16 * cb + ln) * TS + (colw ^ ((((col0 >> 4) + cb) & 1) << 4))]);
+      const bf16x8 vb8 = ld_tr8(sh.v, VS, 8 * lg, 8 * lg + 4, col0 + 16 * cb, ln);  // tokens 8 lg .. 8 lg + 7
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -484,17 +489,17 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
         for (int r = 0; r < 4; ++r) U[ib][cb][r] = acc[r];
       }
     }
-    __syncthreads();
 
-    // ---- 8. U = T diag(b) V - W S, and diag(g) Q S (S split one channel-block pair at a time)
+    // ---- 8. X = K S and diag(g) Q S (S split one channel-block pair at a time; K and Q
+    //         are exact bf16 operands), then U = T diag(b) V - T diag(b g) X
     float O[2][NCB][4];
     {
-      f32x4 ws[2][NCB], qs[2][NCB];
+      f32x4 xs[2][NCB], qs[2][NCB];
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          ws[ib][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          xs[ib][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
           qs[ib][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
@@ -505,28 +510,45 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
           const int rowk = (16 * ib + ln) * KS + 32 * kp + 4 * lg;
-          const bf16x8 wah = ld_2x64(&sh.wh[rowk], &sh.wh[rowk + 16]);
-          const bf16x8 wal = ld_2x64(&sh.wl[rowk], &sh.wl[rowk + 16]);
+          const bf16x8 ka = ld_2x64(&sh.k[rowk], &sh.k[rowk + 16]);
           const bf16x8 qa = ld_2x64(&sh.q[rowk], &sh.q[rowk + 16]);
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
-            ws[ib][cb] = mma(wah, shi[cb], ws[ib][cb]);
-            ws[ib][cb] = mma(wah, slo[cb], ws[ib][cb]);
-            ws[ib][cb] = mma(wal, shi[cb], ws[ib][cb]);
+            xs[ib][cb] = mma(ka, shi[cb], xs[ib][cb]);
+            xs[ib][cb] = mma(ka, slo[cb], xs[ib][cb]);
             qs[ib][cb] = mma(qa, shi[cb], qs[ib][cb]);
             qs[ib][cb] = mma(qa, slo[cb], qs[ib][cb]);
           }
         }
       }
+      // X (accumulator layout, tokens 4 lg + r and 16 + 4 lg + r) is the B operand of
+      // T diag(b g) X with the tokens paired the same way in the A operand.
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
+      for (int cb = 0; cb < NCB; ++cb) {
+        float x0[4], x1[4];
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
+        for (int r = 0; r < 4; ++r) {
+          x0[r] = xs[0][cb][r];
+          x1[r] = xs[1][cb][r];
+        }
+        bf16x8 xhi, xlo;
+        split_pair(x0, x1, xhi, xlo);
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+          const int rowt = (16 * ib + ln) * BS + 4 * lg;
+          const bf16x8 tah = ld_2x64(&sh.t2h[rowt], &sh.t2h[rowt + 16]);
+          const bf16x8 tal = ld_2x64(&sh.t2l[rowt], &sh.t2l[rowt + 16]);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          acc = mma(tah, xhi, acc);
+          acc = mma(tah, xlo, acc);
+          acc = mma(tal, xhi, acc);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            U[ib][cb][r] -= ws[ib][cb][r];
+            U[ib][cb][r] -= acc[r];
             O[ib][cb][r] = sh.gam[16 * ib + 4 * lg + r] * qs[ib][cb][r];
           }
+        }
+      }
     }
 
     // ---- 9. O += (M o Q K^T) U; write the outputs
@@ -566,8 +588,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     for (int cb = 0; cb < NCB; ++cb) split_pair(U[0][cb], U[1][cb], u2hi[cb], u2lo[cb]);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const uint16_t* kr = &sh.kt[(16 * kb + ln) * TS];
-      const bf16x8 ka = ld_2x64(kr + (colp ^ ((kb & 1) << 4)), kr + (colp ^ ((~kb & 1) << 4)));
+      const bf16x8 ka = ld_tr8(sh.k, KS, 4 * lg, 16 + 4 * lg, 16 * kb, ln);  // K^T, tokens as U's rows
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         f32x4 acc = {gC * S[kb][cb][0], gC * S[kb][cb][1], gC * S[kb][cb][2], gC * S[kb][cb][3]};
