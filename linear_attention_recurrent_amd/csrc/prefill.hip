@@ -197,11 +197,14 @@ __device__ __forceinline__ void st_base(__amdgpu_buffer_rsrc_t r, uint32_t voff,
 __device__ __forceinline__ int tswz(int ch, int tok) { return tok ^ (((ch >> 3) & 3) << 3); }
 
 // T = (I + A)^-1 for a 32 x 32 strictly lower A (fp32 in LDS, row stride MS), by
-// blocks of 16: the two diagonal blocks by forward substitution (waves 0 and 1,
-// lane j: column j, four partial sums per row to shorten the dependent chain),
-// then T_10 = -T_11 (A_10 T_00) with every thread computing one entry.  T's upper
-// right block must already be zero.  xs: 16 x 17 floats of scratch.  Called by
-// the whole workgroup (it synchronises); returns after a barrier.
+// blocks of 16: the two diagonal blocks by forward substitution (waves 0 and 1, lane j:
+// column j), then T_10 = -T_11 (A_10 T_00) with every thread computing one entry.  The
+// substitution is right-looking: once x_p is final it is subtracted from every later
+// row's residual, so the dependent chain is one FMA per row.  Lane j loads column j of
+// its diagonal block of A once; the factor A_mp that every lane needs at step p is then
+// lane p's register, broadcast with v_readlane (no further LDS round trips).  T's upper
+// right block must already be zero.  xs: 16 x 17 floats of scratch.  Called by the
+// whole workgroup (it synchronises); returns after a barrier.
 template <int MS>
 __device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, float* xs, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
@@ -209,13 +212,18 @@ __device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, fl
     const int o = 16 * wave;
     int col = lane;
     asm volatile("" : "+v"(col));  // keeps the 16 (m == col) selects inside the caller's loop
-    float x[16];
+    float gc[16], x[16];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      float s[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int m = 1; m < 16; ++m) gc[m] = g[(o + m) * MS + o + col];  // A(o + m, o + col)
 #pragma unroll
-      for (int pp = 0; pp < m; ++pp) s[pp % 4] = fmaf(g[(o + m) * MS + o + pp], x[pp], s[pp % 4]);
-      x[m] = (m == col ? 1.f : 0.f) - ((s[0] + s[1]) + (s[2] + s[3]));
+    for (int m = 0; m < 16; ++m) x[m] = m == col ? 1.f : 0.f;
+#pragma unroll
+    for (int p = 0; p < 15; ++p) {
+      float f[16];  // column p of the block, read out of lane p before any of it is used
+#pragma unroll
+      for (int m = p + 1; m < 16; ++m) f[m] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gc[m]), p));
+#pragma unroll
+      for (int m = p + 1; m < 16; ++m) x[m] = fmaf(-f[m], x[p], x[m]);
     }
 #pragma unroll
     for (int m = 0; m < 16; ++m) t[(o + m) * MS + o + col] = x[m];
@@ -316,36 +324,36 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
   constexpr int LK = (NPK + kThreads - 1) / kThreads, LV = (NPV + kThreads - 1) / kThreads;
   uint4 nk[LK][2], nq[LK][2], nv[LV][2];
   float ndec = 1.f, nbt = 0.f;
-  auto row_ptr = [&](const uint16_t* x, int t, int d) { return x + ((bseq * T + t) * H + h) * d; };
+  // The chunk's rows of one (sequence, head) as a buffer resource that ends after the
+  // prompt's last row: rows past it read as zeros, with no branch and no 64-bit addresses.
+  auto chunk_rows = [&](const void* x, int t0, int bytes_per_row) {
+    const int rows = T - t0 < C ? T - t0 : C;
+    return make_rsrc(static_cast<const char*>(x) + ((bseq * T + t0) * H + h) * bytes_per_row,
+                     static_cast<uint32_t>(rows * H * bytes_per_row));
+  };
   auto fetch = [&](int t0) {
+    const auto rk = chunk_rows(a.k, t0, 2 * DK), rq = chunk_rows(a.q, t0, 2 * DK), rv = chunk_rows(a.v, t0, 2 * DV);
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
       const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        nk[i][s2] = nq[i][s2] = make_uint4(0, 0, 0, 0);
-        if (pc < NPK && t0 + tok + s2 < T) {
-          nk[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.k, t0 + tok + s2, DK))[seg];
-          nq[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.q, t0 + tok + s2, DK))[seg];
-        }
+        const uint32_t off = static_cast<uint32_t>(((tok + s2) * H * DK + seg * 8) * 2);
+        nk[i][s2] = bload16(rk, off);
+        nq[i][s2] = bload16(rq, off);
       }
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
       const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        nv[i][s2] = make_uint4(0, 0, 0, 0);
-        if (pc < NPV && t0 + tok + s2 < T)
-          nv[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.v, t0 + tok + s2, DV))[seg];
-      }
+      for (int s2 = 0; s2 < 2; ++s2)
+        nv[i][s2] = bload16(rv, static_cast<uint32_t>(((tok + s2) * H * DV + seg * 8) * 2));
     }
-    if (wave == 3) {
-      const int t = t0 + lane;
-      const bool ok = lane < C && t < T;
-      const size_t si = (bseq * T + (ok ? t : 0)) * H + h;
-      ndec = ok ? a.decay[si] : 1.f;
-      nbt = ok ? (kla ? a.eta[si] : a.beta[si]) : 0.f;
+    if (wave == 3) {  // lanes past the chunk or the prompt read zeros
+      const uint32_t off = static_cast<uint32_t>(lane * H * 4);
+      ndec = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(chunk_rows(a.decay, t0, 4), off, 0, 0));
+      nbt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(chunk_rows(kla ? a.eta : a.beta, t0, 4), off, 0, 0));
     }
   };
   fetch(0);
