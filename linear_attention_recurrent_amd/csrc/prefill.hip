@@ -34,10 +34,9 @@
 // may pair any k order consistently between A and B; the state and U feed the
 // B operand straight from accumulator registers with k = {4g + r} u {16 + 4g + r}
 // (so does X, over tokens).
-// Where tokens run along an operand's k index (K^T in the state update, V in T diag(b) V),
-// the GDN kernel reads the token rows through ds_read_b64_tr_b16; the KDA and RWKV6
-// kernels build decay-scaled, split copies token-major instead.  Every operand is read
-// with 8- or 16-byte LDS loads.
+// Every array is stored in token rows; where tokens run along an operand's k index (K^T
+// and its decay-scaled copies in the state update, V), the operand is read through
+// ds_read_b64_tr_b16.  Every operand is read with 8- or 16-byte LDS loads.
 #include "launch.hpp"
 
 namespace dl {
@@ -190,11 +189,6 @@ __device__ __forceinline__ void st_base(__amdgpu_buffer_rsrc_t r, uint32_t voff,
   else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
 }
 
-// Token-major copies of K and V (one row per channel, tokens along the row) are
-// stored with the token index XORed by 8 ((channel / 8) mod 4): a group of 8 (or
-// 4) consecutive tokens stays contiguous, and the transposing 2-byte stores of
-// the 16 lanes that share a token spread over the LDS banks.
-__device__ __forceinline__ int tswz(int ch, int tok) { return tok ^ (((ch >> 3) & 3) << 3); }
 
 // T = (I + A)^-1 for a 32 x 32 strictly lower A (fp32 in LDS, row stride MS), by
 // blocks of 16: the two diagonal blocks by forward substitution (waves 0 and 1, lane j:
@@ -240,6 +234,16 @@ __device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, fl
   for (int m = 0; m < 16; ++m) y = fmaf(t[(16 + i) * MS + 16 + m], xs[m * 17 + j], y);
   t[(16 + i) * MS + j] = -y;
   __syncthreads();
+}
+
+// Rows t0 .. t0 + C - 1 of one (sequence, head) of a [batch][T][heads][row] input as a
+// buffer resource that ends after the prompt's last row: rows past it read as zeros, with
+// no branch and no 64-bit address arithmetic per load.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rows(const void* x, size_t bseq, size_t h, int T, int H,
+                                                              int t0, int bytes_per_row) {
+  const int rows = T - t0 < kChunk ? T - t0 : kChunk;
+  return make_rsrc(static_cast<const char*>(x) + ((bseq * T + t0) * H + h) * bytes_per_row,
+                   static_cast<uint32_t>(rows * H * bytes_per_row));
 }
 
 // Output rows t0 .. t0 + C - 1 of one sequence as a buffer resource that covers only
@@ -324,15 +328,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
   constexpr int LK = (NPK + kThreads - 1) / kThreads, LV = (NPV + kThreads - 1) / kThreads;
   uint4 nk[LK][2], nq[LK][2], nv[LV][2];
   float ndec = 1.f, nbt = 0.f;
-  // The chunk's rows of one (sequence, head) as a buffer resource that ends after the
-  // prompt's last row: rows past it read as zeros, with no branch and no 64-bit addresses.
-  auto chunk_rows = [&](const void* x, int t0, int bytes_per_row) {
-    const int rows = T - t0 < C ? T - t0 : C;
-    return make_rsrc(static_cast<const char*>(x) + ((bseq * T + t0) * H + h) * bytes_per_row,
-                     static_cast<uint32_t>(rows * H * bytes_per_row));
-  };
+  auto rows_of = [&](const void* x, int t0, int bytes_per_row) { return chunk_rows(x, bseq, h, T, H, t0, bytes_per_row); };
   auto fetch = [&](int t0) {
-    const auto rk = chunk_rows(a.k, t0, 2 * DK), rq = chunk_rows(a.q, t0, 2 * DK), rv = chunk_rows(a.v, t0, 2 * DV);
+    const auto rk = rows_of(a.k, t0, 2 * DK), rq = rows_of(a.q, t0, 2 * DK), rv = rows_of(a.v, t0, 2 * DV);
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
       const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
@@ -352,8 +350,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     }
     if (wave == 3) {  // lanes past the chunk or the prompt read zeros
       const uint32_t off = static_cast<uint32_t>(lane * H * 4);
-      ndec = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(chunk_rows(a.decay, t0, 4), off, 0, 0));
-      nbt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(chunk_rows(kla ? a.eta : a.beta, t0, 4), off, 0, 0));
+      ndec = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rows_of(a.decay, t0, 4), off, 0, 0));
+      nbt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rows_of(kla ? a.eta : a.beta, t0, 4), off, 0, 0));
     }
   };
   fetch(0);
@@ -655,9 +653,10 @@ __device__ __forceinline__ void prefix_over_tokens(float* cc, float* glast, int 
 template <int DK, int DV>
 struct PrefillKdaLds {
   static constexpr int C = kChunk;
-  static constexpr int KS = DK + 8;  // bf16 row stride of K, Q, W and Q o G
-  static constexpr int TS = C + 8;   // bf16 row stride of the token-major arrays
-  static constexpr int MS = C + 1;   // fp32 row stride of the C x C matrices
+  static constexpr int KS = DK + 8;   // bf16 row stride of K, Q, W and Q o G
+  static constexpr int RS = DK + 16;  // bf16 row stride of K o G and K o G_C / G, and
+  static constexpr int VS = DV + 16;  // of V: 8 mod 32 words (transposing reads)
+  static constexpr int MS = C + 1;    // fp32 row stride of the C x C matrices
   static constexpr int BS = C + 8;   // bf16 row stride of the split C x C matrices
   static constexpr int CS = DK + 4;  // fp32 row stride of the per-channel decays
   float beta[C];
@@ -681,10 +680,10 @@ struct PrefillKdaLds {
     uint16_t wl[C * KS];  // then W (lo part)
   };
   uint16_t qgh[C * KS], qgl[C * KS];  // Q o G, token rows, split
-  uint16_t vt[DV * TS];               // V token-major
-  uint16_t kgh[DK * TS], kgl[DK * TS];  // K o G, token-major, split
-  uint16_t kdh[DK * TS], kdl[DK * TS];  // K o G_C / G, token-major, split
-  float cc[C * CS];                     // log2 decays, then their prefix sums over the chunk
+  uint16_t v[C * VS];                 // V, token rows
+  uint16_t kgh[C * RS], kgl[C * RS];  // K o G, token rows, split
+  uint16_t kdh[C * RS], kdl[C * RS];  // K o G_C / G, token rows, split
+  float cc[C * CS];                   // log2 decays, then their prefix sums over the chunk
 };
 
 template <int DK, int DV, bool BF>
@@ -695,7 +694,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
   constexpr int NKB = DK / 16;
   constexpr int NKP = DK / 32;
   using Lds = PrefillKdaLds<DK, DV>;
-  constexpr int KS = Lds::KS, TS = Lds::TS, MS = Lds::MS, BS = Lds::BS, CS = Lds::CS;
+  constexpr int KS = Lds::KS, RS = Lds::RS, VS = Lds::VS, MS = Lds::MS, BS = Lds::BS, CS = Lds::CS;
   __shared__ __align__(16) Lds sh;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -704,9 +703,6 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
   const int H = pa.heads, T = a.tokens;
   const size_t bseq = static_cast<size_t>(tile / H), h = static_cast<size_t>(tile % H);
   const int col0 = wave * CW;
-  const int sw0 = (ln >> 3) << 3;
-  const int colw = (8 * lg) ^ sw0;
-  const int colp = (4 * lg) ^ sw0;
 
   float S[NKB][NCB][4];
   constexpr int EB = BF ? 2 : 4;
@@ -728,58 +724,43 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
   uint4 nk[LK][2], nq[LK][2], nv[LV][2];
   float4 nd[ND];
   float nbt = 0.f;
-  auto row_ptr = [&](const uint16_t* x, int t, int d) { return x + ((bseq * T + t) * H + h) * d; };
-  auto fetch = [&](int t0) {
+  auto rows_of = [&](const void* x, int t0, int bytes_per_row) { return chunk_rows(x, bseq, h, T, H, t0, bytes_per_row); };
+  auto fetch = [&](int t0) {  // rows past the prompt read as zeros
+    const auto rk = rows_of(a.k, t0, 2 * DK), rq = rows_of(a.q, t0, 2 * DK), rv = rows_of(a.v, t0, 2 * DV);
+    const auto rd = rows_of(a.decay, t0, 4 * DK);
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
       const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        nk[i][s2] = nq[i][s2] = make_uint4(0, 0, 0, 0);
-        if (pc < NPK && t0 + tok + s2 < T) {
-          nk[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.k, t0 + tok + s2, DK))[seg];
-          nq[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.q, t0 + tok + s2, DK))[seg];
-        }
+        const uint32_t off = static_cast<uint32_t>(((tok + s2) * H * DK + seg * 8) * 2);
+        nk[i][s2] = bload16(rk, off);
+        nq[i][s2] = bload16(rq, off);
       }
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
       const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        nv[i][s2] = make_uint4(0, 0, 0, 0);
-        if (pc < NPV && t0 + tok + s2 < T)
-          nv[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.v, t0 + tok + s2, DV))[seg];
-      }
+      for (int s2 = 0; s2 < 2; ++s2)
+        nv[i][s2] = bload16(rv, static_cast<uint32_t>(((tok + s2) * H * DV + seg * 8) * 2));
     }
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
       const int pc = tid + i * kThreads, tok = pc / (DK / 4), seg = pc % (DK / 4);
-      nd[i] = make_float4(1.f, 1.f, 1.f, 1.f);
-      if (t0 + tok < T)
-        nd[i] = reinterpret_cast<const float4*>(a.decay + ((bseq * T + t0 + tok) * H + h) * DK)[seg];
+      const uint4 w = bload16(rd, static_cast<uint32_t>((tok * H * DK + seg * 4) * 4));
+      nd[i] = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
     }
-    if (wave == 3) {
-      const int t = t0 + lane;
-      const bool ok = lane < C && t < T;
-      const size_t si = (bseq * T + (ok ? t : 0)) * H + h;
-      nbt = ok ? (kla ? a.eta[si] : a.beta[si]) : 0.f;
-    }
-  };
-  auto interleave = [](const uint4 w0, const uint4 w1, uint32_t (&o)[8]) {
-    const uint32_t a0[4] = {w0.x, w0.y, w0.z, w0.w}, a1[4] = {w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o[2 * e] = (a0[e] & 0xffffu) | (a1[e] << 16);
-      o[2 * e + 1] = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
-    }
+    if (wave == 3)
+      nbt = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rows_of(kla ? a.eta : a.beta, t0, 4),
+                                                                 static_cast<uint32_t>(lane * H * 4), 0, 0));
   };
   fetch(0);
 
   for (int t0 = 0; t0 < T; t0 += C) {
     __syncthreads();
 
-    // ---- 1. K, Q rows; V token-major; clamped log2 decays; ||k||^2; step sizes
+    // ---- 1. K, Q and V rows; clamped log2 decays; ||k||^2; step sizes
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
       const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
@@ -807,21 +788,17 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     for (int i = 0; i < LV; ++i) {
       const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
       if (pc < NPV) {
-        uint32_t vw[8];
-        interleave(nv[i][0], nv[i][1], vw);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ch = seg * 8 + e;
-          *reinterpret_cast<uint32_t*>(&sh.vt[ch * TS + tswz(ch, tok)]) = vw[e];
-        }
+        for (int s2 = 0; s2 < 2; ++s2) *reinterpret_cast<uint4*>(&sh.v[(tok + s2) * VS + seg * 8]) = nv[i][s2];
       }
     }
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
       const int pc = tid + i * kThreads, tok = pc / (DK / 4), seg = pc % (DK / 4);
+      const bool ok = t0 + tok < T;  // tokens past the prompt do not decay the state
       *reinterpret_cast<float4*>(&sh.cc[tok * CS + seg * 4]) =
-          make_float4(step_log2_decay(nd[i].x), step_log2_decay(nd[i].y), step_log2_decay(nd[i].z),
-                      step_log2_decay(nd[i].w));
+          make_float4(ok ? step_log2_decay(nd[i].x) : 0.f, ok ? step_log2_decay(nd[i].y) : 0.f,
+                      ok ? step_log2_decay(nd[i].z) : 0.f, ok ? step_log2_decay(nd[i].w) : 0.f);
     }
     if (wave == 3 && lane < C) sh.braw[lane] = nbt;
     if (t0 + C < T) fetch(t0 + C);
@@ -844,7 +821,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     }
     __syncthreads();
 
-    // ---- 3. decay-folded operands: Q o G (rows), K o G and K o G_C / G (token-major), split
+    // ---- 3. decay-folded operands Q o G, K o G and K o G_C / G (token rows), split
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
       const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
@@ -857,32 +834,29 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
           load8(&sh.cc[(tok + s2) * CS + seg * 8], cf[s2]);
         }
         load8(&sh.cc[(C - 1) * CS + seg * 8], cl);
-        uint32_t qh[2][4], ql[2][4], kgh2[8], kgl2[8], kdh2[8], kdl2[8];
+        uint32_t qh[2][4], ql[2][4], kgh2[2][4], kgl2[2][4], kdh2[2][4], kdl2[2][4];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
+        for (int e = 0; e < 8; e += 2) {  // channels e, e + 1 packed
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
-            split2(qf[s2][e] * fexp2(cf[s2][e]), qf[s2][e + 1] * fexp2(cf[s2][e + 1]), qh[s2][e / 2], ql[s2][e / 2]);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {  // channel seg*8 + e: tokens tok, tok + 1 packed
-          split2(kf[0][e] * fexp2(cf[0][e]), kf[1][e] * fexp2(cf[1][e]), kgh2[e], kgl2[e]);
-          split2(kf[0][e] * fexp2(cl[e] - cf[0][e]), kf[1][e] * fexp2(cl[e] - cf[1][e]), kdh2[e], kdl2[e]);
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const float g0 = fexp2(cf[s2][e]), g1 = fexp2(cf[s2][e + 1]);
+            split2(qf[s2][e] * g0, qf[s2][e + 1] * g1, qh[s2][e / 2], ql[s2][e / 2]);
+            split2(kf[s2][e] * g0, kf[s2][e + 1] * g1, kgh2[s2][e / 2], kgl2[s2][e / 2]);
+            split2(kf[s2][e] * fexp2(cl[e] - cf[s2][e]), kf[s2][e + 1] * fexp2(cl[e + 1] - cf[s2][e + 1]),
+                   kdh2[s2][e / 2], kdl2[s2][e / 2]);
+          }
         }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          *reinterpret_cast<uint4*>(&sh.qgh[(tok + s2) * KS + seg * 8]) =
-              make_uint4(qh[s2][0], qh[s2][1], qh[s2][2], qh[s2][3]);
-          *reinterpret_cast<uint4*>(&sh.qgl[(tok + s2) * KS + seg * 8]) =
-              make_uint4(ql[s2][0], ql[s2][1], ql[s2][2], ql[s2][3]);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ch = seg * 8 + e, o = ch * TS + tswz(ch, tok);
-          *reinterpret_cast<uint32_t*>(&sh.kgh[o]) = kgh2[e];
-          *reinterpret_cast<uint32_t*>(&sh.kgl[o]) = kgl2[e];
-          *reinterpret_cast<uint32_t*>(&sh.kdh[o]) = kdh2[e];
-          *reinterpret_cast<uint32_t*>(&sh.kdl[o]) = kdl2[e];
+          auto row = [&](uint16_t* x, int stride, const uint32_t (&w)[2][4]) {
+            *reinterpret_cast<uint4*>(&x[(tok + s2) * stride + seg * 8]) = make_uint4(w[s2][0], w[s2][1], w[s2][2], w[s2][3]);
+          };
+          row(sh.qgh, KS, qh);
+          row(sh.qgl, KS, ql);
+          row(sh.kgh, RS, kgh2);
+          row(sh.kgl, RS, kgl2);
+          row(sh.kdh, RS, kdh2);
+          row(sh.kdl, RS, kdl2);
         }
       }
     }
@@ -1024,8 +998,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     for (int e = 0; e < NKB / 2; ++e) {
       const int blk = wave + 4 * e;
       const int ib = blk / NKB, cb = blk % NKB;
-      const int o = (16 * cb + ln) * TS + (colw ^ ((cb & 1) << 4));
-      const bf16x8 kah = ld_b128(&sh.kgh[o]), kal = ld_b128(&sh.kgl[o]);
+      const bf16x8 kah = ld_tr8(sh.kgh, RS, 8 * lg, 8 * lg + 4, 16 * cb, ln);  // tokens 8 lg .. 8 lg + 7
+      const bf16x8 kal = ld_tr8(sh.kgl, RS, 8 * lg, 8 * lg + 4, 16 * cb, ln);
       const bf16x8 tbh = ld_b128(&sh.t1h[(16 * ib + ln) * BS + 8 * lg]);
       const bf16x8 tbl = ld_b128(&sh.t1l[(16 * ib + ln) * BS + 8 * lg]);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1042,7 +1016,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     float U[2][NCB][4];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      const bf16x8 vb8 = ld_b128(&sh.vt[(col0 + 16 * cb + ln) * TS + (colw ^ ((((col0 >> 4) + cb) & 1) << 4))]);
+      const bf16x8 vb8 = ld_tr8(sh.v, VS, 8 * lg, 8 * lg + 4, col0 + 16 * cb, ln);
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1127,10 +1101,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     for (int cb = 0; cb < NCB; ++cb) split_pair(U[0][cb], U[1][cb], u2hi[cb], u2lo[cb]);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const int ro = (16 * kb + ln) * TS;
-      const int c0 = colp ^ ((kb & 1) << 4), c1 = colp ^ ((~kb & 1) << 4);
-      const bf16x8 kah = ld_2x64(&sh.kdh[ro + c0], &sh.kdh[ro + c1]);
-      const bf16x8 kal = ld_2x64(&sh.kdl[ro + c0], &sh.kdl[ro + c1]);
+      const bf16x8 kah = ld_tr8(sh.kdh, RS, 4 * lg, 16 + 4 * lg, 16 * kb, ln);  // tokens as U's rows
+      const bf16x8 kal = ld_tr8(sh.kdl, RS, 4 * lg, 16 + 4 * lg, 16 * kb, ln);
       float gl[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) gl[r] = sh.glast[16 * kb + 4 * lg + r];
@@ -1169,7 +1141,8 @@ template <int DK, int DV>
 struct PrefillRwkvLds {
   static constexpr int C = kChunk;
   static constexpr int KS = DK + 8;
-  static constexpr int TS = C + 8;
+  static constexpr int RS = DK + 16;  // K o G_C / G and V: 8 mod 32 words (transposing reads)
+  static constexpr int VS = DV + 16;
   static constexpr int BS = C + 8;
   static constexpr int CS = DK + 4;
   float bonus[DK];
@@ -1179,9 +1152,9 @@ struct PrefillRwkvLds {
   uint16_t k[C * KS];                 // K, token rows
   uint16_t q[C * KS];                 // R, token rows
   uint16_t rgh[C * KS], rgl[C * KS];  // R o G_prev, token rows, split
-  uint16_t vt[DV * TS];               // V token-major
-  uint16_t kdh[DK * TS], kdl[DK * TS];  // K o G_C / G, token-major, split
-  float cc[C * CS];                     // log2 decays, then their prefix sums
+  uint16_t v[C * VS];                 // V, token rows
+  uint16_t kdh[C * RS], kdl[C * RS];  // K o G_C / G, token rows, split
+  float cc[C * CS];                   // log2 decays, then their prefix sums
 };
 
 template <int DK, int DV, bool BF>
@@ -1192,7 +1165,7 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
   constexpr int NKB = DK / 16;
   constexpr int NKP = DK / 32;
   using Lds = PrefillRwkvLds<DK, DV>;
-  constexpr int KS = Lds::KS, TS = Lds::TS, BS = Lds::BS, CS = Lds::CS;
+  constexpr int KS = Lds::KS, RS = Lds::RS, VS = Lds::VS, BS = Lds::BS, CS = Lds::CS;
   __shared__ __align__(16) Lds sh;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1201,8 +1174,6 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
   const int H = pa.heads, T = a.tokens;
   const size_t bseq = static_cast<size_t>(tile / H), h = static_cast<size_t>(tile % H);
   const int col0 = wave * CW;
-  const int sw0 = (ln >> 3) << 3;
-  const int colw = (8 * lg) ^ sw0;
 
   float S[NKB][NCB][4];
   constexpr int EB = BF ? 2 : 4;
@@ -1223,44 +1194,32 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
   constexpr int ND = C * DK / 4 / kThreads;
   uint4 nk[LK][2], nq[LK][2], nv[LV][2];
   float4 nd[ND];
-  auto row_ptr = [&](const uint16_t* x, int t, int d) { return x + ((bseq * T + t) * H + h) * d; };
-  auto fetch = [&](int t0) {
+  auto rows_of = [&](const void* x, int t0, int bytes_per_row) { return chunk_rows(x, bseq, h, T, H, t0, bytes_per_row); };
+  auto fetch = [&](int t0) {  // rows past the prompt read as zeros
+    const auto rk = rows_of(a.k, t0, 2 * DK), rq = rows_of(a.q, t0, 2 * DK), rv = rows_of(a.v, t0, 2 * DV);
+    const auto rd = rows_of(a.decay, t0, 4 * DK);
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
       const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        nk[i][s2] = nq[i][s2] = make_uint4(0, 0, 0, 0);
-        if (pc < NPK && t0 + tok + s2 < T) {
-          nk[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.k, t0 + tok + s2, DK))[seg];
-          nq[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.q, t0 + tok + s2, DK))[seg];
-        }
+        const uint32_t off = static_cast<uint32_t>(((tok + s2) * H * DK + seg * 8) * 2);
+        nk[i][s2] = bload16(rk, off);
+        nq[i][s2] = bload16(rq, off);
       }
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
       const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        nv[i][s2] = make_uint4(0, 0, 0, 0);
-        if (pc < NPV && t0 + tok + s2 < T)
-          nv[i][s2] = reinterpret_cast<const uint4*>(row_ptr(a.v, t0 + tok + s2, DV))[seg];
-      }
+      for (int s2 = 0; s2 < 2; ++s2)
+        nv[i][s2] = bload16(rv, static_cast<uint32_t>(((tok + s2) * H * DV + seg * 8) * 2));
     }
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
       const int pc = tid + i * kThreads, tok = pc / (DK / 4), seg = pc % (DK / 4);
-      nd[i] = make_float4(1.f, 1.f, 1.f, 1.f);
-      if (t0 + tok < T)
-        nd[i] = reinterpret_cast<const float4*>(a.decay + ((bseq * T + t0 + tok) * H + h) * DK)[seg];
-    }
-  };
-  auto interleave = [](const uint4 w0, const uint4 w1, uint32_t (&o)[8]) {
-    const uint32_t a0[4] = {w0.x, w0.y, w0.z, w0.w}, a1[4] = {w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      o[2 * e] = (a0[e] & 0xffffu) | (a1[e] << 16);
-      o[2 * e + 1] = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
+      const uint4 w = bload16(rd, static_cast<uint32_t>((tok * H * DK + seg * 4) * 4));
+      nd[i] = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
     }
   };
   fetch(0);
@@ -1268,7 +1227,7 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
   for (int t0 = 0; t0 < T; t0 += C) {
     __syncthreads();
 
-    // ---- 1. K, R rows; V token-major; clamped log2 decays
+    // ---- 1. K, R and V rows; clamped log2 decays
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
       const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
@@ -1284,21 +1243,17 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
     for (int i = 0; i < LV; ++i) {
       const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
       if (pc < NPV) {
-        uint32_t vw[8];
-        interleave(nv[i][0], nv[i][1], vw);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ch = seg * 8 + e;
-          *reinterpret_cast<uint32_t*>(&sh.vt[ch * TS + tswz(ch, tok)]) = vw[e];
-        }
+        for (int s2 = 0; s2 < 2; ++s2) *reinterpret_cast<uint4*>(&sh.v[(tok + s2) * VS + seg * 8]) = nv[i][s2];
       }
     }
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
       const int pc = tid + i * kThreads, tok = pc / (DK / 4), seg = pc % (DK / 4);
+      const bool ok = t0 + tok < T;  // tokens past the prompt do not decay the state
       *reinterpret_cast<float4*>(&sh.cc[tok * CS + seg * 4]) =
-          make_float4(step_log2_decay(nd[i].x), step_log2_decay(nd[i].y), step_log2_decay(nd[i].z),
-                      step_log2_decay(nd[i].w));
+          make_float4(ok ? step_log2_decay(nd[i].x) : 0.f, ok ? step_log2_decay(nd[i].y) : 0.f,
+                      ok ? step_log2_decay(nd[i].z) : 0.f, ok ? step_log2_decay(nd[i].w) : 0.f);
     }
     if (t0 + C < T) fetch(t0 + C);
     __syncthreads();
@@ -1307,7 +1262,7 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
     prefix_over_tokens<DK, CS>(sh.cc, sh.glast, tid);
     __syncthreads();
 
-    // ---- 3. R o G_prev (rows) and K o G_C / G (token-major), split; the bonus diagonal
+    // ---- 3. R o G_prev and K o G_C / G (token rows), split; the bonus diagonal
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
       const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
@@ -1324,28 +1279,26 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
 #pragma unroll
           for (int e = 0; e < 8; ++e) cp[e] = 0.f;
         load8(&sh.cc[(C - 1) * CS + seg * 8], cl);
-        uint32_t rh[2][4], rl[2][4], kdh2[8], kdl2[8];
+        uint32_t rh[2][4], rl[2][4], kdh2[2][4], kdl2[2][4];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
+        for (int e = 0; e < 8; e += 2) {  // channels e, e + 1 packed
           // token tok reads G_{tok-1}, token tok + 1 reads G_tok
           split2(rf[0][e] * fexp2(cp[e]), rf[0][e + 1] * fexp2(cp[e + 1]), rh[0][e / 2], rl[0][e / 2]);
           split2(rf[1][e] * fexp2(cf[0][e]), rf[1][e + 1] * fexp2(cf[0][e + 1]), rh[1][e / 2], rl[1][e / 2]);
-        }
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          split2(kf[0][e] * fexp2(cl[e] - cf[0][e]), kf[1][e] * fexp2(cl[e] - cf[1][e]), kdh2[e], kdl2[e]);
+          for (int s2 = 0; s2 < 2; ++s2)
+            split2(kf[s2][e] * fexp2(cl[e] - cf[s2][e]), kf[s2][e + 1] * fexp2(cl[e + 1] - cf[s2][e + 1]),
+                   kdh2[s2][e / 2], kdl2[s2][e / 2]);
+        }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          *reinterpret_cast<uint4*>(&sh.rgh[(tok + s2) * KS + seg * 8]) =
-              make_uint4(rh[s2][0], rh[s2][1], rh[s2][2], rh[s2][3]);
-          *reinterpret_cast<uint4*>(&sh.rgl[(tok + s2) * KS + seg * 8]) =
-              make_uint4(rl[s2][0], rl[s2][1], rl[s2][2], rl[s2][3]);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ch = seg * 8 + e, o = ch * TS + tswz(ch, tok);
-          *reinterpret_cast<uint32_t*>(&sh.kdh[o]) = kdh2[e];
-          *reinterpret_cast<uint32_t*>(&sh.kdl[o]) = kdl2[e];
+          auto row = [&](uint16_t* x, int stride, const uint32_t (&w)[2][4]) {
+            *reinterpret_cast<uint4*>(&x[(tok + s2) * stride + seg * 8]) = make_uint4(w[s2][0], w[s2][1], w[s2][2], w[s2][3]);
+          };
+          row(sh.rgh, KS, rh);
+          row(sh.rgl, KS, rl);
+          row(sh.kdh, RS, kdh2);
+          row(sh.kdl, RS, kdl2);
         }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -1510,7 +1463,7 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
     bf16x8 vb[NCB];  // V[token 8 lg + s][this lane's column], the B operand of P V and of the update
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
-      vb[cb] = ld_b128(&sh.vt[(col0 + 16 * cb + ln) * TS + (colw ^ ((((col0 >> 4) + cb) & 1) << 4))]);
+      vb[cb] = ld_tr8(sh.v, VS, 8 * lg, 8 * lg + 4, col0 + 16 * cb, ln);
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
       const bf16x8 pah = ld_b128(&sh.pmh[(16 * ib + ln) * BS + 8 * lg]);
@@ -1529,8 +1482,8 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
     // ---- 6. S = diag(G_C) S + (K o G_C / G)^T V
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const int o = (16 * kb + ln) * TS + (colw ^ ((kb & 1) << 4));
-      const bf16x8 kah = ld_b128(&sh.kdh[o]), kal = ld_b128(&sh.kdl[o]);
+      const bf16x8 kah = ld_tr8(sh.kdh, RS, 8 * lg, 8 * lg + 4, 16 * kb, ln);  // tokens 8 lg .. 8 lg + 7
+      const bf16x8 kal = ld_tr8(sh.kdl, RS, 8 * lg, 8 * lg + 4, 16 * kb, ln);
       float gl[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) gl[r] = sh.glast[16 * kb + 4 * lg + r];
