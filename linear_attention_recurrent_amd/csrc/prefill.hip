@@ -681,6 +681,7 @@ struct PrefillKdaLds {
   };
   uint16_t qgh[C * KS], qgl[C * KS];  // Q o G, token rows, split
   uint16_t v[C * VS];                 // V, token rows
+  float part[4 * 6 * 4 * 64];         // per-wave partial sums of A and P
   uint16_t kgh[C * RS], kgl[C * RS];  // K o G, token rows, split
   uint16_t kdh[C * RS], kdl[C * RS];  // K o G_C / G, token rows, split
   float cc[C * CS];                   // log2 decays, then their prefix sums over the chunk
@@ -866,9 +867,11 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     //        rows and columns 0..15, R = token 15 for the blocks of rows 16..31.
     //        Row factors are then <= 1 and column factors at most the decay over 16
     //        tokens, so when no channel decays by more than 2^-60 over either half of
-    //        the chunk the products run on MFMA with three-way split operands (three
-    //        waves, one 16 x 16 block each; these sums over channels can cancel, so
-    //        they keep 24 bits).  Otherwise every pair is formed directly.
+    //        the chunk the products run on MFMA with three-way split operands (these
+    //        sums over channels can cancel, so they keep 24 bits).  Each wave takes 32
+    //        channels of all three lower blocks, building each row and column operand
+    //        once; the four partial sums are added in a fixed order through LDS.
+    //        Otherwise every pair is formed directly.
     bool direct;
     {
       bool big = false;
@@ -877,58 +880,81 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
       direct = __syncthreads_or(big);
     }
     if (!direct) {
-      if (wave < 3) {
-        const int ib = wave == 0 ? 0 : 1, jb = wave == 2 ? 1 : 0;
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+      constexpr int NKS = DK / 32;           // 32-channel steps
+      constexpr int NW = NKS < 4 ? NKS : 4;  // waves that hold partial sums
+      // acc: A and P of the blocks (0,0), (1,0), (1,1) in that order
+      f32x4 acc[6];
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) {
-          const int ch0 = 32 * kk + 8 * lg;
-          float cr[8], cj[8], ref[8], kr[8], qr[8], kc[8];
-          load8(&sh.cc[(16 * ib + ln) * CS + ch0], cr);
-          load8(&sh.cc[(16 * jb + ln) * CS + ch0], cj);
-          if (ib == 1) load8(&sh.cc[15 * CS + ch0], ref);
-          else
+      for (int m = 0; m < 6; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kk = wave; kk < NKS; kk += 4) {
+        const int ch0 = 32 * kk + 8 * lg;
+        float c0[8], c1[8], ref[8], k0[8], k1[8], q0[8], q1[8];
+        load8(&sh.cc[ln * CS + ch0], c0);         // token ln
+        load8(&sh.cc[(16 + ln) * CS + ch0], c1);  // token 16 + ln
+        load8(&sh.cc[15 * CS + ch0], ref);
+        unpack8(*reinterpret_cast<const uint4*>(&sh.k[ln * KS + ch0]), k0);
+        unpack8(*reinterpret_cast<const uint4*>(&sh.k[(16 + ln) * KS + ch0]), k1);
+        unpack8(*reinterpret_cast<const uint4*>(&sh.q[ln * KS + ch0]), q0);
+        unpack8(*reinterpret_cast<const uint4*>(&sh.q[(16 + ln) * KS + ch0]), q1);
+        // rows: token ln with R = start, token 16 + ln with R = 15; columns: token ln with
+        // R = start and with R = 15, token 16 + ln with R = 15
+        uint32_t ka[3][4], qa[3][4], kb[3][4], qb[3][4], c00[3][4], c10[3][4], c11[3][4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ref[e] = 0.f;
-          unpack8(*reinterpret_cast<const uint4*>(&sh.k[(16 * ib + ln) * KS + ch0]), kr);
-          unpack8(*reinterpret_cast<const uint4*>(&sh.q[(16 * ib + ln) * KS + ch0]), qr);
-          unpack8(*reinterpret_cast<const uint4*>(&sh.k[(16 * jb + ln) * KS + ch0]), kc);
-          uint32_t ap[3][4], qp[3][4], bp[3][4];
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float r0 = fexp2(cr[e] - ref[e]), r1 = fexp2(cr[e + 1] - ref[e + 1]);
-            const float c0 = fexp2(ref[e] - cj[e]), c1 = fexp2(ref[e + 1] - cj[e + 1]);
-            split3(kr[e] * r0, kr[e + 1] * r1, ap[0][e / 2], ap[1][e / 2], ap[2][e / 2]);
-            split3(qr[e] * r0, qr[e + 1] * r1, qp[0][e / 2], qp[1][e / 2], qp[2][e / 2]);
-            split3(kc[e] * c0, kc[e + 1] * c1, bp[0][e / 2], bp[1][e / 2], bp[2][e / 2]);
-          }
-          bf16x8 Ax[3], Qx[3], Bx[3];
-#pragma unroll
-          for (int u = 0; u < 3; ++u) {
-            Ax[u] = pack8(ap[u][0], ap[u][1], ap[u][2], ap[u][3]);
-            Qx[u] = pack8(qp[u][0], qp[u][1], qp[u][2], qp[u][3]);
-            Bx[u] = pack8(bp[u][0], bp[u][1], bp[u][2], bp[u][3]);
-          }
-          accA = mma3(Ax, Bx, accA);
-          accP = mma3(Qx, Bx, accP);
+        for (int e = 0; e < 8; e += 2) {
+          const float r0a = fexp2(c0[e]), r0b = fexp2(c0[e + 1]);
+          const float r1a = fexp2(c1[e] - ref[e]), r1b = fexp2(c1[e + 1] - ref[e + 1]);
+          split3(k0[e] * r0a, k0[e + 1] * r0b, ka[0][e / 2], ka[1][e / 2], ka[2][e / 2]);
+          split3(q0[e] * r0a, q0[e + 1] * r0b, qa[0][e / 2], qa[1][e / 2], qa[2][e / 2]);
+          split3(k1[e] * r1a, k1[e + 1] * r1b, kb[0][e / 2], kb[1][e / 2], kb[2][e / 2]);
+          split3(q1[e] * r1a, q1[e + 1] * r1b, qb[0][e / 2], qb[1][e / 2], qb[2][e / 2]);
+          split3(k0[e] * fexp2(-c0[e]), k0[e + 1] * fexp2(-c0[e + 1]), c00[0][e / 2], c00[1][e / 2], c00[2][e / 2]);
+          split3(k0[e] * fexp2(ref[e] - c0[e]), k0[e + 1] * fexp2(ref[e + 1] - c0[e + 1]), c10[0][e / 2],
+                 c10[1][e / 2], c10[2][e / 2]);
+          split3(k1[e] * fexp2(ref[e] - c1[e]), k1[e + 1] * fexp2(ref[e + 1] - c1[e + 1]), c11[0][e / 2],
+                 c11[1][e / 2], c11[2][e / 2]);
         }
-        const int j = 16 * jb + ln;
-        float pm[4];
+        auto ops = [](const uint32_t (&w)[3][4], bf16x8 (&x)[3]) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * ib + 4 * lg + r;
-          sh.g[i * MS + j] = j < i ? sh.beta[i] * accA[r] : 0.f;
-          pm[r] = j <= i ? accP[r] : 0.f;
-        }
+          for (int u = 0; u < 3; ++u) x[u] = pack8(w[u][0], w[u][1], w[u][2], w[u][3]);
+        };
+        bf16x8 KA[3], QA[3], KB[3], QB[3], C00[3], C10[3], C11[3];
+        ops(ka, KA);
+        ops(qa, QA);
+        ops(kb, KB);
+        ops(qb, QB);
+        ops(c00, C00);
+        ops(c10, C10);
+        ops(c11, C11);
+        acc[0] = mma3(KA, C00, acc[0]);
+        acc[1] = mma3(QA, C00, acc[1]);
+        acc[2] = mma3(KB, C10, acc[2]);
+        acc[3] = mma3(QB, C10, acc[3]);
+        acc[4] = mma3(KB, C11, acc[4]);
+        acc[5] = mma3(QB, C11, acc[5]);
+      }
+      if (wave < NW) {
 #pragma unroll
-        for (int r = 0; r < 4; r += 2) {
-          const int i = 16 * ib + 4 * lg + r;
+        for (int m = 0; m < 6; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sh.part[((wave * 6 + m) * 4 + r) * 64 + lane] = acc[m][r];
+      }
+      __syncthreads();
+      // thread (r = wave, lane): entry r of this lane in each of the six block products
+      const int r = wave, j0 = ln;
+#pragma unroll
+      for (int m = 0; m < 6; ++m) {
+        float sum = sh.part[(m * 4 + r) * 64 + lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) sum += sh.part[((w * 6 + m) * 4 + r) * 64 + lane];
+        const int blk = m >> 1, ib = blk == 0 ? 0 : 1, jb = blk == 2 ? 1 : 0;
+        const int i = 16 * ib + 4 * lg + r, j = 16 * jb + j0;
+        if ((m & 1) == 0) {
+          sh.g[i * MS + j] = j < i ? sh.beta[i] * sum : 0.f;
+        } else {
           uint32_t hi, lo;
-          split2(pm[r], pm[r + 1], hi, lo);
+          split2(j <= i ? sum : 0.f, 0.f, hi, lo);
           sh.pmh[i * BS + j] = static_cast<uint16_t>(hi);
-          sh.pmh[(i + 1) * BS + j] = static_cast<uint16_t>(hi >> 16);
           sh.pml[i * BS + j] = static_cast<uint16_t>(lo);
-          sh.pml[(i + 1) * BS + j] = static_cast<uint16_t>(lo >> 16);
         }
       }
     } else {
