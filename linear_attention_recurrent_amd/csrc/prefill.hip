@@ -69,13 +69,6 @@ __device__ __forceinline__ bf16x8 ld_b128(const uint16_t* p) {
   return pack8(w.x, w.y, w.z, w.w);
 }
 
-// Two groups of four bf16 (8 bytes each) as one operand: slots 0..3, then 4..7.
-__device__ __forceinline__ bf16x8 ld_2x64(const uint16_t* p0, const uint16_t* p1) {
-  const uint2 a = *reinterpret_cast<const uint2*>(p0);
-  const uint2 b = *reinterpret_cast<const uint2*>(p1);
-  return pack8(a.x, a.y, b.x, b.y);
-}
-
 // ds_read_b64_tr_b16: each lane names 4 consecutive bf16 (8 bytes); within each group of
 // 16 lanes, lane l receives element l % 4 of the reads of lanes l / 4 + 4 s, s = 0..3.
 // With lane j of a group reading row r0 + j / 4 at column c0 + 4 (j % 4) of a row-major
@@ -93,6 +86,26 @@ __device__ __forceinline__ bf16x8 ld_tr8(const uint16_t* base, int rs, int r0, i
   const int off = (j >> 2) * rs + c0 + 4 * (j & 3);
   const uint2 a = ld_tr4(base + r0 * rs + off), b = ld_tr4(base + r1 * rs + off);
   return pack8(a.x, a.y, b.x, b.y);
+}
+
+// The same with this lane's own column (already mapped to storage order).
+__device__ __forceinline__ bf16x8 ld_tr8_at(const uint16_t* base, int rs, int r0, int r1, int col, int j) {
+  const int off = (j >> 2) * rs + col;
+  const uint2 a = ld_tr4(base + r0 * rs + off), b = ld_tr4(base + r1 * rs + off);
+  return pack8(a.x, a.y, b.x, b.y);
+}
+
+// Rows that are the A operand of a product whose B operand comes from accumulator
+// registers (k = {4g + r} u {16 + 4g + r}) keep each 32-element block in that k order:
+// logical elements 4g .. 4g + 3 and 16 + 4g .. 16 + 4g + 3 side by side, so the operand
+// is one 16-byte read (two 8-byte reads of one lane, merged by the compiler into
+// ds_read2_b64, cost several times as much on gfx950).  kperm(e) is the storage position
+// of logical element e; groups of 4 stay contiguous.
+__device__ __forceinline__ int kperm(int e) { return (e & ~31) | ((e & 12) << 1) | ((e & 16) >> 2) | (e & 3); }
+// 8 logical elements e0 .. e0 + 7 (e0 a multiple of 8) of such a row.
+__device__ __forceinline__ void st_kperm8(uint16_t* row, int e0, uint4 w) {
+  *reinterpret_cast<uint2*>(&row[kperm(e0)]) = make_uint2(w.x, w.y);
+  *reinterpret_cast<uint2*>(&row[kperm(e0 + 4)]) = make_uint2(w.z, w.w);
 }
 
 // Inclusive prefix sum over lanes 0..31 of a wave with DPP moves: shifts by 1, 2, 4 and 8
@@ -261,11 +274,12 @@ __device__ __forceinline__ void st_out(__amdgpu_buffer_rsrc_t r, uint32_t off, f
 template <int DK, int DV>
 struct PrefillLds {
   static constexpr int C = kChunk;
-  static constexpr int KS = DK + 8;   // bf16 row stride of the K and Q arrays (16-byte pad)
-  static constexpr int VS = DV + 16;  // bf16 row stride of V: 8 mod 32 words, so the four
-                                      // rows of a transposing read fall on distinct banks
+  // Row strides (bf16) of 8 mod 16 words: 16-byte and transposing reads of 16 consecutive
+  // rows then fall on distinct banks (gfx950: 64 banks of 4 bytes).
+  static constexpr int KS = DK + 16;  // K and Q (k order, kperm)
+  static constexpr int VS = DV + 16;  // V
+  static constexpr int TB = C + 16;   // split C x C matrices
   static constexpr int MS = C + 1;    // fp32 row stride of the C x C matrices
-  static constexpr int BS = C + 8;   // bf16 row stride of the split C x C matrices
   float c[C];      // cumulative log2 decay within the chunk
   float gam[C];    // 2^c
   float beta[C];   // step size (0 for tokens past the end)
@@ -277,14 +291,14 @@ struct PrefillLds {
     float t[C * MS];  // then T = (I + A)^-1
   };
   union {
-    uint16_t t1h[C * BS];  // T diag(b) (hi part)
+    uint16_t t1h[C * TB];  // T diag(b) (hi part)
     float xs[16 * 17];     // before it: scratch for the off-diagonal block of T
   };
-  uint16_t t1l[C * BS];
-  uint16_t t2h[C * BS], t2l[C * BS];  // T diag(b g)
-  uint16_t pmh[C * BS], pml[C * BS];  // M o Q K^T
-  uint16_t k[C * KS];  // K, token rows
-  uint16_t q[C * KS];  // Q, token rows
+  uint16_t t1l[C * TB];
+  uint16_t t2h[C * TB], t2l[C * TB];  // T diag(b g), k order
+  uint16_t pmh[C * TB], pml[C * TB];  // M o Q K^T, k order
+  uint16_t k[C * KS];  // K, token rows, k order
+  uint16_t q[C * KS];  // Q, token rows, k order
   uint16_t v[C * VS];  // V, token rows
 };
 
@@ -296,7 +310,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
   constexpr int NKB = DK / 16;  // 16-channel blocks
   constexpr int NKP = DK / 32;  // pairs of channel blocks (one MFMA k-step each)
   using Lds = PrefillLds<DK, DV>;
-  constexpr int KS = Lds::KS, VS = Lds::VS, MS = Lds::MS, BS = Lds::BS;
+  constexpr int KS = Lds::KS, VS = Lds::VS, MS = Lds::MS, TB = Lds::TB;
   static_assert(NCB >= 1 && NKP >= 1, "head sizes 64 or 128");
   __shared__ __align__(16) Lds sh;
 
@@ -366,8 +380,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
       if (pc < NPK) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          *reinterpret_cast<uint4*>(&sh.k[(tok + s2) * KS + seg * 8]) = nk[i][s2];
-          *reinterpret_cast<uint4*>(&sh.q[(tok + s2) * KS + seg * 8]) = nq[i][s2];
+          st_kperm8(&sh.k[(tok + s2) * KS], seg * 8, nk[i][s2]);
+          st_kperm8(&sh.q[(tok + s2) * KS], seg * 8, nq[i][s2]);
         }
         if (kla) {
 #pragma unroll
@@ -413,7 +427,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
         const uint16_t* xa = blk < 3 ? sh.k : sh.q;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk)
+        for (int kk = 0; kk < DK / 32; ++kk)  // both operands in the same (storage) channel order
           acc = mma(ld_b128(&xa[(16 * ib + ln) * KS + 32 * kk + 8 * lg]),
                     ld_b128(&sh.k[(16 * jb + ln) * KS + 32 * kk + 8 * lg]), acc);
         float* dst = blk < 3 ? sh.g : sh.p;
@@ -443,10 +457,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
         const int i0 = tid / C + e * (kThreads / C), i1 = i0 + kThreads / C;
         uint32_t hi, lo;
         split2(pm[e], pm[e + 1], hi, lo);
-        sh.pmh[i0 * BS + j] = static_cast<uint16_t>(hi);
-        sh.pmh[i1 * BS + j] = static_cast<uint16_t>(hi >> 16);
-        sh.pml[i0 * BS + j] = static_cast<uint16_t>(lo);
-        sh.pml[i1 * BS + j] = static_cast<uint16_t>(lo >> 16);
+        sh.pmh[i0 * TB + kperm(j)] = static_cast<uint16_t>(hi);
+        sh.pmh[i1 * TB + kperm(j)] = static_cast<uint16_t>(hi >> 16);
+        sh.pml[i0 * TB + kperm(j)] = static_cast<uint16_t>(lo);
+        sh.pml[i1 * TB + kperm(j)] = static_cast<uint16_t>(lo >> 16);
       }
     }
     __syncthreads();
@@ -468,15 +482,15 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
         const int i0 = tid / C + e * (kThreads / C), i1 = i0 + kThreads / C;
         uint32_t hi, lo;
         split2(tv[e] * bj, tv[e + 1] * bj, hi, lo);
-        sh.t1h[i0 * BS + j] = static_cast<uint16_t>(hi);
-        sh.t1h[i1 * BS + j] = static_cast<uint16_t>(hi >> 16);
-        sh.t1l[i0 * BS + j] = static_cast<uint16_t>(lo);
-        sh.t1l[i1 * BS + j] = static_cast<uint16_t>(lo >> 16);
+        sh.t1h[i0 * TB + j] = static_cast<uint16_t>(hi);
+        sh.t1h[i1 * TB + j] = static_cast<uint16_t>(hi >> 16);
+        sh.t1l[i0 * TB + j] = static_cast<uint16_t>(lo);
+        sh.t1l[i1 * TB + j] = static_cast<uint16_t>(lo >> 16);
         split2(tv[e] * bgj, tv[e + 1] * bgj, hi, lo);
-        sh.t2h[i0 * BS + j] = static_cast<uint16_t>(hi);
-        sh.t2h[i1 * BS + j] = static_cast<uint16_t>(hi >> 16);
-        sh.t2l[i0 * BS + j] = static_cast<uint16_t>(lo);
-        sh.t2l[i1 * BS + j] = static_cast<uint16_t>(lo >> 16);
+        sh.t2h[i0 * TB + kperm(j)] = static_cast<uint16_t>(hi);
+        sh.t2h[i1 * TB + kperm(j)] = static_cast<uint16_t>(hi >> 16);
+        sh.t2l[i0 * TB + kperm(j)] = static_cast<uint16_t>(lo);
+        sh.t2l[i1 * TB + kperm(j)] = static_cast<uint16_t>(lo >> 16);
       }
     }
     __syncthreads();
@@ -489,8 +503,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma(ld_b128(&sh.t1h[(16 * ib + ln) * BS + 8 * lg]), vb8, acc);
-        acc = mma(ld_b128(&sh.t1l[(16 * ib + ln) * BS + 8 * lg]), vb8, acc);
+        acc = mma(ld_b128(&sh.t1h[(16 * ib + ln) * TB + 8 * lg]), vb8, acc);
+        acc = mma(ld_b128(&sh.t1l[(16 * ib + ln) * TB + 8 * lg]), vb8, acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) U[ib][cb][r] = acc[r];
       }
@@ -515,9 +529,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
         for (int cb = 0; cb < NCB; ++cb) split_pair(S[2 * kp][cb], S[2 * kp + 1][cb], shi[cb], slo[cb]);
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
-          const int rowk = (16 * ib + ln) * KS + 32 * kp + 4 * lg;
-          const bf16x8 ka = ld_2x64(&sh.k[rowk], &sh.k[rowk + 16]);
-          const bf16x8 qa = ld_2x64(&sh.q[rowk], &sh.q[rowk + 16]);
+          const int rowk = (16 * ib + ln) * KS + 32 * kp + 8 * lg;  // channels 32 kp + 4 lg + {0..3, 16..19}
+          const bf16x8 ka = ld_b128(&sh.k[rowk]);
+          const bf16x8 qa = ld_b128(&sh.q[rowk]);
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
             xs[ib][cb] = mma(ka, shi[cb], xs[ib][cb]);
@@ -541,9 +555,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
         split_pair(x0, x1, xhi, xlo);
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
-          const int rowt = (16 * ib + ln) * BS + 4 * lg;
-          const bf16x8 tah = ld_2x64(&sh.t2h[rowt], &sh.t2h[rowt + 16]);
-          const bf16x8 tal = ld_2x64(&sh.t2l[rowt], &sh.t2l[rowt + 16]);
+          const int rowt = (16 * ib + ln) * TB + 8 * lg;
+          const bf16x8 tah = ld_b128(&sh.t2h[rowt]);
+          const bf16x8 tal = ld_b128(&sh.t2l[rowt]);
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
           acc = mma(tah, xhi, acc);
           acc = mma(tah, xlo, acc);
@@ -566,9 +580,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
       split_pair(U[0][cb], U[1][cb], uhi, ulo);
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
-        const int rowp = (16 * ib + ln) * BS + 4 * lg;
-        const bf16x8 pah = ld_2x64(&sh.pmh[rowp], &sh.pmh[rowp + 16]);
-        const bf16x8 pal = ld_2x64(&sh.pml[rowp], &sh.pml[rowp + 16]);
+        const int rowp = (16 * ib + ln) * TB + 8 * lg;
+        const bf16x8 pah = ld_b128(&sh.pmh[rowp]);
+        const bf16x8 pal = ld_b128(&sh.pml[rowp]);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mma(pah, uhi, acc);
         acc = mma(pah, ulo, acc);
@@ -594,7 +608,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     for (int cb = 0; cb < NCB; ++cb) split_pair(U[0][cb], U[1][cb], u2hi[cb], u2lo[cb]);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const bf16x8 ka = ld_tr8(sh.k, KS, 4 * lg, 16 + 4 * lg, 16 * kb, ln);  // K^T, tokens as U's rows
+      // K^T, tokens as U's rows; this lane's 4 channels 16 kb + 4 (ln % 4) in storage order
+      const bf16x8 ka = ld_tr8_at(sh.k, KS, 4 * lg, 16 + 4 * lg, kperm(16 * kb + 4 * (ln & 3)), ln);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         f32x4 acc = {gC * S[kb][cb][0], gC * S[kb][cb][1], gC * S[kb][cb][2], gC * S[kb][cb][3]};
@@ -653,12 +668,13 @@ __device__ __forceinline__ void prefix_over_tokens(float* cc, float* glast, int 
 template <int DK, int DV>
 struct PrefillKdaLds {
   static constexpr int C = kChunk;
-  static constexpr int KS = DK + 8;   // bf16 row stride of K, Q, W and Q o G
+  // Row strides (bf16) of 8 mod 16 words, for 16-byte and transposing reads (see PrefillLds).
+  static constexpr int KS = DK + 16;  // K, Q, W and Q o G (the last two in k order, kperm)
   static constexpr int RS = DK + 16;  // bf16 row stride of K o G and K o G_C / G, and
   static constexpr int VS = DV + 16;  // of V: 8 mod 32 words (transposing reads)
   static constexpr int MS = C + 1;    // fp32 row stride of the C x C matrices
-  static constexpr int BS = C + 8;   // bf16 row stride of the split C x C matrices
-  static constexpr int CS = DK + 4;  // fp32 row stride of the per-channel decays
+  static constexpr int TB = C + 16;  // split C x C matrices
+  static constexpr int CS = DK + 8;  // fp32 row stride of the per-channel decays
   float beta[C];
   float braw[C];
   float knorm[C];
@@ -666,20 +682,20 @@ struct PrefillKdaLds {
   float g[C * MS];  // A (strictly lower part)
   float t[C * MS];  // T = (I + A)^-1
   union {
-    uint16_t t1h[C * BS];  // T diag(b) (hi part)
+    uint16_t t1h[C * TB];  // T diag(b) (hi part)
     float xs[16 * 17];     // before it: scratch of the inverse
   };
-  uint16_t t1l[C * BS];
-  uint16_t pmh[C * BS], pml[C * BS];  // P (lower triangle, split)
+  uint16_t t1l[C * TB];
+  uint16_t pmh[C * TB], pml[C * TB];  // P (lower triangle, split, k order)
   union {
-    uint16_t k[C * KS];  // K, token rows
-    uint16_t wh[C * KS];  // then W (hi part)
+    uint16_t k[C * KS];   // K, token rows
+    uint16_t wh[C * KS];  // then W (hi part, k order)
   };
   union {
-    uint16_t q[C * KS];  // Q, token rows
-    uint16_t wl[C * KS];  // then W (lo part)
+    uint16_t q[C * KS];   // Q, token rows
+    uint16_t wl[C * KS];  // then W (lo part, k order)
   };
-  uint16_t qgh[C * KS], qgl[C * KS];  // Q o G, token rows, split
+  uint16_t qgh[C * KS], qgl[C * KS];  // Q o G, token rows, split, k order
   uint16_t v[C * VS];                 // V, token rows
   float part[4 * 6 * 4 * 64];         // per-wave partial sums of A and P
   uint16_t kgh[C * RS], kgl[C * RS];  // K o G, token rows, split
@@ -695,7 +711,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
   constexpr int NKB = DK / 16;
   constexpr int NKP = DK / 32;
   using Lds = PrefillKdaLds<DK, DV>;
-  constexpr int KS = Lds::KS, RS = Lds::RS, VS = Lds::VS, MS = Lds::MS, BS = Lds::BS, CS = Lds::CS;
+  constexpr int KS = Lds::KS, RS = Lds::RS, VS = Lds::VS, MS = Lds::MS, TB = Lds::TB;
+  constexpr int CS = Lds::CS;
   __shared__ __align__(16) Lds sh;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -815,8 +832,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     for (int e = tid; e < C * C; e += kThreads) {
       const int i = e / C, j = e % C;
       if (j > i) {
-        sh.pmh[i * BS + j] = 0;
-        sh.pml[i * BS + j] = 0;
+        sh.pmh[i * TB + kperm(j)] = 0;
+        sh.pml[i * TB + kperm(j)] = 0;
       }
       if (i < 16 && j >= 16) sh.t[i * MS + j] = 0.f;
     }
@@ -852,8 +869,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
           auto row = [&](uint16_t* x, int stride, const uint32_t (&w)[2][4]) {
             *reinterpret_cast<uint4*>(&x[(tok + s2) * stride + seg * 8]) = make_uint4(w[s2][0], w[s2][1], w[s2][2], w[s2][3]);
           };
-          row(sh.qgh, KS, qh);
-          row(sh.qgl, KS, ql);
+          st_kperm8(&sh.qgh[(tok + s2) * KS], seg * 8, make_uint4(qh[s2][0], qh[s2][1], qh[s2][2], qh[s2][3]));
+          st_kperm8(&sh.qgl[(tok + s2) * KS], seg * 8, make_uint4(ql[s2][0], ql[s2][1], ql[s2][2], ql[s2][3]));
           row(sh.kgh, RS, kgh2);
           row(sh.kgl, RS, kgl2);
           row(sh.kdh, RS, kdh2);
@@ -953,8 +970,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
         } else {
           uint32_t hi, lo;
           split2(j <= i ? sum : 0.f, 0.f, hi, lo);
-          sh.pmh[i * BS + j] = static_cast<uint16_t>(hi);
-          sh.pml[i * BS + j] = static_cast<uint16_t>(lo);
+          sh.pmh[i * TB + kperm(j)] = static_cast<uint16_t>(hi);
+          sh.pml[i * TB + kperm(j)] = static_cast<uint16_t>(lo);
         }
       }
     } else {
@@ -989,8 +1006,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
           if (j < r) sh.g[r * MS + j] = sh.beta[r] * av;
           uint32_t hi, lo;
           split2(pv, 0.f, hi, lo);
-          sh.pmh[r * BS + j] = static_cast<uint16_t>(hi);
-          sh.pml[r * BS + j] = static_cast<uint16_t>(lo);
+          sh.pmh[r * TB + kperm(j)] = static_cast<uint16_t>(hi);
+          sh.pml[r * TB + kperm(j)] = static_cast<uint16_t>(lo);
         }
       }
     }
@@ -1011,10 +1028,10 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
         const int i0 = tid / C + e * (kThreads / C), i1 = i0 + kThreads / C;
         uint32_t hi, lo;
         split2(tv[e] * bj, tv[e + 1] * bj, hi, lo);
-        sh.t1h[i0 * BS + j] = static_cast<uint16_t>(hi);
-        sh.t1h[i1 * BS + j] = static_cast<uint16_t>(hi >> 16);
-        sh.t1l[i0 * BS + j] = static_cast<uint16_t>(lo);
-        sh.t1l[i1 * BS + j] = static_cast<uint16_t>(lo >> 16);
+        sh.t1h[i0 * TB + j] = static_cast<uint16_t>(hi);
+        sh.t1h[i1 * TB + j] = static_cast<uint16_t>(hi >> 16);
+        sh.t1l[i0 * TB + j] = static_cast<uint16_t>(lo);
+        sh.t1l[i1 * TB + j] = static_cast<uint16_t>(lo >> 16);
       }
     }
     __syncthreads();
@@ -1026,8 +1043,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
       const int ib = blk / NKB, cb = blk % NKB;
       const bf16x8 kah = ld_tr8(sh.kgh, RS, 8 * lg, 8 * lg + 4, 16 * cb, ln);  // tokens 8 lg .. 8 lg + 7
       const bf16x8 kal = ld_tr8(sh.kgl, RS, 8 * lg, 8 * lg + 4, 16 * cb, ln);
-      const bf16x8 tbh = ld_b128(&sh.t1h[(16 * ib + ln) * BS + 8 * lg]);
-      const bf16x8 tbl = ld_b128(&sh.t1l[(16 * ib + ln) * BS + 8 * lg]);
+      const bf16x8 tbh = ld_b128(&sh.t1h[(16 * ib + ln) * TB + 8 * lg]);
+      const bf16x8 tbl = ld_b128(&sh.t1l[(16 * ib + ln) * TB + 8 * lg]);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       acc = mma(kah, tbh, acc);
       acc = mma(kah, tbl, acc);
@@ -1035,7 +1052,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
       uint32_t h01, l01, h23, l23;
       split2(acc[0], acc[1], h01, l01);
       split2(acc[2], acc[3], h23, l23);
-      const int wo = (16 * ib + ln) * KS + 16 * cb + 4 * lg;
+      const int wo = (16 * ib + ln) * KS + kperm(16 * cb + 4 * lg);  // 4 channels, k order
       *reinterpret_cast<uint2*>(&sh.wh[wo]) = make_uint2(h01, h23);
       *reinterpret_cast<uint2*>(&sh.wl[wo]) = make_uint2(l01, l23);
     }
@@ -1046,8 +1063,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma(ld_b128(&sh.t1h[(16 * ib + ln) * BS + 8 * lg]), vb8, acc);
-        acc = mma(ld_b128(&sh.t1l[(16 * ib + ln) * BS + 8 * lg]), vb8, acc);
+        acc = mma(ld_b128(&sh.t1h[(16 * ib + ln) * TB + 8 * lg]), vb8, acc);
+        acc = mma(ld_b128(&sh.t1l[(16 * ib + ln) * TB + 8 * lg]), vb8, acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) U[ib][cb][r] = acc[r];
       }
@@ -1072,11 +1089,9 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
         for (int cb = 0; cb < NCB; ++cb) split_pair(S[2 * kp][cb], S[2 * kp + 1][cb], shi[cb], slo[cb]);
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
-          const int rowk = (16 * ib + ln) * KS + 32 * kp + 4 * lg;
-          const bf16x8 wah = ld_2x64(&sh.wh[rowk], &sh.wh[rowk + 16]);
-          const bf16x8 wal = ld_2x64(&sh.wl[rowk], &sh.wl[rowk + 16]);
-          const bf16x8 qah = ld_2x64(&sh.qgh[rowk], &sh.qgh[rowk + 16]);
-          const bf16x8 qal = ld_2x64(&sh.qgl[rowk], &sh.qgl[rowk + 16]);
+          const int rowk = (16 * ib + ln) * KS + 32 * kp + 8 * lg;  // channels 32 kp + 4 lg + {0..3, 16..19}
+          const bf16x8 wah = ld_b128(&sh.wh[rowk]), wal = ld_b128(&sh.wl[rowk]);
+          const bf16x8 qah = ld_b128(&sh.qgh[rowk]), qal = ld_b128(&sh.qgl[rowk]);
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
             ws[ib][cb] = mma(wah, shi[cb], ws[ib][cb]);
@@ -1108,9 +1123,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
       split_pair(U[0][cb], U[1][cb], uhi, ulo);
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
-        const int rowp = (16 * ib + ln) * BS + 4 * lg;
-        const bf16x8 pah = ld_2x64(&sh.pmh[rowp], &sh.pmh[rowp + 16]);
-        const bf16x8 pal = ld_2x64(&sh.pml[rowp], &sh.pml[rowp + 16]);
+        const int rowp = (16 * ib + ln) * TB + 8 * lg;
+        const bf16x8 pah = ld_b128(&sh.pmh[rowp]), pal = ld_b128(&sh.pml[rowp]);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mma(pah, uhi, acc);
         acc = mma(pah, ulo, acc);
@@ -1166,18 +1180,18 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
 template <int DK, int DV>
 struct PrefillRwkvLds {
   static constexpr int C = kChunk;
-  static constexpr int KS = DK + 8;
-  static constexpr int RS = DK + 16;  // K o G_C / G and V: 8 mod 32 words (transposing reads)
+  static constexpr int KS = DK + 16;  // K, R and R o G_prev rows (the last in k order, kperm)
+  static constexpr int RS = DK + 16;  // K o G_C / G and V: 8 mod 16 words (transposing reads)
   static constexpr int VS = DV + 16;
-  static constexpr int BS = C + 8;
-  static constexpr int CS = DK + 4;
+  static constexpr int TB = C + 16;   // P, split (16-byte reads)
+  static constexpr int CS = DK + 8;
   float bonus[DK];
   float glast[DK];                    // 2^c of the chunk's last token per channel
   float pd[C];                        // the bonus diagonal of P
-  uint16_t pmh[C * BS], pml[C * BS];  // P, split
-  uint16_t k[C * KS];                 // K, token rows
-  uint16_t q[C * KS];                 // R, token rows
-  uint16_t rgh[C * KS], rgl[C * KS];  // R o G_prev, token rows, split
+  uint16_t pmh[C * TB], pml[C * TB];  // P, split
+  uint16_t k[C * KS];                // K, token rows
+  uint16_t q[C * KS];                // R, token rows
+  uint16_t rgh[C * KS], rgl[C * KS];  // R o G_prev, token rows, split, k order
   uint16_t v[C * VS];                 // V, token rows
   uint16_t kdh[C * RS], kdl[C * RS];  // K o G_C / G, token rows, split
   float cc[C * CS];                   // log2 decays, then their prefix sums
@@ -1191,7 +1205,7 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
   constexpr int NKB = DK / 16;
   constexpr int NKP = DK / 32;
   using Lds = PrefillRwkvLds<DK, DV>;
-  constexpr int KS = Lds::KS, RS = Lds::RS, VS = Lds::VS, BS = Lds::BS, CS = Lds::CS;
+  constexpr int KS = Lds::KS, RS = Lds::RS, VS = Lds::VS, TB = Lds::TB, CS = Lds::CS;
   __shared__ __align__(16) Lds sh;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1321,8 +1335,8 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
           auto row = [&](uint16_t* x, int stride, const uint32_t (&w)[2][4]) {
             *reinterpret_cast<uint4*>(&x[(tok + s2) * stride + seg * 8]) = make_uint4(w[s2][0], w[s2][1], w[s2][2], w[s2][3]);
           };
-          row(sh.rgh, KS, rh);
-          row(sh.rgl, KS, rl);
+          st_kperm8(&sh.rgh[(tok + s2) * KS], seg * 8, make_uint4(rh[s2][0], rh[s2][1], rh[s2][2], rh[s2][3]));
+          st_kperm8(&sh.rgl[(tok + s2) * KS], seg * 8, make_uint4(rl[s2][0], rl[s2][1], rl[s2][2], rl[s2][3]));
           row(sh.kdh, RS, kdh2);
           row(sh.kdl, RS, kdl2);
         }
@@ -1393,18 +1407,18 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
           const int i = 16 * ib + 4 * lg + r;
           uint32_t hi, lo;
           split2(pm[r], pm[r + 1], hi, lo);
-          sh.pmh[i * BS + j] = static_cast<uint16_t>(hi);
-          sh.pmh[(i + 1) * BS + j] = static_cast<uint16_t>(hi >> 16);
-          sh.pml[i * BS + j] = static_cast<uint16_t>(lo);
-          sh.pml[(i + 1) * BS + j] = static_cast<uint16_t>(lo >> 16);
+          sh.pmh[i * TB + j] = static_cast<uint16_t>(hi);
+          sh.pmh[(i + 1) * TB + j] = static_cast<uint16_t>(hi >> 16);
+          sh.pml[i * TB + j] = static_cast<uint16_t>(lo);
+          sh.pml[(i + 1) * TB + j] = static_cast<uint16_t>(lo >> 16);
         }
       } else {
         // the upper right block of P is zero
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = (lane >> 4) + 4 * e, j = 16 + ln;
-          sh.pmh[i * BS + j] = 0;
-          sh.pml[i * BS + j] = 0;
+          sh.pmh[i * TB + j] = 0;
+          sh.pml[i * TB + j] = 0;
         }
       }
     } else {
@@ -1416,8 +1430,8 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
         if (jj >= i) {
           uint32_t hi, lo;
           split2(jj == i ? sh.pd[i] : 0.f, 0.f, hi, lo);
-          sh.pmh[i * BS + jj] = static_cast<uint16_t>(hi);
-          sh.pml[i * BS + jj] = static_cast<uint16_t>(lo);
+          sh.pmh[i * TB + jj] = static_cast<uint16_t>(hi);
+          sh.pml[i * TB + jj] = static_cast<uint16_t>(lo);
         }
       }
       float rr[2][SL], cr[2][SL];
@@ -1444,8 +1458,8 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
         if (sl == 0) {
           uint32_t hi, lo;
           split2(pv, 0.f, hi, lo);
-          sh.pmh[r * BS + j] = static_cast<uint16_t>(hi);
-          sh.pml[r * BS + j] = static_cast<uint16_t>(lo);
+          sh.pmh[r * TB + j] = static_cast<uint16_t>(hi);
+          sh.pml[r * TB + j] = static_cast<uint16_t>(lo);
         }
       }
     }
@@ -1466,9 +1480,8 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
         for (int cb = 0; cb < NCB; ++cb) split_pair(S[2 * kp][cb], S[2 * kp + 1][cb], shi[cb], slo[cb]);
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
-          const int rowk = (16 * ib + ln) * KS + 32 * kp + 4 * lg;
-          const bf16x8 rah = ld_2x64(&sh.rgh[rowk], &sh.rgh[rowk + 16]);
-          const bf16x8 ral = ld_2x64(&sh.rgl[rowk], &sh.rgl[rowk + 16]);
+          const int rowk = (16 * ib + ln) * KS + 32 * kp + 8 * lg;  // channels 32 kp + 4 lg + {0..3, 16..19}
+          const bf16x8 rah = ld_b128(&sh.rgh[rowk]), ral = ld_b128(&sh.rgl[rowk]);
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
             qs[ib][cb] = mma(rah, shi[cb], qs[ib][cb]);
@@ -1492,8 +1505,8 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
       vb[cb] = ld_tr8(sh.v, VS, 8 * lg, 8 * lg + 4, col0 + 16 * cb, ln);
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
-      const bf16x8 pah = ld_b128(&sh.pmh[(16 * ib + ln) * BS + 8 * lg]);
-      const bf16x8 pal = ld_b128(&sh.pml[(16 * ib + ln) * BS + 8 * lg]);
+      const bf16x8 pah = ld_b128(&sh.pmh[(16 * ib + ln) * TB + 8 * lg]);
+      const bf16x8 pal = ld_b128(&sh.pml[(16 * ib + ln) * TB + 8 * lg]);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
