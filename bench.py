@@ -271,10 +271,10 @@ def prefill_model(dk: int, dv: int, C: int = PREFILL_CHUNK, variant: int = 0) ->
         method = 2 * C * C * dk * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 3
         issued = (2 * lower * 6 + 2 * C * C * dk * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 3 * 2
                   + 2 * C * C * dv * 3 + 2 * C * dk * dv * 3)
-    else:  # K K^T, Q K^T (lower blocks), T V, X = K S, Q S, T X, P U, K^T U
-        method = 2 * C * C * dk * 2 + 2 * C * C * dv * 3 + 2 * C * dk * dv * 3
-        issued = (2 * lower + 2 * C * C * dv * 2 + 2 * C * dk * dv * 2 * 2 + 2 * C * C * dv * 3
-                  + 2 * C * C * dv * 3 + 2 * C * dk * dv * 2)
+    else:  # K K^T, Q K^T (lower blocks), X = K S, Q S, T diag(b) (V - diag(g) X), P U, K^T U
+        method = 2 * C * C * dk * 2 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 3
+        issued = (2 * lower + 2 * C * dk * dv * 2 * 2 + 2 * C * C * dv * 3 + 2 * C * C * dv * 3
+                  + 2 * C * dk * dv * 2)
     return {"bytes": byts, "method_flops": method / C, "issued_flops": issued / C}
 
 

@@ -18,10 +18,10 @@
 // Mapping.  One workgroup (4 waves) per tile; wave w owns value columns
 // [w dv/4, (w+1) dv/4) of the state, held in MFMA accumulator layout, so the
 // dv dimension needs no communication between waves.  Chunk-shared matrices
-// (K K^T, Q K^T, T and its column-scaled copies) are built once per chunk in LDS.
-// The state enters U as T diag(b g) (K S): X = K S takes the exact bf16 keys
-// against the split state, and X then feeds T diag(b g) X from registers, so no
-// C x dk product of T with K is formed or staged.
+// (K K^T, Q K^T, T diag(b)) are built once per chunk in LDS.  The state enters U as
+// U = T diag(b) (V - diag(g) X) with X = K S: X takes the exact bf16 keys against the
+// split state, R = V - diag(g) X is formed in fp32 where X sits in registers, and R
+// feeds T diag(b) R, so no C x dk product of T with K is formed or staged.
 // Products run on v_mfma_f32_16x16x32_bf16: keys, queries and values are bf16
 // already (exact operands); an fp32 operand x is split into bf16 hi + lo with
 // x - hi - lo below 2^-17 |x|, and a product of two split operands takes the
@@ -33,7 +33,7 @@
 // B[8g + s][n] for s < 8; the result holds D[4g + r][n] for r < 4.  Sums over k
 // may pair any k order consistently between A and B; the state and U feed the
 // B operand straight from accumulator registers with k = {4g + r} u {16 + 4g + r}
-// (so does X, over tokens).
+// (so does R, over tokens).
 // Every array is stored in token rows; where tokens run along an operand's k index (K^T
 // and its decay-scaled copies in the state update, V), the operand is read through
 // ds_read_b64_tr_b16.  Every operand is read with 8- or 16-byte LDS loads.
@@ -291,11 +291,10 @@ struct PrefillLds {
     float t[C * MS];  // then T = (I + A)^-1
   };
   union {
-    uint16_t t1h[C * TB];  // T diag(b) (hi part)
+    uint16_t t1h[C * TB];  // T diag(b) (hi part, k order)
     float xs[16 * 17];     // before it: scratch for the off-diagonal block of T
   };
   uint16_t t1l[C * TB];
-  uint16_t t2h[C * TB], t2l[C * TB];  // T diag(b g), k order
   uint16_t pmh[C * TB], pml[C * TB];  // M o Q K^T, k order
   uint16_t k[C * KS];  // K, token rows, k order
   uint16_t q[C * KS];  // Q, token rows, k order
@@ -470,10 +469,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     // ---- 4, 5. T = (I + A)^-1
     invert_unit_lower32<MS>(sh.g, sh.t, sh.xs, tid);
 
-    // ---- 6. T diag(b) and T diag(b g), split
+    // ---- 6. T diag(b), split, in k order (the A operand of T diag(b) R below)
     {
       const int j = tid % C;
-      const float bj = sh.beta[j], bgj = bj * sh.gam[j];
+      const float bj = sh.beta[j];
       float tv[C * C / kThreads];
 #pragma unroll
       for (int e = 0; e < C * C / kThreads; ++e) tv[e] = sh.t[(tid / C + e * (kThreads / C)) * MS + j];
@@ -482,37 +481,20 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
         const int i0 = tid / C + e * (kThreads / C), i1 = i0 + kThreads / C;
         uint32_t hi, lo;
         split2(tv[e] * bj, tv[e + 1] * bj, hi, lo);
-        sh.t1h[i0 * TB + j] = static_cast<uint16_t>(hi);
-        sh.t1h[i1 * TB + j] = static_cast<uint16_t>(hi >> 16);
-        sh.t1l[i0 * TB + j] = static_cast<uint16_t>(lo);
-        sh.t1l[i1 * TB + j] = static_cast<uint16_t>(lo >> 16);
-        split2(tv[e] * bgj, tv[e + 1] * bgj, hi, lo);
-        sh.t2h[i0 * TB + kperm(j)] = static_cast<uint16_t>(hi);
-        sh.t2h[i1 * TB + kperm(j)] = static_cast<uint16_t>(hi >> 16);
-        sh.t2l[i0 * TB + kperm(j)] = static_cast<uint16_t>(lo);
-        sh.t2l[i1 * TB + kperm(j)] = static_cast<uint16_t>(lo >> 16);
+        sh.t1h[i0 * TB + kperm(j)] = static_cast<uint16_t>(hi);
+        sh.t1h[i1 * TB + kperm(j)] = static_cast<uint16_t>(hi >> 16);
+        sh.t1l[i0 * TB + kperm(j)] = static_cast<uint16_t>(lo);
+        sh.t1l[i1 * TB + kperm(j)] = static_cast<uint16_t>(lo >> 16);
       }
     }
     __syncthreads();
 
-    // ---- 7. this wave's columns of T diag(b) V
-    float U[2][NCB][4];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const bf16x8 vb8 = ld_tr8(sh.v, VS, 8 * lg, 8 * lg + 4, col0 + 16 * cb, ln);  // tokens 8 lg .. 8 lg + 7
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma(ld_b128(&sh.t1h[(16 * ib + ln) * TB + 8 * lg]), vb8, acc);
-        acc = mma(ld_b128(&sh.t1l[(16 * ib + ln) * TB + 8 * lg]), vb8, acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) U[ib][cb][r] = acc[r];
-      }
-    }
-
-    // ---- 8. X = K S and diag(g) Q S (S split one channel-block pair at a time; K and Q
-    //         are exact bf16 operands), then U = T diag(b) V - T diag(b g) X
-    float O[2][NCB][4];
+    // ---- 7, 8. X = K S and Q S (S split one channel-block pair at a time; K and Q are
+    //            exact bf16 operands); R = V - diag(g) X in fp32 at X's accumulator
+    //            positions (tokens 4 lg + r and 16 + 4 lg + r), which makes R the B operand
+    //            of U = T diag(b) R with the tokens paired the same way in the A operand;
+    //            and diag(g) Q S for the outputs
+    float U[2][NCB][4], O[2][NCB][4];
     {
       f32x4 xs[2][NCB], qs[2][NCB];
 #pragma unroll
@@ -541,30 +523,30 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
           }
         }
       }
-      // X (accumulator layout, tokens 4 lg + r and 16 + 4 lg + r) is the B operand of
-      // T diag(b g) X with the tokens paired the same way in the A operand.
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        float x0[4], x1[4];
+        float vf[8];  // V at this lane's accumulator positions
+        unpack8(__builtin_bit_cast(uint4, ld_tr8(sh.v, VS, 4 * lg, 16 + 4 * lg, col0 + 16 * cb, ln)), vf);
+        float r0[4], r1[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          x0[r] = xs[0][cb][r];
-          x1[r] = xs[1][cb][r];
+          r0[r] = fmaf(-sh.gam[4 * lg + r], xs[0][cb][r], vf[r]);
+          r1[r] = fmaf(-sh.gam[16 + 4 * lg + r], xs[1][cb][r], vf[4 + r]);
         }
-        bf16x8 xhi, xlo;
-        split_pair(x0, x1, xhi, xlo);
+        bf16x8 rhi, rlo;
+        split_pair(r0, r1, rhi, rlo);
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
           const int rowt = (16 * ib + ln) * TB + 8 * lg;
-          const bf16x8 tah = ld_b128(&sh.t2h[rowt]);
-          const bf16x8 tal = ld_b128(&sh.t2l[rowt]);
+          const bf16x8 tah = ld_b128(&sh.t1h[rowt]);
+          const bf16x8 tal = ld_b128(&sh.t1l[rowt]);
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          acc = mma(tah, xhi, acc);
-          acc = mma(tah, xlo, acc);
-          acc = mma(tal, xhi, acc);
+          acc = mma(tah, rhi, acc);
+          acc = mma(tah, rlo, acc);
+          acc = mma(tal, rhi, acc);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            U[ib][cb][r] -= acc[r];
+            U[ib][cb][r] = acc[r];
             O[ib][cb][r] = sh.gam[16 * ib + 4 * lg + r] * qs[ib][cb][r];
           }
         }
