@@ -267,10 +267,10 @@ def prefill_model(dk: int, dv: int, C: int = PREFILL_CHUNK, variant: int = 0) ->
     if variant == 2:  # P, (R o G) S, P V, state update
         method = 2 * C * C * dk + 2 * C * dk * dv + 2 * C * C * dv + 2 * C * dk * dv
         issued = lower * 6 + 2 * C * dk * dv * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 2
-    elif variant == 1:  # A and P, W = T (K o G), T V, W S, (Q o G) S, P U, state update
-        method = 2 * C * C * dk * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 3
-        issued = (2 * lower * 6 + 2 * C * C * dk * 3 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 3 * 2
-                  + 2 * C * C * dv * 3 + 2 * C * dk * dv * 3)
+    elif variant == 1:  # A and P, X = (K o G) S, (Q o G) S, T diag(b) (V - X), P U, state update
+        method = 2 * C * C * dk * 2 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 3
+        issued = (2 * lower * 6 + 2 * C * dk * dv * 3 * 2 + 2 * C * C * dv * 3 + 2 * C * C * dv * 3
+                  + 2 * C * dk * dv * 3)
     else:  # K K^T, Q K^T (lower blocks), X = K S, Q S, T diag(b) (V - diag(g) X), P U, K^T U
         method = 2 * C * C * dk * 2 + 2 * C * C * dv * 2 + 2 * C * dk * dv * 3
         issued = (2 * lower + 2 * C * dk * dv * 2 * 2 + 2 * C * C * dv * 3 + 2 * C * C * dv * 3

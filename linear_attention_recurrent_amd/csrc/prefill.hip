@@ -640,19 +640,19 @@ __device__ __forceinline__ void prefix_over_tokens(float* cc, float* glast, int 
 // KDA decays each key channel on its own: with G_i = a_1 ... a_i (a dk-vector,
 // cumulative within the chunk, kept as log2 in cc) the chunk form becomes
 //   A_ij = b_i sum_c k_i[c] k_j[c] G_i[c] / G_j[c]  (j < i),   T = (I + A)^-1
-//   U    = T diag(b) V - T diag(b) (K o G) S
+//   U    = T diag(b) (V - (K o G) S)
 //   O    = (Q o G) S + P U,   P_ij = sum_c q_i[c] k_j[c] G_i[c] / G_j[c]  (j <= i)
 //   S'   = diag(G_C) S + (K o G_C / G)^T U
 // (the same unrolling of u_i as for GDN, with diag(G) in place of the scalar g).
-// The decay-weighted products A and P are formed directly, one 2^(c_i - c_j) per
-// channel and pair, so any decay down to the -126 clamp stays exact; every other
-// product runs on MFMA with the decay folded into a split operand.
+// Every product runs on MFMA with the decay folded into a split operand; the
+// decay-weighted C x C products A and P use a reference token per block (step 4) and
+// fall back to forming each pair directly when a chunk's decays are too strong for it.
 template <int DK, int DV>
 struct PrefillKdaLds {
   static constexpr int C = kChunk;
   // Row strides (bf16) of 8 mod 16 words, for 16-byte and transposing reads (see PrefillLds).
-  static constexpr int KS = DK + 16;  // K, Q, W and Q o G (the last two in k order, kperm)
-  static constexpr int RS = DK + 16;  // bf16 row stride of K o G and K o G_C / G, and
+  static constexpr int KS = DK + 16;  // K, Q, K o G and Q o G (the last two in k order, kperm)
+  static constexpr int RS = DK + 16;  // bf16 row stride of K o G_C / G, and
   static constexpr int VS = DV + 16;  // of V: 8 mod 32 words (transposing reads)
   static constexpr int MS = C + 1;    // fp32 row stride of the C x C matrices
   static constexpr int TB = C + 16;  // split C x C matrices
@@ -664,23 +664,17 @@ struct PrefillKdaLds {
   float g[C * MS];  // A (strictly lower part)
   float t[C * MS];  // T = (I + A)^-1
   union {
-    uint16_t t1h[C * TB];  // T diag(b) (hi part)
+    uint16_t t1h[C * TB];  // T diag(b) (hi part, k order)
     float xs[16 * 17];     // before it: scratch of the inverse
   };
   uint16_t t1l[C * TB];
   uint16_t pmh[C * TB], pml[C * TB];  // P (lower triangle, split, k order)
-  union {
-    uint16_t k[C * KS];   // K, token rows
-    uint16_t wh[C * KS];  // then W (hi part, k order)
-  };
-  union {
-    uint16_t q[C * KS];   // Q, token rows
-    uint16_t wl[C * KS];  // then W (lo part, k order)
-  };
+  uint16_t k[C * KS];  // K, token rows
+  uint16_t q[C * KS];  // Q, token rows
   uint16_t qgh[C * KS], qgl[C * KS];  // Q o G, token rows, split, k order
   uint16_t v[C * VS];                 // V, token rows
   float part[4 * 6 * 4 * 64];         // per-wave partial sums of A and P
-  uint16_t kgh[C * RS], kgl[C * RS];  // K o G, token rows, split
+  uint16_t kgh[C * KS], kgl[C * KS];  // K o G, token rows, split, k order
   uint16_t kdh[C * RS], kdl[C * RS];  // K o G_C / G, token rows, split
   float cc[C * CS];                   // log2 decays, then their prefix sums over the chunk
 };
@@ -853,8 +847,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
           };
           st_kperm8(&sh.qgh[(tok + s2) * KS], seg * 8, make_uint4(qh[s2][0], qh[s2][1], qh[s2][2], qh[s2][3]));
           st_kperm8(&sh.qgl[(tok + s2) * KS], seg * 8, make_uint4(ql[s2][0], ql[s2][1], ql[s2][2], ql[s2][3]));
-          row(sh.kgh, RS, kgh2);
-          row(sh.kgl, RS, kgl2);
+          st_kperm8(&sh.kgh[(tok + s2) * KS], seg * 8, make_uint4(kgh2[s2][0], kgh2[s2][1], kgh2[s2][2], kgh2[s2][3]));
+          st_kperm8(&sh.kgl[(tok + s2) * KS], seg * 8, make_uint4(kgl2[s2][0], kgl2[s2][1], kgl2[s2][2], kgl2[s2][3]));
           row(sh.kdh, RS, kdh2);
           row(sh.kdl, RS, kdl2);
         }
@@ -998,7 +992,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     // ---- 5. T = (I + A)^-1
     invert_unit_lower32<MS>(sh.g, sh.t, sh.xs, tid);
 
-    // ---- 6. T diag(b), split
+    // ---- 6. T diag(b), split, in k order (the A operand of T diag(b) R below)
     {
       const int j = tid % C;
       const float bj = sh.beta[j];
@@ -1010,58 +1004,25 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
         const int i0 = tid / C + e * (kThreads / C), i1 = i0 + kThreads / C;
         uint32_t hi, lo;
         split2(tv[e] * bj, tv[e + 1] * bj, hi, lo);
-        sh.t1h[i0 * TB + j] = static_cast<uint16_t>(hi);
-        sh.t1h[i1 * TB + j] = static_cast<uint16_t>(hi >> 16);
-        sh.t1l[i0 * TB + j] = static_cast<uint16_t>(lo);
-        sh.t1l[i1 * TB + j] = static_cast<uint16_t>(lo >> 16);
+        sh.t1h[i0 * TB + kperm(j)] = static_cast<uint16_t>(hi);
+        sh.t1h[i1 * TB + kperm(j)] = static_cast<uint16_t>(hi >> 16);
+        sh.t1l[i0 * TB + kperm(j)] = static_cast<uint16_t>(lo);
+        sh.t1l[i1 * TB + kperm(j)] = static_cast<uint16_t>(lo >> 16);
       }
     }
     __syncthreads();
 
-    // ---- 7. W = T diag(b) (K o G) via its transpose (to LDS, split); this wave's T diag(b) V
-#pragma unroll
-    for (int e = 0; e < NKB / 2; ++e) {
-      const int blk = wave + 4 * e;
-      const int ib = blk / NKB, cb = blk % NKB;
-      const bf16x8 kah = ld_tr8(sh.kgh, RS, 8 * lg, 8 * lg + 4, 16 * cb, ln);  // tokens 8 lg .. 8 lg + 7
-      const bf16x8 kal = ld_tr8(sh.kgl, RS, 8 * lg, 8 * lg + 4, 16 * cb, ln);
-      const bf16x8 tbh = ld_b128(&sh.t1h[(16 * ib + ln) * TB + 8 * lg]);
-      const bf16x8 tbl = ld_b128(&sh.t1l[(16 * ib + ln) * TB + 8 * lg]);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mma(kah, tbh, acc);
-      acc = mma(kah, tbl, acc);
-      acc = mma(kal, tbh, acc);
-      uint32_t h01, l01, h23, l23;
-      split2(acc[0], acc[1], h01, l01);
-      split2(acc[2], acc[3], h23, l23);
-      const int wo = (16 * ib + ln) * KS + kperm(16 * cb + 4 * lg);  // 4 channels, k order
-      *reinterpret_cast<uint2*>(&sh.wh[wo]) = make_uint2(h01, h23);
-      *reinterpret_cast<uint2*>(&sh.wl[wo]) = make_uint2(l01, l23);
-    }
-    float U[2][NCB][4];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const bf16x8 vb8 = ld_tr8(sh.v, VS, 8 * lg, 8 * lg + 4, col0 + 16 * cb, ln);
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma(ld_b128(&sh.t1h[(16 * ib + ln) * TB + 8 * lg]), vb8, acc);
-        acc = mma(ld_b128(&sh.t1l[(16 * ib + ln) * TB + 8 * lg]), vb8, acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) U[ib][cb][r] = acc[r];
-      }
-    }
-    __syncthreads();
-
-    // ---- 8. U = T diag(b) V - W S and (Q o G) S
-    float O[2][NCB][4];
+    // ---- 7, 8. X = (K o G) S and (Q o G) S (split operands, S one channel-block pair at a
+    //            time); R = V - X in fp32 at X's accumulator positions, the B operand of
+    //            U = T diag(b) R
+    float U[2][NCB][4], O[2][NCB][4];
     {
-      f32x4 ws[2][NCB], qs[2][NCB];
+      f32x4 xs[2][NCB], qs[2][NCB];
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          ws[ib][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          xs[ib][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
           qs[ib][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
@@ -1072,13 +1033,13 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
           const int rowk = (16 * ib + ln) * KS + 32 * kp + 8 * lg;  // channels 32 kp + 4 lg + {0..3, 16..19}
-          const bf16x8 wah = ld_b128(&sh.wh[rowk]), wal = ld_b128(&sh.wl[rowk]);
+          const bf16x8 kah = ld_b128(&sh.kgh[rowk]), kal = ld_b128(&sh.kgl[rowk]);
           const bf16x8 qah = ld_b128(&sh.qgh[rowk]), qal = ld_b128(&sh.qgl[rowk]);
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
-            ws[ib][cb] = mma(wah, shi[cb], ws[ib][cb]);
-            ws[ib][cb] = mma(wah, slo[cb], ws[ib][cb]);
-            ws[ib][cb] = mma(wal, shi[cb], ws[ib][cb]);
+            xs[ib][cb] = mma(kah, shi[cb], xs[ib][cb]);
+            xs[ib][cb] = mma(kah, slo[cb], xs[ib][cb]);
+            xs[ib][cb] = mma(kal, shi[cb], xs[ib][cb]);
             qs[ib][cb] = mma(qah, shi[cb], qs[ib][cb]);
             qs[ib][cb] = mma(qah, slo[cb], qs[ib][cb]);
             qs[ib][cb] = mma(qal, shi[cb], qs[ib][cb]);
@@ -1086,14 +1047,33 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
         }
       }
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib)
+      for (int cb = 0; cb < NCB; ++cb) {
+        float vf[8];  // V at this lane's accumulator positions
+        unpack8(__builtin_bit_cast(uint4, ld_tr8(sh.v, VS, 4 * lg, 16 + 4 * lg, col0 + 16 * cb, ln)), vf);
+        float r0[4], r1[4];
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
+        for (int r = 0; r < 4; ++r) {
+          r0[r] = vf[r] - xs[0][cb][r];
+          r1[r] = vf[4 + r] - xs[1][cb][r];
+        }
+        bf16x8 rhi, rlo;
+        split_pair(r0, r1, rhi, rlo);
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+          const int rowt = (16 * ib + ln) * TB + 8 * lg;
+          const bf16x8 tah = ld_b128(&sh.t1h[rowt]);
+          const bf16x8 tal = ld_b128(&sh.t1l[rowt]);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          acc = mma(tah, rhi, acc);
+          acc = mma(tah, rlo, acc);
+          acc = mma(tal, rhi, acc);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            U[ib][cb][r] -= ws[ib][cb][r];
+            U[ib][cb][r] = acc[r];
             O[ib][cb][r] = qs[ib][cb][r];
           }
+        }
+      }
     }
 
     // ---- 9. O += P U; outputs
