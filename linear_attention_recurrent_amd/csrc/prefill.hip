@@ -34,9 +34,12 @@
 // may pair any k order consistently between A and B; the state and U feed the
 // B operand straight from accumulator registers with k = {4g + r} u {16 + 4g + r}
 // (so does R, over tokens).
-// Every array is stored in token rows; where tokens run along an operand's k index (K^T
-// and its decay-scaled copies in the state update, V), the operand is read through
-// ds_read_b64_tr_b16.  Every operand is read with 8- or 16-byte LDS loads.
+// Every array is stored in token rows.  Rows that are the A operand against such an
+// accumulator-layout B operand keep each 32-element block in that k order (kperm), so
+// the operand is one 16-byte read; where tokens run along an operand's k index (K^T and
+// its decay-scaled copies in the state update, V) the rows are read through
+// ds_read_b64_tr_b16.  Row strides follow gfx950's banks (64 banks of 4 bytes): 8 mod 16
+// words for 16-byte and transposing reads.
 #include "launch.hpp"
 
 namespace dl {
