@@ -239,16 +239,20 @@ __device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, fl
     for (int m = 0; m < 16; ++m) t[(o + m) * MS + o + col] = x[m];
   }
   __syncthreads();
-  const int i = tid >> 4, j = tid & 15;
-  float s = 0.f;
+  const int i = (tid >> 4) & 15, j = tid & 15;  // the first 256 threads: one entry each
+  if (tid < 256) {
+    float s = 0.f;
 #pragma unroll
-  for (int m = 0; m < 16; ++m) s = fmaf(g[(16 + i) * MS + m], t[m * MS + j], s);
-  xs[i * 17 + j] = s;
+    for (int m = 0; m < 16; ++m) s = fmaf(g[(16 + i) * MS + m], t[m * MS + j], s);
+    xs[i * 17 + j] = s;
+  }
   __syncthreads();
-  float y = 0.f;
+  if (tid < 256) {
+    float y = 0.f;
 #pragma unroll
-  for (int m = 0; m < 16; ++m) y = fmaf(t[(16 + i) * MS + 16 + m], xs[m * 17 + j], y);
-  t[(16 + i) * MS + j] = -y;
+    for (int m = 0; m < 16; ++m) y = fmaf(t[(16 + i) * MS + 16 + m], xs[m * 17 + j], y);
+    t[(16 + i) * MS + j] = -y;
+  }
   __syncthreads();
 }
 
@@ -682,10 +686,16 @@ struct PrefillKdaLds {
   float cc[C * CS];                   // log2 decays, then their prefix sums over the chunk
 };
 
+// KDA workgroup size: 8 waves, 16 value columns each, when dv = 128 (two waves share each
+// SIMD, since the LDS of one tile leaves room for one workgroup per CU), else 4.
+template <int DV>
+constexpr int kda_threads() { return DV == 128 ? 512 : 256; }
+
 template <int DK, int DV, bool BF>
-__global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, PrefillArgs a) {
+__global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs pa, PrefillArgs a) {
   constexpr int C = kChunk;
-  constexpr int CW = DV / 4;
+  constexpr int NT = kda_threads<DV>(), NWV = NT / 64;  // threads, waves
+  constexpr int CW = DV / NWV;
   constexpr int NCB = CW / 16;
   constexpr int NKB = DK / 16;
   constexpr int NKP = DK / 32;
@@ -716,8 +726,8 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
   const bool kla = a.eta != nullptr;
   constexpr int KP = DK / 8, VP = DV / 8;
   constexpr int NPK = C / 2 * KP, NPV = C / 2 * VP;
-  constexpr int LK = (NPK + kThreads - 1) / kThreads, LV = (NPV + kThreads - 1) / kThreads;
-  constexpr int ND = C * DK / 4 / kThreads;  // float4 decay pieces per thread
+  constexpr int LK = (NPK + NT - 1) / NT, LV = (NPV + NT - 1) / NT;
+  constexpr int ND = C * DK / 4 / NT;  // float4 decay pieces per thread
   uint4 nk[LK][2], nq[LK][2], nv[LV][2];
   float4 nd[ND];
   float nbt = 0.f;
@@ -727,7 +737,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     const auto rd = rows_of(a.decay, t0, 4 * DK);
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
+      const int pc = tid + i * NT, tok = 2 * (pc / KP), seg = pc % KP;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const uint32_t off = static_cast<uint32_t>(((tok + s2) * H * DK + seg * 8) * 2);
@@ -737,14 +747,14 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
-      const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
+      const int pc = tid + i * NT, tok = 2 * (pc / VP), seg = pc % VP;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
         nv[i][s2] = bload16(rv, static_cast<uint32_t>(((tok + s2) * H * DV + seg * 8) * 2));
     }
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
-      const int pc = tid + i * kThreads, tok = pc / (DK / 4), seg = pc % (DK / 4);
+      const int pc = tid + i * NT, tok = pc / (DK / 4), seg = pc % (DK / 4);
       const uint4 w = bload16(rd, static_cast<uint32_t>((tok * H * DK + seg * 4) * 4));
       nd[i] = make_float4(__uint_as_float(w.x), __uint_as_float(w.y), __uint_as_float(w.z), __uint_as_float(w.w));
     }
@@ -760,7 +770,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     // ---- 1. K, Q and V rows; clamped log2 decays; ||k||^2; step sizes
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
+      const int pc = tid + i * NT, tok = 2 * (pc / KP), seg = pc % KP;
       if (pc < NPK) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -783,7 +793,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
-      const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
+      const int pc = tid + i * NT, tok = 2 * (pc / VP), seg = pc % VP;
       if (pc < NPV) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) *reinterpret_cast<uint4*>(&sh.v[(tok + s2) * VS + seg * 8]) = nv[i][s2];
@@ -791,7 +801,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     }
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
-      const int pc = tid + i * kThreads, tok = pc / (DK / 4), seg = pc % (DK / 4);
+      const int pc = tid + i * NT, tok = pc / (DK / 4), seg = pc % (DK / 4);
       const bool ok = t0 + tok < T;  // tokens past the prompt do not decay the state
       *reinterpret_cast<float4*>(&sh.cc[tok * CS + seg * 4]) =
           make_float4(ok ? step_log2_decay(nd[i].x) : 0.f, ok ? step_log2_decay(nd[i].y) : 0.f,
@@ -808,7 +818,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
       const bool ok = t0 + tid < T;
       sh.beta[tid] = !ok ? 0.f : kla ? sh.braw[tid] / (sh.knorm[tid] + a.eps) : sh.braw[tid];
     }
-    for (int e = tid; e < C * C; e += kThreads) {
+    for (int e = tid; e < C * C; e += NT) {
       const int i = e / C, j = e % C;
       if (j > i) {
         sh.pmh[i * TB + kperm(j)] = 0;
@@ -821,7 +831,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     // ---- 3. decay-folded operands Q o G, K o G and K o G_C / G (token rows), split
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
+      const int pc = tid + i * NT, tok = 2 * (pc / KP), seg = pc % KP;
       if (pc < NPK) {
         float kf[2][8], qf[2][8], cf[2][8], cl[8];
 #pragma unroll
@@ -865,83 +875,106 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     //        tokens, so when no channel decays by more than 2^-60 over either half of
     //        the chunk the products run on MFMA with three-way split operands (these
     //        sums over channels can cancel, so they keep 24 bits).  Each wave takes 32
-    //        channels of all three lower blocks, building each row and column operand
-    //        once; the four partial sums are added in a fixed order through LDS.
+    //        channels of A and P (with eight waves, of block (0,0) or of the two blocks
+    //        of rows 16..31; with four, of all three), building each row and column
+    //        operand once; the partial sums over channel steps are added in a fixed
+    //        order through LDS.
     //        Otherwise every pair is formed directly.
     bool direct;
     {
       bool big = false;
-      for (int ch = tid; ch < DK; ch += kThreads)
+      for (int ch = tid; ch < DK; ch += NT)
         big = big || -sh.cc[15 * CS + ch] > 60.f || sh.cc[15 * CS + ch] - sh.cc[(C - 1) * CS + ch] > 60.f;
       direct = __syncthreads_or(big);
     }
     if (!direct) {
-      constexpr int NKS = DK / 32;           // 32-channel steps
-      constexpr int NW = NKS < 4 ? NKS : 4;  // waves that hold partial sums
-      // acc: A and P of the blocks (0,0), (1,0), (1,1) in that order
+      constexpr int NKS = DK / 32;   // 32-channel steps
+      constexpr int SPLIT = NWV / 4;  // 2: waves 0..3 take block (0,0), waves 4..7 the blocks
+                                      //    (1,0) and (1,1); 1: each wave all three
+      const int ks0 = wave & 3;
+      const bool top = SPLIT == 1 || wave < 4, bottom = SPLIT == 1 || wave >= 4;
+      // acc: A and P of the blocks (0,0), (1,0), (1,1) in that order (A even, P odd)
       f32x4 acc[6];
 #pragma unroll
       for (int m = 0; m < 6; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int kk = wave; kk < NKS; kk += 4) {
+      auto ops = [](const uint32_t (&w)[3][4], bf16x8 (&x)[3]) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u) x[u] = pack8(w[u][0], w[u][1], w[u][2], w[u][3]);
+      };
+      for (int kk = ks0; kk < NKS; kk += 4) {
         const int ch0 = 32 * kk + 8 * lg;
-        float c0[8], c1[8], ref[8], k0[8], k1[8], q0[8], q1[8];
-        load8(&sh.cc[ln * CS + ch0], c0);         // token ln
-        load8(&sh.cc[(16 + ln) * CS + ch0], c1);  // token 16 + ln
+        float ref[8];
         load8(&sh.cc[15 * CS + ch0], ref);
-        unpack8(*reinterpret_cast<const uint4*>(&sh.k[ln * KS + ch0]), k0);
-        unpack8(*reinterpret_cast<const uint4*>(&sh.k[(16 + ln) * KS + ch0]), k1);
-        unpack8(*reinterpret_cast<const uint4*>(&sh.q[ln * KS + ch0]), q0);
-        unpack8(*reinterpret_cast<const uint4*>(&sh.q[(16 + ln) * KS + ch0]), q1);
-        // rows: token ln with R = start, token 16 + ln with R = 15; columns: token ln with
-        // R = start and with R = 15, token 16 + ln with R = 15
-        uint32_t ka[3][4], qa[3][4], kb[3][4], qb[3][4], c00[3][4], c10[3][4], c11[3][4];
+        if (top) {  // rows: token ln with R = start; columns: token ln with R = start
+          float c0[8], k0[8], q0[8];
+          load8(&sh.cc[ln * CS + ch0], c0);
+          unpack8(*reinterpret_cast<const uint4*>(&sh.k[ln * KS + ch0]), k0);
+          unpack8(*reinterpret_cast<const uint4*>(&sh.q[ln * KS + ch0]), q0);
+          uint32_t ka[3][4], qa[3][4], c00[3][4];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float r0a = fexp2(c0[e]), r0b = fexp2(c0[e + 1]);
-          const float r1a = fexp2(c1[e] - ref[e]), r1b = fexp2(c1[e + 1] - ref[e + 1]);
-          split3(k0[e] * r0a, k0[e + 1] * r0b, ka[0][e / 2], ka[1][e / 2], ka[2][e / 2]);
-          split3(q0[e] * r0a, q0[e + 1] * r0b, qa[0][e / 2], qa[1][e / 2], qa[2][e / 2]);
-          split3(k1[e] * r1a, k1[e + 1] * r1b, kb[0][e / 2], kb[1][e / 2], kb[2][e / 2]);
-          split3(q1[e] * r1a, q1[e + 1] * r1b, qb[0][e / 2], qb[1][e / 2], qb[2][e / 2]);
-          split3(k0[e] * fexp2(-c0[e]), k0[e + 1] * fexp2(-c0[e + 1]), c00[0][e / 2], c00[1][e / 2], c00[2][e / 2]);
-          split3(k0[e] * fexp2(ref[e] - c0[e]), k0[e + 1] * fexp2(ref[e + 1] - c0[e + 1]), c10[0][e / 2],
-                 c10[1][e / 2], c10[2][e / 2]);
-          split3(k1[e] * fexp2(ref[e] - c1[e]), k1[e + 1] * fexp2(ref[e + 1] - c1[e + 1]), c11[0][e / 2],
-                 c11[1][e / 2], c11[2][e / 2]);
+          for (int e = 0; e < 8; e += 2) {
+            const float r0a = fexp2(c0[e]), r0b = fexp2(c0[e + 1]);
+            split3(k0[e] * r0a, k0[e + 1] * r0b, ka[0][e / 2], ka[1][e / 2], ka[2][e / 2]);
+            split3(q0[e] * r0a, q0[e + 1] * r0b, qa[0][e / 2], qa[1][e / 2], qa[2][e / 2]);
+            split3(k0[e] * fexp2(-c0[e]), k0[e + 1] * fexp2(-c0[e + 1]), c00[0][e / 2], c00[1][e / 2],
+                   c00[2][e / 2]);
+          }
+          bf16x8 KA[3], QA[3], C00[3];
+          ops(ka, KA);
+          ops(qa, QA);
+          ops(c00, C00);
+          acc[0] = mma3(KA, C00, acc[0]);
+          acc[1] = mma3(QA, C00, acc[1]);
         }
-        auto ops = [](const uint32_t (&w)[3][4], bf16x8 (&x)[3]) {
+        if (bottom) {  // rows: token 16 + ln with R = 15; columns: token ln and 16 + ln with R = 15
+          float c0[8], c1[8], k0[8], k1[8], q1[8];
+          load8(&sh.cc[ln * CS + ch0], c0);
+          load8(&sh.cc[(16 + ln) * CS + ch0], c1);
+          unpack8(*reinterpret_cast<const uint4*>(&sh.k[ln * KS + ch0]), k0);
+          unpack8(*reinterpret_cast<const uint4*>(&sh.k[(16 + ln) * KS + ch0]), k1);
+          unpack8(*reinterpret_cast<const uint4*>(&sh.q[(16 + ln) * KS + ch0]), q1);
+          uint32_t kb[3][4], qb[3][4], c10[3][4], c11[3][4];
 #pragma unroll
-          for (int u = 0; u < 3; ++u) x[u] = pack8(w[u][0], w[u][1], w[u][2], w[u][3]);
-        };
-        bf16x8 KA[3], QA[3], KB[3], QB[3], C00[3], C10[3], C11[3];
-        ops(ka, KA);
-        ops(qa, QA);
-        ops(kb, KB);
-        ops(qb, QB);
-        ops(c00, C00);
-        ops(c10, C10);
-        ops(c11, C11);
-        acc[0] = mma3(KA, C00, acc[0]);
-        acc[1] = mma3(QA, C00, acc[1]);
-        acc[2] = mma3(KB, C10, acc[2]);
-        acc[3] = mma3(QB, C10, acc[3]);
-        acc[4] = mma3(KB, C11, acc[4]);
-        acc[5] = mma3(QB, C11, acc[5]);
+          for (int e = 0; e < 8; e += 2) {
+            const float r1a = fexp2(c1[e] - ref[e]), r1b = fexp2(c1[e + 1] - ref[e + 1]);
+            split3(k1[e] * r1a, k1[e + 1] * r1b, kb[0][e / 2], kb[1][e / 2], kb[2][e / 2]);
+            split3(q1[e] * r1a, q1[e + 1] * r1b, qb[0][e / 2], qb[1][e / 2], qb[2][e / 2]);
+            split3(k0[e] * fexp2(ref[e] - c0[e]), k0[e + 1] * fexp2(ref[e + 1] - c0[e + 1]), c10[0][e / 2],
+                   c10[1][e / 2], c10[2][e / 2]);
+            split3(k1[e] * fexp2(ref[e] - c1[e]), k1[e + 1] * fexp2(ref[e + 1] - c1[e + 1]), c11[0][e / 2],
+                   c11[1][e / 2], c11[2][e / 2]);
+          }
+          bf16x8 KB[3], QB[3], C10[3], C11[3];
+          ops(kb, KB);
+          ops(qb, QB);
+          ops(c10, C10);
+          ops(c11, C11);
+          acc[2] = mma3(KB, C10, acc[2]);
+          acc[3] = mma3(QB, C10, acc[3]);
+          acc[4] = mma3(KB, C11, acc[4]);
+          acc[5] = mma3(QB, C11, acc[5]);
+        }
       }
-      if (wave < NW) {
+      // part[channel step][m][r][lane], each entry written by the one wave that formed it
+      constexpr int NKW = NKS < 4 ? NKS : 4;  // channel steps held
+      if (ks0 < NKW) {
 #pragma unroll
-        for (int m = 0; m < 6; ++m)
+        for (int m = 0; m < 6; ++m) {
+          if (m < 2 ? !top : !bottom) continue;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sh.part[((wave * 6 + m) * 4 + r) * 64 + lane] = acc[m][r];
+          for (int r = 0; r < 4; ++r) sh.part[((ks0 * 6 + m) * 4 + r) * 64 + lane] = acc[m][r];
+        }
       }
       __syncthreads();
-      // thread (r = wave, lane): entry r of this lane in each of the six block products
-      const int r = wave, j0 = ln;
+      // thread (r = wave % 4, lane): entry r of this lane in the block products (with eight
+      // waves, waves 0..3 finish A and waves 4..7 P), partial sums added in channel order
+      const int r = wave & 3, j0 = ln;
 #pragma unroll
       for (int m = 0; m < 6; ++m) {
-        float sum = sh.part[(m * 4 + r) * 64 + lane];
+        if (SPLIT == 2 && (m & 1) != (wave >> 2)) continue;
+        float sum = 0.f;
 #pragma unroll
-        for (int w = 1; w < NW; ++w) sum += sh.part[((w * 6 + m) * 4 + r) * 64 + lane];
+        for (int w = 0; w < NKW; ++w) sum += sh.part[((w * 6 + m) * 4 + r) * 64 + lane];
         const int blk = m >> 1, ib = blk == 0 ? 0 : 1, jb = blk == 2 ? 1 : 0;
         const int i = 16 * ib + 4 * lg + r, j = 16 * jb + j0;
         if ((m & 1) == 0) {
@@ -953,7 +986,7 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
           sh.pml[i * TB + kperm(j)] = static_cast<uint16_t>(lo);
         }
       }
-    } else {
+    } else if (tid < 256) {
       // pairwise: thread (row pair ip, ip' = 31 - ip; channel slice sl)
       constexpr int SL = DK / 16;  // channels per slice
       const int ip = tid >> 4, sl = tid & 15;
@@ -999,12 +1032,12 @@ __global__ void __launch_bounds__(kThreads) prefill_kda_kernel(PoolArgs pa, Pref
     {
       const int j = tid % C;
       const float bj = sh.beta[j];
-      float tv[C * C / kThreads];
+      float tv[C * C / NT];
 #pragma unroll
-      for (int e = 0; e < C * C / kThreads; ++e) tv[e] = sh.t[(tid / C + e * (kThreads / C)) * MS + j];
+      for (int e = 0; e < C * C / NT; ++e) tv[e] = sh.t[(tid / C + e * (NT / C)) * MS + j];
 #pragma unroll
-      for (int e = 0; e < C * C / kThreads; e += 2) {
-        const int i0 = tid / C + e * (kThreads / C), i1 = i0 + kThreads / C;
+      for (int e = 0; e < C * C / NT; e += 2) {
+        const int i0 = tid / C + e * (NT / C), i1 = i0 + NT / C;
         uint32_t hi, lo;
         split2(tv[e] * bj, tv[e + 1] * bj, hi, lo);
         sh.t1h[i0 * TB + kperm(j)] = static_cast<uint16_t>(hi);
@@ -1516,7 +1549,7 @@ hipError_t launch_prefill(int variant, bool bf16_base, int dk, int dv, int tiles
                           const PrefillArgs& a, hipStream_t stream) {
 #define DL_PREFILL(BF_, DK_, DV_)                                                   \
   do {                                                                              \
-    if (variant == DL_KDA) prefill_kda_kernel<DK_, DV_, BF_><<<tiles, kThreads, 0, stream>>>(p, a); \
+    if (variant == DL_KDA) prefill_kda_kernel<DK_, DV_, BF_><<<tiles, kda_threads<DV_>(), 0, stream>>>(p, a); \
     else if (variant == DL_RWKV6) prefill_rwkv_kernel<DK_, DV_, BF_><<<tiles, kThreads, 0, stream>>>(p, a); \
     else prefill_kernel<DK_, DV_, BF_><<<tiles, kThreads, 0, stream>>>(p, a);        \
   } while (0)
