@@ -1186,6 +1186,7 @@ struct PrefillRwkvLds {
   float bonus[DK];
   float glast[DK];                    // 2^c of the chunk's last token per channel
   float pd[C];                        // the bonus diagonal of P
+  float part[2 * 3 * 4 * 64];         // per-wave partial sums of P
   uint16_t pmh[C * TB], pml[C * TB];  // P, split
   uint16_t k[C * KS];                // K, token rows
   uint16_t q[C * KS];                // R, token rows
@@ -1358,66 +1359,93 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
       direct = __syncthreads_or(big);  // also orders step 3's stores before the reads below
     }
     if (!direct) {
-      if (wave < 3) {
-        const int ib = wave == 0 ? 0 : 1, jb = wave == 2 ? 1 : 0;
-        f32x4 accP = {0.f, 0.f, 0.f, 0.f};
-        const int ri = 16 * ib + ln;  // this lane's row of the A operand
+      // wave w: channel steps kk = w % 2, w % 2 + 2, ...; waves 0, 1 the block (0,0), waves
+      // 2, 3 the blocks (1,0) and (1,1), so each row and column operand is built once; the
+      // two partial sums per entry are added in a fixed order through LDS
+      constexpr int NKS = DK / 32, NKW = NKS < 2 ? NKS : 2;
+      const int ks0 = wave & 1;
+      const bool top = wave < 2;
+      f32x4 acc[3];  // blocks (0,0), (1,0), (1,1)
 #pragma unroll
-        for (int kk = 0; kk < DK / 32; ++kk) {
-          const int ch0 = 32 * kk + 8 * lg;
-          float cr[8], cj[8], ref[8], rr[8], kc[8];
-          if (ri > 0) load8(&sh.cc[(ri - 1) * CS + ch0], cr);
+      for (int m = 0; m < 3; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      auto ops = [](const uint32_t (&w)[3][4], bf16x8 (&x)[3]) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u) x[u] = pack8(w[u][0], w[u][1], w[u][2], w[u][3]);
+      };
+      for (int kk = ks0; kk < NKS; kk += 2) {
+        const int ch0 = 32 * kk + 8 * lg;
+        float k0[8], c0[8];
+        unpack8(*reinterpret_cast<const uint4*>(&sh.k[ln * KS + ch0]), k0);
+        load8(&sh.cc[ln * CS + ch0], c0);
+        if (top) {  // rows: r of token ln with G_{ln-1} (R = start); columns: token ln (R = start)
+          float cp[8], r0[8];
+          if (ln > 0) load8(&sh.cc[(ln - 1) * CS + ch0], cp);
           else
 #pragma unroll
-            for (int e = 0; e < 8; ++e) cr[e] = 0.f;
-          load8(&sh.cc[(16 * jb + ln) * CS + ch0], cj);
-          if (ib == 1) load8(&sh.cc[15 * CS + ch0], ref);
-          else
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ref[e] = 0.f;
-          unpack8(*reinterpret_cast<const uint4*>(&sh.q[ri * KS + ch0]), rr);
-          unpack8(*reinterpret_cast<const uint4*>(&sh.k[(16 * jb + ln) * KS + ch0]), kc);
-          uint32_t ap[3][4], bp[3][4];
+            for (int e = 0; e < 8; ++e) cp[e] = 0.f;
+          unpack8(*reinterpret_cast<const uint4*>(&sh.q[ln * KS + ch0]), r0);
+          uint32_t ra[3][4], c00[3][4];
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
-            split3(rr[e] * fexp2(cr[e] - ref[e]), rr[e + 1] * fexp2(cr[e + 1] - ref[e + 1]), ap[0][e / 2],
-                   ap[1][e / 2], ap[2][e / 2]);
-            split3(kc[e] * fexp2(ref[e] - cj[e]), kc[e + 1] * fexp2(ref[e + 1] - cj[e + 1]), bp[0][e / 2],
-                   bp[1][e / 2], bp[2][e / 2]);
+            split3(r0[e] * fexp2(cp[e]), r0[e + 1] * fexp2(cp[e + 1]), ra[0][e / 2], ra[1][e / 2], ra[2][e / 2]);
+            split3(k0[e] * fexp2(-c0[e]), k0[e + 1] * fexp2(-c0[e + 1]), c00[0][e / 2], c00[1][e / 2],
+                   c00[2][e / 2]);
           }
-          bf16x8 Ax[3], Bx[3];
+          bf16x8 RA[3], C00[3];
+          ops(ra, RA);
+          ops(c00, C00);
+          acc[0] = mma3(RA, C00, acc[0]);
+        } else {  // rows: token 16 + ln with G_{15 + ln} (R = 15); columns: tokens ln, 16 + ln (R = 15)
+          float ref[8], cp[8], c1[8], k1[8], r1[8];
+          load8(&sh.cc[15 * CS + ch0], ref);
+          load8(&sh.cc[(15 + ln) * CS + ch0], cp);
+          load8(&sh.cc[(16 + ln) * CS + ch0], c1);
+          unpack8(*reinterpret_cast<const uint4*>(&sh.k[(16 + ln) * KS + ch0]), k1);
+          unpack8(*reinterpret_cast<const uint4*>(&sh.q[(16 + ln) * KS + ch0]), r1);
+          uint32_t rb[3][4], c10[3][4], c11[3][4];
 #pragma unroll
-          for (int u = 0; u < 3; ++u) {
-            Ax[u] = pack8(ap[u][0], ap[u][1], ap[u][2], ap[u][3]);
-            Bx[u] = pack8(bp[u][0], bp[u][1], bp[u][2], bp[u][3]);
+          for (int e = 0; e < 8; e += 2) {
+            split3(r1[e] * fexp2(cp[e] - ref[e]), r1[e + 1] * fexp2(cp[e + 1] - ref[e + 1]), rb[0][e / 2],
+                   rb[1][e / 2], rb[2][e / 2]);
+            split3(k0[e] * fexp2(ref[e] - c0[e]), k0[e + 1] * fexp2(ref[e + 1] - c0[e + 1]), c10[0][e / 2],
+                   c10[1][e / 2], c10[2][e / 2]);
+            split3(k1[e] * fexp2(ref[e] - c1[e]), k1[e + 1] * fexp2(ref[e + 1] - c1[e + 1]), c11[0][e / 2],
+                   c11[1][e / 2], c11[2][e / 2]);
           }
-          accP = mma3(Ax, Bx, accP);
+          bf16x8 RB[3], C10[3], C11[3];
+          ops(rb, RB);
+          ops(c10, C10);
+          ops(c11, C11);
+          acc[1] = mma3(RB, C10, acc[1]);
+          acc[2] = mma3(RB, C11, acc[2]);
         }
-        const int j = 16 * jb + ln;
-        float pm[4];
+      }
+      if (ks0 < NKW) {  // part[channel-step slot][block][r][lane]
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * ib + 4 * lg + r;
-          pm[r] = j < i ? accP[r] : j == i ? sh.pd[i] : 0.f;
-        }
+        for (int m = 0; m < 3; ++m) {
+          if (top != (m == 0)) continue;
 #pragma unroll
-        for (int r = 0; r < 4; r += 2) {
-          const int i = 16 * ib + 4 * lg + r;
-          uint32_t hi, lo;
-          split2(pm[r], pm[r + 1], hi, lo);
-          sh.pmh[i * TB + j] = static_cast<uint16_t>(hi);
-          sh.pmh[(i + 1) * TB + j] = static_cast<uint16_t>(hi >> 16);
-          sh.pml[i * TB + j] = static_cast<uint16_t>(lo);
-          sh.pml[(i + 1) * TB + j] = static_cast<uint16_t>(lo >> 16);
+          for (int r = 0; r < 4; ++r) sh.part[((ks0 * 3 + m) * 4 + r) * 64 + lane] = acc[m][r];
         }
-      } else {
-        // the upper right block of P is zero
+      }
+      __syncthreads();
+      // thread (r = wave, lane): entry r of this lane in each block; the upper right block is zero
+      const int r = wave;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = (lane >> 4) + 4 * e, j = 16 + ln;
-          sh.pmh[i * TB + j] = 0;
-          sh.pml[i * TB + j] = 0;
+      for (int m = 0; m < 4; ++m) {
+        const int ib = m == 0 || m == 3 ? 0 : 1, jb = m >= 2 ? 1 : 0;  // (0,0), (1,0), (1,1), (0,1)
+        const int i = 16 * ib + 4 * lg + r, j = 16 * jb + ln;
+        float pm = 0.f;
+        if (m < 3) {
+          float sum = 0.f;
+#pragma unroll
+          for (int w = 0; w < NKW; ++w) sum += sh.part[((w * 3 + m) * 4 + r) * 64 + lane];
+          pm = j < i ? sum : j == i ? sh.pd[i] : 0.f;
         }
+        uint32_t hi, lo;
+        split2(pm, 0.f, hi, lo);
+        sh.pmh[i * TB + j] = static_cast<uint16_t>(hi);
+        sh.pml[i * TB + j] = static_cast<uint16_t>(lo);
       }
     } else {
       // pairwise: thread (row pair ip, 31 - ip; channel slice sl); j < row, plus the diagonal
