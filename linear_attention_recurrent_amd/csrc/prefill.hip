@@ -828,44 +828,29 @@ __global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs
     }
     __syncthreads();
 
-    // ---- 3. decay-folded operands Q o G, K o G and K o G_C / G (token rows), split
+    // ---- 3. decay-folded operands Q o G, K o G and K o G_C / G (token rows), split;
+    //         thread (token, 8-channel segment)
+    for (int pc = tid; pc < C * KP; pc += NT) {
+      const int tok = pc / KP, seg = pc % KP;
+      float kf[8], qf[8], cf[8], cl[8];
+      unpack8(*reinterpret_cast<const uint4*>(&sh.k[tok * KS + seg * 8]), kf);
+      unpack8(*reinterpret_cast<const uint4*>(&sh.q[tok * KS + seg * 8]), qf);
+      load8(&sh.cc[tok * CS + seg * 8], cf);
+      load8(&sh.cc[(C - 1) * CS + seg * 8], cl);
+      uint32_t qh[4], ql[4], kgh2[4], kgl2[4], kdh2[4], kdl2[4];
 #pragma unroll
-    for (int i = 0; i < LK; ++i) {
-      const int pc = tid + i * NT, tok = 2 * (pc / KP), seg = pc % KP;
-      if (pc < NPK) {
-        float kf[2][8], qf[2][8], cf[2][8], cl[8];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          unpack8(*reinterpret_cast<const uint4*>(&sh.k[(tok + s2) * KS + seg * 8]), kf[s2]);
-          unpack8(*reinterpret_cast<const uint4*>(&sh.q[(tok + s2) * KS + seg * 8]), qf[s2]);
-          load8(&sh.cc[(tok + s2) * CS + seg * 8], cf[s2]);
-        }
-        load8(&sh.cc[(C - 1) * CS + seg * 8], cl);
-        uint32_t qh[2][4], ql[2][4], kgh2[2][4], kgl2[2][4], kdh2[2][4], kdl2[2][4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {  // channels e, e + 1 packed
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const float g0 = fexp2(cf[s2][e]), g1 = fexp2(cf[s2][e + 1]);
-            split2(qf[s2][e] * g0, qf[s2][e + 1] * g1, qh[s2][e / 2], ql[s2][e / 2]);
-            split2(kf[s2][e] * g0, kf[s2][e + 1] * g1, kgh2[s2][e / 2], kgl2[s2][e / 2]);
-            split2(kf[s2][e] * fexp2(cl[e] - cf[s2][e]), kf[s2][e + 1] * fexp2(cl[e + 1] - cf[s2][e + 1]),
-                   kdh2[s2][e / 2], kdl2[s2][e / 2]);
-          }
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          auto row = [&](uint16_t* x, int stride, const uint32_t (&w)[2][4]) {
-            *reinterpret_cast<uint4*>(&x[(tok + s2) * stride + seg * 8]) = make_uint4(w[s2][0], w[s2][1], w[s2][2], w[s2][3]);
-          };
-          st_kperm8(&sh.qgh[(tok + s2) * KS], seg * 8, make_uint4(qh[s2][0], qh[s2][1], qh[s2][2], qh[s2][3]));
-          st_kperm8(&sh.qgl[(tok + s2) * KS], seg * 8, make_uint4(ql[s2][0], ql[s2][1], ql[s2][2], ql[s2][3]));
-          st_kperm8(&sh.kgh[(tok + s2) * KS], seg * 8, make_uint4(kgh2[s2][0], kgh2[s2][1], kgh2[s2][2], kgh2[s2][3]));
-          st_kperm8(&sh.kgl[(tok + s2) * KS], seg * 8, make_uint4(kgl2[s2][0], kgl2[s2][1], kgl2[s2][2], kgl2[s2][3]));
-          row(sh.kdh, RS, kdh2);
-          row(sh.kdl, RS, kdl2);
-        }
+      for (int e = 0; e < 8; e += 2) {  // channels e, e + 1 packed
+        const float g0 = fexp2(cf[e]), g1 = fexp2(cf[e + 1]);
+        split2(qf[e] * g0, qf[e + 1] * g1, qh[e / 2], ql[e / 2]);
+        split2(kf[e] * g0, kf[e + 1] * g1, kgh2[e / 2], kgl2[e / 2]);
+        split2(kf[e] * fexp2(cl[e] - cf[e]), kf[e + 1] * fexp2(cl[e + 1] - cf[e + 1]), kdh2[e / 2], kdl2[e / 2]);
       }
+      st_kperm8(&sh.qgh[tok * KS], seg * 8, make_uint4(qh[0], qh[1], qh[2], qh[3]));
+      st_kperm8(&sh.qgl[tok * KS], seg * 8, make_uint4(ql[0], ql[1], ql[2], ql[3]));
+      st_kperm8(&sh.kgh[tok * KS], seg * 8, make_uint4(kgh2[0], kgh2[1], kgh2[2], kgh2[3]));
+      st_kperm8(&sh.kgl[tok * KS], seg * 8, make_uint4(kgl2[0], kgl2[1], kgl2[2], kgl2[3]));
+      *reinterpret_cast<uint4*>(&sh.kdh[tok * RS + seg * 8]) = make_uint4(kdh2[0], kdh2[1], kdh2[2], kdh2[3]);
+      *reinterpret_cast<uint4*>(&sh.kdl[tok * RS + seg * 8]) = make_uint4(kdl2[0], kdl2[1], kdl2[2], kdl2[3]);
     }
 
     // ---- 4. A and P.  G_i / G_j = (G_i / G_R)(G_R / G_j) splits the decay of a pair
@@ -1301,53 +1286,34 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
     prefix_over_tokens<DK, CS>(sh.cc, sh.glast, tid);
     __syncthreads();
 
-    // ---- 3. R o G_prev and K o G_C / G (token rows), split; the bonus diagonal
+    // ---- 3. R o G_prev and K o G_C / G (token rows), split; the bonus diagonal;
+    //         thread (token, 8-channel segment)
+    for (int pc = tid; pc < C * KP; pc += kThreads) {
+      const int tok = pc / KP, seg = pc % KP;
+      float kf[8], rf[8], cf[8], cp[8], cl[8];
+      unpack8(*reinterpret_cast<const uint4*>(&sh.k[tok * KS + seg * 8]), kf);
+      unpack8(*reinterpret_cast<const uint4*>(&sh.q[tok * KS + seg * 8]), rf);
+      load8(&sh.cc[tok * CS + seg * 8], cf);
+      if (tok > 0) load8(&sh.cc[(tok - 1) * CS + seg * 8], cp);  // G_{tok-1}
+      else
 #pragma unroll
-    for (int i = 0; i < LK; ++i) {
-      const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
-      if (pc < NPK) {
-        float kf[2][8], rf[2][8], cf[2][8], cp[8], cl[8];
+        for (int e = 0; e < 8; ++e) cp[e] = 0.f;
+      load8(&sh.cc[(C - 1) * CS + seg * 8], cl);
+      uint32_t rh[4], rl[4], kdh2[4], kdl2[4];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          unpack8(*reinterpret_cast<const uint4*>(&sh.k[(tok + s2) * KS + seg * 8]), kf[s2]);
-          unpack8(*reinterpret_cast<const uint4*>(&sh.q[(tok + s2) * KS + seg * 8]), rf[s2]);
-          load8(&sh.cc[(tok + s2) * CS + seg * 8], cf[s2]);
-        }
-        if (tok > 0) load8(&sh.cc[(tok - 1) * CS + seg * 8], cp);  // G_prev of token tok
-        else
-#pragma unroll
-          for (int e = 0; e < 8; ++e) cp[e] = 0.f;
-        load8(&sh.cc[(C - 1) * CS + seg * 8], cl);
-        uint32_t rh[2][4], rl[2][4], kdh2[2][4], kdl2[2][4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {  // channels e, e + 1 packed
-          // token tok reads G_{tok-1}, token tok + 1 reads G_tok
-          split2(rf[0][e] * fexp2(cp[e]), rf[0][e + 1] * fexp2(cp[e + 1]), rh[0][e / 2], rl[0][e / 2]);
-          split2(rf[1][e] * fexp2(cf[0][e]), rf[1][e + 1] * fexp2(cf[0][e + 1]), rh[1][e / 2], rl[1][e / 2]);
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
-            split2(kf[s2][e] * fexp2(cl[e] - cf[s2][e]), kf[s2][e + 1] * fexp2(cl[e + 1] - cf[s2][e + 1]),
-                   kdh2[s2][e / 2], kdl2[s2][e / 2]);
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          auto row = [&](uint16_t* x, int stride, const uint32_t (&w)[2][4]) {
-            *reinterpret_cast<uint4*>(&x[(tok + s2) * stride + seg * 8]) = make_uint4(w[s2][0], w[s2][1], w[s2][2], w[s2][3]);
-          };
-          st_kperm8(&sh.rgh[(tok + s2) * KS], seg * 8, make_uint4(rh[s2][0], rh[s2][1], rh[s2][2], rh[s2][3]));
-          st_kperm8(&sh.rgl[(tok + s2) * KS], seg * 8, make_uint4(rl[s2][0], rl[s2][1], rl[s2][2], rl[s2][3]));
-          row(sh.kdh, RS, kdh2);
-          row(sh.kdl, RS, kdl2);
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          float d = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) d = fmaf(rf[s2][e] * sh.bonus[seg * 8 + e], kf[s2][e], d);
-          d = group_sum<KP>(d);
-          if (seg == 0) sh.pd[tok + s2] = d;
-        }
+      for (int e = 0; e < 8; e += 2) {  // channels e, e + 1 packed
+        split2(rf[e] * fexp2(cp[e]), rf[e + 1] * fexp2(cp[e + 1]), rh[e / 2], rl[e / 2]);
+        split2(kf[e] * fexp2(cl[e] - cf[e]), kf[e + 1] * fexp2(cl[e + 1] - cf[e + 1]), kdh2[e / 2], kdl2[e / 2]);
       }
+      st_kperm8(&sh.rgh[tok * KS], seg * 8, make_uint4(rh[0], rh[1], rh[2], rh[3]));
+      st_kperm8(&sh.rgl[tok * KS], seg * 8, make_uint4(rl[0], rl[1], rl[2], rl[3]));
+      *reinterpret_cast<uint4*>(&sh.kdh[tok * RS + seg * 8]) = make_uint4(kdh2[0], kdh2[1], kdh2[2], kdh2[3]);
+      *reinterpret_cast<uint4*>(&sh.kdl[tok * RS + seg * 8]) = make_uint4(kdl2[0], kdl2[1], kdl2[2], kdl2[3]);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(rf[e] * sh.bonus[seg * 8 + e], kf[e], d);
+      d = group_sum<KP>(d);
+      if (seg == 0) sh.pd[tok] = d;
     }
 
     // ---- 4. P (see the KDA kernel for the reference-token split; rows use G_{i-1})
