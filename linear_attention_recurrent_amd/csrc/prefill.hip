@@ -342,31 +342,26 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
 
   const bool kla = a.eta != nullptr;
   // Inputs of the next chunk are loaded into registers while this chunk is computed;
-  // each thread takes one 16-byte piece (8 channels) of two consecutive tokens.
+  // each job is one 16-byte piece (8 channels) of one token.
   constexpr int KP = DK / 8, VP = DV / 8;                         // pieces per row
-  constexpr int NPK = C / 2 * KP, NPV = C / 2 * VP;               // (token pair, piece) jobs
+  constexpr int NPK = C * KP, NPV = C * VP;                       // (token, piece) jobs
   constexpr int LK = (NPK + kThreads - 1) / kThreads, LV = (NPV + kThreads - 1) / kThreads;
-  uint4 nk[LK][2], nq[LK][2], nv[LV][2];
+  uint4 nk[LK], nq[LK], nv[LV];
   float ndec = 1.f, nbt = 0.f;
   auto rows_of = [&](const void* x, int t0, int bytes_per_row) { return chunk_rows(x, bseq, h, T, H, t0, bytes_per_row); };
   auto fetch = [&](int t0) {
     const auto rk = rows_of(a.k, t0, 2 * DK), rq = rows_of(a.q, t0, 2 * DK), rv = rows_of(a.v, t0, 2 * DV);
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const uint32_t off = static_cast<uint32_t>(((tok + s2) * H * DK + seg * 8) * 2);
-        nk[i][s2] = bload16(rk, off);
-        nq[i][s2] = bload16(rq, off);
-      }
+      const int pc = tid + i * kThreads, tok = pc / KP, seg = pc % KP;  // jobs past the chunk read zeros
+      const uint32_t off = static_cast<uint32_t>((tok * H * DK + seg * 8) * 2);
+      nk[i] = bload16(rk, off);
+      nq[i] = bload16(rq, off);
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
-      const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        nv[i][s2] = bload16(rv, static_cast<uint32_t>(((tok + s2) * H * DV + seg * 8) * 2));
+      const int pc = tid + i * kThreads, tok = pc / VP, seg = pc % VP;
+      nv[i] = bload16(rv, static_cast<uint32_t>((tok * H * DV + seg * 8) * 2));
     }
     if (wave == 3) {  // lanes past the chunk or the prompt read zeros
       const uint32_t off = static_cast<uint32_t>(lane * H * 4);
@@ -382,34 +377,25 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     // ---- 1. this chunk's rows of K, Q, V (zeros past the end) into LDS; ||k||^2; decays
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
+      const int pc = tid + i * kThreads, tok = pc / KP, seg = pc % KP;
       if (pc < NPK) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          st_kperm8(&sh.k[(tok + s2) * KS], seg * 8, nk[i][s2]);
-          st_kperm8(&sh.q[(tok + s2) * KS], seg * 8, nq[i][s2]);
-        }
+        st_kperm8(&sh.k[tok * KS], seg * 8, nk[i]);
+        st_kperm8(&sh.q[tok * KS], seg * 8, nq[i]);
         if (kla) {
+          float f[8];
+          unpack8(nk[i], f);
+          float ss = 0.f;
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            float f[8];
-            unpack8(nk[i][s2], f);
-            float ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
-            ss = group_sum<KP>(ss);
-            if (seg == 0) sh.knorm[tok + s2] = ss;
-          }
+          for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+          ss = group_sum<KP>(ss);
+          if (seg == 0) sh.knorm[tok] = ss;
         }
       }
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
-      const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
-      if (pc < NPV) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) *reinterpret_cast<uint4*>(&sh.v[(tok + s2) * VS + seg * 8]) = nv[i][s2];
-      }
+      const int pc = tid + i * kThreads, tok = pc / VP, seg = pc % VP;
+      if (pc < NPV) *reinterpret_cast<uint4*>(&sh.v[tok * VS + seg * 8]) = nv[i];
     }
     if (wave == 3) {
       // lanes 0..31: one token each; inclusive prefix sum of the clamped log2 decays
@@ -725,10 +711,10 @@ __global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs
 
   const bool kla = a.eta != nullptr;
   constexpr int KP = DK / 8, VP = DV / 8;
-  constexpr int NPK = C / 2 * KP, NPV = C / 2 * VP;
+  constexpr int NPK = C * KP, NPV = C * VP;  // (token, piece) jobs
   constexpr int LK = (NPK + NT - 1) / NT, LV = (NPV + NT - 1) / NT;
   constexpr int ND = C * DK / 4 / NT;  // float4 decay pieces per thread
-  uint4 nk[LK][2], nq[LK][2], nv[LV][2];
+  uint4 nk[LK], nq[LK], nv[LV];
   float4 nd[ND];
   float nbt = 0.f;
   auto rows_of = [&](const void* x, int t0, int bytes_per_row) { return chunk_rows(x, bseq, h, T, H, t0, bytes_per_row); };
@@ -737,20 +723,15 @@ __global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs
     const auto rd = rows_of(a.decay, t0, 4 * DK);
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int pc = tid + i * NT, tok = 2 * (pc / KP), seg = pc % KP;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const uint32_t off = static_cast<uint32_t>(((tok + s2) * H * DK + seg * 8) * 2);
-        nk[i][s2] = bload16(rk, off);
-        nq[i][s2] = bload16(rq, off);
-      }
+      const int pc = tid + i * NT, tok = pc / KP, seg = pc % KP;  // jobs past the chunk read zeros
+      const uint32_t off = static_cast<uint32_t>((tok * H * DK + seg * 8) * 2);
+      nk[i] = bload16(rk, off);
+      nq[i] = bload16(rq, off);
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
-      const int pc = tid + i * NT, tok = 2 * (pc / VP), seg = pc % VP;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        nv[i][s2] = bload16(rv, static_cast<uint32_t>(((tok + s2) * H * DV + seg * 8) * 2));
+      const int pc = tid + i * NT, tok = pc / VP, seg = pc % VP;
+      nv[i] = bload16(rv, static_cast<uint32_t>((tok * H * DV + seg * 8) * 2));
     }
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
@@ -770,34 +751,25 @@ __global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs
     // ---- 1. K, Q and V rows; clamped log2 decays; ||k||^2; step sizes
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int pc = tid + i * NT, tok = 2 * (pc / KP), seg = pc % KP;
+      const int pc = tid + i * NT, tok = pc / KP, seg = pc % KP;
       if (pc < NPK) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          *reinterpret_cast<uint4*>(&sh.k[(tok + s2) * KS + seg * 8]) = nk[i][s2];
-          *reinterpret_cast<uint4*>(&sh.q[(tok + s2) * KS + seg * 8]) = nq[i][s2];
-        }
+        *reinterpret_cast<uint4*>(&sh.k[tok * KS + seg * 8]) = nk[i];
+        *reinterpret_cast<uint4*>(&sh.q[tok * KS + seg * 8]) = nq[i];
         if (kla) {
+          float f[8];
+          unpack8(nk[i], f);
+          float ss = 0.f;
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            float f[8];
-            unpack8(nk[i][s2], f);
-            float ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
-            ss = group_sum<KP>(ss);
-            if (seg == 0) sh.knorm[tok + s2] = ss;
-          }
+          for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+          ss = group_sum<KP>(ss);
+          if (seg == 0) sh.knorm[tok] = ss;
         }
       }
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
-      const int pc = tid + i * NT, tok = 2 * (pc / VP), seg = pc % VP;
-      if (pc < NPV) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) *reinterpret_cast<uint4*>(&sh.v[(tok + s2) * VS + seg * 8]) = nv[i][s2];
-      }
+      const int pc = tid + i * NT, tok = pc / VP, seg = pc % VP;
+      if (pc < NPV) *reinterpret_cast<uint4*>(&sh.v[tok * VS + seg * 8]) = nv[i];
     }
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
@@ -1213,10 +1185,10 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
   for (int ch = tid; ch < DK; ch += kThreads) sh.bonus[ch] = a.bonus[h * DK + ch];
 
   constexpr int KP = DK / 8, VP = DV / 8;
-  constexpr int NPK = C / 2 * KP, NPV = C / 2 * VP;
+  constexpr int NPK = C * KP, NPV = C * VP;  // (token, piece) jobs
   constexpr int LK = (NPK + kThreads - 1) / kThreads, LV = (NPV + kThreads - 1) / kThreads;
   constexpr int ND = C * DK / 4 / kThreads;
-  uint4 nk[LK][2], nq[LK][2], nv[LV][2];
+  uint4 nk[LK], nq[LK], nv[LV];
   float4 nd[ND];
   auto rows_of = [&](const void* x, int t0, int bytes_per_row) { return chunk_rows(x, bseq, h, T, H, t0, bytes_per_row); };
   auto fetch = [&](int t0) {  // rows past the prompt read as zeros
@@ -1224,20 +1196,15 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
     const auto rd = rows_of(a.decay, t0, 4 * DK);
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const uint32_t off = static_cast<uint32_t>(((tok + s2) * H * DK + seg * 8) * 2);
-        nk[i][s2] = bload16(rk, off);
-        nq[i][s2] = bload16(rq, off);
-      }
+      const int pc = tid + i * kThreads, tok = pc / KP, seg = pc % KP;  // jobs past the chunk read zeros
+      const uint32_t off = static_cast<uint32_t>((tok * H * DK + seg * 8) * 2);
+      nk[i] = bload16(rk, off);
+      nq[i] = bload16(rq, off);
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
-      const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        nv[i][s2] = bload16(rv, static_cast<uint32_t>(((tok + s2) * H * DV + seg * 8) * 2));
+      const int pc = tid + i * kThreads, tok = pc / VP, seg = pc % VP;
+      nv[i] = bload16(rv, static_cast<uint32_t>((tok * H * DV + seg * 8) * 2));
     }
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
@@ -1254,22 +1221,16 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
     // ---- 1. K, R and V rows; clamped log2 decays
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int pc = tid + i * kThreads, tok = 2 * (pc / KP), seg = pc % KP;
+      const int pc = tid + i * kThreads, tok = pc / KP, seg = pc % KP;
       if (pc < NPK) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          *reinterpret_cast<uint4*>(&sh.k[(tok + s2) * KS + seg * 8]) = nk[i][s2];
-          *reinterpret_cast<uint4*>(&sh.q[(tok + s2) * KS + seg * 8]) = nq[i][s2];
-        }
+        *reinterpret_cast<uint4*>(&sh.k[tok * KS + seg * 8]) = nk[i];
+        *reinterpret_cast<uint4*>(&sh.q[tok * KS + seg * 8]) = nq[i];
       }
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
-      const int pc = tid + i * kThreads, tok = 2 * (pc / VP), seg = pc % VP;
-      if (pc < NPV) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) *reinterpret_cast<uint4*>(&sh.v[(tok + s2) * VS + seg * 8]) = nv[i][s2];
-      }
+      const int pc = tid + i * kThreads, tok = pc / VP, seg = pc % VP;
+      if (pc < NPV) *reinterpret_cast<uint4*>(&sh.v[tok * VS + seg * 8]) = nv[i];
     }
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
