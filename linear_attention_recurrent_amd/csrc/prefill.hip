@@ -1143,18 +1143,21 @@ struct PrefillRwkvLds {
   float bonus[DK];
   float glast[DK];                    // 2^c of the chunk's last token per channel
   float pd[C];                        // the bonus diagonal of P
-  float part[2 * 3 * 4 * 64];         // per-wave partial sums of P
   uint16_t pmh[C * TB], pml[C * TB];  // P, split
   uint16_t k[C * KS];                // K, token rows
   uint16_t q[C * KS];                // R, token rows
   uint16_t rgh[C * KS], rgl[C * KS];  // R o G_prev, token rows, split, k order
   uint16_t v[C * VS];                 // V, token rows
   uint16_t kdh[C * RS], kdl[C * RS];  // K o G_C / G, token rows, split
-  float cc[C * CS];                   // log2 decays, then their prefix sums
+  union {
+    float cc[C * CS];              // log2 decays, then their prefix sums
+    float part[2 * 3 * 4 * 64];    // after the last read of cc: per-wave partial sums of P
+  };
 };
 
+// 64 x 64 tiles fit three workgroups per CU (52 KB of LDS, at most 168 VGPRs).
 template <int DK, int DV, bool BF>
-__global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, PrefillArgs a) {
+__global__ void __launch_bounds__(kThreads, DK == 64 && DV == 64 ? 3 : 1) prefill_rwkv_kernel(PoolArgs pa, PrefillArgs a) {
   constexpr int C = kChunk;
   constexpr int CW = DV / 4;
   constexpr int NCB = CW / 16;
@@ -1347,6 +1350,7 @@ __global__ void __launch_bounds__(kThreads) prefill_rwkv_kernel(PoolArgs pa, Pre
           acc[2] = mma3(RB, C11, acc[2]);
         }
       }
+      __syncthreads();  // part overlays cc
       if (ks0 < NKW) {  // part[channel-step slot][block][r][lane]
 #pragma unroll
         for (int m = 0; m < 3; ++m) {
