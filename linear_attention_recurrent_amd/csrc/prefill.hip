@@ -274,8 +274,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rows(float* out, size_t bs
   const int rows = T - t0 < C ? T - t0 : C;
   return make_rsrc(out + (bseq * T + t0) * H * DV, rows * H * DV * 4);
 }
-__device__ __forceinline__ void st_out(__amdgpu_buffer_rsrc_t r, uint32_t off, float x) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+// Four consecutive columns of one output row in one 16-byte store.  The output products
+// are formed transposed (the operands of the MFMA swapped), so a lane's four accumulator
+// rows are four adjacent value columns of a single token.
+__device__ __forceinline__ void st_out4(__amdgpu_buffer_rsrc_t r, uint32_t off, const f32x4 x) {
+  using u32x4 = __attribute__((ext_vector_type(4))) unsigned int;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, off, 0, 0);
 }
 
 template <int DK, int DV>
@@ -486,8 +490,11 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     //            exact bf16 operands); R = V - diag(g) X in fp32 at X's accumulator
     //            positions (tokens 4 lg + r and 16 + 4 lg + r), which makes R the B operand
     //            of U = T diag(b) R with the tokens paired the same way in the A operand;
-    //            and diag(g) Q S for the outputs
+    //            and (diag(g) Q S)^T for the outputs (S as the A operand: lanes hold tokens)
+    //            S is replaced by g_C S (the first term of the update in step 10) as it is
+    //            split, so the split's remainders are formed in the old S's registers
     float U[2][NCB][4], O[2][NCB][4];
+    const float gC = sh.gam[C - 1], cC = sh.c[C - 1];
     {
       f32x4 xs[2][NCB], qs[2][NCB];
 #pragma unroll
@@ -501,7 +508,17 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
       for (int kp = 0; kp < NKP; ++kp) {
         bf16x8 shi[NCB], slo[NCB];
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) split_pair(S[2 * kp][cb], S[2 * kp + 1][cb], shi[cb], slo[cb]);
+        for (int cb = 0; cb < NCB; ++cb) {
+          float x0[4], x1[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x0[r] = S[2 * kp][cb][r];
+            x1[r] = S[2 * kp + 1][cb][r];
+            S[2 * kp][cb][r] = gC * x0[r];
+            S[2 * kp + 1][cb][r] = gC * x1[r];
+          }
+          split_pair(x0, x1, shi[cb], slo[cb]);
+        }
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
           const int rowk = (16 * ib + ln) * KS + 32 * kp + 8 * lg;  // channels 32 kp + 4 lg + {0..3, 16..19}
@@ -511,8 +528,8 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
           for (int cb = 0; cb < NCB; ++cb) {
             xs[ib][cb] = mma(ka, shi[cb], xs[ib][cb]);
             xs[ib][cb] = mma(ka, slo[cb], xs[ib][cb]);
-            qs[ib][cb] = mma(qa, shi[cb], qs[ib][cb]);
-            qs[ib][cb] = mma(qa, slo[cb], qs[ib][cb]);
+            qs[ib][cb] = mma(shi[cb], qa, qs[ib][cb]);
+            qs[ib][cb] = mma(slo[cb], qa, qs[ib][cb]);
           }
         }
       }
@@ -540,15 +557,26 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             U[ib][cb][r] = acc[r];
-            O[ib][cb][r] = sh.gam[16 * ib + 4 * lg + r] * qs[ib][cb][r];
+            O[ib][cb][r] = sh.gam[16 * ib + ln] * qs[ib][cb][r];
           }
         }
       }
     }
 
-    // ---- 9. O += (M o Q K^T) U; write the outputs
+    // ---- 9. O^T += U^T (M o Q K^T)^T; write the outputs (lane: token 16 ib + ln,
+    //         columns 16 cb + 4 lg .. + 3).  diag(2^(c_C - c_j)) U, the factor of the
+    //         update in step 10, is formed first, so the split below consumes U.
+    float U2[2][NCB][4];
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float f = fexp2(cC - sh.c[16 * ib + 4 * lg + r]);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) U2[ib][cb][r] = U[ib][cb][r] * f;
+      }
     const auto orows = out_rows(a.out, bseq, T, H, DV, t0, C);
-    const uint32_t olane = static_cast<uint32_t>((4 * lg * H + static_cast<int>(h)) * DV + col0 + ln) * 4;
+    const uint32_t olane = static_cast<uint32_t>((ln * H + static_cast<int>(h)) * DV + col0 + 4 * lg) * 4;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       bf16x8 uhi, ulo;
@@ -558,36 +586,25 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
         const int rowp = (16 * ib + ln) * TB + 8 * lg;
         const bf16x8 pah = ld_b128(&sh.pmh[rowp]);
         const bf16x8 pal = ld_b128(&sh.pml[rowp]);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma(pah, uhi, acc);
-        acc = mma(pah, ulo, acc);
-        acc = mma(pal, uhi, acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          st_out(orows, olane + static_cast<uint32_t>((16 * ib + r) * H * DV + 16 * cb) * 4, O[ib][cb][r] + acc[r]);
+        f32x4 acc = {O[ib][cb][0], O[ib][cb][1], O[ib][cb][2], O[ib][cb][3]};
+        acc = mma(uhi, pah, acc);
+        acc = mma(ulo, pah, acc);
+        acc = mma(uhi, pal, acc);
+        st_out4(orows, olane + static_cast<uint32_t>(16 * ib * H * DV + 16 * cb) * 4, acc);
       }
     }
 
-    // ---- 10. S = g_C S + K^T (diag(2^(c_C - c_j)) U)
-    const float gC = sh.gam[C - 1], cC = sh.c[C - 1];
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float f = fexp2(cC - sh.c[16 * ib + 4 * lg + r]);
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) U[ib][cb][r] *= f;
-      }
+    // ---- 10. S = g_C S + K^T (diag(2^(c_C - c_j)) U), g_C S formed in step 7
     bf16x8 u2hi[NCB], u2lo[NCB];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) split_pair(U[0][cb], U[1][cb], u2hi[cb], u2lo[cb]);
+    for (int cb = 0; cb < NCB; ++cb) split_pair(U2[0][cb], U2[1][cb], u2hi[cb], u2lo[cb]);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       // K^T, tokens as U's rows; this lane's 4 channels 16 kb + 4 (ln % 4) in storage order
       const bf16x8 ka = ld_tr8_at(sh.k, KS, 4 * lg, 16 + 4 * lg, kperm(16 * kb + 4 * (ln & 3)), ln);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        f32x4 acc = {gC * S[kb][cb][0], gC * S[kb][cb][1], gC * S[kb][cb][2], gC * S[kb][cb][3]};
+        f32x4 acc = {S[kb][cb][0], S[kb][cb][1], S[kb][cb][2], S[kb][cb][3]};
         acc = mma(ka, u2hi[cb], acc);
         acc = mma(ka, u2lo[cb], acc);
 #pragma unroll
@@ -1005,9 +1022,11 @@ __global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs
     }
     __syncthreads();
 
-    // ---- 7, 8. X = (K o G) S and (Q o G) S (split operands, S one channel-block pair at a
-    //            time); R = V - X in fp32 at X's accumulator positions, the B operand of
-    //            U = T diag(b) R
+    // ---- 7, 8. X = (K o G) S and ((Q o G) S)^T (split operands, S one channel-block pair
+    //            at a time; S is the A operand of the second, so its lanes hold tokens);
+    //            R = V - X in fp32 at X's accumulator positions, the B operand of
+    //            U = T diag(b) R.  S is replaced by diag(G_C) S (the first term of the
+    //            update in step 10) as it is split, so the split consumes the old S.
     float U[2][NCB][4], O[2][NCB][4];
     {
       f32x4 xs[2][NCB], qs[2][NCB];
@@ -1021,8 +1040,20 @@ __global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs
 #pragma unroll
       for (int kp = 0; kp < NKP; ++kp) {
         bf16x8 shi[NCB], slo[NCB];
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(&sh.glast[32 * kp + 4 * lg]);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sh.glast[32 * kp + 16 + 4 * lg]);
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) split_pair(S[2 * kp][cb], S[2 * kp + 1][cb], shi[cb], slo[cb]);
+        for (int cb = 0; cb < NCB; ++cb) {
+          float x0[4], x1[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x0[r] = S[2 * kp][cb][r];
+            x1[r] = S[2 * kp + 1][cb][r];
+            S[2 * kp][cb][r] = g0[r] * x0[r];
+            S[2 * kp + 1][cb][r] = g1[r] * x1[r];
+          }
+          split_pair(x0, x1, shi[cb], slo[cb]);
+        }
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
           const int rowk = (16 * ib + ln) * KS + 32 * kp + 8 * lg;  // channels 32 kp + 4 lg + {0..3, 16..19}
@@ -1033,9 +1064,9 @@ __global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs
             xs[ib][cb] = mma(kah, shi[cb], xs[ib][cb]);
             xs[ib][cb] = mma(kah, slo[cb], xs[ib][cb]);
             xs[ib][cb] = mma(kal, shi[cb], xs[ib][cb]);
-            qs[ib][cb] = mma(qah, shi[cb], qs[ib][cb]);
-            qs[ib][cb] = mma(qah, slo[cb], qs[ib][cb]);
-            qs[ib][cb] = mma(qal, shi[cb], qs[ib][cb]);
+            qs[ib][cb] = mma(shi[cb], qah, qs[ib][cb]);
+            qs[ib][cb] = mma(slo[cb], qah, qs[ib][cb]);
+            qs[ib][cb] = mma(shi[cb], qal, qs[ib][cb]);
           }
         }
       }
@@ -1069,44 +1100,38 @@ __global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs
       }
     }
 
-    // ---- 9. O += P U; outputs
+    // ---- 9. O^T += U^T P^T; outputs (lane: token 16 ib + ln, columns 16 cb + 4 lg .. + 3).
+    //         U's split serves here and in step 10.
+    bf16x8 uhi[NCB], ulo[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) split_pair(U[0][cb], U[1][cb], uhi[cb], ulo[cb]);
     const auto orows = out_rows(a.out, bseq, T, H, DV, t0, C);
-    const uint32_t olane = static_cast<uint32_t>((4 * lg * H + static_cast<int>(h)) * DV + col0 + ln) * 4;
+    const uint32_t olane = static_cast<uint32_t>((ln * H + static_cast<int>(h)) * DV + col0 + 4 * lg) * 4;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      bf16x8 uhi, ulo;
-      split_pair(U[0][cb], U[1][cb], uhi, ulo);
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib) {
         const int rowp = (16 * ib + ln) * TB + 8 * lg;
         const bf16x8 pah = ld_b128(&sh.pmh[rowp]), pal = ld_b128(&sh.pml[rowp]);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma(pah, uhi, acc);
-        acc = mma(pah, ulo, acc);
-        acc = mma(pal, uhi, acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          st_out(orows, olane + static_cast<uint32_t>((16 * ib + r) * H * DV + 16 * cb) * 4, O[ib][cb][r] + acc[r]);
+        f32x4 acc = {O[ib][cb][0], O[ib][cb][1], O[ib][cb][2], O[ib][cb][3]};
+        acc = mma(uhi[cb], pah, acc);
+        acc = mma(ulo[cb], pah, acc);
+        acc = mma(uhi[cb], pal, acc);
+        st_out4(orows, olane + static_cast<uint32_t>(16 * ib * H * DV + 16 * cb) * 4, acc);
       }
     }
 
-    // ---- 10. S = diag(G_C) S + (K o G_C / G)^T U
-    bf16x8 u2hi[NCB], u2lo[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) split_pair(U[0][cb], U[1][cb], u2hi[cb], u2lo[cb]);
+    // ---- 10. S = diag(G_C) S + (K o G_C / G)^T U, diag(G_C) S formed in step 7
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const bf16x8 kah = ld_tr8(sh.kdh, RS, 4 * lg, 16 + 4 * lg, 16 * kb, ln);  // tokens as U's rows
       const bf16x8 kal = ld_tr8(sh.kdl, RS, 4 * lg, 16 + 4 * lg, 16 * kb, ln);
-      float gl[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) gl[r] = sh.glast[16 * kb + 4 * lg + r];
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        f32x4 acc = {gl[0] * S[kb][cb][0], gl[1] * S[kb][cb][1], gl[2] * S[kb][cb][2], gl[3] * S[kb][cb][3]};
-        acc = mma(kah, u2hi[cb], acc);
-        acc = mma(kah, u2lo[cb], acc);
-        acc = mma(kal, u2hi[cb], acc);
+        f32x4 acc = {S[kb][cb][0], S[kb][cb][1], S[kb][cb][2], S[kb][cb][3]};
+        acc = mma(kah, uhi[cb], acc);
+        acc = mma(kah, ulo[cb], acc);
+        acc = mma(kal, uhi[cb], acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) S[kb][cb][r] = acc[r];
       }
@@ -1422,7 +1447,8 @@ __global__ void __launch_bounds__(kThreads, DK == 64 && DV == 64 ? 3 : 1) prefil
     }
     __syncthreads();
 
-    // ---- 5. O = (R o G_prev) S + P V; outputs
+    // ---- 5. O^T = S^T (R o G_prev)^T + V^T P^T (the operands swapped: each lane holds four
+    //         adjacent columns of one token, token 16 ib + ln, columns 16 cb + 4 lg .. + 3)
     float O[2][NCB][4];
     {
       f32x4 qs[2][NCB];
@@ -1432,18 +1458,32 @@ __global__ void __launch_bounds__(kThreads, DK == 64 && DV == 64 ? 3 : 1) prefil
         for (int cb = 0; cb < NCB; ++cb) qs[ib][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kp = 0; kp < NKP; ++kp) {
+        // S is replaced by diag(G_C) S (the first term of the update in step 6) as it is
+        // split, so the split consumes the old S
         bf16x8 shi[NCB], slo[NCB];
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(&sh.glast[32 * kp + 4 * lg]);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sh.glast[32 * kp + 16 + 4 * lg]);
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) split_pair(S[2 * kp][cb], S[2 * kp + 1][cb], shi[cb], slo[cb]);
+        for (int cb = 0; cb < NCB; ++cb) {
+          float x0[4], x1[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x0[r] = S[2 * kp][cb][r];
+            x1[r] = S[2 * kp + 1][cb][r];
+            S[2 * kp][cb][r] = g0[r] * x0[r];
+            S[2 * kp + 1][cb][r] = g1[r] * x1[r];
+          }
+          split_pair(x0, x1, shi[cb], slo[cb]);
+        }
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) {
           const int rowk = (16 * ib + ln) * KS + 32 * kp + 8 * lg;  // channels 32 kp + 4 lg + {0..3, 16..19}
           const bf16x8 rah = ld_b128(&sh.rgh[rowk]), ral = ld_b128(&sh.rgl[rowk]);
 #pragma unroll
           for (int cb = 0; cb < NCB; ++cb) {
-            qs[ib][cb] = mma(rah, shi[cb], qs[ib][cb]);
-            qs[ib][cb] = mma(rah, slo[cb], qs[ib][cb]);
-            qs[ib][cb] = mma(ral, shi[cb], qs[ib][cb]);
+            qs[ib][cb] = mma(shi[cb], rah, qs[ib][cb]);
+            qs[ib][cb] = mma(slo[cb], rah, qs[ib][cb]);
+            qs[ib][cb] = mma(shi[cb], ral, qs[ib][cb]);
           }
         }
       }
@@ -1455,8 +1495,8 @@ __global__ void __launch_bounds__(kThreads, DK == 64 && DV == 64 ? 3 : 1) prefil
           for (int r = 0; r < 4; ++r) O[ib][cb][r] = qs[ib][cb][r];
     }
     const auto orows = out_rows(a.out, bseq, T, H, DV, t0, C);
-    const uint32_t olane = static_cast<uint32_t>((4 * lg * H + static_cast<int>(h)) * DV + col0 + ln) * 4;
-    bf16x8 vb[NCB];  // V[token 8 lg + s][this lane's column], the B operand of P V and of the update
+    const uint32_t olane = static_cast<uint32_t>((ln * H + static_cast<int>(h)) * DV + col0 + 4 * lg) * 4;
+    bf16x8 vb[NCB];  // V[token 8 lg + s][this lane's column]: the A operand of V^T P^T, the B operand of the update
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
       vb[cb] = ld_tr8(sh.v, VS, 8 * lg, 8 * lg + 4, col0 + 16 * cb, ln);
@@ -1466,26 +1506,21 @@ __global__ void __launch_bounds__(kThreads, DK == 64 && DV == 64 ? 3 : 1) prefil
       const bf16x8 pal = ld_b128(&sh.pml[(16 * ib + ln) * TB + 8 * lg]);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mma(pah, vb[cb], acc);
-        acc = mma(pal, vb[cb], acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          st_out(orows, olane + static_cast<uint32_t>((16 * ib + r) * H * DV + 16 * cb) * 4, O[ib][cb][r] + acc[r]);
+        f32x4 acc = {O[ib][cb][0], O[ib][cb][1], O[ib][cb][2], O[ib][cb][3]};
+        acc = mma(vb[cb], pah, acc);
+        acc = mma(vb[cb], pal, acc);
+        st_out4(orows, olane + static_cast<uint32_t>(16 * ib * H * DV + 16 * cb) * 4, acc);
       }
     }
 
-    // ---- 6. S = diag(G_C) S + (K o G_C / G)^T V
+    // ---- 6. S = diag(G_C) S + (K o G_C / G)^T V, diag(G_C) S formed in step 5
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const bf16x8 kah = ld_tr8(sh.kdh, RS, 8 * lg, 8 * lg + 4, 16 * kb, ln);  // tokens 8 lg .. 8 lg + 7
       const bf16x8 kal = ld_tr8(sh.kdl, RS, 8 * lg, 8 * lg + 4, 16 * kb, ln);
-      float gl[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) gl[r] = sh.glast[16 * kb + 4 * lg + r];
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        f32x4 acc = {gl[0] * S[kb][cb][0], gl[1] * S[kb][cb][1], gl[2] * S[kb][cb][2], gl[3] * S[kb][cb][3]};
+        f32x4 acc = {S[kb][cb][0], S[kb][cb][1], S[kb][cb][2], S[kb][cb][3]};
         acc = mma(kah, vb[cb], acc);
         acc = mma(kal, vb[cb], acc);
 #pragma unroll
