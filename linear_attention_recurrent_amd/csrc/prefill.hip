@@ -206,35 +206,68 @@ __device__ __forceinline__ void st_base(__amdgpu_buffer_rsrc_t r, uint32_t voff,
 }
 
 
+// x_i -= g_i' y for i < N (N <= 4), where g' is g as held by lane P of this lane's row of
+// 16 lanes: one v_fmac_f32_dpp each, with a row_newbcast source (the broadcast and the
+// negation are operand modifiers).  The leading s_nop 1 gives the two wait states that a
+// DPP read of a VGPR needs after a VALU write of it (the compiler does not see into the
+// asm to add them); inside the block no instruction writes a DPP source.
+// one FMA: x operand i, g operand j, y operand k, P operand l
+#define DL_FNMA_BC(i, j, k, l) \
+  "v_fmac_f32_dpp %" #i ", -%" #j ", %" #k " row_newbcast:%" #l " row_mask:0xf bank_mask:0xf\n\t"
+template <int P, int N>
+__device__ __forceinline__ void fnma_row_bcast(float* x, const float* g, float y) {
+  static_assert(N >= 1 && N <= 4, "one to four rows");
+  if constexpr (N == 4)
+    asm volatile("s_nop 1\n\t" DL_FNMA_BC(0, 4, 8, 9) DL_FNMA_BC(1, 5, 8, 9) DL_FNMA_BC(2, 6, 8, 9)
+                     DL_FNMA_BC(3, 7, 8, 9)
+                 : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])
+                 : "v"(g[0]), "v"(g[1]), "v"(g[2]), "v"(g[3]), "v"(y), "n"(P));
+  else if constexpr (N == 3)
+    asm volatile("s_nop 1\n\t" DL_FNMA_BC(0, 3, 6, 7) DL_FNMA_BC(1, 4, 6, 7) DL_FNMA_BC(2, 5, 6, 7)
+                 : "+v"(x[0]), "+v"(x[1]), "+v"(x[2])
+                 : "v"(g[0]), "v"(g[1]), "v"(g[2]), "v"(y), "n"(P));
+  else if constexpr (N == 2)
+    asm volatile("s_nop 1\n\t" DL_FNMA_BC(0, 2, 4, 5) DL_FNMA_BC(1, 3, 4, 5)
+                 : "+v"(x[0]), "+v"(x[1])
+                 : "v"(g[0]), "v"(g[1]), "v"(y), "n"(P));
+  else
+    asm volatile("s_nop 1\n\t" DL_FNMA_BC(0, 1, 2, 3) : "+v"(x[0]) : "v"(g[0]), "v"(y), "n"(P));
+}
+#undef DL_FNMA_BC
+
+// Forward substitution steps P .. 14 for one 16 x 16 unit lower block, one column per
+// lane: once x_P is final, x_m -= A_mP x_P for every later row m (right-looking, so the
+// dependent chain is one FMA per row); A_mP is this lane's gc[m] as held by lane P.
+template <int P, int M = P + 1>
+__device__ __forceinline__ void substitute_from(float (&x)[16], const float (&gc)[16]) {
+  if constexpr (P < 15) {
+    constexpr int N = 16 - M < 4 ? 16 - M : 4;
+    fnma_row_bcast<P, N>(&x[M], &gc[M], x[P]);
+    if constexpr (M + N < 16) substitute_from<P, M + N>(x, gc);
+    else substitute_from<P + 1>(x, gc);
+  }
+}
+
 // T = (I + A)^-1 for a 32 x 32 strictly lower A (fp32 in LDS, row stride MS), by
-// blocks of 16: the two diagonal blocks by forward substitution (waves 0 and 1, lane j:
-// column j), then T_10 = -T_11 (A_10 T_00) with every thread computing one entry.  The
-// substitution is right-looking: once x_p is final it is subtracted from every later
-// row's residual, so the dependent chain is one FMA per row.  Lane j loads column j of
-// its diagonal block of A once; the factor A_mp that every lane needs at step p is then
-// lane p's register, broadcast with v_readlane (no further LDS round trips).  T's upper
-// right block must already be zero.  xs: 16 x 17 floats of scratch.  Called by the
-// whole workgroup (it synchronises); returns after a barrier.
-template <int MS>
+// blocks of 16: the two diagonal blocks by forward substitution (lane: column), either
+// both in wave 0 (ONE_WAVE: lanes 0..15 the first block, lanes 16..31 the second; half
+// the instructions) or one in each of waves 0 and 1 (lanes 0..15; half the latency), then
+// T_10 = -T_11 (A_10 T_00) with every thread computing one entry.  T's upper right block
+// must already be zero.  xs: 16 x 17 floats of scratch.  Called by the whole workgroup
+// (it synchronises); returns after a barrier.
+template <int MS, bool ONE_WAVE>
 __device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, float* xs, int tid) {
-  const int lane = tid & 63, wave = tid >> 6;
-  if (wave < 2 && lane < 16) {
-    const int o = 16 * wave;
-    int col = lane;
-    asm volatile("" : "+v"(col));  // keeps the 16 (m == col) selects inside the caller's loop
+  if (ONE_WAVE ? tid < 32 : (tid < 128 && (tid & 63) < 16)) {
+    const int o = ONE_WAVE ? (tid & 16) : (tid >> 6) * 16;
+    int col = tid & 15;
+    asm volatile("" : "+v"(col));  // keeps the 16 (m == col) selects as selects
     float gc[16], x[16];
+    gc[0] = 0.f;
 #pragma unroll
     for (int m = 1; m < 16; ++m) gc[m] = g[(o + m) * MS + o + col];  // A(o + m, o + col)
 #pragma unroll
     for (int m = 0; m < 16; ++m) x[m] = m == col ? 1.f : 0.f;
-#pragma unroll
-    for (int p = 0; p < 15; ++p) {
-      float f[16];  // column p of the block, read out of lane p before any of it is used
-#pragma unroll
-      for (int m = p + 1; m < 16; ++m) f[m] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gc[m]), p));
-#pragma unroll
-      for (int m = p + 1; m < 16; ++m) x[m] = fmaf(-f[m], x[p], x[m]);
-    }
+    substitute_from<0>(x, gc);
 #pragma unroll
     for (int m = 0; m < 16; ++m) t[(o + m) * MS + o + col] = x[m];
   }
@@ -464,7 +497,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     for (int e = tid; e < 16 * 16; e += kThreads) sh.t[(e / 16) * MS + 16 + e % 16] = 0.f;
 
     // ---- 4, 5. T = (I + A)^-1
-    invert_unit_lower32<MS>(sh.g, sh.t, sh.xs, tid);
+    invert_unit_lower32<MS, true>(sh.g, sh.t, sh.xs, tid);
 
     // ---- 6. T diag(b), split, in k order (the A operand of T diag(b) R below)
     {
@@ -1000,7 +1033,7 @@ __global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs
     __syncthreads();
 
     // ---- 5. T = (I + A)^-1
-    invert_unit_lower32<MS>(sh.g, sh.t, sh.xs, tid);
+    invert_unit_lower32<MS, true>(sh.g, sh.t, sh.xs, tid);
 
     // ---- 6. T diag(b), split, in k order (the A operand of T diag(b) R below)
     {
