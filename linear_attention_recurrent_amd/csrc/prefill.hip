@@ -249,16 +249,15 @@ __device__ __forceinline__ void substitute_from(float (&x)[16], const float (&gc
 }
 
 // T = (I + A)^-1 for a 32 x 32 strictly lower A (fp32 in LDS, row stride MS), by
-// blocks of 16: the two diagonal blocks by forward substitution (lane: column), either
-// both in wave 0 (ONE_WAVE: lanes 0..15 the first block, lanes 16..31 the second; half
-// the instructions) or one in each of waves 0 and 1 (lanes 0..15; half the latency), then
-// T_10 = -T_11 (A_10 T_00) with every thread computing one entry.  T's upper right block
-// must already be zero.  xs: 16 x 17 floats of scratch.  Called by the whole workgroup
-// (it synchronises); returns after a barrier.
-template <int MS, bool ONE_WAVE>
+// blocks of 16: the two diagonal blocks by forward substitution in wave 0 (lanes 0..15
+// the first block, lanes 16..31 the second; lane: column), then T_10 = -T_11 (A_10 T_00)
+// with every thread computing one entry.  T's upper right block must already be zero.
+// xs: 16 x 17 floats of scratch.  Called by the whole workgroup (it synchronises);
+// returns after a barrier.
+template <int MS>
 __device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, float* xs, int tid) {
-  if (ONE_WAVE ? tid < 32 : (tid < 128 && (tid & 63) < 16)) {
-    const int o = ONE_WAVE ? (tid & 16) : (tid >> 6) * 16;
+  if (tid < 32) {
+    const int o = tid & 16;
     int col = tid & 15;
     asm volatile("" : "+v"(col));  // keeps the 16 (m == col) selects as selects
     float gc[16], x[16];
@@ -497,7 +496,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     for (int e = tid; e < 16 * 16; e += kThreads) sh.t[(e / 16) * MS + 16 + e % 16] = 0.f;
 
     // ---- 4, 5. T = (I + A)^-1
-    invert_unit_lower32<MS, true>(sh.g, sh.t, sh.xs, tid);
+    invert_unit_lower32<MS>(sh.g, sh.t, sh.xs, tid);
 
     // ---- 6. T diag(b), split, in k order (the A operand of T diag(b) R below)
     {
@@ -1033,7 +1032,7 @@ __global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs
     __syncthreads();
 
     // ---- 5. T = (I + A)^-1
-    invert_unit_lower32<MS, true>(sh.g, sh.t, sh.xs, tid);
+    invert_unit_lower32<MS>(sh.g, sh.t, sh.xs, tid);
 
     // ---- 6. T diag(b), split, in k order (the A operand of T diag(b) R below)
     {
