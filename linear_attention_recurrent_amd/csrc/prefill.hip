@@ -271,18 +271,29 @@ __device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, fl
     for (int m = 0; m < 16; ++m) t[(o + m) * MS + o + col] = x[m];
   }
   __syncthreads();
-  const int i = (tid >> 4) & 15, j = tid & 15;  // the first 256 threads: one entry each
+  // the first 256 threads: one entry each; rows of A and T are read 4 at a time (MS is a
+  // multiple of 4), the sums still run over m in order
+  static_assert(MS % 4 == 0, "16-byte row reads");
+  const int i = (tid >> 4) & 15, j = tid & 15;
   if (tid < 256) {
     float s = 0.f;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) s = fmaf(g[(16 + i) * MS + m], t[m * MS + j], s);
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 a4 = *reinterpret_cast<const f32x4*>(&g[(16 + i) * MS + 4 * q]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s = fmaf(a4[u], t[(4 * q + u) * MS + j], s);
+    }
     xs[i * 17 + j] = s;
   }
   __syncthreads();
   if (tid < 256) {
     float y = 0.f;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) y = fmaf(t[(16 + i) * MS + 16 + m], xs[m * 17 + j], y);
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 t4 = *reinterpret_cast<const f32x4*>(&t[(16 + i) * MS + 16 + 4 * q]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) y = fmaf(t4[u], xs[(4 * q + u) * 17 + j], y);
+    }
     t[(16 + i) * MS + j] = -y;
   }
   __syncthreads();
@@ -322,7 +333,7 @@ struct PrefillLds {
   static constexpr int KS = DK + 16;  // K and Q (k order, kperm)
   static constexpr int VS = DV + 16;  // V
   static constexpr int TB = C + 16;   // split C x C matrices
-  static constexpr int MS = C + 1;    // fp32 row stride of the C x C matrices
+  static constexpr int MS = C + 4;    // fp32 row stride of the C x C matrices (16-byte rows)
   float c[C];      // cumulative log2 decay within the chunk
   float gam[C];    // 2^c
   float beta[C];   // step size (0 for tokens past the end)
@@ -468,27 +479,26 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     }
     __syncthreads();
 
-    // ---- 3. A = strictly lower b_i 2^(c_i - c_j) G_ij (in place); M o P split
+    // ---- 3. A = strictly lower b_i 2^(c_i - c_j) G_ij (in place); M o P split.  Thread:
+    //         columns j, j + 1 (adjacent in k order too) of rows i and i + 16
     {
-      const int j = tid % C;
-      const float cj = sh.c[j];
-      float pm[C * C / kThreads];
+      static_assert(C * C == 4 * kThreads, "four entries a thread");
+      const int j = 2 * (tid % 16);
+      const float cj0 = sh.c[j], cj1 = sh.c[j + 1];
 #pragma unroll
-      for (int e = 0; e < C * C / kThreads; ++e) {
-        const int i = tid / C + e * (kThreads / C);
-        const float dij = fexp2(fminf(sh.c[i] - cj, 0.f));  // used only where j <= i
-        if (j < i) sh.g[i * MS + j] *= sh.beta[i] * dij;
-        pm[e] = j <= i ? dij * sh.p[i * MS + j] : 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < C * C / kThreads; e += 2) {
-        const int i0 = tid / C + e * (kThreads / C), i1 = i0 + kThreads / C;
+      for (int e = 0; e < 2; ++e) {
+        const int i = tid / 16 + 16 * e;
+        const float ci = sh.c[i], bi = sh.beta[i];
+        const float d0 = fexp2(fminf(ci - cj0, 0.f)), d1 = fexp2(fminf(ci - cj1, 0.f));  // used where j <= i
+        float2 gv = *reinterpret_cast<const float2*>(&sh.g[i * MS + j]);
+        const float2 pv = *reinterpret_cast<const float2*>(&sh.p[i * MS + j]);
+        if (j < i) gv.x *= bi * d0;
+        if (j + 1 < i) gv.y *= bi * d1;
+        *reinterpret_cast<float2*>(&sh.g[i * MS + j]) = gv;
         uint32_t hi, lo;
-        split2(pm[e], pm[e + 1], hi, lo);
-        sh.pmh[i0 * TB + kperm(j)] = static_cast<uint16_t>(hi);
-        sh.pmh[i1 * TB + kperm(j)] = static_cast<uint16_t>(hi >> 16);
-        sh.pml[i0 * TB + kperm(j)] = static_cast<uint16_t>(lo);
-        sh.pml[i1 * TB + kperm(j)] = static_cast<uint16_t>(lo >> 16);
+        split2(j <= i ? d0 * pv.x : 0.f, j + 1 <= i ? d1 * pv.y : 0.f, hi, lo);
+        *reinterpret_cast<uint32_t*>(&sh.pmh[i * TB + kperm(j)]) = hi;
+        *reinterpret_cast<uint32_t*>(&sh.pml[i * TB + kperm(j)]) = lo;
       }
     }
     __syncthreads();
@@ -500,20 +510,18 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
 
     // ---- 6. T diag(b), split, in k order (the A operand of T diag(b) R below)
     {
-      const int j = tid % C;
-      const float bj = sh.beta[j];
-      float tv[C * C / kThreads];
+      // thread: columns j, j + 1 (adjacent in k order too) of C * C / (2 kThreads) rows
+      constexpr int RPT = C * C / (2 * kThreads);
+      const int j = 2 * (tid % 16);
+      const float b0 = sh.beta[j], b1 = sh.beta[j + 1];
 #pragma unroll
-      for (int e = 0; e < C * C / kThreads; ++e) tv[e] = sh.t[(tid / C + e * (kThreads / C)) * MS + j];
-#pragma unroll
-      for (int e = 0; e < C * C / kThreads; e += 2) {
-        const int i0 = tid / C + e * (kThreads / C), i1 = i0 + kThreads / C;
+      for (int e = 0; e < RPT; ++e) {
+        const int i = tid / 16 + e * (kThreads / 16);
+        const float2 tv = *reinterpret_cast<const float2*>(&sh.t[i * MS + j]);
         uint32_t hi, lo;
-        split2(tv[e] * bj, tv[e + 1] * bj, hi, lo);
-        sh.t1h[i0 * TB + kperm(j)] = static_cast<uint16_t>(hi);
-        sh.t1h[i1 * TB + kperm(j)] = static_cast<uint16_t>(hi >> 16);
-        sh.t1l[i0 * TB + kperm(j)] = static_cast<uint16_t>(lo);
-        sh.t1l[i1 * TB + kperm(j)] = static_cast<uint16_t>(lo >> 16);
+        split2(tv.x * b0, tv.y * b1, hi, lo);
+        *reinterpret_cast<uint32_t*>(&sh.t1h[i * TB + kperm(j)]) = hi;
+        *reinterpret_cast<uint32_t*>(&sh.t1l[i * TB + kperm(j)]) = lo;
       }
     }
     __syncthreads();
@@ -696,7 +704,7 @@ struct PrefillKdaLds {
   static constexpr int KS = DK + 16;  // K, Q, K o G and Q o G (the last two in k order, kperm)
   static constexpr int RS = DK + 16;  // bf16 row stride of K o G_C / G, and
   static constexpr int VS = DV + 16;  // of V: 8 mod 32 words (transposing reads)
-  static constexpr int MS = C + 1;    // fp32 row stride of the C x C matrices
+  static constexpr int MS = C + 4;    // fp32 row stride of the C x C matrices (16-byte rows)
   static constexpr int TB = C + 16;  // split C x C matrices
   static constexpr int CS = DK + 8;  // fp32 row stride of the per-channel decays
   float beta[C];
@@ -1036,20 +1044,18 @@ __global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs
 
     // ---- 6. T diag(b), split, in k order (the A operand of T diag(b) R below)
     {
-      const int j = tid % C;
-      const float bj = sh.beta[j];
-      float tv[C * C / NT];
+      // thread: columns j, j + 1 (adjacent in k order too) of C * C / (2 NT) rows
+      constexpr int RPT = C * C / (2 * NT);
+      const int j = 2 * (tid % 16);
+      const float b0 = sh.beta[j], b1 = sh.beta[j + 1];
 #pragma unroll
-      for (int e = 0; e < C * C / NT; ++e) tv[e] = sh.t[(tid / C + e * (NT / C)) * MS + j];
-#pragma unroll
-      for (int e = 0; e < C * C / NT; e += 2) {
-        const int i0 = tid / C + e * (NT / C), i1 = i0 + NT / C;
+      for (int e = 0; e < RPT; ++e) {
+        const int i = tid / 16 + e * (NT / 16);
+        const float2 tv = *reinterpret_cast<const float2*>(&sh.t[i * MS + j]);
         uint32_t hi, lo;
-        split2(tv[e] * bj, tv[e + 1] * bj, hi, lo);
-        sh.t1h[i0 * TB + kperm(j)] = static_cast<uint16_t>(hi);
-        sh.t1h[i1 * TB + kperm(j)] = static_cast<uint16_t>(hi >> 16);
-        sh.t1l[i0 * TB + kperm(j)] = static_cast<uint16_t>(lo);
-        sh.t1l[i1 * TB + kperm(j)] = static_cast<uint16_t>(lo >> 16);
+        split2(tv.x * b0, tv.y * b1, hi, lo);
+        *reinterpret_cast<uint32_t*>(&sh.t1h[i * TB + kperm(j)]) = hi;
+        *reinterpret_cast<uint32_t*>(&sh.t1l[i * TB + kperm(j)]) = lo;
       }
     }
     __syncthreads();
