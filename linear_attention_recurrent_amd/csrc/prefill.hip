@@ -248,14 +248,20 @@ __device__ __forceinline__ void substitute_from(float (&x)[16], const float (&gc
   }
 }
 
-// T = (I + A)^-1 for a 32 x 32 strictly lower A (fp32 in LDS, row stride MS), by
-// blocks of 16: the two diagonal blocks by forward substitution in wave 0 (lanes 0..15
-// the first block, lanes 16..31 the second; lane: column), then T_10 = -T_11 (A_10 T_00)
-// with every thread computing one entry.  T's upper right block must already be zero.
-// xs: 16 x 17 floats of scratch.  Called by the whole workgroup (it synchronises);
-// returns after a barrier.
-template <int MS>
-__device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, float* xs, int tid) {
+// T diag(b) for T = (I + A)^-1 and a 32 x 32 strictly lower A (fp32 in LDS, row stride
+// MS), split (hi, lo) into th and tl in k order (row stride TB): the A operand of
+// T diag(b) R.  By blocks of 16: the two diagonal blocks by forward substitution in wave 0
+// (lanes 0..15 the first block, lanes 16..31 the second; lane: column) into t (fp32);
+// then, on the first 256 threads, one entry each of Y = A_10 T_00, while 256 threads
+// (the same ones for a workgroup of 256, the next ones for 512) split the diagonal blocks
+// of T diag(b), two adjacent columns each; then T_10 = -T_11 Y, one entry a thread, times
+// b and split.  The upper right blocks of th and tl must already be zero.  xs: 16 x 17
+// floats of scratch.  Called by the whole workgroup (it synchronises); returns after a
+// barrier.
+template <int MS, int TB, int NT>
+__device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, float* xs, const float* b,
+                                                    uint16_t* th, uint16_t* tl, int tid) {
+  static_assert(NT == 256 || NT == 512, "workgroup of 256 or 512 threads");
   if (tid < 32) {
     const int o = tid & 16;
     int col = tid & 15;
@@ -271,8 +277,7 @@ __device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, fl
     for (int m = 0; m < 16; ++m) t[(o + m) * MS + o + col] = x[m];
   }
   __syncthreads();
-  // the first 256 threads: one entry each; rows of A and T are read 4 at a time (MS is a
-  // multiple of 4), the sums still run over m in order
+  // rows of A and T are read 4 at a time (MS is a multiple of 4); the sums run over m in order
   static_assert(MS % 4 == 0, "16-byte row reads");
   const int i = (tid >> 4) & 15, j = tid & 15;
   if (tid < 256) {
@@ -285,6 +290,17 @@ __device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, fl
     }
     xs[i * 17 + j] = s;
   }
+  {
+    const int sid = NT == 512 ? tid - 256 : tid;  // diagonal block o / 16, row r, columns c, c + 1
+    if (sid >= 0) {
+      const int o = (sid >> 7) * 16, r = (sid >> 3) & 15, c = 2 * (sid & 7);
+      const float2 tv = *reinterpret_cast<const float2*>(&t[(o + r) * MS + o + c]);
+      uint32_t hi, lo;
+      split2(tv.x * b[o + c], tv.y * b[o + c + 1], hi, lo);
+      *reinterpret_cast<uint32_t*>(&th[(o + r) * TB + kperm(o + c)]) = hi;
+      *reinterpret_cast<uint32_t*>(&tl[(o + r) * TB + kperm(o + c)]) = lo;
+    }
+  }
   __syncthreads();
   if (tid < 256) {
     float y = 0.f;
@@ -294,7 +310,10 @@ __device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, fl
 #pragma unroll
       for (int u = 0; u < 4; ++u) y = fmaf(t4[u], xs[(4 * q + u) * 17 + j], y);
     }
-    t[(16 + i) * MS + j] = -y;
+    uint32_t hi, lo;
+    split2(-y * b[j], 0.f, hi, lo);
+    th[(16 + i) * TB + kperm(j)] = static_cast<uint16_t>(hi);
+    tl[(16 + i) * TB + kperm(j)] = static_cast<uint16_t>(lo);
   }
   __syncthreads();
 }
@@ -342,12 +361,10 @@ struct PrefillLds {
   float g[C * MS];  // K K^T, then A (strictly lower part)
   union {
     float p[C * MS];  // Q K^T
-    float t[C * MS];  // then T = (I + A)^-1
+    float t[C * MS];  // then the diagonal blocks of T = (I + A)^-1
   };
-  union {
-    uint16_t t1h[C * TB];  // T diag(b) (hi part, k order)
-    float xs[16 * 17];     // before it: scratch for the off-diagonal block of T
-  };
+  float xs[16 * 17];     // scratch for the off-diagonal block of T
+  uint16_t t1h[C * TB];  // T diag(b) (hi part, k order; upper right block zero)
   uint16_t t1l[C * TB];
   uint16_t pmh[C * TB], pml[C * TB];  // M o Q K^T, k order
   uint16_t k[C * KS];  // K, token rows, k order
@@ -417,6 +434,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     }
   };
   fetch(0);
+  for (int e = tid; e < 16 * TB; e += kThreads) {  // rows 0..15 (tokens 16..31 stay zero)
+    sh.t1h[e] = 0;
+    sh.t1l[e] = 0;
+  }
 
   for (int t0 = 0; t0 < T; t0 += C) {
     __syncthreads();  // every wave is done with the previous chunk's LDS arrays
@@ -502,29 +523,10 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
       }
     }
     __syncthreads();
-    // T (aliasing P from here on): zero its upper-right block
-    for (int e = tid; e < 16 * 16; e += kThreads) sh.t[(e / 16) * MS + 16 + e % 16] = 0.f;
 
-    // ---- 4, 5. T = (I + A)^-1
-    invert_unit_lower32<MS>(sh.g, sh.t, sh.xs, tid);
-
-    // ---- 6. T diag(b), split, in k order (the A operand of T diag(b) R below)
-    {
-      // thread: columns j, j + 1 (adjacent in k order too) of C * C / (2 kThreads) rows
-      constexpr int RPT = C * C / (2 * kThreads);
-      const int j = 2 * (tid % 16);
-      const float b0 = sh.beta[j], b1 = sh.beta[j + 1];
-#pragma unroll
-      for (int e = 0; e < RPT; ++e) {
-        const int i = tid / 16 + e * (kThreads / 16);
-        const float2 tv = *reinterpret_cast<const float2*>(&sh.t[i * MS + j]);
-        uint32_t hi, lo;
-        split2(tv.x * b0, tv.y * b1, hi, lo);
-        *reinterpret_cast<uint32_t*>(&sh.t1h[i * TB + kperm(j)]) = hi;
-        *reinterpret_cast<uint32_t*>(&sh.t1l[i * TB + kperm(j)]) = lo;
-      }
-    }
-    __syncthreads();
+    // ---- 4, 5, 6. T = (I + A)^-1 (T aliasing P from here on); T diag(b), split, in k
+    //               order (the A operand of T diag(b) R below)
+    invert_unit_lower32<MS, TB, kThreads>(sh.g, sh.t, sh.xs, sh.beta, sh.t1h, sh.t1l, tid);
 
     // ---- 7, 8. X = K S and Q S (S split one channel-block pair at a time; K and Q are
     //            exact bf16 operands); R = V - diag(g) X in fp32 at X's accumulator
@@ -712,11 +714,9 @@ struct PrefillKdaLds {
   float knorm[C];
   float glast[DK];  // 2^c of the chunk's last token per channel
   float g[C * MS];  // A (strictly lower part)
-  float t[C * MS];  // T = (I + A)^-1
-  union {
-    uint16_t t1h[C * TB];  // T diag(b) (hi part, k order)
-    float xs[16 * 17];     // before it: scratch of the inverse
-  };
+  float t[C * MS];    // the diagonal blocks of T = (I + A)^-1
+  float xs[16 * 17];  // scratch of the inverse
+  uint16_t t1h[C * TB];  // T diag(b) (hi part, k order; upper right block zero)
   uint16_t t1l[C * TB];
   uint16_t pmh[C * TB], pml[C * TB];  // P (lower triangle, split, k order)
   uint16_t k[C * KS];  // K, token rows
@@ -853,7 +853,10 @@ __global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs
         sh.pmh[i * TB + kperm(j)] = 0;
         sh.pml[i * TB + kperm(j)] = 0;
       }
-      if (i < 16 && j >= 16) sh.t[i * MS + j] = 0.f;
+      if (i < 16 && j >= 16) {
+        sh.t1h[i * TB + kperm(j)] = 0;
+        sh.t1l[i * TB + kperm(j)] = 0;
+      }
     }
     __syncthreads();
 
@@ -1039,26 +1042,9 @@ __global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs
     }
     __syncthreads();
 
-    // ---- 5. T = (I + A)^-1
-    invert_unit_lower32<MS>(sh.g, sh.t, sh.xs, tid);
-
-    // ---- 6. T diag(b), split, in k order (the A operand of T diag(b) R below)
-    {
-      // thread: columns j, j + 1 (adjacent in k order too) of C * C / (2 NT) rows
-      constexpr int RPT = C * C / (2 * NT);
-      const int j = 2 * (tid % 16);
-      const float b0 = sh.beta[j], b1 = sh.beta[j + 1];
-#pragma unroll
-      for (int e = 0; e < RPT; ++e) {
-        const int i = tid / 16 + e * (NT / 16);
-        const float2 tv = *reinterpret_cast<const float2*>(&sh.t[i * MS + j]);
-        uint32_t hi, lo;
-        split2(tv.x * b0, tv.y * b1, hi, lo);
-        *reinterpret_cast<uint32_t*>(&sh.t1h[i * TB + kperm(j)]) = hi;
-        *reinterpret_cast<uint32_t*>(&sh.t1l[i * TB + kperm(j)]) = lo;
-      }
-    }
-    __syncthreads();
+    // ---- 5, 6. T = (I + A)^-1; T diag(b), split, in k order (the A operand of
+    //            T diag(b) R below)
+    invert_unit_lower32<MS, TB, NT>(sh.g, sh.t, sh.xs, sh.beta, sh.t1h, sh.t1l, tid);
 
     // ---- 7, 8. X = (K o G) S and ((Q o G) S)^T (split operands, S one channel-block pair
     //            at a time; S is the A operand of the second, so its lanes hold tokens);
