@@ -801,6 +801,18 @@ __global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs
                                                                  static_cast<uint32_t>(lane * H * 4), 0, 0));
   };
   fetch(0);
+  // entries above the diagonal of P and the upper right block of the split T: written once
+  for (int e = tid; e < C * C; e += NT) {
+    const int i = e / C, j = e % C;
+    if (j > i) {
+      sh.pmh[i * TB + kperm(j)] = 0;
+      sh.pml[i * TB + kperm(j)] = 0;
+    }
+    if (i < 16 && j >= 16) {
+      sh.t1h[i * TB + kperm(j)] = 0;
+      sh.t1l[i * TB + kperm(j)] = 0;
+    }
+  }
 
   for (int t0 = 0; t0 < T; t0 += C) {
     __syncthreads();
@@ -840,23 +852,11 @@ __global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs
     if (t0 + C < T) fetch(t0 + C);
     __syncthreads();
 
-    // ---- 2. prefix sums of the log2 decays over the chunk's tokens; step sizes; zero the
-    //         upper triangle of P and T's upper block
+    // ---- 2. prefix sums of the log2 decays over the chunk's tokens; step sizes
     prefix_over_tokens<DK, CS>(sh.cc, sh.glast, tid);
     if (tid < C) {
       const bool ok = t0 + tid < T;
       sh.beta[tid] = !ok ? 0.f : kla ? sh.braw[tid] / (sh.knorm[tid] + a.eps) : sh.braw[tid];
-    }
-    for (int e = tid; e < C * C; e += NT) {
-      const int i = e / C, j = e % C;
-      if (j > i) {
-        sh.pmh[i * TB + kperm(j)] = 0;
-        sh.pml[i * TB + kperm(j)] = 0;
-      }
-      if (i < 16 && j >= 16) {
-        sh.t1h[i * TB + kperm(j)] = 0;
-        sh.t1l[i * TB + kperm(j)] = 0;
-      }
     }
     __syncthreads();
 
