@@ -15,9 +15,9 @@
 // which is the token-by-token recurrence rewritten: unrolling u_i gives
 // (I + A) U = diag(b) (V - diag(g) K S).
 //
-// Mapping.  One workgroup (4 waves) per tile; wave w owns value columns
-// [w dv/4, (w+1) dv/4) of the state, held in MFMA accumulator layout, so the
-// dv dimension needs no communication between waves.  Chunk-shared matrices
+// Mapping.  One workgroup per tile (eight waves for dv = 128, else four); wave w owns
+// value columns [w dv/W, (w+1) dv/W) of the state (W waves), held in MFMA accumulator
+// layout, so the dv dimension needs no communication between waves.  Chunk-shared matrices
 // (K K^T, Q K^T, T diag(b)) are built once per chunk in LDS.  The state enters U as
 // U = T diag(b) (V - diag(g) X) with X = K S: X takes the exact bf16 keys against the
 // split state, R = V - diag(g) X is formed in fp32 where X sits in registers, and R
@@ -51,7 +51,7 @@ using u32x4 = __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t;
 using bf16x2 = __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16;
 
 constexpr int kChunk = 32;  // tokens per chunk
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // RWKV6 workgroup
 
 // 2^x with the bare hardware instruction (about 1 ulp).  Every argument here is a
 // difference of cumulative log2 decays; results below 2^-126 (the normal range)
@@ -372,10 +372,16 @@ struct PrefillLds {
   uint16_t v[C * VS];  // V, token rows
 };
 
+// Threads of a GDN workgroup: eight waves of 16 value columns each for dv = 128 (up to
+// 128 VGPRs, so four waves share each SIMD: two workgroups per CU), else four.
+template <int DV>
+constexpr int gdn_threads() { return DV == 128 ? 512 : 256; }
+
 template <int DK, int DV, bool BF>
-__global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, PrefillArgs a) {
+__global__ void __launch_bounds__(gdn_threads<DV>(), gdn_threads<DV>() == 512 ? 4 : 2) prefill_kernel(PoolArgs pa, PrefillArgs a) {
   constexpr int C = kChunk;
-  constexpr int CW = DV / 4;    // value columns per wave
+  constexpr int NT = gdn_threads<DV>(), NWV = NT / 64;  // threads, waves
+  constexpr int CW = DV / NWV;  // value columns per wave
   constexpr int NCB = CW / 16;  // 16-column blocks per wave
   constexpr int NKB = DK / 16;  // 16-channel blocks
   constexpr int NKP = DK / 32;  // pairs of channel blocks (one MFMA k-step each)
@@ -409,7 +415,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
   // each job is one 16-byte piece (8 channels) of one token.
   constexpr int KP = DK / 8, VP = DV / 8;                         // pieces per row
   constexpr int NPK = C * KP, NPV = C * VP;                       // (token, piece) jobs
-  constexpr int LK = (NPK + kThreads - 1) / kThreads, LV = (NPV + kThreads - 1) / kThreads;
+  constexpr int LK = (NPK + NT - 1) / NT, LV = (NPV + NT - 1) / NT;
   uint4 nk[LK], nq[LK], nv[LV];
   float ndec = 1.f, nbt = 0.f;
   auto rows_of = [&](const void* x, int t0, int bytes_per_row) { return chunk_rows(x, bseq, h, T, H, t0, bytes_per_row); };
@@ -417,14 +423,14 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     const auto rk = rows_of(a.k, t0, 2 * DK), rq = rows_of(a.q, t0, 2 * DK), rv = rows_of(a.v, t0, 2 * DV);
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int pc = tid + i * kThreads, tok = pc / KP, seg = pc % KP;  // jobs past the chunk read zeros
+      const int pc = tid + i * NT, tok = pc / KP, seg = pc % KP;  // jobs past the chunk read zeros
       const uint32_t off = static_cast<uint32_t>((tok * H * DK + seg * 8) * 2);
       nk[i] = bload16(rk, off);
       nq[i] = bload16(rq, off);
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
-      const int pc = tid + i * kThreads, tok = pc / VP, seg = pc % VP;
+      const int pc = tid + i * NT, tok = pc / VP, seg = pc % VP;
       nv[i] = bload16(rv, static_cast<uint32_t>((tok * H * DV + seg * 8) * 2));
     }
     if (wave == 3) {  // lanes past the chunk or the prompt read zeros
@@ -434,7 +440,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     }
   };
   fetch(0);
-  for (int e = tid; e < 16 * TB; e += kThreads) {  // rows 0..15 (tokens 16..31 stay zero)
+  for (int e = tid; e < 16 * TB; e += NT) {  // rows 0..15 (tokens 16..31 stay zero)
     sh.t1h[e] = 0;
     sh.t1l[e] = 0;
   }
@@ -445,7 +451,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     // ---- 1. this chunk's rows of K, Q, V (zeros past the end) into LDS; ||k||^2; decays
 #pragma unroll
     for (int i = 0; i < LK; ++i) {
-      const int pc = tid + i * kThreads, tok = pc / KP, seg = pc % KP;
+      const int pc = tid + i * NT, tok = pc / KP, seg = pc % KP;
       if (pc < NPK) {
         st_kperm8(&sh.k[tok * KS], seg * 8, nk[i]);
         st_kperm8(&sh.q[tok * KS], seg * 8, nq[i]);
@@ -462,7 +468,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     }
 #pragma unroll
     for (int i = 0; i < LV; ++i) {
-      const int pc = tid + i * kThreads, tok = pc / VP, seg = pc % VP;
+      const int pc = tid + i * NT, tok = pc / VP, seg = pc % VP;
       if (pc < NPV) *reinterpret_cast<uint4*>(&sh.v[tok * VS + seg * 8]) = nv[i];
     }
     if (wave == 3) {
@@ -477,11 +483,13 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
     if (t0 + C < T) fetch(t0 + C);
     __syncthreads();
 
-    // ---- 2. G = K K^T and P = Q K^T on the lower blocks (waves 0..2); step sizes (wave 3)
-    if (wave < 3) {
+    // ---- 2. G = K K^T and P = Q K^T on the lower blocks (six blocks over the first waves);
+    //         step sizes (the last wave)
+    constexpr int BPW = NWV >= 6 ? 1 : 2;  // blocks per wave
+    if (wave < 6 / BPW) {
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int blk = 2 * wave + e;  // 0..2: G blocks (0,0), (1,0), (1,1); 3..5: the same of P
+      for (int e = 0; e < BPW; ++e) {
+        const int blk = BPW * wave + e;  // 0..2: G blocks (0,0), (1,0), (1,1); 3..5: the same of P
         const int sub = blk % 3;
         const int ib = sub == 0 ? 0 : 1, jb = sub == 2 ? 1 : 0;
         const uint16_t* xa = blk < 3 ? sh.k : sh.q;
@@ -494,21 +502,21 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
 #pragma unroll
         for (int r = 0; r < 4; ++r) dst[(16 * ib + 4 * lg + r) * MS + 16 * jb + ln] = acc[r];
       }
-    } else if (lane < C) {
+    } else if (wave == NWV - 1 && lane < C) {
       const bool ok = t0 + lane < T;
       sh.beta[lane] = !ok ? 0.f : kla ? sh.braw[lane] / (sh.knorm[lane] + a.eps) : sh.braw[lane];
     }
     __syncthreads();
 
     // ---- 3. A = strictly lower b_i 2^(c_i - c_j) G_ij (in place); M o P split.  Thread:
-    //         columns j, j + 1 (adjacent in k order too) of rows i and i + 16
+    //         columns j, j + 1 (adjacent in k order too) of rows i, i + NT / 16, ...
     {
-      static_assert(C * C == 4 * kThreads, "four entries a thread");
+      constexpr int RPT = C * C / (2 * NT);  // rows a thread
       const int j = 2 * (tid % 16);
       const float cj0 = sh.c[j], cj1 = sh.c[j + 1];
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int i = tid / 16 + 16 * e;
+      for (int e = 0; e < RPT; ++e) {
+        const int i = tid / 16 + (NT / 16) * e;
         const float ci = sh.c[i], bi = sh.beta[i];
         const float d0 = fexp2(fminf(ci - cj0, 0.f)), d1 = fexp2(fminf(ci - cj1, 0.f));  // used where j <= i
         float2 gv = *reinterpret_cast<const float2*>(&sh.g[i * MS + j]);
@@ -526,7 +534,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_kernel(PoolArgs pa, Prefi
 
     // ---- 4, 5, 6. T = (I + A)^-1 (T aliasing P from here on); T diag(b), split, in k
     //               order (the A operand of T diag(b) R below)
-    invert_unit_lower32<MS, TB, kThreads>(sh.g, sh.t, sh.xs, sh.beta, sh.t1h, sh.t1l, tid);
+    invert_unit_lower32<MS, TB, NT>(sh.g, sh.t, sh.xs, sh.beta, sh.t1h, sh.t1l, tid);
 
     // ---- 7, 8. X = K S and Q S (S split one channel-block pair at a time; K and Q are
     //            exact bf16 operands); R = V - diag(g) X in fp32 at X's accumulator
@@ -1569,7 +1577,7 @@ hipError_t launch_prefill(int variant, bool bf16_base, int dk, int dv, int tiles
   do {                                                                              \
     if (variant == DL_KDA) prefill_kda_kernel<DK_, DV_, BF_><<<tiles, kda_threads<DV_>(), 0, stream>>>(p, a); \
     else if (variant == DL_RWKV6) prefill_rwkv_kernel<DK_, DV_, BF_><<<tiles, kThreads, 0, stream>>>(p, a); \
-    else prefill_kernel<DK_, DV_, BF_><<<tiles, kThreads, 0, stream>>>(p, a);        \
+    else prefill_kernel<DK_, DV_, BF_><<<tiles, gdn_threads<DV_>(), 0, stream>>>(p, a);        \
   } while (0)
 #define DL_PREFILL_SHAPES(BF_)                                  \
   do {                                                          \
