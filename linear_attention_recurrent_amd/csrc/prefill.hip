@@ -235,24 +235,30 @@ __device__ __forceinline__ void fnma_row_bcast(float* x, const float* g, float y
 }
 #undef DL_FNMA_BC
 
-// Forward substitution steps P .. 14 for one 16 x 16 unit lower block, one column per
-// lane: once x_P is final, x_m -= A_mP x_P for every later row m (right-looking, so the
-// dependent chain is one FMA per row); A_mP is this lane's gc[m] as held by lane P.
-template <int P, int M = P + 1>
-__device__ __forceinline__ void substitute_from(float (&x)[16], const float (&gc)[16]) {
-  if constexpr (P < 15) {
-    constexpr int N = 16 - M < 4 ? 16 - M : 4;
+// Forward substitution steps P .. BS - 2 for one BS x BS unit lower block, one column
+// per lane: once x_P is final, x_m -= A_mP x_P for every later row m (right-looking, so
+// the dependent chain is one FMA per row); A_mP is this lane's gc[m] as held by lane P.
+template <int BS, int P, int M = P + 1>
+__device__ __forceinline__ void substitute_from(float (&x)[BS], const float (&gc)[BS]) {
+  if constexpr (P < BS - 1) {
+    constexpr int N = BS - M < 4 ? BS - M : 4;
     fnma_row_bcast<P, N>(&x[M], &gc[M], x[P]);
-    if constexpr (M + N < 16) substitute_from<P, M + N>(x, gc);
-    else substitute_from<P + 1>(x, gc);
+    if constexpr (M + N < BS) substitute_from<BS, P, M + N>(x, gc);
+    else substitute_from<BS, P + 1>(x, gc);
   }
 }
 
+// Orders one wave's LDS accesses: the wave's earlier LDS writes have completed before
+// any later access (other lanes of the wave read what these lanes wrote).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // T diag(b) for T = (I + A)^-1 and a 32 x 32 strictly lower A (fp32 in LDS, row stride
 // MS), split (hi, lo) into th and tl in k order (row stride TB): the A operand of
-// T diag(b) R.  By blocks of 16: the two diagonal blocks by forward substitution in wave 0
-// (lanes 0..15 the first block, lanes 16..31 the second; lane: column) into t (fp32);
-// then, on the first 256 threads, one entry each of Y = A_10 T_00, while 256 threads
+// T diag(b) R.  Wave 0 inverts the two diagonal 16 x 16 blocks into t (fp32): the four
+// diagonal 8 x 8 blocks by forward substitution (one per row of 16 lanes; lane: column),
+// then in each 16 x 16 block T_10 = -T_11 (A_10 T_00) over 8 x 8 blocks, two entries a
+// lane.  Then, on the first 256 threads, one entry each of Y = A_10 T_00 for the 16 x 16
+// blocks, while 256 threads
 // (the same ones for a workgroup of 256, the next ones for 512) split the diagonal blocks
 // of T diag(b), two adjacent columns each; then T_10 = -T_11 Y, one entry a thread, times
 // b and split.  The upper right blocks of th and tl must already be zero.  xs: 16 x 17
@@ -262,19 +268,56 @@ template <int MS, int TB, int NT>
 __device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, float* xs, const float* b,
                                                     uint16_t* th, uint16_t* tl, int tid) {
   static_assert(NT == 256 || NT == 512, "workgroup of 256 or 512 threads");
-  if (tid < 32) {
-    const int o = tid & 16;
-    int col = tid & 15;
-    asm volatile("" : "+v"(col));  // keeps the 16 (m == col) selects as selects
-    float gc[16], x[16];
-    gc[0] = 0.f;
+  static_assert(MS % 4 == 0, "16-byte row reads");
+  if (tid < 64) {
+    {  // the 8 x 8 block at o8 (lanes 8..15 of a row repeat columns 0..7 and store nothing)
+      const int o8 = 8 * (tid >> 4);
+      int col = tid & 7;
+      asm volatile("" : "+v"(col));  // keeps the 8 (m == col) selects as selects
+      float gc[8], x[8];
+      gc[0] = 0.f;
 #pragma unroll
-    for (int m = 1; m < 16; ++m) gc[m] = g[(o + m) * MS + o + col];  // A(o + m, o + col)
+      for (int m = 1; m < 8; ++m) gc[m] = g[(o8 + m) * MS + o8 + col];  // A(o8 + m, o8 + col)
 #pragma unroll
-    for (int m = 0; m < 16; ++m) x[m] = m == col ? 1.f : 0.f;
-    substitute_from<0>(x, gc);
+      for (int m = 0; m < 8; ++m) x[m] = m == col ? 1.f : 0.f;
+      substitute_from<8, 0>(x, gc);
+      if ((tid & 15) < 8) {
 #pragma unroll
-    for (int m = 0; m < 16; ++m) t[(o + m) * MS + o + col] = x[m];
+        for (int m = 0; m < 8; ++m) t[(o8 + m) * MS + o8 + col] = x[m];
+      }
+    }
+    // 16 x 16 block o: lane (i, columns j, j + 1) of Y8 = A_10 T_00 and T_10 = -T_11 Y8,
+    // where the blocks are 8 x 8; the upper right 8 x 8 block of T is zero
+    const int o = 16 * (tid >> 5), i = (tid >> 2) & 7, j = 2 * (tid & 3);
+    *reinterpret_cast<float2*>(&t[(o + i) * MS + o + 8 + j]) = make_float2(0.f, 0.f);
+    wave_lds_sync();
+    {
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(&g[(o + 8 + i) * MS + o]);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(&g[(o + 8 + i) * MS + o + 4]);
+      float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const float am = m < 4 ? a0[m] : a1[m - 4];
+        const float2 d = *reinterpret_cast<const float2*>(&t[(o + m) * MS + o + j]);
+        y0 = fmaf(am, d.x, y0);
+        y1 = fmaf(am, d.y, y1);
+      }
+      *reinterpret_cast<float2*>(&xs[((o >> 1) + i) * 8 + j]) = make_float2(y0, y1);
+    }
+    wave_lds_sync();
+    {
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(&t[(o + 8 + i) * MS + o + 8]);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(&t[(o + 8 + i) * MS + o + 12]);
+      float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const float dm = m < 4 ? d0[m] : d1[m - 4];
+        const float2 y = *reinterpret_cast<const float2*>(&xs[((o >> 1) + m) * 8 + j]);
+        z0 = fmaf(dm, y.x, z0);
+        z1 = fmaf(dm, y.y, z1);
+      }
+      *reinterpret_cast<float2*>(&t[(o + 8 + i) * MS + o + j]) = make_float2(-z0, -z1);
+    }
   }
   __syncthreads();
   // rows of A and T are read 4 at a time (MS is a multiple of 4); the sums run over m in order
@@ -357,7 +400,6 @@ struct PrefillLds {
   float gam[C];    // 2^c
   float beta[C];   // step size (0 for tokens past the end)
   float braw[C];   // beta or eta as given
-  float knorm[C];  // ||k||^2 (Kaczmarz step size)
   float g[C * MS];  // K K^T, then A (strictly lower part)
   union {
     float p[C * MS];  // Q K^T
@@ -455,15 +497,6 @@ __global__ void __launch_bounds__(gdn_threads<DV>(), gdn_threads<DV>() == 512 ? 
       if (pc < NPK) {
         st_kperm8(&sh.k[tok * KS], seg * 8, nk[i]);
         st_kperm8(&sh.q[tok * KS], seg * 8, nq[i]);
-        if (kla) {
-          float f[8];
-          unpack8(nk[i], f);
-          float ss = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
-          ss = group_sum<KP>(ss);
-          if (seg == 0) sh.knorm[tok] = ss;
-        }
       }
     }
 #pragma unroll
@@ -484,7 +517,7 @@ __global__ void __launch_bounds__(gdn_threads<DV>(), gdn_threads<DV>() == 512 ? 
     __syncthreads();
 
     // ---- 2. G = K K^T and P = Q K^T on the lower blocks (six blocks over the first waves);
-    //         step sizes (the last wave)
+    //         the step sizes, from G's diagonal for the Kaczmarz one
     constexpr int BPW = NWV >= 6 ? 1 : 2;  // blocks per wave
     if (wave < 6 / BPW) {
 #pragma unroll
@@ -501,10 +534,12 @@ __global__ void __launch_bounds__(gdn_threads<DV>(), gdn_threads<DV>() == 512 ? 
         float* dst = blk < 3 ? sh.g : sh.p;
 #pragma unroll
         for (int r = 0; r < 4; ++r) dst[(16 * ib + 4 * lg + r) * MS + 16 * jb + ln] = acc[r];
+        if ((blk == 0 || blk == 2) && lg == (ln >> 2)) {  // G's diagonal entry (ln, ln): ||k||^2
+          const int i = 16 * ib + ln, r = ln & 3;
+          const float kk = r == 0 ? acc[0] : r == 1 ? acc[1] : r == 2 ? acc[2] : acc[3];
+          sh.beta[i] = t0 + i >= T ? 0.f : kla ? sh.braw[i] / (kk + a.eps) : sh.braw[i];
+        }
       }
-    } else if (wave == NWV - 1 && lane < C) {
-      const bool ok = t0 + lane < T;
-      sh.beta[lane] = !ok ? 0.f : kla ? sh.braw[lane] / (sh.knorm[lane] + a.eps) : sh.braw[lane];
     }
     __syncthreads();
 
