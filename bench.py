@@ -194,11 +194,14 @@ def cpu_baseline(workload: int, target_s: float = 25.0) -> dict:
         p.join()
     wall = max(r[1] for r in res)
     work = sum(r[2] for r in res)
+    rates = sorted(r[2] / r[1] for r in res)  # one core each, all cores busy
     _CPU_JOB.clear()
     return {"value": work / wall, "unit": "state-steps/s", "cores": cores, "kind": "oracle",
+            "single_core_value": rates[len(rates) // 2],
             "sample": f"fp64 NumPy eager oracle on the same workload: {steps} steps (inputs cycling "
                       f"over 64 drawn steps) x all {B}x{H} tiles, tiles split over {cores} forked "
-                      f"single-threaded workers, {wall:.1f} s (slowest worker; input drawing not timed)"}
+                      f"single-threaded workers, {wall:.1f} s (slowest worker; input drawing not timed); "
+                      f"single_core_value: the median worker's own rate"}
 
 
 # -------------------------------------------------------------- GPU legs ----
