@@ -53,6 +53,13 @@ using bf16x2 = __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16;
 constexpr int kChunk = 32;  // tokens per chunk
 constexpr int kThreads = 256;  // RWKV6 workgroup
 
+// max(log2 d, -126) with the bare v_log_f32: for d not below the smallest normal float the
+// same value as log2f (which only adds a rescaling for denormal inputs), and for smaller d
+// the same clamped value.
+__device__ __forceinline__ float chunk_log2_decay(float d) {
+  return fmaxf(__builtin_amdgcn_logf(d), kMinLog2Decay);
+}
+
 // 2^x with the bare hardware instruction (about 1 ulp).  Every argument here is a
 // difference of cumulative log2 decays; results below 2^-126 (the normal range)
 // stand for products of decays that are negligible next to the other terms.
@@ -506,7 +513,7 @@ __global__ void __launch_bounds__(gdn_threads<DV>(), gdn_threads<DV>() == 512 ? 
     }
     if (wave == 3) {
       // lanes 0..31: one token each; inclusive prefix sum of the clamped log2 decays
-      const float l2 = scan32((lane < C && t0 + lane < T) ? step_log2_decay(ndec) : 0.f);
+      const float l2 = scan32((lane < C && t0 + lane < T) ? chunk_log2_decay(ndec) : 0.f);
       if (lane < C) {
         sh.c[lane] = l2;
         sh.gam[lane] = fexp2(l2);
@@ -888,8 +895,8 @@ __global__ void __launch_bounds__(kda_threads<DV>()) prefill_kda_kernel(PoolArgs
       const int pc = tid + i * NT, tok = pc / (DK / 4), seg = pc % (DK / 4);
       const bool ok = t0 + tok < T;  // tokens past the prompt do not decay the state
       *reinterpret_cast<float4*>(&sh.cc[tok * CS + seg * 4]) =
-          make_float4(ok ? step_log2_decay(nd[i].x) : 0.f, ok ? step_log2_decay(nd[i].y) : 0.f,
-                      ok ? step_log2_decay(nd[i].z) : 0.f, ok ? step_log2_decay(nd[i].w) : 0.f);
+          make_float4(ok ? chunk_log2_decay(nd[i].x) : 0.f, ok ? chunk_log2_decay(nd[i].y) : 0.f,
+                      ok ? chunk_log2_decay(nd[i].z) : 0.f, ok ? chunk_log2_decay(nd[i].w) : 0.f);
     }
     if (wave == 3 && lane < C) sh.braw[lane] = nbt;
     if (t0 + C < T) fetch(t0 + C);
@@ -1332,8 +1339,8 @@ __global__ void __launch_bounds__(kThreads, DK == 64 && DV == 64 ? 3 : 1) prefil
       const int pc = tid + i * kThreads, tok = pc / (DK / 4), seg = pc % (DK / 4);
       const bool ok = t0 + tok < T;  // tokens past the prompt do not decay the state
       *reinterpret_cast<float4*>(&sh.cc[tok * CS + seg * 4]) =
-          make_float4(ok ? step_log2_decay(nd[i].x) : 0.f, ok ? step_log2_decay(nd[i].y) : 0.f,
-                      ok ? step_log2_decay(nd[i].z) : 0.f, ok ? step_log2_decay(nd[i].w) : 0.f);
+          make_float4(ok ? chunk_log2_decay(nd[i].x) : 0.f, ok ? chunk_log2_decay(nd[i].y) : 0.f,
+                      ok ? chunk_log2_decay(nd[i].z) : 0.f, ok ? chunk_log2_decay(nd[i].w) : 0.f);
     }
     if (t0 + C < T) fetch(t0 + C);
     __syncthreads();
