@@ -156,19 +156,55 @@ __device__ __forceinline__ float step_log2_decay(float d) {
   return fmaxf(log2f(d), kMinLog2Decay);
 }
 
-// Sum over groups of `width` consecutive lanes (width a power of two <= 64).
+// x as held by the lane that DPP control CTRL selects within this lane's row of 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_from(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// x as held by lane l ^ 16 (ROWS == 16) or l ^ 32 (ROWS == 32): one v_permlane16_swap or
+// v_permlane32_swap of x with itself, which leaves the partner's value in one of its two
+// results, and a select.
+template <int ROWS>
+__device__ __forceinline__ float lane_xor_rows(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const int lane = __lane_id();
+  if constexpr (ROWS == 16) {
+    // results: rows (0, 0, 2, 2) and (1, 1, 3, 3) of x
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  } else {
+    // results: halves (0, 0) and (1, 1) of x
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  }
+}
+
+// Sum over groups of WIDTH consecutive lanes (a power of two <= 64), received by every
+// lane of the group.  Each step adds the value of a partner lane whose own partner is this
+// lane (lane ^ 1 and lane ^ 2 by quad permutations, then the mirror images within 8 and
+// within 16 lanes by DPP, then lane ^ 16 and lane ^ 32 by permlane swaps), so the two
+// lanes of a pair add the same two numbers and every lane of a group ends with the same
+// bits.
 template <int WIDTH>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int off = WIDTH / 2; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  static_assert(WIDTH >= 1 && WIDTH <= 64 && (WIDTH & (WIDTH - 1)) == 0, "lane groups");
+  if constexpr (WIDTH >= 2) x += dpp_from<0xB1>(x);   // quad_perm(1, 0, 3, 2): lane ^ 1
+  if constexpr (WIDTH >= 4) x += dpp_from<0x4E>(x);   // quad_perm(2, 3, 0, 1): lane ^ 2
+  if constexpr (WIDTH >= 8) x += dpp_from<0x141>(x);  // row_half_mirror: 7 - lane within 8
+  if constexpr (WIDTH >= 16) x += dpp_from<0x140>(x); // row_mirror: 15 - lane within 16
+  if constexpr (WIDTH >= 32) x += lane_xor_rows<16>(x);
+  if constexpr (WIDTH >= 64) x += lane_xor_rows<32>(x);
   return x;
 }
 
 // Sum the lanes of a wave that hold the same column group: lanes cg, cg+CG, cg+2CG, ...
+// (CG = 16 or 32: partners lane ^ 16 and lane ^ 32, by permlane swaps).
 template <int CG>
 __device__ __forceinline__ float colgroup_sum(float x) {
-#pragma unroll
-  for (int off = CG; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+  static_assert(CG == 16 || CG == 32 || CG == 64, "column groups of 16 or 32 lanes");
+  if constexpr (CG <= 16) x += lane_xor_rows<16>(x);
+  if constexpr (CG <= 32) x += lane_xor_rows<32>(x);
   return x;
 }
 
