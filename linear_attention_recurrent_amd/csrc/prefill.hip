@@ -265,12 +265,11 @@ __device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcn
 // diagonal 8 x 8 blocks by forward substitution (one per row of 16 lanes; lane: column),
 // then in each 16 x 16 block T_10 = -T_11 (A_10 T_00) over 8 x 8 blocks, two entries a
 // lane.  Then, on the first 256 threads, one entry each of Y = A_10 T_00 for the 16 x 16
-// blocks, while 256 threads
-// (the same ones for a workgroup of 256, the next ones for 512) split the diagonal blocks
-// of T diag(b), two adjacent columns each; then T_10 = -T_11 Y, one entry a thread, times
-// b and split.  The upper right blocks of th and tl must already be zero.  xs: 16 x 17
-// floats of scratch.  Called by the whole workgroup (it synchronises); returns after a
-// barrier.
+// blocks, while 256 threads (the same ones for a workgroup of 256, the next ones for 512)
+// split the diagonal blocks of T diag(b), two adjacent columns each; then
+// T_10 = -T_11 Y, one entry a thread, times b and split.  The upper right blocks of th
+// and tl must already be zero.  xs: 16 x 17 floats of scratch.  Called by the whole
+// workgroup (it synchronises); returns after a barrier.
 template <int MS, int TB, int NT>
 __device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, float* xs, const float* b,
                                                     uint16_t* th, uint16_t* tl, int tid) {
@@ -328,7 +327,6 @@ __device__ __forceinline__ void invert_unit_lower32(const float* g, float* t, fl
   }
   __syncthreads();
   // rows of A and T are read 4 at a time (MS is a multiple of 4); the sums run over m in order
-  static_assert(MS % 4 == 0, "16-byte row reads");
   const int i = (tid >> 4) & 15, j = tid & 15;
   if (tid < 256) {
     float s = 0.f;
