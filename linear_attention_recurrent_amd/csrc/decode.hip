@@ -217,7 +217,11 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
   constexpr bool VEC = VAR != DL_GDN;  // per-key-channel decay
   constexpr int CW = VEC ? DK : 1;     // floats per log_c entry
   constexpr int RPC = G::RPC;
-  constexpr int NBUF = FOLD ? G::NC : G::NB;  // base chunks held in registers
+  // Base chunks held in registers: the whole tile on a folding step, and for GDN with an
+  // fp32 base, whose registers allow it at the same occupancy (the fold already holds the
+  // tile), on every step; otherwise NB chunks streamed (a bf16 tile in flight whole was
+  // slower).
+  constexpr int NBUF = FOLD || (VAR == DL_GDN && !BF) ? G::NC : G::NB;
   using UT = std::conditional_t<VAR == DL_RWKV6, uint16_t, float>;
   using URaw = std::conditional_t<VAR == DL_RWKV6, uint2, float4>;  // 4 log factors, raw
 
@@ -282,7 +286,7 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
   // is waited for first must not sit behind the base chunks in the queue.
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- 2. the base: the first NB chunks on an appending step.  A folding step
+  // ---- 2. the base: the first NBUF chunks on an appending step.  A folding step
   // loads the whole tile after step 3, so the tile and step 3's registers are
   // not live together.
   auto* tb = BIO::tile(p.base, (size_t)tile * DK * DV);
@@ -373,9 +377,9 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
     float4 x[RPC];
 #pragma unroll
     for (int rr = 0; rr < RPC; ++rr) x[rr] = buf[c % NBUF][rr];
-    if (!FOLD && c + G::NB < G::NC) {
+    if (!FOLD && c + NBUF < G::NC) {
 #pragma unroll
-      for (int rr = 0; rr < RPC; ++rr) buf[c % NBUF][rr] = BIO::load(tb, gidx(c + G::NB, rr));
+      for (int rr = 0; rr < RPC; ++rr) buf[c % NBUF][rr] = BIO::load(tb, gidx(c + NBUF, rr));
     }
     const float4 k4 = *reinterpret_cast<const float4*>(sh.yk + rg * G::RPT + c * RPC);
     ak = f4_fma(k4.x, x[0], ak);
