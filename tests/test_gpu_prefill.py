@@ -339,3 +339,46 @@ def test_hip_graph_replays_of_prefill_and_decode():
             assert torch.equal(dec[i], dec_ref[i]), (r, i)
         for name, tnsr in pool.tensors().items():
             assert torch.equal(tnsr, ref_pool.tensors()[name]), (r, name)
+
+
+# ------------------------------------------- seeded mixed configurations ------
+def _mixed_case(i):
+    """Case i: a variant (GDN with normalised keys, KDA, RWKV6, GDN with the Kaczmarz step
+    size), head sizes, batch, heads, log length and ragged start fills, decode steps, a
+    prompt, then decode steps again, all drawn from one seeded generator."""
+    g = np.random.default_rng(1000 + i)
+    w = int(g.choice([1, 3, 4, 6]))
+    dk, dv = int(g.choice([64, 128])), int(g.choice([64, 128]))
+    B, H = int(g.integers(1, 4)), int(g.integers(1, 4))
+    L = int(g.choice([1, 2, 4, 8, 16, 32]))
+    d0, T, d1 = int(g.integers(0, 21)), int(g.integers(0, 101)), int(g.integers(0, 21))
+    kla = True if w == 6 else (bool(g.integers(0, 2)) if w == 3 else None)
+    fill0 = g.integers(0, L, size=B).astype(np.int32)
+    return dict(w=w, dk=dk, dv=dv, B=B, H=H, L=L, d0=d0, T=T, d1=d1, kla=kla, fill0=fill0)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_seeded_mixed_decode_prefill_decode(i):
+    """Decode steps from ragged fills, a prompt (which folds the pending logs first), more
+    decode steps: every output and the final state against one eager oracle run."""
+    c = _mixed_case(i)
+    steps = c["d0"] + c["T"] + c["d1"]
+    print(f"case {i}: {c}", flush=True)
+    inp = make_inputs(c["w"], max(steps, 1), batch=c["B"], heads=c["H"], log_len=c["L"], pool=max(steps, 1),
+                      fill0=c["fill0"], dk=c["dk"], dv=c["dv"], kla=c["kla"])
+    up = Uploaded(inp)
+    pool = new_pool(inp, up=up)
+    outs = []
+    for t in range(c["d0"]):
+        dl.dl_decode_step(pool, up.io(t))
+        outs.append(up.out.cpu().numpy())
+    po = run_prefill(pool, up, c["d0"], c["T"], inp.eps)
+    assert int(pool.fill.max().item()) == 0
+    outs.extend(list(po))
+    for t in range(c["d0"] + c["T"], steps):
+        dl.dl_decode_step(pool, up.io(t))
+        outs.append(up.out.cpu().numpy())
+    ref_S, ref_o = oracle.run_eager(inp, steps)
+    if steps:
+        _close(f"outputs, case {i}", np.stack(outs), ref_o[:steps], (-1,))
+    _close(f"state, case {i}", materialized_state(pool), ref_S, (-2, -1))
