@@ -12,8 +12,11 @@ write the whole state every step) on the same inputs, a cache-cold variant
 last-level cache), and the fp64 CPU oracle on the host cores.
 
   python bench.py [--gpus 1] [--steps 1024] [--warmup 32] [--workload 2]
-                  [--no-cpu-baseline] [--graph] [--only deltalog|eager|copy]
-                  [--base-dtype f32|bf16]
+                  [--no-cpu-baseline] [--graph] [--only deltalog|eager|copy|prefill|merge]
+                  [--base-dtype f32|bf16] [--log-len L]
+
+`--only merge` times dl_merge_on on full logs with each arithmetic unit of the
+fold (vector FMAs, fp32 MFMA) and prints their times.
 """
 from __future__ import annotations
 
@@ -205,12 +208,12 @@ def cpu_baseline(workload: int, target_s: float = 25.0) -> dict:
 
 
 # -------------------------------------------------------------- GPU legs ----
-def gpu_setup(workload, pool_slots, log_len=None):
+def gpu_setup(workload, pool_slots, log_len=None, dk=None, dv=None):
     import torch
 
     from linear_attention_recurrent_amd import deltalog as dl
     w = WORKLOADS[workload]
-    inp = make_inputs(workload, pool_slots, pool=pool_slots, log_len=log_len)
+    inp = make_inputs(workload, pool_slots, pool=pool_slots, log_len=log_len, dk=dk, dv=dv)
     dev = torch.device("cuda", 0)
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
     T = dict(q=bf(inp.q), k=bf(inp.k), v=bf(inp.v), decay=torch.from_numpy(inp.decay).to(dev),
@@ -325,6 +328,45 @@ def prefill_leg(args, inp, Tn, base_dt, reps: int = 5) -> dict:
             "bytes_per_state_step": m["bytes"], "issued_flops_per_state_step": m["issued_flops"]}
 
 
+def merge_leg(args, inp, Tn, ios, base_dt, reps: int = 20) -> dict:
+    """Time dl_merge_on with each arithmetic unit on full logs: every tile holds L - 1
+    real entries (the most a log holds between calls).  Before each merge the fill and
+    the base are restored by device copies outside the events, so every timed merge
+    does the same work; only the merge launch is between the events."""
+    import torch
+
+    from linear_attention_recurrent_amd import deltalog as dl
+    B, H, dk, dv, L, var = inp.batch, inp.heads, inp.dk, inp.dv, inp.log_len, inp.variant
+    dev = torch.device("cuda", 0)
+    P = len(ios)
+    pool = dl.DeltaLogPool(var, B, H, dk, dv, L, dev, base_dt)
+    dl.dl_init_state(pool, Tn["s0"], None)
+    for t in range(L - 1):
+        dl.dl_decode_step(pool, ios[t % P])
+    fill0, base0 = pool.fill.clone(), pool.base.clone()
+    stream = torch.cuda.current_stream()
+    eb = 2 if base_dt == dl.BASE_BF16 else 4
+    nbytes = B * H * (2 * eb * dk * dv + (L - 1) * entry_bytes(var, dk, dv) + 8)
+    out = {"workload": f"{VARIANT_NAMES[var]} B={B} H={H} dk={dk} dv={dv}, {L - 1} entries per tile"
+                       + (", bf16 base" if base_dt == dl.BASE_BF16 else ""),
+           "bytes_per_merge": nbytes, "reps": reps}
+    for unit, name in ((dl.UNIT_VALU, "valu"), (dl.UNIT_MFMA, "mfma")):
+        evs = []
+        for _ in range(reps + 2):
+            pool.fill.copy_(fill0)
+            pool.base.copy_(base0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dl.dl_merge_on(pool, 1, unit)
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in evs[2:]])) * 1e3
+        out[name] = {"us_per_merge": us, "hbm_gbs_algorithmic": nbytes / us / 1e3}
+    out["mfma_speedup"] = out["valu"]["us_per_merge"] / out["mfma"]["us_per_merge"]
+    return out
+
+
 def serving_leg(args, cpu) -> dict:
     """The 48-layer serving pool: one pool per layer (B = 512, H = 32, 128/128, ragged
     start fills shared by a sequence's layers), one step = one dl_decode_step per layer.
@@ -413,10 +455,14 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6],
                     help="5 = the 48-layer serving pool (B=512, ragged fills); --log-len picks its L")
     ap.add_argument("--log-len", type=int, default=None)
+    ap.add_argument("--dk", type=int, default=None, choices=[64, 128],
+                    help="override the workload's key head size (merge leg)")
+    ap.add_argument("--dv", type=int, default=None, choices=[64, 128],
+                    help="override the workload's value head size (merge leg)")
     ap.add_argument("--pool-slots", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step loop as a HIP graph")
-    ap.add_argument("--only", choices=["deltalog", "eager", "copy", "prefill"], default=None,
+    ap.add_argument("--only", choices=["deltalog", "eager", "copy", "prefill", "merge"], default=None,
                     help="run one leg only (for profiling runs)")
     ap.add_argument("--prefill-tokens", type=int, default=4096,
                     help="prompt length of the prefill leg (GDN workloads)")
@@ -458,7 +504,9 @@ def main():
         print(json.dumps(serving_leg(args, cpu)))
         return
 
-    inp, T, ios, w = gpu_setup(args.workload, args.pool_slots, args.log_len)
+    if (args.dk or args.dv) and args.only != "merge":
+        raise SystemExit("--dk/--dv apply to the merge leg only (--only merge)")
+    inp, T, ios, w = gpu_setup(args.workload, args.pool_slots, args.log_len, args.dk, args.dv)
     B, H, dk, dv, L, var = inp.batch, inp.heads, inp.dk, inp.dv, inp.log_len, inp.variant
     P = args.pool_slots
     tiles = B * H
@@ -482,6 +530,9 @@ def main():
         state = T["s0"].clone()
         secs_e = time_loop(lambda t: dl.dl_eager_step(var, state, ios[t % P]), K, W, chunk)
         result["eager"] = secs_e
+    if args.only == "merge":
+        print(json.dumps(merge_leg(args, inp, T, ios, base_dt)))
+        return
     if args.only == "prefill" or args.only is None:
         result["prefill"] = prefill_leg(args, inp, T, base_dt)
     if args.only is not None:

@@ -146,6 +146,21 @@ int dl_decode_step(const dl_dims *dims, const dl_pool *pool, const dl_step_io *i
  * outside [1, L]. */
 int dl_merge(const dl_dims *dims, const dl_pool *pool, int32_t min_fill, void *stream);
 
+/* Arithmetic unit of a fold, for dl_merge_on. */
+enum {
+  DL_UNIT_AUTO = 0, /* what dl_merge uses: the unit measured faster for the pool's shape and L */
+  DL_UNIT_VALU = 1, /* vector FMAs; the tile is streamed once per 16 or 32 staged entries     */
+  DL_UNIT_MFMA = 2  /* v_mfma_f32_16x16x4_f32 (fp32 products and sums); the tile stays in
+                       registers, one read and one write at any log length                  */
+};
+
+/* dl_merge with the fold's arithmetic unit named by the caller (the merge of
+ * the DeltaLog Abstract, a rank-n update of each base, n = the tile's fill).
+ * Both units compute the same fp32 update and differ only in the order of the
+ * additions (relative differences of order 1e-7).  Errors: those of dl_merge,
+ * and DL_EINVAL for a unit outside the enum above. */
+int dl_merge_on(const dl_dims *dims, const dl_pool *pool, int32_t min_fill, int32_t unit, void *stream);
+
 /* The eager comparator (DeltaLog Abstract: materialize and write back the
  * full recurrent state after every generated token): reads `state` (device,
  * fp32 [batch][heads][dk][dv]), writes the updated state in place and io->out.

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdeltalog.so")
-SOURCES = ["decode.hip", "eager.hip", "prefill.hip", "api.cpp"]
+SOURCES = ["decode.hip", "merge_mfma.hip", "eager.hip", "prefill.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

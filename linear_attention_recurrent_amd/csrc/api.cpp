@@ -104,14 +104,43 @@ int dl_decode_step(const dl_dims* dims, const dl_pool* pool, const dl_step_io* i
                                       static_cast<hipStream_t>(stream)));
 }
 
-int dl_merge(const dl_dims* dims, const dl_pool* pool, int32_t min_fill, void* stream) {
+// The fold's arithmetic unit for a merge.  DL_UNIT_AUTO takes the matrix-core fold where it
+// measured faster than the vector fold on full logs (one MI355X, every tile holding L - 1
+// entries): from L = 8 on 64 x 64 tiles (RWKV6: 1.04x at L = 8, 1.3x at 16, 1.6x at 32; the
+// vector fold 1.1x faster at L = 4) and from L = 16 on the others (128 x 128, GDN and KDA,
+// fp32 and bf16 bases: 1.04-1.09x at L = 16, 1.7x at 32, 2.5x at 64, a tie at 12, the vector
+// fold up to 1.14x faster at 4; 64 x 128 and 128 x 64: 1.16x and 1.25x at 16, 0.97x and 1.00x
+// at 8).
+static bool merge_on_mfma(const dl_dims* dims, int32_t unit) {
+  if (unit == DL_UNIT_VALU) return false;
+  if (unit == DL_UNIT_MFMA) return true;
+  const int min_len = (dims->dk == 64 && dims->dv == 64) ? 8 : 16;
+  return dims->log_len >= min_len;
+}
+
+// Fold every log holding >= min_fill entries (arguments already checked).
+static hipError_t launch_fold(const dl_dims* dims, const dl_pool* pool, int32_t min_fill, int32_t unit,
+                              hipStream_t st) {
+  const int tiles = dims->batch * dims->heads;
+  if (merge_on_mfma(dims, unit))
+    return dl::launch_merge_mfma(dims->variant, bf16_base(dims), dims->dk, dims->dv, tiles,
+                                 pool_args(dims, pool), min_fill, st);
+  return dl::launch_merge(dims->variant, bf16_base(dims), dims->dk, dims->dv, tiles, pool_args(dims, pool),
+                          min_fill, st);
+}
+
+int dl_merge_on(const dl_dims* dims, const dl_pool* pool, int32_t min_fill, int32_t unit, void* stream) {
   int rc = check_dims(dims);
   if (rc != DL_OK) return rc;
   if (min_fill < 1 || min_fill > dims->log_len) return DL_EINVAL;
+  if (unit != DL_UNIT_AUTO && unit != DL_UNIT_VALU && unit != DL_UNIT_MFMA) return DL_EINVAL;
   if (dims->batch == 0) return DL_OK;
   if ((rc = check_pool(pool, dims->variant)) != DL_OK) return rc;
-  return hip_status(dl::launch_merge(dims->variant, bf16_base(dims), dims->dk, dims->dv, dims->batch * dims->heads,
-                                     pool_args(dims, pool), min_fill, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_fold(dims, pool, min_fill, unit, static_cast<hipStream_t>(stream)));
+}
+
+int dl_merge(const dl_dims* dims, const dl_pool* pool, int32_t min_fill, void* stream) {
+  return dl_merge_on(dims, pool, min_fill, DL_UNIT_AUTO, stream);
 }
 
 int dl_eager_step(const dl_dims* dims, float* state, const dl_step_io* io, void* stream) {
@@ -145,8 +174,7 @@ int dl_prefill(const dl_dims* dims, const dl_pool* pool, const dl_prefill_io* io
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const int tiles = dims->batch * dims->heads;
   // fold any pending log first: the prefill starts from the dense state in the base
-  hipError_t e = dl::launch_merge(dims->variant, bf16_base(dims), dims->dk, dims->dv, tiles,
-                                  pool_args(dims, pool), 1, st);
+  hipError_t e = launch_fold(dims, pool, 1, DL_UNIT_AUTO, st);
   if (e != hipSuccess || io->tokens == 0) return hip_status(e);
   const dl::PrefillArgs a{io->q, io->k, io->v, io->decay, io->beta, io->eta, io->bonus, io->out, io->eps, io->tokens};
   return hip_status(dl::launch_prefill(dims->variant, bf16_base(dims), dims->dk, dims->dv, tiles,

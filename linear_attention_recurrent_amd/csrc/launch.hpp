@@ -12,6 +12,8 @@ hipError_t launch_decode(int variant, bool bf16_base, int dk, int dv, int tiles,
                          const StepArgs& s, hipStream_t stream);
 hipError_t launch_merge(int variant, bool bf16_base, int dk, int dv, int tiles, const PoolArgs& p,
                         int min_fill, hipStream_t stream);
+hipError_t launch_merge_mfma(int variant, bool bf16_base, int dk, int dv, int tiles, const PoolArgs& p,
+                             int min_fill, hipStream_t stream);
 hipError_t launch_init(int variant, bool bf16_base, int dk, int dv, int tiles, const PoolArgs& p,
                        const float* init_base, hipStream_t stream);
 hipError_t launch_prefill(int variant, bool bf16_base, int dk, int dv, int tiles, const PoolArgs& p,

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libdeltalog.so")
 GDN, KDA, RWKV6 = 0, 1, 2
 DL_OK, DL_EINVAL, DL_EUNSUPPORTED, DL_EALIGN, DL_EHIP = 0, -1, -2, -3, -4
 BASE_F32, BASE_BF16 = 0, 1
+UNIT_AUTO, UNIT_VALU, UNIT_MFMA = 0, 1, 2  # arithmetic unit of a fold (dl_merge_on)
 MAX_LOG_LEN = 128
 
 
@@ -70,11 +71,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                   ctypes.POINTER(ctypes.c_int32), vp]
     lib.dl_decode_step.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Pool), ctypes.POINTER(StepIO), vp]
     lib.dl_merge.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Pool), ctypes.c_int32, vp]
+    lib.dl_merge_on.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Pool), ctypes.c_int32, ctypes.c_int32, vp]
     lib.dl_eager_step.argtypes = [ctypes.POINTER(Dims), vp, ctypes.POINTER(StepIO), vp]
     lib.dl_prefill.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Pool), ctypes.POINTER(PrefillIO), vp]
     lib.dl_status_string.argtypes = [ctypes.c_int]
     lib.dl_status_string.restype = ctypes.c_char_p
-    for f in (lib.dl_init_state, lib.dl_decode_step, lib.dl_merge, lib.dl_eager_step, lib.dl_prefill):
+    for f in (lib.dl_init_state, lib.dl_decode_step, lib.dl_merge, lib.dl_merge_on, lib.dl_eager_step,
+              lib.dl_prefill):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -209,6 +212,13 @@ def dl_merge(pool: DeltaLogPool, min_fill: int = 1, stream=None) -> None:
     rc = load_library().dl_merge(ctypes.byref(pool.c_dims), ctypes.byref(pool.c_pool), int(min_fill),
                                  _stream(stream))
     _check(rc, "dl_merge")
+
+
+def dl_merge_on(pool: DeltaLogPool, min_fill: int = 1, unit: int = 0, stream=None) -> None:
+    """dl_merge with the fold's arithmetic unit given (DL_UNIT_AUTO, DL_UNIT_VALU, DL_UNIT_MFMA)."""
+    rc = load_library().dl_merge_on(ctypes.byref(pool.c_dims), ctypes.byref(pool.c_pool), int(min_fill),
+                                    int(unit), _stream(stream))
+    _check(rc, "dl_merge_on")
 
 
 def dl_eager_step(variant: int, state: torch.Tensor, io: StepIO, stream=None) -> None:

@@ -27,9 +27,10 @@ def lib():
 
 def test_header_declares_the_calls():
     names = declared_functions()
-    for n in ("dl_init_state", "dl_decode_step", "dl_merge", "dl_eager_step", "dl_prefill", "dl_status_string"):
+    for n in ("dl_init_state", "dl_decode_step", "dl_merge", "dl_merge_on", "dl_eager_step", "dl_prefill",
+              "dl_status_string"):
         assert n in names
-    assert len(names) == 6, names
+    assert len(names) == 7, names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -115,6 +116,11 @@ def test_merge_init_eager_errors(lib):
     assert lib.dl_merge(ctypes.byref(d), ctypes.byref(p), 0, None) == dl.DL_EINVAL
     assert lib.dl_merge(ctypes.byref(d), ctypes.byref(p), 17, None) == dl.DL_EINVAL
     assert lib.dl_merge(ctypes.byref(d), None, 1, None) == dl.DL_EINVAL
+    for unit in (-1, 3):
+        assert lib.dl_merge_on(ctypes.byref(d), ctypes.byref(p), 1, unit, None) == dl.DL_EINVAL
+    for unit in (dl.UNIT_AUTO, dl.UNIT_VALU, dl.UNIT_MFMA):
+        assert lib.dl_merge_on(ctypes.byref(d), ctypes.byref(p), 0, unit, None) == dl.DL_EINVAL
+        assert lib.dl_merge_on(ctypes.byref(d), None, 1, unit, None) == dl.DL_EINVAL
     fills = (ctypes.c_int32 * 2)(0, 16)
     assert lib.dl_init_state(ctypes.byref(d), ctypes.byref(p), None, fills, None) == dl.DL_EINVAL
     fills = (ctypes.c_int32 * 2)(-1, 0)
@@ -134,6 +140,7 @@ def test_batch_zero_returns_ok_without_looking_at_pointers(lib):
     noio = dl.StepIO(None, None, None, None, None, None, None)
     assert lib.dl_decode_step(ctypes.byref(d), ctypes.byref(empty), ctypes.byref(noio), None) == dl.DL_OK
     assert lib.dl_merge(ctypes.byref(d), ctypes.byref(empty), 1, None) == dl.DL_OK
+    assert lib.dl_merge_on(ctypes.byref(d), ctypes.byref(empty), 1, dl.UNIT_MFMA, None) == dl.DL_OK
     assert lib.dl_init_state(ctypes.byref(d), ctypes.byref(empty), None, None, None) == dl.DL_OK
     assert lib.dl_eager_step(ctypes.byref(d), None, ctypes.byref(noio), None) == dl.DL_OK
 
