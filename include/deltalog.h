@@ -150,7 +150,7 @@ int dl_merge(const dl_dims *dims, const dl_pool *pool, int32_t min_fill, void *s
 enum {
   DL_UNIT_AUTO = 0, /* what dl_merge uses: the unit measured faster for the pool's shape and L */
   DL_UNIT_VALU = 1, /* vector FMAs; the tile is streamed once per 16 or 32 staged entries     */
-  DL_UNIT_MFMA = 2  /* v_mfma_f32_16x16x4_f32 (fp32 products and sums); the tile stays in
+  DL_UNIT_MFMA = 2  /* v_mfma_f32_4x4x1_16b_f32 (fp32 products and sums); the tile stays in
                        registers, one read and one write at any log length                  */
 };
 

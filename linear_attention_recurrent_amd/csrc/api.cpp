@@ -104,17 +104,21 @@ int dl_decode_step(const dl_dims* dims, const dl_pool* pool, const dl_step_io* i
                                       static_cast<hipStream_t>(stream)));
 }
 
-// The fold's arithmetic unit for a merge.  DL_UNIT_AUTO takes the matrix-core fold where it
-// measured faster than the vector fold on full logs (one MI355X, every tile holding L - 1
-// entries): from L = 8 on 64 x 64 tiles (RWKV6: 1.04x at L = 8, 1.3x at 16, 1.6x at 32; the
-// vector fold 1.1x faster at L = 4) and from L = 16 on the others (128 x 128, GDN and KDA,
-// fp32 and bf16 bases: 1.04-1.09x at L = 16, 1.7x at 32, 2.5x at 64, a tie at 12, the vector
-// fold up to 1.14x faster at 4; 64 x 128 and 128 x 64: 1.16x and 1.25x at 16, 0.97x and 1.00x
-// at 8).
+// The fold's arithmetic unit for a merge.  DL_UNIT_AUTO takes the matrix-core fold from the
+// shortest log length at which it measured faster than the vector fold on full logs (one
+// MI355X, every tile holding L - 1 entries):
+//   64 x 64          L >= 4   (RWKV6: 1.03x at 4, 1.13x at 8, 1.55x at 32; 0.98x at 2)
+//   128 x 64         L >= 8   (1.10x at 8, 1.35x at 16)
+//   128 x 128, bf16  L >= 8   (GDN: 1.09x at 8, 1.21x at 16; 0.98x at 4)
+//   otherwise        L >= 16  (GDN 128 x 128: 1.16x at 16, 2.5x at 64, 1.02x at 8, 0.95x at 4;
+//                              KDA 1.09x at 16, 0.98x at 8; 64 x 128: 1.19x at 16, 0.99x at 8)
 static bool merge_on_mfma(const dl_dims* dims, int32_t unit) {
   if (unit == DL_UNIT_VALU) return false;
   if (unit == DL_UNIT_MFMA) return true;
-  const int min_len = (dims->dk == 64 && dims->dv == 64) ? 8 : 16;
+  int min_len = 16;
+  if (dims->dk == 64 && dims->dv == 64) min_len = 4;
+  else if (dims->dk == 128 && dims->dv == 64) min_len = 8;
+  else if (dims->dk == 128 && dims->dv == 128 && bf16_base(dims)) min_len = 8;
   return dims->log_len >= min_len;
 }
 

@@ -6,15 +6,18 @@
 //   B <- diag(2^c_now) B + sum_{e<n} diag(2^(c_now - c_e)) k_e u_e^T
 // with c_now the cumulative log2-decay of the newest entry.  Here the whole tile
 // stays in registers for the fold, so it is read and written once at any log
-// length, and the sum is a product W^T U (W[e][i] = 2^(c_now[i] - c_e[i]) k_e[i],
-// U[e][j] = u_e[j]) on v_mfma_f32_16x16x4_f32: fp32 operands, fp32 accumulation,
-// four log entries per instruction.
+// length, and each entry's rank-1 term goes through v_mfma_f32_4x4x1_16b_f32
+// (sixteen independent 4 x 4 x 1 products per instruction, fp32 operands and
+// accumulation): one instruction adds u_e[cols] w_e[rows] to 16 blocks of 4 rows x
+// 4 columns, w_e[i] = 2^(c_now[i] - c_e[i]) k_e[i].
 //
-// Register layout.  The instruction is issued with the factor block first
-// (A[m][k] = U[e0 + k][col m]) and the weights second (B[k][n] = W[e0 + k][row n]),
-// so its 16 x 16 result holds, in lane (g, r16) = (lane / 16, lane % 16), rows
-// r16 and columns 4g .. 4g + 3 of a 16 x 16 block of the tile: one float4 of one
-// state row per lane and block, the layout of a plain 16-byte load of the tile.
+// Register layout.  Block b (lanes 4b .. 4b + 3) takes the factors as its first
+// operand (lane 4b + m supplies the factor of column m of the block) and the weights
+// as its second (lane 4b + r supplies the weight of row r), so lane 4b + r holds row r
+// and the block's four columns: one float4 of one state row, the layout of a 16-byte
+// load.  The 16 blocks of an instruction cover the same four rows and 64 consecutive
+// columns, so a wave's load or store instruction moves four rows x 256 bytes of the
+// tile (the 16 x 16 x 4 instruction would give 16 rows x 64 bytes).
 #include <type_traits>
 
 #include "dl_device.hpp"
@@ -27,34 +30,21 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int DK, int DV, bool BF>
 struct MfmaFoldGeo {
-  // Eight waves on a 64 KiB fp32 tile (eight 16 x 16 blocks a wave), four on the smaller
-  // tiles, which measured faster with four (64 x 64: 1.51x against 1.58x the vector unit).
-  static constexpr int NT = DK * DV >= 16384 ? 512 : 256;
-  static constexpr int NW = NT / 64;
-  static constexpr int RB = DK / 16, CB = DV / 16;  // 16 x 16 blocks of the tile
-  static constexpr int NWR = RB < NW ? RB : NW;     // waves along the rows
-  static constexpr int NWC = NW / NWR;              // and along the columns
-  static constexpr int RBW = RB / NWR;              // row blocks per wave
-  static constexpr int CBW = CB / NWC;              // column blocks per wave
-  // With a bf16 base, column blocks go in pairs so that a lane's eight values of one row
-  // (four in each block) are adjacent in memory: one 16-byte load.
-  static constexpr bool PAIR = BF;
-  static constexpr int ME = 16;  // log entries staged at a time (four instructions deep)
-  // LDS row strides of 16 mod 64 words: the four lane groups of one operand read
-  // (entries e0 + g, 16 rows or columns each) hit 64 distinct banks.
-  static constexpr int WS = DK + 16;
-  static constexpr int US = DV + 16;
-  static_assert(NWR * RBW == RB && NWC * CBW == CB && (!PAIR || CBW % 2 == 0), "tile geometry");
-  // Column of the tile held by index m (0..15) of column block cb: 16 cb + m, or with
-  // pairs, 32 (cb / 2) + 8 (m / 4) + 4 (cb % 2) + m % 4.
-  __device__ static constexpr int col(int cb, int m) {
-    return PAIR ? 32 * (cb / 2) + 8 * (m / 4) + 4 * (cb % 2) + m % 4 : 16 * cb + m;
-  }
-  // Where the factors of columns c .. c + 3 (c a multiple of 4) go in a staged LDS row:
-  // position 16 cb + m holds column col(cb, m), so one operand read is 16 consecutive words.
-  __device__ static constexpr int upos(int c) {
-    return PAIR ? 16 * (2 * (c / 32) + (c % 8) / 4) + 4 * ((c % 32) / 8) : c;
-  }
+  static constexpr int NW = DK / 16;  // waves: each owns 16 consecutive rows
+  static constexpr int NT = NW * 64;
+  static constexpr int RQ = 4;        // four-row groups per wave
+  static constexpr int NCG = DV / 64; // 64-column groups
+  // With a bf16 base and dv = 128, the two column groups interleave by fours so that a
+  // lane's eight values of one row are adjacent in memory: one 16-byte load.
+  static constexpr bool PAIR = BF && NCG == 2;
+  static constexpr int ME = 16;       // log entries staged at a time
+  static constexpr int WS = DK + 4;   // LDS row strides (words)
+  static constexpr int US = DV + 4;
+  // Column held by index m (0..3) of block b (0..15) in column group c.
+  __device__ static constexpr int col(int c, int b, int m) { return PAIR ? 8 * b + 4 * c + m : 64 * c + 4 * b + m; }
+  // Where the factors of columns j .. j + 3 (j a multiple of 4) go in a staged LDS row:
+  // position 64 c + 4 b + m holds column col(c, b, m), so one operand read is 64 consecutive words.
+  __device__ static constexpr int upos(int j) { return PAIR ? 64 * ((j / 4) % 2) + 4 * (j / 8) : j; }
 };
 
 template <int VAR, int DK, int DV, bool BF>
@@ -65,128 +55,165 @@ __global__ void __launch_bounds__((MfmaFoldGeo<DK, DV, BF>::NT)) merge_mfma_kern
   constexpr int CW = VEC ? DK : 1;     // floats per log_c entry
   using UT = std::conditional_t<VAR == DL_RWKV6, uint16_t, float>;
   using URaw = std::conditional_t<VAR == DL_RWKV6, uint2, float4>;  // four factors, raw
-  __shared__ __attribute__((aligned(16))) float s_c[CW];  // c_now, natural order
   __shared__ __attribute__((aligned(16))) float s_g[CW];  // 2^c_now
   __shared__ __attribute__((aligned(16))) float s_w[G::ME * G::WS];
   __shared__ __attribute__((aligned(16))) float s_u[G::ME * G::US];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int wr = wave % G::NWR, wc = wave / G::NWR;  // this wave's row and column block groups
+  const int b = lane >> 2, r4 = lane & 3;  // block and row within the four-row group
   const int tile = blockIdx.x;
   const int n = p.fill[tile];
   if (n < min_fill || n == 0) return;  // uniform: the whole workgroup leaves
   const size_t lbase = (size_t)tile * p.L;
   const UT* log_u = static_cast<const UT*>(p.log_u);
 
-  // The tile: lane (g, r16) holds row 16 (wr RBW + rb) + r16 and, of column block
-  // cb = wc CBW + j, the columns col(cb, 4 g) .. col(cb, 4 g) + 3.
-  auto* tb = BIO::tile(p.base, (size_t)tile * DK * DV);
-  auto row = [&](int rb) { return 16 * (wr * G::RBW + rb) + r16; };
-  f32x4 acc[G::RBW][G::CBW];
-#pragma unroll
-  for (int rb = 0; rb < G::RBW; ++rb) {
-    if constexpr (G::PAIR) {
-#pragma unroll
-      for (int j = 0; j < G::CBW; j += 2) {
-        const uint4 w = *reinterpret_cast<const uint4*>(tb + (size_t)row(rb) * DV + G::col(wc * G::CBW + j, 4 * g));
-        const float4 a = widen4(make_uint2(w.x, w.y)), b = widen4(make_uint2(w.z, w.w));
-        acc[rb][j] = f32x4{a.x, a.y, a.z, a.w};
-        acc[rb][j + 1] = f32x4{b.x, b.y, b.z, b.w};
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < G::CBW; ++j) {
-        const float4 x = BIO::load(tb, ((size_t)row(rb) * DV + G::col(wc * G::CBW + j, 4 * g)) / 4);
-        acc[rb][j] = f32x4{x.x, x.y, x.z, x.w};
-      }
-    }
-  }
-
-  for (int i = tid; i < CW; i += G::NT) {
-    const float c = p.log_c[(lbase + n - 1) * CW + i];
-    s_c[i] = c;
-    s_g[i] = exp2f(c);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int rb = 0; rb < G::RBW; ++rb) {
-    const float sc = s_g[VEC ? row(rb) : 0];
-#pragma unroll
-    for (int j = 0; j < G::CBW; ++j) acc[rb][j] *= sc;
-  }
-
-  for (int e0 = 0; e0 < n; e0 += G::ME) {
-    const int cnt = min(G::ME, n - e0);
-    __syncthreads();  // the previous stage's operand reads are done
-    // fold weights, eight channels of one entry per job (zeros past the fill)
-    for (int job = tid; job < G::ME * DK / 8; job += G::NT) {
+  // Stage entries [e0, e0 + cnt) into LDS: fold weights (eight channels of one entry per
+  // job, c_now read from the newest entry directly) and factors (four columns per job).
+  const float* cnow = p.log_c + (lbase + n - 1) * CW;
+  auto stage = [&](int e0, int cnt) {
+    for (int job = tid; job < cnt * DK / 8; job += G::NT) {
       const int m = job / (DK / 8), i0 = (job % (DK / 8)) * 8, e = e0 + m;
       float w[8];
-      if (m < cnt) {
-        float kf[8];
-        unpack8(*reinterpret_cast<const uint4*>(p.log_k + (lbase + e) * DK + i0), kf);
-        if constexpr (VEC) {
-          float ce[8];
-          load8(p.log_c + (lbase + e) * DK + i0, ce);
+      float kf[8];
+      unpack8(*reinterpret_cast<const uint4*>(p.log_k + (lbase + e) * DK + i0), kf);
+      if constexpr (VEC) {
+        float ce[8], cn[8];
+        load8(p.log_c + (lbase + e) * DK + i0, ce);
+        load8(cnow + i0, cn);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) w[i] = exp2f(s_c[i0 + i] - ce[i]) * kf[i];
-        } else {
-          const float sc = exp2f(s_c[0] - p.log_c[lbase + e]);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) w[i] = sc * kf[i];
-        }
+        for (int i = 0; i < 8; ++i) w[i] = exp2f(cn[i] - ce[i]) * kf[i];
       } else {
+        const float sc = exp2f(cnow[0] - p.log_c[lbase + e]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = 0.f;
+        for (int i = 0; i < 8; ++i) w[i] = sc * kf[i];
       }
       float4* dst = reinterpret_cast<float4*>(s_w + m * G::WS + i0);
       dst[0] = make_float4(w[0], w[1], w[2], w[3]);
       dst[1] = make_float4(w[4], w[5], w[6], w[7]);
     }
-    // update factors, four columns of one entry per job
-    for (int job = tid; job < G::ME * DV / 4; job += G::NT) {
+    for (int job = tid; job < cnt * DV / 4; job += G::NT) {
       const int m = job / (DV / 4), j0 = (job % (DV / 4)) * 4;
-      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (m < cnt) u = widen4(*reinterpret_cast<const URaw*>(log_u + (lbase + e0 + m) * DV + j0));
+      const float4 u = widen4(*reinterpret_cast<const URaw*>(log_u + (lbase + e0 + m) * DV + j0));
       *reinterpret_cast<float4*>(s_u + m * G::US + G::upos(j0)) = u;
     }
-    __syncthreads();
+  };
+  auto fold = [&](int cnt, f32x4 (&acc)[G::RQ][G::NCG]) {
+    for (int m = 0; m < cnt; ++m) {  // one entry per instruction
+      float bw[G::RQ], au[G::NCG];
 #pragma unroll
-    for (int ks = 0; ks < G::ME / 4; ++ks) {
-      if (4 * ks >= cnt) break;  // uniform
-      const int m = 4 * ks + g;  // this lane group's entry
-      float bw[G::RBW];
+      for (int q = 0; q < G::RQ; ++q) bw[q] = s_w[m * G::WS + 16 * wave + 4 * q + r4];
 #pragma unroll
-      for (int rb = 0; rb < G::RBW; ++rb) bw[rb] = s_w[m * G::WS + row(rb)];
+      for (int c = 0; c < G::NCG; ++c) au[c] = s_u[m * G::US + 64 * c + lane];
 #pragma unroll
-      for (int j = 0; j < G::CBW; ++j) {
-        const float au = s_u[m * G::US + 16 * (wc * G::CBW + j) + r16];
+      for (int q = 0; q < G::RQ; ++q)
 #pragma unroll
-        for (int rb = 0; rb < G::RBW; ++rb)
-          acc[rb][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(au, bw[rb], acc[rb][j], 0, 0, 0);
+        for (int c = 0; c < G::NCG; ++c)
+          acc[q][c] = __builtin_amdgcn_mfma_f32_4x4x1f32(au[c], bw[q], acc[q][c], 0, 0, 0);
+    }
+  };
+
+  // The small loads first: the first stage's log inputs are issued ahead of the tile and
+  // waited for alone, so their LDS stores are made while the tile streams in.  Slots past
+  // the stage read zeros through out-of-range buffer offsets (no branch around a load).
+  const int cnt0 = min(G::ME, n);
+  constexpr int JW = (G::ME * DK / 8 + G::NT - 1) / G::NT;  // weight jobs per thread
+  constexpr int JU = (G::ME * DV / 4 + G::NT - 1) / G::NT;  // factor jobs per thread
+  const auto rk = make_rsrc(p.log_k + lbase * DK, (uint32_t)(p.L * DK * 2));
+  const auto rc = make_rsrc(p.log_c + lbase * CW, (uint32_t)(p.L * CW * 4));
+  const auto ru = make_rsrc(log_u + lbase * DV, (uint32_t)(p.L * DV * sizeof(UT)));
+  uint4 k8[JW];
+  float ce[JW][VEC ? 8 : 1], cn[JW][VEC ? 8 : 1];
+  float4 u4[JU];
+#pragma unroll
+  for (int jw = 0; jw < JW; ++jw) {
+    const int job = tid + jw * G::NT, m = job / (DK / 8), i0 = (job % (DK / 8)) * 8;
+    const bool ok = m < cnt0;
+    k8[jw] = bload16(rk, ok ? (uint32_t)((m * DK + i0) * 2) : kOutOfRange);
+    if constexpr (VEC) {
+      bload8f(rc, ok ? (uint32_t)((m * DK + i0) * 4) : kOutOfRange, ce[jw]);
+      bload8f(rc, (uint32_t)(((n - 1) * DK + i0) * 4), cn[jw]);
+    } else {
+      ce[jw][0] = bload4f(rc, ok ? (uint32_t)(m * 4) : kOutOfRange);
+      cn[jw][0] = bload4f(rc, (uint32_t)((n - 1) * 4));
+    }
+  }
+#pragma unroll
+  for (int ju = 0; ju < JU; ++ju) {
+    const int job = tid + ju * G::NT, m = job / (DV / 4), j0 = (job % (DV / 4)) * 4;
+    u4[ju] = bload_factor4(ru, m < cnt0 ? (uint32_t)((m * DV + j0) * sizeof(UT)) : kOutOfRange, UT{});
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // The tile: lane (b, r4) holds row 16 wave + 4 q + r4, columns col(c, b, 0..3).
+  auto* tb = BIO::tile(p.base, (size_t)tile * DK * DV);
+  auto row = [&](int q) { return 16 * wave + 4 * q + r4; };
+  f32x4 acc[G::RQ][G::NCG];
+#pragma unroll
+  for (int q = 0; q < G::RQ; ++q) {
+    if constexpr (G::PAIR) {
+      const uint4 w = *reinterpret_cast<const uint4*>(tb + (size_t)row(q) * DV + G::col(0, b, 0));
+      const float4 x = widen4(make_uint2(w.x, w.y)), y = widen4(make_uint2(w.z, w.w));
+      acc[q][0] = f32x4{x.x, x.y, x.z, x.w};
+      acc[q][1] = f32x4{y.x, y.y, y.z, y.w};
+    } else {
+#pragma unroll
+      for (int c = 0; c < G::NCG; ++c) {
+        const float4 x = BIO::load(tb, ((size_t)row(q) * DV + G::col(c, b, 0)) / 4);
+        acc[q][c] = f32x4{x.x, x.y, x.z, x.w};
       }
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
+  // the first stage into LDS, and the scale
+#pragma unroll
+  for (int jw = 0; jw < JW; ++jw) {
+    const int job = tid + jw * G::NT, m = job / (DK / 8), i0 = (job % (DK / 8)) * 8;
+    if (m < cnt0) {
+      float kf[8], w[8];
+      unpack8(k8[jw], kf);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = exp2f(cn[jw][VEC ? i : 0] - ce[jw][VEC ? i : 0]) * kf[i];
+      float4* dst = reinterpret_cast<float4*>(s_w + m * G::WS + i0);
+      dst[0] = make_float4(w[0], w[1], w[2], w[3]);
+      dst[1] = make_float4(w[4], w[5], w[6], w[7]);
+    }
+  }
+#pragma unroll
+  for (int ju = 0; ju < JU; ++ju) {
+    const int job = tid + ju * G::NT, m = job / (DV / 4), j0 = (job % (DV / 4)) * 4;
+    if (m < cnt0) *reinterpret_cast<float4*>(s_u + m * G::US + G::upos(j0)) = u4[ju];
+  }
+  for (int i = tid; i < CW; i += G::NT) s_g[i] = exp2f(cnow[i]);
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < G::RQ; ++q) {
+    const float sc = s_g[VEC ? row(q) : 0];
+#pragma unroll
+    for (int c = 0; c < G::NCG; ++c) acc[q][c] *= sc;
+  }
+  fold(cnt0, acc);
+  for (int e0 = G::ME; e0 < n; e0 += G::ME) {
+    const int cnt = min(G::ME, n - e0);
+    __syncthreads();  // the previous stage's operand reads are done
+    stage(e0, cnt);
+    __syncthreads();
+    fold(cnt, acc);
+  }
 
 #pragma unroll
-  for (int rb = 0; rb < G::RBW; ++rb) {
+  for (int q = 0; q < G::RQ; ++q) {
     if constexpr (G::PAIR) {
-#pragma unroll
-      for (int j = 0; j < G::CBW; j += 2) {
-        const f32x4 a = acc[rb][j], b = acc[rb][j + 1];
-        const uint4 w = make_uint4(f32_to_bf16_rne(a[0]) | (f32_to_bf16_rne(a[1]) << 16),
-                                   f32_to_bf16_rne(a[2]) | (f32_to_bf16_rne(a[3]) << 16),
-                                   f32_to_bf16_rne(b[0]) | (f32_to_bf16_rne(b[1]) << 16),
-                                   f32_to_bf16_rne(b[2]) | (f32_to_bf16_rne(b[3]) << 16));
-        *reinterpret_cast<uint4*>(tb + (size_t)row(rb) * DV + G::col(wc * G::CBW + j, 4 * g)) = w;
-      }
+      const f32x4 x = acc[q][0], y = acc[q][1];
+      const uint4 w = make_uint4(f32_to_bf16_rne(x[0]) | (f32_to_bf16_rne(x[1]) << 16),
+                                 f32_to_bf16_rne(x[2]) | (f32_to_bf16_rne(x[3]) << 16),
+                                 f32_to_bf16_rne(y[0]) | (f32_to_bf16_rne(y[1]) << 16),
+                                 f32_to_bf16_rne(y[2]) | (f32_to_bf16_rne(y[3]) << 16));
+      *reinterpret_cast<uint4*>(tb + (size_t)row(q) * DV + G::col(0, b, 0)) = w;
     } else {
 #pragma unroll
-      for (int j = 0; j < G::CBW; ++j) {
-        const f32x4 x = acc[rb][j];
-        BIO::store(tb, ((size_t)row(rb) * DV + G::col(wc * G::CBW + j, 4 * g)) / 4,
-                   make_float4(x[0], x[1], x[2], x[3]));
+      for (int c = 0; c < G::NCG; ++c) {
+        const f32x4 x = acc[q][c];
+        BIO::store(tb, ((size_t)row(q) * DV + G::col(c, b, 0)) / 4, make_float4(x[0], x[1], x[2], x[3]));
       }
     }
   }

@@ -1,5 +1,5 @@
 """GPU parity of the fold's two arithmetic units (dl_merge_on): vector FMAs on a
-streamed tile, and v_mfma_f32_16x16x4_f32 on a register-resident tile.
+streamed tile, and v_mfma_f32_4x4x1_16b_f32 on a register-resident tile.
 
 Each case decodes from ragged start fills, then merges a copy of the pool with
 each unit.  Integer results are exact: the fills of merged tiles become 0, the
