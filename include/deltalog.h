@@ -156,8 +156,10 @@ enum {
 
 /* dl_merge with the fold's arithmetic unit named by the caller (the merge of
  * the DeltaLog Abstract, a rank-n update of each base, n = the tile's fill).
- * Both units compute the same fp32 update and differ only in the order of the
- * additions (relative differences of order 1e-7).  Errors: those of dl_merge,
+ * On an fp32 base both units give the same bits: each scales the base, then
+ * adds the entries one at a time in log order with one fused multiply-add per
+ * element.  A bf16 base is rounded once by the MFMA fold and once per stage of
+ * 16 entries (32 at 64 x 64) by the vector fold.  Errors: those of dl_merge,
  * and DL_EINVAL for a unit outside the enum above. */
 int dl_merge_on(const dl_dims *dims, const dl_pool *pool, int32_t min_fill, int32_t unit, void *stream);
 
