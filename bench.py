@@ -9,7 +9,8 @@ cycled).  Prints one JSON line.
 Also measured in the same run: the eager comparator (dl_eager_step, read and
 write the whole state every step) on the same inputs, a cache-cold variant
 (three independent pools used in turn, 480 MB, more than the 256 MB
-last-level cache), and the fp64 CPU oracle on the host cores.
+last-level cache), dl_prefill of a long prompt, dl_merge_on on full logs with
+each arithmetic unit of the fold, and the fp64 CPU oracle on the host cores.
 
   python bench.py [--gpus 1] [--steps 1024] [--warmup 32] [--workload 2]
                   [--no-cpu-baseline] [--graph] [--only deltalog|eager|copy|prefill|merge]
@@ -615,6 +616,7 @@ def main():
                              "hbm_gbs_algorithmic": mdl["total"] * tiles / t_cold / 1e9,
                              "frac": mdl["total"] * tiles / t_cold / 1e9 / HBM_PEAK_GBS},
         "prefill": result.get("prefill"),
+        "merge": merge_leg(args, inp, T, ios, base_dt),
     }
     print(json.dumps(line))
 
