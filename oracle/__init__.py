@@ -13,4 +13,4 @@ Modules:
 """
 from .recurrences import eager_step, gdn_step, kaczmarz_beta, kda_step, rwkv6_step  # noqa: F401
 from .deferred import DeferredTile, round_to_bf16  # noqa: F401
-from .drive import deferred_tiles, rel_err, run_deferred, run_eager, step_arrays  # noqa: F401
+from .drive import deferred_tiles, elem_rel_err, rel_err, run_deferred, run_eager, step_arrays  # noqa: F401

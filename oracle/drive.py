@@ -122,3 +122,23 @@ def rel_err(got: np.ndarray, ref: np.ndarray, axes=None) -> float:
     den = np.max(np.abs(ref), axis=axes)
     den = np.where(den == 0, 1.0, den)
     return float(np.max(num / den))
+
+
+def elem_rel_err(got: np.ndarray, ref: np.ndarray, axes=None, floor: float = 1e-6) -> float:
+    """Largest element-wise relative error |got - ref| / max(|ref|, floor * max|ref|).
+
+    The floor is taken per tensor (the same trailing `axes` as rel_err), so an
+    element whose reference is near zero is measured against a millionth of its
+    tensor's largest magnitude instead of against itself.  A tensor whose
+    reference is all zeros is measured in absolute terms.  This is the
+    element-wise companion of rel_err, reported beside it; the parity bar is
+    rel_err's.
+    """
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if axes is None:
+        axes = tuple(range(ref.ndim))
+    scale = np.max(np.abs(ref), axis=axes, keepdims=True)
+    scale = np.where(scale == 0, 1.0 / floor, scale)
+    den = np.maximum(np.abs(ref), floor * scale)
+    return float(np.max(np.abs(got - ref) / den))

@@ -167,3 +167,178 @@ def test_deferred_mutant_is_caught(cls):
 def test_kaczmarz_mutant_is_caught(kbeta):
     with pytest.raises(AssertionError):
         P.pin_kaczmarz_step_size(oracle.eager_step, kbeta)
+
+
+# ------------------------------------------------------ the seeded driver ----
+def _rel_err_mutant(kind):
+    def rel_err(got, ref, axes=None):
+        got = np.asarray(got, np.float64)
+        ref = np.asarray(ref, np.float64)
+        if axes is None:
+            axes = tuple(range(ref.ndim))
+        d = np.abs(got - ref)
+        num = np.mean(d, axis=axes) if kind == "mean_of_errors" else np.max(d, axis=axes)
+        if kind == "global_scale":
+            den = np.max(np.abs(ref)) + 0 * num
+        elif kind == "scale_from_got":
+            den = np.max(np.abs(got), axis=axes)
+        elif kind == "signed_scale":
+            den = np.max(ref, axis=axes)
+        else:
+            den = np.max(np.abs(ref), axis=axes)
+        if kind != "zero_reference_unhandled":
+            den = np.where(den == 0, 1.0, den)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r = num / den
+        return float(np.mean(r) if kind == "mean_over_tensors" else np.max(r))
+    return rel_err
+
+
+@pytest.mark.parametrize("kind", ["global_scale", "mean_of_errors", "scale_from_got", "signed_scale",
+                                  "mean_over_tensors", "zero_reference_unhandled"])
+def test_rel_err_mutant_is_caught(kind):
+    with pytest.raises(AssertionError):
+        P.pin_rel_err(_rel_err_mutant(kind))
+
+
+def _elem_rel_err_mutant(kind):
+    def elem_rel_err(got, ref, axes=None, floor=1e-6):
+        got = np.asarray(got, np.float64)
+        ref = np.asarray(ref, np.float64)
+        if axes is None:
+            axes = tuple(range(ref.ndim))
+        if kind == "global_floor":
+            scale = np.max(np.abs(ref)) + np.zeros(np.max(np.abs(ref), axis=axes, keepdims=True).shape)
+        else:
+            scale = np.max(np.abs(ref), axis=axes, keepdims=True)
+        scale = np.where(scale == 0, 1.0 / floor, scale)
+        if kind == "no_floor":
+            den = np.abs(ref)
+        elif kind == "floor_added":
+            den = np.abs(ref) + floor * scale
+        else:
+            den = np.maximum(np.abs(ref), floor * scale)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            return float(np.max(np.abs(got - ref) / den))
+    return elem_rel_err
+
+
+@pytest.mark.parametrize("kind", ["global_floor", "no_floor", "floor_added"])
+def test_elem_rel_err_mutant_is_caught(kind):
+    with pytest.raises(AssertionError):
+        P.pin_elem_rel_err(_elem_rel_err_mutant(kind))
+
+
+def _step_arrays_mutant(kind):
+    import oracle.drive as D
+
+    def step_arrays(inp, t, sel=None):
+        if kind == "bits_as_integers":
+            saved = D.bf16_bits_to_f32
+            D.bf16_bits_to_f32 = lambda b: np.asarray(b, np.uint16).astype(np.float32)
+            try:
+                return oracle.step_arrays(inp, t, sel)
+            finally:
+                D.bf16_bits_to_f32 = saved
+        if kind == "bits_as_half":
+            saved = D.bf16_bits_to_f32
+            D.bf16_bits_to_f32 = lambda b: np.asarray(b, np.uint16).view(np.float16).astype(np.float32)
+            try:
+                with np.errstate(all="ignore"):
+                    return oracle.step_arrays(inp, t, sel)
+            finally:
+                D.bf16_bits_to_f32 = saved
+        if kind == "sel_swapped":
+            return oracle.step_arrays(inp, t, None if sel is None else [(h, b) for b, h in sel])
+        out = oracle.step_arrays(inp, t, sel)
+        if kind == "bonus_per_sequence" and out["bonus"] is not None:
+            bo = inp.bonus.astype(np.float64)
+            out["bonus"] = (np.stack([bo[b] for b in range(inp.batch)])[:, None].repeat(inp.heads, 1)
+                            if sel is None else np.stack([bo[b] for b, _ in sel]))
+        if kind == "step_not_slot" and inp.eta is not None:
+            et = inp.eta[t].astype(np.float64)  # t instead of t mod P
+            et = et if sel is None else np.array([et[b, h] for b, h in sel])
+            out["beta"] = oracle.kaczmarz_beta(et, out["k"], inp.eps)
+        if kind == "eps_dropped" and inp.eta is not None:
+            et = inp.eta[inp.slot(t)].astype(np.float64)
+            et = et if sel is None else np.array([et[b, h] for b, h in sel])
+            out["beta"] = oracle.kaczmarz_beta(et, out["k"], 0.0)
+        return out
+    return step_arrays
+
+
+@pytest.mark.parametrize("kind", ["bits_as_integers", "bits_as_half", "sel_swapped", "bonus_per_sequence",
+                                  "step_not_slot", "eps_dropped"])
+def test_step_arrays_mutant_is_caught(kind):
+    with pytest.raises((AssertionError, IndexError)):
+        P.pin_step_arrays(_step_arrays_mutant(kind))
+
+
+def _run_eager_mutant(kind):
+    from oracle.drive import step_arrays
+    from oracle.recurrences import eager_step
+
+    def run_eager(inp, steps, sel=None, keep_outputs=True, check_every=None, s0=None):
+        if s0 is None or kind == "s0_ignored":
+            order = sorted(sel) if (kind == "sel_sorted" and sel is not None) else sel
+            s0 = inp.s0 if sel is None else np.stack([inp.s0[b, h] for b, h in order])
+        S = np.array(s0, dtype=np.float64)
+        outs = [] if keep_outputs else None
+        snaps = {}
+        marks = set(check_every or ())
+        prev_o = None
+        for t in range(steps - 1 if kind == "one_step_short" else steps):
+            a = step_arrays(inp, t, sel)
+            if kind == "snapshot_before_step" and t in marks:
+                snaps[t] = S.copy()
+            S, o = eager_step(inp.variant, S, a["q"], a["k"], a["v"], a["decay"], a["beta"], a["bonus"])
+            if keep_outputs:
+                outs.append(o if kind != "previous_output" or prev_o is None else prev_o)
+            prev_o = o
+            if t in marks and kind != "snapshot_before_step":
+                snaps[t] = S.copy()
+        res = (S, None if outs is None else np.stack(outs))
+        return res + (snaps,) if check_every is not None else res
+    return run_eager
+
+
+@pytest.mark.parametrize("kind", ["one_step_short", "snapshot_before_step", "previous_output", "sel_sorted",
+                                  "s0_ignored"])
+def test_run_eager_mutant_is_caught(kind):
+    with pytest.raises(AssertionError):
+        P.pin_run_eager(_run_eager_mutant(kind))
+
+
+def _run_deferred_mutant(kind):
+    from oracle.drive import deferred_tiles, step_arrays
+
+    def run_deferred(inp, steps, sel, log_len=None, low_bit_base=False):
+        if kind == "fill0_ignored":
+            saved = inp.fill0
+            inp.fill0 = np.zeros_like(saved)
+        try:
+            tiles = deferred_tiles(inp, sel, None if kind == "log_len_ignored" else log_len, low_bit_base)
+        finally:
+            if kind == "fill0_ignored":
+                inp.fill0 = saved
+        outs, fills, slots = [], [], []
+        for t in range(steps):
+            a = step_arrays(inp, t, sel)
+            row_o, row_f, row_s = [], [], []
+            for i, tile in enumerate(tiles):
+                before = tile.fill
+                beta = None if a["beta"] is None else a["beta"][i]
+                row_o.append(tile.step(a["q"][i], a["k"][i], a["v"][i], a["decay"][i], beta))
+                row_f.append(before if kind == "fill_before_step" else tile.fill)
+                row_s.append(tile.fill if kind == "slot_after_step" else tile.last_slot)
+            outs.append(np.stack(row_o))
+            fills.append(row_f)
+            slots.append(row_s)
+        return tiles, np.stack(outs), np.array(fills), np.array(slots)
+    return run_deferred
+
+
+@pytest.mark.parametrize("kind", ["fill0_ignored", "log_len_ignored", "fill_before_step", "slot_after_step"])
+def test_run_deferred_mutant_is_caught(kind):
+    with pytest.raises(AssertionError):
+        P.pin_run_deferred(_run_deferred_mutant(kind))

@@ -76,3 +76,24 @@ def test_low_bit_base_deferred_model():
         assert np.array_equal(low.base, oracle.round_to_bf16(twin.base))
         assert np.array_equal(oracle.round_to_bf16(low.base), low.base)
     assert low.merges == 2
+
+
+# ------------------------------------------------------ the seeded driver ----
+def test_rel_err():
+    P.pin_rel_err(oracle.rel_err)
+
+
+def test_elem_rel_err():
+    P.pin_elem_rel_err(oracle.elem_rel_err)
+
+
+def test_step_arrays():
+    P.pin_step_arrays(oracle.step_arrays)
+
+
+def test_run_eager():
+    P.pin_run_eager(oracle.run_eager)
+
+
+def test_run_deferred():
+    P.pin_run_deferred(oracle.run_deferred)
