@@ -2,13 +2,14 @@
  * deltalog.h -- C ABI of the DeltaLog decode library for AMD MI355X (gfx950).
  *
  * What it computes.  "DeltaLog: Deferred Materialization of Recurrent States
- * for Linear Attention Decoding" (newx.sg page, Abstract) represents a linear
- * attention layer's recurrent state as a dense base state plus a bounded log of
- * recent compact updates: most decode steps only append update factors to the
- * log, periodic merge steps fold the log back into the base, and every output
- * equals the one eager decoding (read the whole state, update it, write it
- * back every token) would give.  The same page's AI Summary states that the
- * appends replace full state write-backs.  This library implements that
+ * for Linear Attention Decoding" (newx.sg page, Abstract) keeps a linear
+ * attention layer's recurrent state as two parts, a dense base and a log of
+ * bounded length that holds the latest low-rank updates.  A typical decode step
+ * only adds one update's factors to the log; now and then a merge folds the
+ * logged updates into the base; and every output is the one eager decoding
+ * (read the whole state, update it, write it back after each token) would
+ * give.  The page's AI Summary says the same: small appends take the place of
+ * whole-state write-backs.  This library implements that
  * scheme, and the eager comparator, for three recurrences the page names
  * (GDN, KDA, RWKV6).  With S the dk x dv state of one head, rows indexed by key
  * channel, and one decode step t:
@@ -139,8 +140,8 @@ int dl_init_state(const dl_dims *dims, const dl_pool *pool, const float *init_ba
 int dl_decode_step(const dl_dims *dims, const dl_pool *pool, const dl_step_io *io, void *stream);
 
 /* Fold the log of every tile whose fill is >= min_fill (1 <= min_fill <= L)
- * into its base and set its fill to 0 (DeltaLog Abstract: merge steps fold
- * the accumulated updates back into the dense base).  min_fill = 1 folds every
+ * into its base and set its fill to 0 (DeltaLog Abstract: the merge that
+ * moves logged updates into the base).  min_fill = 1 folds every
  * non-empty log, after which `base` holds the dense state S_t of every tile
  * (for a checkpoint, or to read the state).  Errors: DL_EINVAL for min_fill
  * outside [1, L]. */
@@ -163,8 +164,8 @@ enum {
  * and DL_EINVAL for a unit outside the enum above. */
 int dl_merge_on(const dl_dims *dims, const dl_pool *pool, int32_t min_fill, int32_t unit, void *stream);
 
-/* The eager comparator (DeltaLog Abstract: materialize and write back the
- * full recurrent state after every generated token): reads `state` (device,
+/* The eager comparator (DeltaLog Abstract: the usual decoder, which rewrites
+ * the whole recurrent state after each generated token): reads `state` (device,
  * fp32 [batch][heads][dk][dv]), writes the updated state in place and io->out.
  * dims->log_len is ignored (may be any value in [1, 128]); base_dtype must be
  * DL_BASE_F32 (else DL_EUNSUPPORTED). */

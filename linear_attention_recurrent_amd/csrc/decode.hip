@@ -4,8 +4,9 @@
 // a dense base B plus a bounded log of rank-1 updates (k_j, u_j, c_j), with
 // c the cumulative log2-decay since the last merge ("DeltaLog: Deferred
 // Materialization of Recurrent States for Linear Attention Decoding",
-// Abstract: dense base state plus a bounded log of recent compact updates,
-// appends on most steps, periodic merges into the base).
+// Abstract: the state is a dense base and a length-bounded log of low-rank
+// updates; most steps only add to the log, and a merge now and then folds it
+// into the base).
 //
 // Decode step, per (sequence, head) tile, n = entries in the log:
 //   reads   r_k = B^T (2^c_t . k_t)  and  r_q = B^T (2^c_t . q_t)   one streamed pass over B

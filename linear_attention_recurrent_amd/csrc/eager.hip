@@ -2,8 +2,8 @@
 //
 // This is the comparator the DeltaLog page ("DeltaLog: Deferred
 // Materialization of Recurrent States for Linear Attention Decoding",
-// Abstract) measures against: existing decoders materialize and write back
-// the full recurrent state after every generated token.  Per (sequence, head)
+// Abstract) measures against: the usual decoder rewrites the whole recurrent
+// state in memory after each token it generates.  Per (sequence, head)
 // tile, with d the decay (alpha for GDN, a dk-vector for KDA and RWKV6):
 //   GDN/KDA  p = (diag(d) S)^T k,  u = beta (v - p),  S' = diag(d) S + k u^T,
 //            o = S'^T q = (diag(d) S)^T q + (k . q) u

@@ -2,7 +2,7 @@
 //
 // The same rank-n update as the vector fold in decode.hip ("DeltaLog: Deferred
 // Materialization of Recurrent States for Linear Attention Decoding", Abstract:
-// periodic merges fold the log of compact updates back into the dense base):
+// a merge folds the logged low-rank updates into the base from time to time):
 //   B <- diag(2^c_now) B + sum_{e<n} diag(2^(c_now - c_e)) k_e u_e^T
 // with c_now the cumulative log2-decay of the newest entry.  Here the whole tile
 // stays in registers for the fold, so it is read and written once at any log

@@ -4,11 +4,12 @@ TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import this module.
 
 This is DeltaLog's representation as the DeltaLog page ("DeltaLog: Deferred
 Materialization of Recurrent States for Linear Attention Decoding", Abstract)
-describes it: the recurrent state is a dense base state plus a bounded log of
-recent compact updates; most decode steps only append update factors to the
-log, and periodic merge steps fold the accumulated updates back into the base,
-so the model observes the same dense state as eager decoding.  The AI Summary
-of the same page says the appends replace full write-backs.
+describes it: the recurrent state is split into a dense base and a log of
+bounded length holding the latest low-rank updates; a typical decode step only
+adds an update's factors to the log, and now and then a merge folds the logged
+updates into the base, so the dense state the model sees is the eager one.
+The page's AI Summary says the same of appends taking the place of full
+write-backs.
 
 Representation used here (written for clarity, not speed, and independent of
 the GPU code, which keeps cumulative log2-decays instead).  With a low-bit base

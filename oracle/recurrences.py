@@ -5,28 +5,28 @@ TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import this module.
 Each function takes one decode step on every (sequence, head) state at once.
 States are float64 arrays [..., dk, dv] whose rows are key channels and whose
 columns are value channels; vectors are float64 [..., dk] or [..., dv].  The
-arithmetic is the plain dense (eager) recurrence, the one that "materializes
-and writes back the full recurrent state after every generated token"
-(DeltaLog page, Abstract).  DeltaLog reaches exactly this state ("the model
-observes the same dense state as in eager decoding", same passage), so this
-is the definition the deferred GPU path must reproduce up to rounding.
+arithmetic is the plain dense (eager) recurrence, the one the DeltaLog page's
+Abstract describes as the usual decoder, which rewrites the whole recurrent
+state after each token.  The same passage says DeltaLog leaves what the model
+computes unchanged, so the deferred state equals this one exactly, and this is
+the definition the deferred GPU path must reproduce up to rounding.
 
 Readings (the pages name the models but print no equations for them):
 
 * Gated DeltaNet: gated state decay followed by a delta-rule residual write
-  (Kaczmarz Linear Attention abstract, on the DeltaLog card page; "subtract
-  the current read before writing a new value", Gated DeltaNet-2 abstract on
-  the Q-Delta card page).  The read uses the decayed state, the write is the
+  (Kaczmarz Linear Attention abstract, on the DeltaLog card page; the Gated
+  DeltaNet-2 abstract on the Q-Delta card page describes a delta rule as
+  taking away what the state already returns for the key before writing).  The read uses the decayed state, the write is the
   rank-1 outer product k u^T, and the output is read from the updated state:
       D   = alpha * S
       u   = beta * (v - D^T k)
       S'  = D + k u^T
       o   = S'^T q
   No 1/sqrt(dk) query scale.
-* KDA: the same with channel-wise decay on the key rows, D = diag(a) S (KDA
-  "sharpens forgetting with channel-wise decay", Gated DeltaNet-2 abstract).
-  With a = alpha * 1 it is Gated DeltaNet ("reducing ... to Gated DeltaNet
-  when the decay also collapses", same abstract).
+* KDA: the same with channel-wise decay on the key rows, D = diag(a) S (per
+  channel forgetting, Gated DeltaNet-2 abstract).  With a = alpha * 1 it is
+  Gated DeltaNet (the same abstract: KDA becomes Gated DeltaNet once its decay
+  is one scalar).
 * RWKV6: diagonal per-channel decay, an additive outer-product write and a
   bonus readout through the pre-update state:
       o   = S^T r + (sum_i r_i bonus_i k_i) v

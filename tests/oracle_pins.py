@@ -190,7 +190,7 @@ def pin_kda_reduces_to_gdn(step):
 # ------------------------------------------------------------------- P6/P7 -
 def pin_deferred_equals_eager(tile_cls, step, log_lens=(1, 2, 3, 8, 16, 64), T=150):
     """Deferred base + log equals the eager recurrence at every step (DeltaLog
-    Abstract: the model observes the same dense state as in eager decoding),
+    Abstract: the deferred form leaves the dense state the model sees unchanged),
     and the merge schedule is the closed form (n0 + t) mod L."""
     for variant in (0, 1, 2):
         for L in log_lens:
