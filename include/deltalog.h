@@ -139,12 +139,21 @@ int dl_init_state(const dl_dims *dims, const dl_pool *pool, const float *init_ba
  * not match the variant (GDN/KDA: exactly one of beta and eta; RWKV6: bonus only). */
 int dl_decode_step(const dl_dims *dims, const dl_pool *pool, const dl_step_io *io, void *stream);
 
+/* Merge modes: the two named values of dl_merge's min_fill. */
+enum {
+  DL_MERGE_DUE = 0, /* fold only logs that are due, i.e. full: a decode step folds a log in
+                       the same call that fills it, so between calls none is due and this
+                       mode leaves the pool unchanged (after the argument checks)          */
+  DL_MERGE_ALL = 1  /* fold every non-empty log: min_fill = 1                               */
+};
+
 /* Fold the log of every tile whose fill is >= min_fill (1 <= min_fill <= L)
  * into its base and set its fill to 0 (DeltaLog Abstract: the merge that
- * moves logged updates into the base).  min_fill = 1 folds every
- * non-empty log, after which `base` holds the dense state S_t of every tile
- * (for a checkpoint, or to read the state).  Errors: DL_EINVAL for min_fill
- * outside [1, L]. */
+ * moves logged updates into the base).  min_fill = DL_MERGE_ALL (1) folds
+ * every non-empty log, after which `base` holds the dense state S_t of every
+ * tile (for a checkpoint, or to read the state); min_fill = DL_MERGE_DUE (0)
+ * folds only full logs, of which there are none between calls.  Errors:
+ * DL_EINVAL for min_fill outside [0, L]. */
 int dl_merge(const dl_dims *dims, const dl_pool *pool, int32_t min_fill, void *stream);
 
 /* Arithmetic unit of a fold, for dl_merge_on. */
@@ -160,8 +169,9 @@ enum {
  * On an fp32 base both units give the same bits: each scales the base, then
  * adds the entries one at a time in log order with one fused multiply-add per
  * element.  A bf16 base is rounded once by the MFMA fold and once per stage of
- * 16 entries (32 at 64 x 64) by the vector fold.  Errors: those of dl_merge,
- * and DL_EINVAL for a unit outside the enum above. */
+ * 16 entries (32 at 64 x 64) by the vector fold.  min_fill as for dl_merge
+ * (DL_MERGE_DUE, DL_MERGE_ALL or a threshold up to L).  Errors: those of
+ * dl_merge, and DL_EINVAL for a unit outside the enum above. */
 int dl_merge_on(const dl_dims *dims, const dl_pool *pool, int32_t min_fill, int32_t unit, void *stream);
 
 /* The eager comparator (DeltaLog Abstract: the usual decoder, which rewrites

@@ -136,10 +136,12 @@ static hipError_t launch_fold(const dl_dims* dims, const dl_pool* pool, int32_t 
 int dl_merge_on(const dl_dims* dims, const dl_pool* pool, int32_t min_fill, int32_t unit, void* stream) {
   int rc = check_dims(dims);
   if (rc != DL_OK) return rc;
-  if (min_fill < 1 || min_fill > dims->log_len) return DL_EINVAL;
+  if (min_fill < DL_MERGE_DUE || min_fill > dims->log_len) return DL_EINVAL;
   if (unit != DL_UNIT_AUTO && unit != DL_UNIT_VALU && unit != DL_UNIT_MFMA) return DL_EINVAL;
   if (dims->batch == 0) return DL_OK;
   if ((rc = check_pool(pool, dims->variant)) != DL_OK) return rc;
+  // a log is due when it holds L entries; the decode step folds it in the call that fills it
+  if (min_fill == DL_MERGE_DUE) return DL_OK;
   return hip_status(launch_fold(dims, pool, min_fill, unit, static_cast<hipStream_t>(stream)));
 }
 

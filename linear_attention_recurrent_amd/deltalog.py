@@ -21,6 +21,7 @@ GDN, KDA, RWKV6 = 0, 1, 2
 DL_OK, DL_EINVAL, DL_EUNSUPPORTED, DL_EALIGN, DL_EHIP = 0, -1, -2, -3, -4
 BASE_F32, BASE_BF16 = 0, 1
 UNIT_AUTO, UNIT_VALU, UNIT_MFMA = 0, 1, 2  # arithmetic unit of a fold (dl_merge_on)
+MERGE_DUE, MERGE_ALL = 0, 1                 # the named values of dl_merge's min_fill
 MAX_LOG_LEN = 128
 
 
@@ -124,7 +125,7 @@ class DeltaLogPool:
     def __init__(self, variant: int, batch: int, heads: int, dk: int, dv: int, log_len: int,
                  device="cuda", base_dtype: int = BASE_F32):
         self.device = torch.device(device)
-        if self.device.index is None:
+        if self.device.type == "cuda" and self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
         self.variant, self.batch, self.heads = int(variant), int(batch), int(heads)
         self.dk, self.dv, self.log_len = int(dk), int(dv), int(log_len)
@@ -138,7 +139,8 @@ class DeltaLogPool:
         self.log_u = torch.empty((B, H, L, dv), dtype=torch.bfloat16 if variant == RWKV6 else torch.float32,
                                  **kw)
         self.log_c = torch.empty((B, H, L, g), dtype=torch.float32, **kw)
-        self.fill = torch.empty((B, H), dtype=torch.int32, **kw)
+        # zeros: a pool used before dl_init_state holds empty logs, never stray fills
+        self.fill = torch.zeros((B, H), dtype=torch.int32, **kw)
         self.c_dims = Dims(self.variant, B, H, self.dk, self.dv, L, self.base_dtype)
         self.c_pool = Pool(self.base.data_ptr(), self.log_k.data_ptr(), self.log_u.data_ptr(),
                            self.log_c.data_ptr(), self.fill.data_ptr())

@@ -113,13 +113,20 @@ def test_merge_init_eager_errors(lib):
     from linear_attention_recurrent_amd import deltalog as dl
     d = _dims(dl, L=16)
     p = _pool(dl)
-    assert lib.dl_merge(ctypes.byref(d), ctypes.byref(p), 0, None) == dl.DL_EINVAL
+    assert lib.dl_merge(ctypes.byref(d), ctypes.byref(p), -1, None) == dl.DL_EINVAL
     assert lib.dl_merge(ctypes.byref(d), ctypes.byref(p), 17, None) == dl.DL_EINVAL
+    # DL_MERGE_DUE: nothing is due between calls, so it checks its arguments and launches nothing
+    # (the pool's pointers are fake here: a launch would fault)
+    assert dl.MERGE_DUE == 0 and dl.MERGE_ALL == 1
+    assert lib.dl_merge(ctypes.byref(d), ctypes.byref(p), dl.MERGE_DUE, None) == dl.DL_OK
+    assert lib.dl_merge(ctypes.byref(d), None, dl.MERGE_DUE, None) == dl.DL_EINVAL
+    assert lib.dl_merge(ctypes.byref(d), ctypes.byref(dl.Pool(M, A, A, A, A)), dl.MERGE_DUE, None) == dl.DL_EALIGN
     assert lib.dl_merge(ctypes.byref(d), None, 1, None) == dl.DL_EINVAL
     for unit in (-1, 3):
         assert lib.dl_merge_on(ctypes.byref(d), ctypes.byref(p), 1, unit, None) == dl.DL_EINVAL
     for unit in (dl.UNIT_AUTO, dl.UNIT_VALU, dl.UNIT_MFMA):
-        assert lib.dl_merge_on(ctypes.byref(d), ctypes.byref(p), 0, unit, None) == dl.DL_EINVAL
+        assert lib.dl_merge_on(ctypes.byref(d), ctypes.byref(p), -1, unit, None) == dl.DL_EINVAL
+        assert lib.dl_merge_on(ctypes.byref(d), ctypes.byref(p), dl.MERGE_DUE, unit, None) == dl.DL_OK
         assert lib.dl_merge_on(ctypes.byref(d), None, 1, unit, None) == dl.DL_EINVAL
     fills = (ctypes.c_int32 * 2)(0, 16)
     assert lib.dl_init_state(ctypes.byref(d), ctypes.byref(p), None, fills, None) == dl.DL_EINVAL
@@ -191,3 +198,16 @@ def test_prefill_errors(lib):
     # batch 0: nothing is looked at
     empty = dl.Pool(None, None, None, None, None)
     assert _prefill(lib, _dims(dl, batch=0), empty, _pio(dl, q=None, k=None, v=None, out=None)) == dl.DL_OK
+
+
+def test_pool_wrapper_starts_with_empty_logs():
+    """The binding's pool allocates its fills as zeros, so a pool used before
+    dl_init_state indexes no log slot (host-side allocation check, on the CPU)."""
+    import torch
+
+    from linear_attention_recurrent_amd import deltalog as dl
+    for variant, dk, dv in ((dl.GDN, 128, 128), (dl.KDA, 128, 64), (dl.RWKV6, 64, 64)):
+        p = dl.DeltaLogPool(variant, 3, 2, dk, dv, 8, device="cpu")
+        assert p.fill.dtype == torch.int32 and tuple(p.fill.shape) == (3, 2)
+        assert int(p.fill.abs().max()) == 0
+        assert tuple(p.log_c.shape) == (3, 2, 8, 1 if variant == dl.GDN else dk)

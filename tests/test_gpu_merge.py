@@ -38,7 +38,8 @@ def _gpu():
 
 def _close(what, got, ref, axes, tol=TOL):
     err = oracle.rel_err(got, ref, axes)
-    print(f"{what}: max per-tensor rel err {err:.3e}", flush=True)
+    print(f"{what}: max per-tensor rel err {err:.3e}, element-wise (floor 1e-6 of the tensor's scale) "
+          f"{oracle.elem_rel_err(got, ref, axes):.3e}", flush=True)
     assert err <= tol, (what, err)
     return err
 

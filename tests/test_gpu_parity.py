@@ -26,7 +26,8 @@ def _gpu():
 
 def _close(what, got, ref, axes):
     err = oracle.rel_err(got, ref, axes)
-    print(f"{what}: max per-tensor rel err {err:.3e}", flush=True)
+    print(f"{what}: max per-tensor rel err {err:.3e}, element-wise (floor 1e-6 of the tensor's scale) "
+          f"{oracle.elem_rel_err(got, ref, axes):.3e}", flush=True)
     assert err <= TOL, (what, err)
     return err
 
