@@ -6,14 +6,22 @@ the log.  Default workload: GDN, batch 64, 32 heads, dk = dv = 128, L = 16,
 all logs starting empty, inputs resident in HBM (a pool of 64 drawn steps,
 cycled).  Prints one JSON line.
 
-Also measured in the same run: the eager comparator (dl_eager_step, read and
-write the whole state every step) on the same inputs, a cache-cold variant
-(three independent pools used in turn, 480 MB, more than the 256 MB
-last-level cache), dl_prefill of a long prompt, dl_merge_on on full logs with
-each arithmetic unit of the fold, and the fp64 CPU oracle on the host cores.
+The headline is cache-cold: independent pools of the workload's shape are used
+in turn (three for this one, 480 MB), more than the 256 MiB last-level cache
+holds, so each step reads its state from HBM as a model with several layers
+does.  The timed steps are a whole number of fold periods of every pool.
+
+Also measured in the same run: the same step on one pool (its working set can
+stay in the last-level cache: reported as cache-resident), the eager comparator
+(dl_eager_step, read and write the whole state every step) on the same inputs,
+cold and cache-resident, read-only ceilings (a torch sum over 1 GiB, and the
+tile-read probe of libdlprobe.so over the same pools), plain copies,
+dl_prefill of a long prompt, dl_merge_on on full logs with each arithmetic unit
+of the fold, and the fp64 CPU oracle on the host cores.
 
   python bench.py [--gpus 1] [--steps 1024] [--warmup 32] [--workload 2]
-                  [--no-cpu-baseline] [--graph] [--only deltalog|eager|copy|prefill|merge]
+                  [--no-cpu-baseline] [--graph]
+                  [--only deltalog|warm|eager|ceiling|copy|prefill|merge]
                   [--base-dtype f32|bf16] [--log-len L]
 
 `--only merge` times dl_merge_on on full logs with each arithmetic unit of the
@@ -36,6 +44,7 @@ sys.path.insert(0, ROOT)
 from inputs import VARIANT_NAMES, WORKLOADS, make_inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published figure
+MALL_BYTES = 256 << 20  # MI355X last-level (Infinity) cache
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["linear_attention_recurrent_amd/csrc/decode.hip",
                   "linear_attention_recurrent_amd/csrc/dl_device.hpp"]
@@ -259,6 +268,35 @@ def time_loop(fn, steps, warmup, graph_chunk=0):
     return start.elapsed_time(end) / 1e3
 
 
+def read_ceilings(pools, tiles, tile_bytes, launches):
+    """Read-only rates on this machine, in the same run: a torch sum over 1 GiB, and the
+    tile-read probe (libdlprobe.so: one workgroup reads one tile, nothing else) over the
+    base tensors of `pools`, used in turn as the decode step uses them."""
+    import ctypes
+
+    import torch
+    dev = torch.device("cuda", 0)
+    out = {}
+    x = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)
+    secs = time_loop(lambda t: x.sum(), 10, 3)
+    out["torch_sum_gbs"] = (1 << 30) * 10 / secs / 1e9
+    del x
+    lib = ctypes.CDLL(os.path.join(ROOT, "linear_attention_recurrent_amd", "libdlprobe.so"))
+    lib.dl_probe_tile_read.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    if pools:
+        def rd(t):
+            rc = lib.dl_probe_tile_read(pools[t % len(pools)].base.data_ptr(), tile_bytes, tiles, sink.data_ptr(),
+                                        stream)
+            if rc != 0:
+                raise RuntimeError(f"dl_probe_tile_read failed ({rc})")
+        secs = time_loop(rd, launches, 2 * len(pools))
+        out["tile_read_gbs"] = tile_bytes * tiles * launches / secs / 1e9
+        out["tile_read_shape"] = f"{tiles} tiles of {tile_bytes} B per launch, {len(pools)} pools in turn"
+    return out
+
+
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD's published figure
 PREFILL_CHUNK = 32
 
@@ -388,7 +426,10 @@ def serving_leg(args, cpu) -> dict:
     pools = [dl.DeltaLogPool(var, B, H, dk, dv, L, dev, base_dt) for _ in range(layers)]
     for p_ in pools:
         dl.dl_init_state(p_, T["s0"], inp.fill0)
-    K, W = args.steps, args.warmup
+    # ragged start fills spread the folds over every step; the timed steps are still a
+    # whole number of fold periods
+    K = -(-args.steps // L) * L
+    W = args.warmup
 
     def step(t):
         io = ios[t % P]
@@ -397,6 +438,9 @@ def serving_leg(args, cpu) -> dict:
     secs = time_loop(step, K, W)
     del pools
     torch.cuda.empty_cache()
+    if args.only == "deltalog":
+        print(json.dumps({"ms_per_step": secs / K * 1e3, "timed_steps": K, "layers": layers}))
+        raise SystemExit(0)
     Ke = max(1, K // 4)
     states = [T["s0"].clone() for _ in range(layers)]
 
@@ -421,7 +465,8 @@ def serving_leg(args, cpu) -> dict:
         "value": work / t_step,
         "unit": "state-steps/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
+        "timed_steps": K,
         "warmup": W,
         "ms_per_step": t_step * 1e3,
         "higher_is_better": True,
@@ -463,8 +508,9 @@ def main():
     ap.add_argument("--pool-slots", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step loop as a HIP graph")
-    ap.add_argument("--only", choices=["deltalog", "eager", "copy", "prefill", "merge"], default=None,
-                    help="run one leg only (for profiling runs)")
+    ap.add_argument("--only", choices=["deltalog", "warm", "eager", "copy", "prefill", "merge", "ceiling"],
+                    default=None, help="run one leg only (for profiling runs): deltalog = the cache-cold "
+                                       "headline leg, warm = one pool (cache-resident)")
     ap.add_argument("--prefill-tokens", type=int, default=4096,
                     help="prompt length of the prefill leg (GDN workloads)")
     ap.add_argument("--base-dtype", choices=["f32", "bf16"], default="f32",
@@ -512,45 +558,65 @@ def main():
     P = args.pool_slots
     tiles = B * H
     K, W = args.steps, args.warmup
-    chunk = 0
-    if args.graph:
-        chunk = L * max(1, 64 // L)
-        K = max(chunk, (K // chunk) * chunk)
-
     bf16_base = args.base_dtype == "bf16"
     base_dt = dl.BASE_BF16 if bf16_base else dl.BASE_F32
-    result = {}
-    if args.only in (None, "deltalog"):
-        pool = dl.DeltaLogPool(var, B, H, dk, dv, L, dev, base_dt)
-        dl.dl_init_state(pool, T["s0"], inp.fill0)
-        # W warmup steps, then K timed steps; both start the timed window at the same phase
-        W_al = ((W + L - 1) // L) * L
-        secs = time_loop(lambda t: dl.dl_decode_step(pool, ios[t % P]), K, W_al, chunk)
-        result["deltalog"] = secs
-    if args.only in (None, "eager"):
-        state = T["s0"].clone()
-        secs_e = time_loop(lambda t: dl.dl_eager_step(var, state, ios[t % P]), K, W, chunk)
-        result["eager"] = secs_e
     if args.only == "merge":
         print(json.dumps(merge_leg(args, inp, T, ios, base_dt)))
         return
-    if args.only == "prefill" or args.only is None:
-        result["prefill"] = prefill_leg(args, inp, T, base_dt)
-    if args.only is not None:
-        if args.only == "prefill":
-            print(json.dumps(result["prefill"]))
-        else:
-            print(json.dumps({k: v / K * 1e3 for k, v in result.items()} | {"unit": "ms per step"}))
+    if args.only == "prefill":
+        print(json.dumps(prefill_leg(args, inp, T, base_dt)))
         return
 
-    # cache-cold variant: three independent pools used in turn
-    pools = [dl.DeltaLogPool(var, B, H, dk, dv, L, dev, base_dt) for _ in range(3)]
-    for p_ in pools:
-        dl.dl_init_state(p_, T["s0"], inp.fill0)
-    W_al = ((W + 3 * L - 1) // (3 * L)) * (3 * L)
-    Kc = (K // (3 * L)) * (3 * L) or 3 * L
-    secs_c = time_loop(lambda t: dl.dl_decode_step(pools[t % 3], ios[t % P]), Kc, W_al)
+    # Cache-cold (the headline): NP independent pools used in turn, so that between two
+    # steps on one pool the other pools' traffic exceeds the 256 MiB last-level cache and
+    # every step reads its state from HBM, as a model with several layers would.  Every
+    # pool goes through whole fold periods: the timed steps are a multiple of NP * L.
+    eb = 2 if bf16_base else 4
+    pool_bytes = tiles * (eb * dk * dv + L * entry_bytes(var, dk, dv) + 4)
+    NP = 1 + -(-MALL_BYTES // pool_bytes)
+    period = NP * L
+    Kc = -(-K // period) * period
+    Wc = -(-W // period) * period
+    chunk = 0
+    if args.graph:
+        chunk = period * max(1, 64 // period)
+        Kc = -(-Kc // chunk) * chunk
+    result = {}
+    pools = []
+    if args.only in (None, "deltalog", "ceiling"):
+        pools = [dl.DeltaLogPool(var, B, H, dk, dv, L, dev, base_dt) for _ in range(NP)]
+        for p_ in pools:
+            dl.dl_init_state(p_, T["s0"], inp.fill0)
+    if args.only in (None, "deltalog"):
+        result["cold"] = time_loop(lambda t: dl.dl_decode_step(pools[t % NP], ios[t % P]), Kc, Wc, chunk)
+    if args.only in (None, "ceiling"):
+        result["ceiling"] = read_ceilings(pools, tiles, eb * dk * dv, Kc)
     del pools
+    # Cache-resident: one pool, whose working set may stay in the last-level cache.
+    Kw = -(-K // L) * L
+    Ww = -(-W // L) * L
+    if args.only in (None, "warm"):
+        pool = dl.DeltaLogPool(var, B, H, dk, dv, L, dev, base_dt)
+        dl.dl_init_state(pool, T["s0"], inp.fill0)
+        result["warm"] = time_loop(lambda t: dl.dl_decode_step(pool, ios[t % P]), Kw, Ww,
+                                   L * max(1, 64 // L) if args.graph else 0)
+        del pool
+    # The eager comparator, on as many states as the cold leg has pools, and on one.
+    if args.only in (None, "eager"):
+        NE = 1 + -(-MALL_BYTES // (tiles * 4 * dk * dv))
+        states = [T["s0"].clone() for _ in range(NE)]
+        result["eager_cold"] = time_loop(lambda t: dl.dl_eager_step(var, states[t % NE], ios[t % P]), Kw, W)
+        result["eager_warm"] = time_loop(lambda t: dl.dl_eager_step(var, states[0], ios[t % P]), Kw, W)
+        del states
+    torch.cuda.empty_cache()
+    if args.only is not None:
+        out = {k: v / (Kc if k == "cold" else Kw) * 1e3 for k, v in result.items() if k != "ceiling"}
+        out.update({"unit": "ms per step", "timed_steps_cold": Kc, "timed_steps": Kw})
+        if "ceiling" in result:
+            out["ceiling"] = result["ceiling"]
+        print(json.dumps(out))
+        return
+    result["prefill"] = prefill_leg(args, inp, T, base_dt)
 
     # copy ceilings on this machine: a plain device copy that fits the last-level cache
     # (2 x 64 MiB) and one that does not (2 x 1 GiB); read + write bytes over time
@@ -563,13 +629,16 @@ def main():
         copy[label] = 2 * nbytes * reps / secs_copy / 1e9
         del src, dst
 
-    mdl = deltalog_bytes_per_state_step(var, dk, dv, L, B, 2 if bf16_base else 4)
+    mdl = deltalog_bytes_per_state_step(var, dk, dv, L, B, eb)
     eag = eager_bytes_per_state_step(var, dk, dv, B)
-    t_step = result["deltalog"] / K
-    t_eager = result["eager"] / K
-    t_cold = secs_c / Kc
-    value = tiles / t_step
-    achieved = mdl["total"] * tiles / t_step / 1e9
+    launch_bytes = mdl["total"] * tiles
+    t_cold = result["cold"] / Kc
+    t_warm = result["warm"] / Kw
+    t_ecold = result["eager_cold"] / Kw
+    t_ewarm = result["eager_warm"] / Kw
+    achieved = launch_bytes / t_cold / 1e9
+    achieved_warm = launch_bytes / t_warm / 1e9
+    ceil = result["ceiling"]
     prof = read_counter_profile(w["name"], bf16_base)
     traffic = None
     counter_write = None
@@ -578,15 +647,15 @@ def main():
         counter_write = {"deltalog": float(prof["write_bytes_per_launch"]) / tiles,
                          "eager": float(prof.get("eager_write_bytes_per_launch", "nan")) / tiles,
                          "source": f"profiles/{counter_profile_name(w['name'], bf16_base)}"}
-
     line = {
         "metric": "decode state-steps/s (B×H per s)",
-        "value": value,
+        "value": tiles / t_cold,
         "unit": "state-steps/s",
         "n_gpus": 1,
         "steps": K,
+        "timed_steps": Kc,
         "warmup": W,
-        "ms_per_step": t_step * 1e3,
+        "ms_per_step": t_cold * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -594,27 +663,36 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w['name']}: {VARIANT_NAMES[var]} decode B={B} H={H} dk={dk} dv={dv} L={L}"
                                + (" (Kaczmarz step size)" if inp.eta is not None else "")
-                               + (", bf16 base" if bf16_base else ""),
+                               + (", bf16 base" if bf16_base else "")
+                               + f", cache-cold: {NP} pools of this shape used in turn, so each step reads "
+                                 f"its state from HBM",
                    "base": "bf16, rounded at each fold" if bf16_base else "f32",
                    "variant": VARIANT_NAMES[var], "batch": B, "heads": H, "dk": dk, "dv": dv,
                    "log_len": L, "initial_fill": "0 for every sequence" if not np.any(inp.fill0) else "ragged",
-                   "input_pool_steps": P, "hip_graph": bool(chunk)},
+                   "pools_in_turn": NP, "input_pool_steps": P, "hip_graph": bool(chunk)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "cpu_baseline": cpu,
         "hbm_gbs_algorithmic": achieved,
+        "hbm_target": {"frac_of_peak_needed": 0.70, "measured_cold_frac": achieved / HBM_PEAK_GBS,
+                       "met": achieved / HBM_PEAK_GBS >= 0.70,
+                       "frac_of_tile_read_ceiling": achieved / ceil["tile_read_gbs"],
+                       "frac_of_torch_sum_ceiling": achieved / ceil["torch_sum_gbs"]},
+        "read_ceiling_gbs": ceil,
+        "cache_resident": {"value": tiles / t_warm, "ms_per_step": t_warm * 1e3, "timed_steps": Kw,
+                           "hbm_gbs_algorithmic": achieved_warm, "frac": achieved_warm / HBM_PEAK_GBS,
+                           "note": "one pool, working set inside the 256 MiB last-level cache: "
+                                   "not an HBM rate"},
         "bytes_per_state_step_model": {"deltalog": mdl["total"], "eager": eag["total"]},
+        "bytes_per_launch_model": launch_bytes,
         "state_write_bytes_per_state_step": {
             "deltalog_model": mdl["state_writes"], "eager_model": eag["state_writes"],
             "cut_model": eag["state_writes"] / mdl["state_writes"], "counters": counter_write},
-        "eager": {"value": tiles / t_eager, "ms_per_step": t_eager * 1e3,
-                  "hbm_gbs_algorithmic": eag["total"] * tiles / t_eager / 1e9,
-                  "deltalog_speedup": t_eager / t_step},
-        "copy_ceiling_gbs": {**copy, "decode_frac_of_fits_cache": achieved / copy["fits_cache"],
-                             "cold_decode_frac_of_cold": mdl["total"] * tiles / t_cold / 1e9 / copy["cold"]},
-        "cold_three_pools": {"value": tiles / t_cold, "ms_per_step": t_cold * 1e3,
-                             "hbm_gbs_algorithmic": mdl["total"] * tiles / t_cold / 1e9,
-                             "frac": mdl["total"] * tiles / t_cold / 1e9 / HBM_PEAK_GBS},
+        "eager": {"value": tiles / t_ecold, "ms_per_step": t_ecold * 1e3, "timed_steps": Kw,
+                  "hbm_gbs_algorithmic": eag["total"] * tiles / t_ecold / 1e9,
+                  "deltalog_speedup": t_ecold / t_cold,
+                  "cache_resident": {"ms_per_step": t_ewarm * 1e3, "deltalog_speedup": t_ewarm / t_warm}},
+        "copy_ceiling_gbs": copy,
         "prefill": result.get("prefill"),
         "merge": merge_leg(args, inp, T, ios, base_dt),
     }

@@ -3,7 +3,9 @@
 Usage: python -m linear_attention_recurrent_amd.build [--verbose]
 
 Each translation unit is compiled to an object (in parallel), then linked into
-linear_attention_recurrent_amd/libdeltalog.so.  Always recompiles.
+linear_attention_recurrent_amd/libdeltalog.so.  The benchmark's read-rate probe
+is linked on its own into linear_attention_recurrent_amd/libdlprobe.so.  Always
+recompiles.
 """
 from __future__ import annotations
 
@@ -19,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdeltalog.so")
 SOURCES = ["decode.hip", "merge_mfma.hip", "eager.hip", "prefill.hip", "api.cpp"]
+PROBE_LIB = os.path.join(PKG, "libdlprobe.so")
+PROBE_SOURCES = ["read_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -56,20 +60,22 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     cc = hipcc()
     objs = []
     cmds = []
-    for src in SOURCES:
+    probe_objs = []
+    for src in SOURCES + PROBE_SOURCES:
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         cmd = [cc] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         if save_temps:
             cmd += ["--save-temps"]
-        objs.append(obj)
+        (probe_objs if src in PROBE_SOURCES else objs).append(obj)
         cmds.append(cmd)
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
-    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs, verbose)
-    os.replace(tmp, LIB)
+    for lib, lib_objs in ((LIB, objs), (PROBE_LIB, probe_objs)):
+        tmp = lib + ".tmp"
+        _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + lib_objs, verbose)
+        os.replace(tmp, lib)
     return LIB
 
 

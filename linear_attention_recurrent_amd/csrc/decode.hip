@@ -446,9 +446,9 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
       const float b = s.eta ? beta / (sh.kk + s.eps) : beta;
       u = b * (vcol - pk);
       o = fmaf(sh.dot, u, oq);
-      if constexpr (!FOLD) static_cast<float*>(p.log_u)[(lbase + n) * DV + tid] = u;
+      if constexpr (!FOLD) store_res(static_cast<float*>(p.log_u) + lbase * DV, (uint32_t)((n * DV + tid) * 4), u);
     }
-    s.out[(size_t)tile * DV + tid] = o;
+    store_res(s.out + (size_t)tile * DV, (uint32_t)(tid * 4), o);
     if constexpr (FOLD) {
       if (reg_stage) sh.uu[n * DV + tid] = u;  // the current update's fold factor
       else sh.ucur[tid] = u;
@@ -456,18 +456,18 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
   }
   if constexpr (!FOLD) {
     if (eg == 0) {
-      *reinterpret_cast<uint4*>(p.log_k + (lbase + n) * DK + ch * 8) = kt8;
+      store_res(p.log_k + lbase * DK, (uint32_t)((n * DK + ch * 8) * 2), kt8);
       if constexpr (VEC) {
-        float4* cp = reinterpret_cast<float4*>(p.log_c + (lbase + n) * DK + ch * 8);
-        cp[0] = *reinterpret_cast<const float4*>(sh.ct + ch * 8);
-        cp[1] = *reinterpret_cast<const float4*>(sh.ct + ch * 8 + 4);
+        float* cb = p.log_c + lbase * DK;
+        store_res(cb, (uint32_t)((n * DK + ch * 8) * 4), *reinterpret_cast<const float4*>(sh.ct + ch * 8));
+        store_res(cb, (uint32_t)((n * DK + ch * 8 + 4) * 4), *reinterpret_cast<const float4*>(sh.ct + ch * 8 + 4));
       } else {
-        if (ch == 0) p.log_c[lbase + n] = sh.ct[0];
+        if (ch == 0) store_res(p.log_c + lbase, (uint32_t)(n * 4), sh.ct[0]);
       }
     }
     if constexpr (VAR == DL_RWKV6) {
       if (tid < DV / 8)
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.log_u) + (lbase + n) * DV + tid * 8) = v8;
+        store_res(static_cast<uint16_t*>(p.log_u) + lbase * DV, (uint32_t)((n * DV + tid * 8) * 2), v8);
     }
     if (tid == 0) p.fill[tile] = n + 1;
   } else {
@@ -520,6 +520,7 @@ __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, 
   __shared__ DecodeLds<DK, DV, (VAR == DL_GDN ? 1 : DK), G::NW, G::MC> sh;
   const int tile = blockIdx.x;
   const int n = p.fill[tile];  // same for the whole workgroup
+  if (n < 0 || n >= p.L) return;  // a fill outside [0, L) (a pool never started): touch nothing
   if (n + 1 == p.L)
     decode_tile<VAR, DK, DV, BF, true>(p, s, tile, n, sh);
   else
@@ -535,7 +536,7 @@ __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) merge_kernel(PoolArgs p, i
   const int tid = threadIdx.x;
   const int tile = blockIdx.x;
   const int n = p.fill[tile];
-  if (n < min_fill || n == 0) return;  // uniform: the whole workgroup leaves
+  if (n < min_fill || n <= 0 || n >= p.L) return;  // uniform: the whole workgroup leaves
   const size_t lbase = (size_t)tile * p.L;
 
   __shared__ __attribute__((aligned(16))) float s_c[CW];  // c of the newest entry, natural order

@@ -124,6 +124,30 @@ __device__ __forceinline__ float4 bload_factor4(__amdgpu_buffer_rsrc_t r, uint32
   return widen4(bload8(r, off));
 }
 
+// Stores of results that nothing later in the same launch reads (outputs, log
+// appends, folded bases), non-temporal (the nt policy streams the line out of
+// the cache rather than keeping it), through a buffer resource at a
+// workgroup-uniform base; `off` is the lane's byte offset.  Measured on MI355X:
+// 1.7 % less time per decode step with the pool larger than the last-level cache.
+constexpr int kStreamStore = 2;  // buffer-store cache-policy bits: nt
+__device__ __forceinline__ void store_res(void* base, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), make_rsrc(base, 0x7fffffff), off, 0, kStreamStore);
+}
+__device__ __forceinline__ void store_res(void* base, uint32_t off, uint2 v) {
+  typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+  const u2v x = {v.x, v.y};
+  __builtin_amdgcn_raw_buffer_store_b64(x, make_rsrc(base, 0x7fffffff), off, 0, kStreamStore);
+}
+__device__ __forceinline__ void store_res(void* base, uint32_t off, uint4 v) {
+  typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+  const u4v x = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(x, make_rsrc(base, 0x7fffffff), off, 0, kStreamStore);
+}
+__device__ __forceinline__ void store_res(void* base, uint32_t off, float4 v) {
+  store_res(base, off, make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                                  __float_as_uint(v.w)));
+}
+
 // fp32 -> bf16 bits, round to nearest, ties to even (finite values).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   const uint32_t b = __float_as_uint(f);
@@ -139,7 +163,7 @@ struct BaseIO<false> {
   using T = float;
   __device__ static T* tile(void* base, size_t elem) { return static_cast<T*>(base) + elem; }
   __device__ static float4 load(const T* t, size_t g) { return reinterpret_cast<const float4*>(t)[g]; }
-  __device__ static void store(T* t, size_t g, float4 x) { reinterpret_cast<float4*>(t)[g] = x; }
+  __device__ static void store(T* t, size_t g, float4 x) { store_res(t, (uint32_t)(g * 16), x); }
 };
 template <>
 struct BaseIO<true> {
@@ -147,8 +171,8 @@ struct BaseIO<true> {
   __device__ static T* tile(void* base, size_t elem) { return static_cast<T*>(base) + elem; }
   __device__ static float4 load(const T* t, size_t g) { return widen4(reinterpret_cast<const uint2*>(t)[g]); }
   __device__ static void store(T* t, size_t g, float4 x) {
-    reinterpret_cast<uint2*>(t)[g] = make_uint2(f32_to_bf16_rne(x.x) | (f32_to_bf16_rne(x.y) << 16),
-                                                f32_to_bf16_rne(x.z) | (f32_to_bf16_rne(x.w) << 16));
+    store_res(t, (uint32_t)(g * 8), make_uint2(f32_to_bf16_rne(x.x) | (f32_to_bf16_rne(x.y) << 16),
+                                               f32_to_bf16_rne(x.z) | (f32_to_bf16_rne(x.w) << 16)));
   }
 };
 

@@ -63,7 +63,7 @@ __global__ void __launch_bounds__((MfmaFoldGeo<DK, DV, BF>::NT)) merge_mfma_kern
   const int b = lane >> 2, r4 = lane & 3;  // block and row within the four-row group
   const int tile = blockIdx.x;
   const int n = p.fill[tile];
-  if (n < min_fill || n == 0) return;  // uniform: the whole workgroup leaves
+  if (n < min_fill || n <= 0 || n >= p.L) return;  // uniform: the whole workgroup leaves
   const size_t lbase = (size_t)tile * p.L;
   const UT* log_u = static_cast<const UT*>(p.log_u);
 

@@ -241,8 +241,27 @@ def test_bad_fill_is_rejected_before_any_work():
         dl.dl_init_state(pool, torch.from_numpy(inp.s0).to(dev()), [8])
     assert ei.value.status == dl.DL_EINVAL
     with pytest.raises(dl.DeltaLogError) as ei:
-        dl.dl_merge(pool, 0)
+        dl.dl_merge(pool, -1)
     assert ei.value.status == dl.DL_EINVAL
+
+
+def test_merge_due_changes_nothing_and_merge_all_folds():
+    """DL_MERGE_DUE (0) folds only full logs, and a decode step never leaves one, so the
+    pool is unchanged; DL_MERGE_ALL (1) folds every non-empty log."""
+    inp = make_inputs(2, 7, batch=2, heads=2, pool=7, fill0=np.array([0, 3], np.int32))
+    up = Uploaded(inp)
+    pool = new_pool(inp, up=up)
+    for t in range(7):
+        dl.dl_decode_step(pool, up.io(t))
+    before = {k: v.clone() for k, v in pool.tensors().items()}
+    dl.dl_merge(pool, dl.MERGE_DUE)
+    torch.cuda.synchronize()
+    assert all(torch.equal(before[k], v) for k, v in pool.tensors().items())
+    dl.dl_merge(pool, dl.MERGE_ALL)
+    torch.cuda.synchronize()
+    assert int(pool.fill.abs().max()) == 0
+    ref_S, _ = oracle.run_eager(inp, 7)
+    _close("state after DL_MERGE_ALL", pool.base.cpu().numpy(), ref_S, (-2, -1))
 
 
 # ------------------------------------------------- Kaczmarz step size (KLA) --
