@@ -84,40 +84,72 @@ __device__ __forceinline__ void log_coefs(const uint4 kj8, const float (&cj)[CWN
   }
 }
 
-// Stage fold entries [e0, e0 + cnt) of a tile into s_w / s_uu for a fold at
-// cumulative decay s_cnow (LDS, natural channel order).  Entries below nlog
-// come from the log: s_w[m][perm(i)] = 2^(c_now[i] - c_e[i]) k_e[i] and
+// Stage fold entries [e0, e0 + cnt) (cnt <= MC) of a tile into s_w / s_uu for a
+// fold at cumulative decay s_cnow (LDS, natural channel order).  Entries below
+// nlog come from the log: s_w[m][perm(i)] = 2^(c_now[i] - c_e[i]) k_e[i] and
 // s_uu[m][j] = u_e[j]; entry nlog, when asked for, is the current update
-// (s_kcur, already permuted, and s_ucur).  Every thread takes part.
+// (s_kcur, already permuted, and s_ucur).  Every thread takes part: all of its
+// loads (16-byte pieces of key, decay and factor rows; slots outside the stage
+// read zeros through out-of-range offsets) are issued before any is used.
 template <int VAR, int DK, int DV, bool HAS_CUR>
 __device__ __forceinline__ void stage_entries(const PoolArgs& p, int tile, int e0, int cnt, int nlog,
                                               const float* s_cnow, const float* s_kcur,
                                               const float* s_ucur, float* s_w, float* s_uu) {
   using G = SGeo<DK, DV>;
+  constexpr bool VEC = VAR != DL_GDN;
+  constexpr int CW = VEC ? DK : 1;
+  using UT = std::conditional_t<VAR == DL_RWKV6, uint16_t, float>;
+  constexpr int KJ = DK / 8;                             // 8-channel jobs per entry
+  constexpr int UJ = DV / 4;                             // 4-column jobs per entry
+  constexpr int JW = (G::MC * KJ + G::NT - 1) / G::NT;  // weight jobs per thread
+  constexpr int JU = (G::MC * UJ + G::NT - 1) / G::NT;  // factor jobs per thread
+  const int tid = threadIdx.x;
   const size_t lbase = (size_t)tile * p.L;
-  for (int idx = threadIdx.x; idx < cnt * DK; idx += G::NT) {
-    const int m = idx / DK, i = idx % DK, e = e0 + m;
-    if (!HAS_CUR || e < nlog) {
-      const float kj = bf16_to_f32(p.log_k[(lbase + e) * DK + i]);
-      const float dc = (VAR == DL_GDN) ? (s_cnow[0] - p.log_c[lbase + e])
-                                       : (s_cnow[i] - p.log_c[(lbase + e) * DK + i]);
-      s_w[m * DK + G::perm(i)] = exp2f(dc) * kj;
-    } else {
-      if constexpr (HAS_CUR) s_w[m * DK + i] = s_kcur[i];  // both permuted: a plain copy
+  const UT* log_u = static_cast<const UT*>(p.log_u);
+  const auto rk = make_rsrc(p.log_k + lbase * DK, (uint32_t)(p.L * DK * 2));
+  const auto rc = make_rsrc(p.log_c + lbase * CW, (uint32_t)(p.L * CW * 4));
+  const auto ru = make_rsrc(log_u + lbase * DV, (uint32_t)(p.L * DV * sizeof(UT)));
+  uint4 k8[JW];
+  float c8[JW][VEC ? 8 : 1];
+  float4 u4[JU];
+#pragma unroll
+  for (int jw = 0; jw < JW; ++jw) {
+    const int job = tid + jw * G::NT, m = job / KJ, i0 = (job % KJ) * 8, e = e0 + m;
+    const bool ok = m < cnt && (!HAS_CUR || e < nlog);
+    k8[jw] = bload16(rk, ok ? (uint32_t)((e * DK + i0) * 2) : kOutOfRange);
+    if constexpr (VEC) bload8f(rc, ok ? (uint32_t)((e * DK + i0) * 4) : kOutOfRange, c8[jw]);
+    else c8[jw][0] = bload4f(rc, ok ? (uint32_t)(e * 4) : kOutOfRange);
+  }
+#pragma unroll
+  for (int ju = 0; ju < JU; ++ju) {
+    const int job = tid + ju * G::NT, m = job / UJ, j0 = (job % UJ) * 4, e = e0 + m;
+    const bool ok = m < cnt && (!HAS_CUR || e < nlog);
+    u4[ju] = bload_factor4(ru, ok ? (uint32_t)((e * DV + j0) * sizeof(UT)) : kOutOfRange, UT{});
+  }
+#pragma unroll
+  for (int jw = 0; jw < JW; ++jw) {
+    const int job = tid + jw * G::NT, m = job / KJ, i0 = (job % KJ) * 8, e = e0 + m;
+    if (m < cnt) {
+      if (!HAS_CUR || e < nlog) {
+        float kf[8];
+        unpack8(k8[jw], kf);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          s_w[m * DK + G::perm(i0 + i)] = exp2f(s_cnow[VEC ? i0 + i : 0] - c8[jw][VEC ? i : 0]) * kf[i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s_w[m * DK + G::perm(i0 + i)] = s_kcur[G::perm(i0 + i)];
+      }
     }
   }
-  for (int idx = threadIdx.x; idx < cnt * DV; idx += G::NT) {
-    const int m = idx / DV, j = idx % DV, e = e0 + m;
-    float u = 0.f;
-    if (!HAS_CUR || e < nlog) {
-      if constexpr (VAR == DL_RWKV6)
-        u = bf16_to_f32(static_cast<const uint16_t*>(p.log_u)[(lbase + e) * DV + j]);
-      else
-        u = static_cast<const float*>(p.log_u)[(lbase + e) * DV + j];
-    } else {
-      if constexpr (HAS_CUR) u = s_ucur[j];
+#pragma unroll
+  for (int ju = 0; ju < JU; ++ju) {
+    const int job = tid + ju * G::NT, m = job / UJ, j0 = (job % UJ) * 4, e = e0 + m;
+    if (m < cnt) {
+      float4* dst = reinterpret_cast<float4*>(s_uu + m * DV + j0);
+      if (HAS_CUR && e >= nlog) *dst = *reinterpret_cast<const float4*>(s_ucur + j0);
+      else *dst = u4[ju];
     }
-    s_uu[m * DV + j] = u;
   }
 }
 
@@ -211,9 +243,9 @@ struct DecodeLds {
 // it keeps the whole base tile in registers (one read), folds every update
 // into it and writes it back once.  Otherwise the base is streamed in chunks
 // and only the output, one log entry and the fill are written.
-template <int VAR, int DK, int DV, bool BF, bool FOLD, typename Lds>
+template <int VAR, int DK, int DV, bool BF, int PF, bool FOLD, typename Lds>
 __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s, int tile, int n, Lds& sh) {
-  using G = SGeo<DK, DV>;
+  using G = SGeo<DK, DV, PF>;
   using BIO = BaseIO<BF>;
   constexpr bool VEC = VAR != DL_GDN;  // per-key-channel decay
   constexpr int CW = VEC ? DK : 1;     // floats per log_c entry
@@ -514,17 +546,19 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
   }
 }
 
-template <int VAR, int DK, int DV, bool BF>
+// PF: log entries loaded ahead of the base (the launcher picks it from L so that a
+// step finds every entry of its log among them, up to 64).
+template <int VAR, int DK, int DV, bool BF, int PF>
 __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, StepArgs s) {
-  using G = SGeo<DK, DV>;
+  using G = SGeo<DK, DV, PF>;
   __shared__ DecodeLds<DK, DV, (VAR == DL_GDN ? 1 : DK), G::NW, G::MC> sh;
   const int tile = blockIdx.x;
   const int n = p.fill[tile];  // same for the whole workgroup
   if (n < 0 || n >= p.L) return;  // a fill outside [0, L) (a pool never started): touch nothing
   if (n + 1 == p.L)
-    decode_tile<VAR, DK, DV, BF, true>(p, s, tile, n, sh);
+    decode_tile<VAR, DK, DV, BF, PF, true>(p, s, tile, n, sh);
   else
-    decode_tile<VAR, DK, DV, BF, false>(p, s, tile, n, sh);
+    decode_tile<VAR, DK, DV, BF, PF, false>(p, s, tile, n, sh);
 }
 
 // dl_merge: fold the logs of tiles holding at least min_fill entries.
@@ -605,9 +639,13 @@ hipError_t launch_decode(int variant, bool bf16_base, int dk, int dv, int tiles,
   PoolArgs pa = p;
   StepArgs sa = s;
   void* args[] = {&pa, &sa};
-#define CALL_DECODE(V, B, K, D)                                                                    \
-  err = hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<V, K, D, B>), dim3(tiles),    \
-                        dim3(SGeo<K, D>::NT), args, 0, stream)
+#define CALL_DECODE(V, B, K, D)                                                                        \
+  do {                                                                                                 \
+    const void* f = reinterpret_cast<const void*>(&decode_kernel<V, K, D, B, 0>);                      \
+    if (p.L - 1 > 32) f = reinterpret_cast<const void*>(&decode_kernel<V, K, D, B, 64>);               \
+    else if (p.L - 1 > SGeo<K, D>::PF) f = reinterpret_cast<const void*>(&decode_kernel<V, K, D, B, 32>); \
+    err = hipLaunchKernel(f, dim3(tiles), dim3(SGeo<K, D>::NT), args, 0, stream);                      \
+  } while (0)
   DL_VARIANTS(variant, bf16_base, dk, dv, CALL_DECODE);
 #undef CALL_DECODE
   return err;

@@ -35,7 +35,9 @@ struct Geo {
 // more tiles fit on a CU than when the whole tile is register-resident.
 // In LDS, per-row vectors are stored permuted by perm(i) = (i % RG)*RPT + i/RG,
 // which makes the RPC rows of one chunk of one thread four consecutive floats.
-template <int DK, int DV>
+// PF_ is the number of log entries whose keys, decays and factors a decode step
+// loads before the base (at least the fold stage size).
+template <int DK, int DV, int PF_ = 0>
 struct SGeo {
   static constexpr int NT = (DK * DV >= 8192) ? 256 : 128;  // threads per workgroup
   static constexpr int CG = DV / 4;                          // float4 column groups
@@ -48,12 +50,14 @@ struct SGeo {
   static constexpr int LPE = DK / 8;                         // lanes per log entry (8 channels each)
   static constexpr int NG = NT / LPE;                        // log entries per pass
   static constexpr int MCT = (DK * DV >= 16384) ? 16 : 32;  // fold stage size aimed at
-  static constexpr int EPF = (MCT + NG - 1) / NG;            // entry passes prefetched
-  static constexpr int UPF = (MCT + RG - 1) / RG;            // log factors prefetched per thread
+  static constexpr int PF = PF_ > MCT ? PF_ : MCT;           // entries prefetched
+  static constexpr int EPF = (PF + NG - 1) / NG;             // entry passes prefetched
+  static constexpr int UPF = (PF + RG - 1) / RG;             // log factors prefetched per thread
   // Log entries per fold stage.  A log of up to MC entries is folded from what
-  // the read pass already holds: the prefetched entry passes cover NG*EPF
-  // entries and the factor prefetch RG*UPF entries.
-  static constexpr int MC = NG * EPF < RG * UPF ? NG * EPF : RG * UPF;
+  // the read pass already holds: the first stage-size entry passes cover
+  // NG*ceil(MCT/NG) entries and the factor prefetch RG*ceil(MCT/RG) entries.
+  static constexpr int MC = NG * ((MCT + NG - 1) / NG) < RG * ((MCT + RG - 1) / RG)
+                                ? NG * ((MCT + NG - 1) / NG) : RG * ((MCT + RG - 1) / RG);
   static_assert(NT % 64 == 0 && NT >= DK && NT >= DV && 64 % CG == 0, "tile geometry");
   static_assert(RPT % RPC == 0 && NC >= 1, "tile geometry");
   static_assert(MC >= 16 && MC <= 32, "fold stage size");
