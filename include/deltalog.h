@@ -174,6 +174,11 @@ enum {
  * dl_merge, and DL_EINVAL for a unit outside the enum above. */
 int dl_merge_on(const dl_dims *dims, const dl_pool *pool, int32_t min_fill, int32_t unit, void *stream);
 
+/* The arithmetic unit dl_merge uses for pools of this shape, base type and log length:
+ * DL_UNIT_VALU or DL_UNIT_MFMA (the table measured on MI355X, in api.cpp), or a
+ * negative status for invalid dims.  Host only: touches no device memory. */
+int dl_merge_unit(const dl_dims *dims);
+
 /* The eager comparator (DeltaLog Abstract: the usual decoder, which rewrites
  * the whole recurrent state after each generated token): reads `state` (device,
  * fp32 [batch][heads][dk][dv]), writes the updated state in place and io->out.

@@ -104,22 +104,29 @@ int dl_decode_step(const dl_dims* dims, const dl_pool* pool, const dl_step_io* i
                                       static_cast<hipStream_t>(stream)));
 }
 
-// The fold's arithmetic unit for a merge.  DL_UNIT_AUTO takes the matrix-core fold from the
-// shortest log length at which it measured faster than the vector fold on full logs (one
-// MI355X, every tile holding L - 1 entries):
-//   64 x 64          L >= 4   (RWKV6: 1.03x at 4, 1.13x at 8, 1.55x at 32; 0.98x at 2)
-//   128 x 64         L >= 8   (1.10x at 8, 1.35x at 16)
-//   128 x 128, bf16  L >= 8   (GDN: 1.09x at 8, 1.21x at 16; 0.98x at 4)
-//   otherwise        L >= 16  (GDN 128 x 128: 1.16x at 16, 2.5x at 64, 1.02x at 8, 0.95x at 4;
-//                              KDA 1.09x at 16, 0.98x at 8; 64 x 128: 1.19x at 16, 0.99x at 8)
+// The shortest log length at which dl_merge folds on the matrix cores: where the fp32
+// MFMA fold measured faster than the vector fold on full logs (one MI355X, every tile
+// holding L - 1 entries; MFMA time over vector time at L = 4, 8, 16, 32, 64):
+//   128 x 128, fp32 base        32   (GDN B=64 H=32: 0.93 0.95 0.90 1.27 1.83;
+//                                      KDA B=128 H=32: 0.91 0.97 0.96 1.32 1.71)
+//   128 x 128, bf16 base, GDN   32   (0.95 1.02 1.02 1.12 1.25)
+//   128 x 128, bf16 base, else  64   (KDA: 0.87 0.82 0.88 0.96 1.23)
+//   128 x 64 / 64 x 128, fp32   64   (0.95 0.97 0.97 0.94 1.24 / 0.96 0.96 0.96 0.91 1.07)
+//   64 x 64, and 128 x 64 / 64 x 128 with a bf16 base: never (at most 1.04, mostly < 0.95)
+// The vector fold streams its stages from one in-register tile and loads each stage's
+// entries with 16-byte loads issued together; the matrix fold holds the tile in MFMA
+// accumulators and wins once the rank-n update's arithmetic outweighs the shared traffic.
+static int merge_mfma_min_len(const dl_dims* d) {
+  const bool bf = bf16_base(d);
+  if (d->dk == 128 && d->dv == 128) return bf ? (d->variant == DL_GDN ? 32 : 64) : 32;
+  if ((d->dk == 128) != (d->dv == 128)) return bf ? DL_MAX_LOG_LEN + 1 : 64;
+  return DL_MAX_LOG_LEN + 1;
+}
+
 static bool merge_on_mfma(const dl_dims* dims, int32_t unit) {
   if (unit == DL_UNIT_VALU) return false;
   if (unit == DL_UNIT_MFMA) return true;
-  int min_len = 16;
-  if (dims->dk == 64 && dims->dv == 64) min_len = 4;
-  else if (dims->dk == 128 && dims->dv == 64) min_len = 8;
-  else if (dims->dk == 128 && dims->dv == 128 && bf16_base(dims)) min_len = 8;
-  return dims->log_len >= min_len;
+  return dims->log_len >= merge_mfma_min_len(dims);
 }
 
 // Fold every log holding >= min_fill entries (arguments already checked).
@@ -147,6 +154,12 @@ int dl_merge_on(const dl_dims* dims, const dl_pool* pool, int32_t min_fill, int3
 
 int dl_merge(const dl_dims* dims, const dl_pool* pool, int32_t min_fill, void* stream) {
   return dl_merge_on(dims, pool, min_fill, DL_UNIT_AUTO, stream);
+}
+
+int dl_merge_unit(const dl_dims* dims) {
+  const int rc = check_dims(dims);
+  if (rc != DL_OK) return rc;
+  return merge_on_mfma(dims, DL_UNIT_AUTO) ? DL_UNIT_MFMA : DL_UNIT_VALU;
 }
 
 int dl_eager_step(const dl_dims* dims, float* state, const dl_step_io* io, void* stream) {

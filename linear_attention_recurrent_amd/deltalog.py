@@ -73,12 +73,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dl_decode_step.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Pool), ctypes.POINTER(StepIO), vp]
     lib.dl_merge.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Pool), ctypes.c_int32, vp]
     lib.dl_merge_on.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Pool), ctypes.c_int32, ctypes.c_int32, vp]
+    lib.dl_merge_unit.argtypes = [ctypes.POINTER(Dims)]
     lib.dl_eager_step.argtypes = [ctypes.POINTER(Dims), vp, ctypes.POINTER(StepIO), vp]
     lib.dl_prefill.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(Pool), ctypes.POINTER(PrefillIO), vp]
     lib.dl_status_string.argtypes = [ctypes.c_int]
     lib.dl_status_string.restype = ctypes.c_char_p
-    for f in (lib.dl_init_state, lib.dl_decode_step, lib.dl_merge, lib.dl_merge_on, lib.dl_eager_step,
-              lib.dl_prefill):
+    for f in (lib.dl_init_state, lib.dl_decode_step, lib.dl_merge, lib.dl_merge_on, lib.dl_merge_unit,
+              lib.dl_eager_step, lib.dl_prefill):
         f.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -221,6 +222,14 @@ def dl_merge_on(pool: DeltaLogPool, min_fill: int = 1, unit: int = 0, stream=Non
     rc = load_library().dl_merge_on(ctypes.byref(pool.c_dims), ctypes.byref(pool.c_pool), int(min_fill),
                                     int(unit), _stream(stream))
     _check(rc, "dl_merge_on")
+
+
+def dl_merge_unit(dims: Dims) -> int:
+    """The unit dl_merge folds with for pools of these dims (UNIT_VALU or UNIT_MFMA)."""
+    rc = load_library().dl_merge_unit(ctypes.byref(dims))
+    if rc < 0:
+        raise DeltaLogError(rc, "dl_merge_unit")
+    return rc
 
 
 def dl_eager_step(variant: int, state: torch.Tensor, io: StepIO, stream=None) -> None:

@@ -27,10 +27,10 @@ def lib():
 
 def test_header_declares_the_calls():
     names = declared_functions()
-    for n in ("dl_init_state", "dl_decode_step", "dl_merge", "dl_merge_on", "dl_eager_step", "dl_prefill",
-              "dl_status_string"):
+    for n in ("dl_init_state", "dl_decode_step", "dl_merge", "dl_merge_on", "dl_merge_unit", "dl_eager_step",
+              "dl_prefill", "dl_status_string"):
         assert n in names
-    assert len(names) == 7, names
+    assert len(names) == 8, names
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -211,3 +211,26 @@ def test_pool_wrapper_starts_with_empty_logs():
         assert p.fill.dtype == torch.int32 and tuple(p.fill.shape) == (3, 2)
         assert int(p.fill.abs().max()) == 0
         assert tuple(p.log_c.shape) == (3, 2, 8, 1 if variant == dl.GDN else dk)
+
+
+# dl_merge's measured unit table, on both sides of every threshold:
+# (variant, dk, dv, bf16 base, the shortest L on matrix cores, or None for never)
+MERGE_TABLE = [
+    (0, 128, 128, False, 32), (1, 128, 128, False, 32), (2, 128, 128, False, 32),
+    (0, 128, 128, True, 32), (1, 128, 128, True, 64), (2, 128, 128, True, 64),
+    (0, 128, 64, False, 64), (1, 64, 128, False, 64), (0, 128, 64, True, None), (1, 64, 128, True, None),
+    (2, 64, 64, False, None), (2, 64, 64, True, None), (0, 64, 64, False, None),
+]
+
+
+def test_merge_unit_table(lib):
+    from linear_attention_recurrent_amd import deltalog as dl
+    for variant, dk, dv, bf16, first in MERGE_TABLE:
+        base = dl.BASE_BF16 if bf16 else dl.BASE_F32
+        for L in (1, 2, 4, 8, 16, 31, 32, 33, 63, 64, 65, 128):
+            want = dl.UNIT_MFMA if first is not None and L >= first else dl.UNIT_VALU
+            got = dl.dl_merge_unit(dl.Dims(variant, 4, 2, dk, dv, L, base))
+            assert got == want, (variant, dk, dv, bf16, L, got)
+    assert lib.dl_merge_unit(ctypes.byref(dl.Dims(0, 4, 2, 96, 128, 16, 0))) == dl.DL_EUNSUPPORTED
+    assert lib.dl_merge_unit(ctypes.byref(dl.Dims(0, 4, 2, 128, 128, 129, 0))) == dl.DL_EINVAL
+    assert lib.dl_merge_unit(None) == dl.DL_EINVAL

@@ -166,35 +166,35 @@ def test_full_size_units_agree_and_match_sampled_tiles(w):
     _close("MFMA-merged sampled tiles", got, ref_S, (-2, -1))
 
 
-# dl_merge's choice of unit, by head sizes, base and L (the measured table in the library).
-# The units agree bit for bit on these cases, so this checks that dl_merge runs and gives
-# those bits on both sides of each threshold; which kernel ran shows in a kernel trace.
+# dl_merge's choice of unit (dl_merge_unit reports the library's measured table).  With a
+# bf16 base and more than 16 entries per 128 x 128 tile the units round differently (the
+# vector fold once per stage of 16 entries, the matrix fold once), so dl_merge's bits show
+# which unit ran; the cases sit on both sides of the 128 x 128 bf16 thresholds.
 AUTO_CASES = [
-    # workload, dk, dv, L, bf16 base, expected unit
-    (4, 64, 64, 2, False, dl.UNIT_VALU),
-    (4, 64, 64, 4, False, dl.UNIT_MFMA),
-    (3, 128, 64, 7, False, dl.UNIT_VALU),
-    (3, 128, 64, 8, False, dl.UNIT_MFMA),
-    (2, 128, 128, 8, True, dl.UNIT_MFMA),
-    (2, 128, 128, 8, False, dl.UNIT_VALU),
-    (2, 128, 128, 15, False, dl.UNIT_VALU),
-    (2, 128, 128, 16, False, dl.UNIT_MFMA),
-    (4, 64, 128, 12, False, dl.UNIT_VALU),
-    (4, 64, 128, 16, False, dl.UNIT_MFMA),
+    # workload, dk, dv, L, expected unit
+    (2, 128, 128, 32, dl.UNIT_MFMA),   # GDN, bf16 base: matrix cores from L = 32
+    (3, 128, 128, 32, dl.UNIT_VALU),   # KDA, bf16 base: vector fold below L = 64
+    (3, 128, 128, 64, dl.UNIT_MFMA),
 ]
 
 
-@pytest.mark.parametrize("w,dk,dv,L,bf16,unit", AUTO_CASES)
-def test_dl_merge_takes_the_measured_unit(w, dk, dv, L, bf16, unit):
-    """dl_merge's result is bit-identical to the unit its table names."""
+@pytest.mark.parametrize("w,dk,dv,L,unit", AUTO_CASES)
+def test_dl_merge_takes_the_measured_unit(w, dk, dv, L, unit):
+    """dl_merge's result is bit-identical to the unit its table names and differs from the
+    other unit's, on bf16 bases whose folds take more than one vector stage."""
     batch, heads = 4, 2
-    steps = L + 3
+    steps = L - 1
     inp = make_inputs(w, steps, batch=batch, heads=heads, log_len=L, dk=dk, dv=dv, pool=steps, seed=700 + L,
-                      fill0=_spread_fills(batch, L))
-    _, pool = _decoded_pool(inp, steps, base_dtype=dl.BASE_BF16 if bf16 else dl.BASE_F32)
+                      fill0=np.zeros(batch, np.int32))
+    _, pool = _decoded_pool(inp, steps, base_dtype=dl.BASE_BF16)
+    assert int(pool.fill.min()) == L - 1
+    assert dl.dl_merge_unit(pool.c_dims) == unit
     _, merged = _merge_copies(pool, 1)
+    other = dl.UNIT_VALU if unit == dl.UNIT_MFMA else dl.UNIT_MFMA
+    assert not torch.equal(merged[dl.UNIT_VALU][1], merged[dl.UNIT_MFMA][1])
     auto = pool.clone()
     dl.dl_merge(auto, 1)
     torch.cuda.synchronize()
     got = auto.base.cpu()
     assert torch.equal(got, merged[unit][1])
+    assert not torch.equal(got, merged[other][1])
