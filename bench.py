@@ -268,10 +268,13 @@ def time_loop(fn, steps, warmup, graph_chunk=0):
     return start.elapsed_time(end) / 1e3
 
 
-def read_ceilings(pools, tiles, tile_bytes, launches):
-    """Read-only rates on this machine, in the same run: a torch sum over 1 GiB, and the
-    tile-read probe (libdlprobe.so: one workgroup reads one tile, nothing else) over the
-    base tensors of `pools`, used in turn as the decode step uses them."""
+def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
+    """Memory rates on this machine for the decode step's access shapes, in the same run: a
+    torch sum over 1 GiB, and the probes of libdlprobe.so (one workgroup per tile, every
+    load issued first, no arithmetic) over the base tensors of `pools`, used in turn as the
+    decode step uses them: the tile read alone, the tile read plus `log_bytes` of log per
+    tile (the mean the step reads), and the tile read and written back (the eager step's
+    traffic)."""
     import ctypes
 
     import torch
@@ -281,19 +284,38 @@ def read_ceilings(pools, tiles, tile_bytes, launches):
     secs = time_loop(lambda t: x.sum(), 10, 3)
     out["torch_sum_gbs"] = (1 << 30) * 10 / secs / 1e9
     del x
+    if not pools:
+        return out
     lib = ctypes.CDLL(os.path.join(ROOT, "linear_attention_recurrent_amd", "libdlprobe.so"))
-    lib.dl_probe_tile_read.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.dl_probe_tile_read.argtypes = [vp, ci, ci, vp, vp]
+    lib.dl_probe_tile_read_log.argtypes = [vp, ci, ci, vp, ci, ci, vp, vp]
+    lib.dl_probe_tile_rw.argtypes = [vp, ci, ci, vp]
     sink = torch.zeros(256, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
-    if pools:
-        def rd(t):
-            rc = lib.dl_probe_tile_read(pools[t % len(pools)].base.data_ptr(), tile_bytes, tiles, sink.data_ptr(),
-                                        stream)
-            if rc != 0:
-                raise RuntimeError(f"dl_probe_tile_read failed ({rc})")
-        secs = time_loop(rd, launches, 2 * len(pools))
-        out["tile_read_gbs"] = tile_bytes * tiles * launches / secs / 1e9
-        out["tile_read_shape"] = f"{tiles} tiles of {tile_bytes} B per launch, {len(pools)} pools in turn"
+    NP = len(pools)
+    lb = min(65536, -(-int(log_bytes) // 16) * 16)
+    logs = [torch.zeros(tiles * lb // 4 + 4, dtype=torch.float32, device=dev) for _ in range(NP)]
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed ({rc})")
+    legs = {
+        "tile_read": (lambda t: check(lib.dl_probe_tile_read(pools[t % NP].base.data_ptr(), tile_bytes, tiles,
+                                                             sink.data_ptr(), stream), "dl_probe_tile_read"),
+                      tile_bytes * tiles),
+        "tile_read_log": (lambda t: check(lib.dl_probe_tile_read_log(pools[t % NP].base.data_ptr(), tile_bytes, tiles,
+                                                                     logs[t % NP].data_ptr(), lb, lb, sink.data_ptr(),
+                                                                     stream), "dl_probe_tile_read_log"),
+                          (tile_bytes + lb) * tiles),
+        "tile_rw": (lambda t: check(lib.dl_probe_tile_rw(pools[t % NP].base.data_ptr(), tile_bytes, tiles, stream),
+                                    "dl_probe_tile_rw"), 2 * tile_bytes * tiles),
+    }
+    for name, (fn, nbytes) in legs.items():
+        secs = time_loop(fn, launches, 2 * NP)
+        out[f"{name}_gbs"] = nbytes * launches / secs / 1e9
+    out["probe_shape"] = (f"{tiles} tiles of {tile_bytes} B per launch, {NP} pools in turn; read_log adds {lb} B "
+                          f"of log per tile; rw writes the tile back (the eager step's traffic)")
     return out
 
 
@@ -590,7 +612,7 @@ def main():
     if args.only in (None, "deltalog"):
         result["cold"] = time_loop(lambda t: dl.dl_decode_step(pools[t % NP], ios[t % P]), Kc, Wc, chunk)
     if args.only in (None, "ceiling"):
-        result["ceiling"] = read_ceilings(pools, tiles, eb * dk * dv, Kc)
+        result["ceiling"] = read_ceilings(pools, tiles, eb * dk * dv, (L - 1) / 2 * entry_bytes(var, dk, dv), Kc)
     del pools
     # Cache-resident: one pool, whose working set may stay in the last-level cache.
     Kw = -(-K // L) * L
@@ -677,6 +699,7 @@ def main():
         "hbm_target": {"frac_of_peak_needed": 0.70, "measured_cold_frac": achieved / HBM_PEAK_GBS,
                        "met": achieved / HBM_PEAK_GBS >= 0.70,
                        "frac_of_tile_read_ceiling": achieved / ceil["tile_read_gbs"],
+                       "frac_of_tile_read_log_ceiling": achieved / ceil["tile_read_log_gbs"],
                        "frac_of_torch_sum_ceiling": achieved / ceil["torch_sum_gbs"]},
         "read_ceiling_gbs": ceil,
         "cache_resident": {"value": tiles / t_warm, "ms_per_step": t_warm * 1e3, "timed_steps": Kw,
@@ -691,6 +714,10 @@ def main():
         "eager": {"value": tiles / t_ecold, "ms_per_step": t_ecold * 1e3, "timed_steps": Kw,
                   "hbm_gbs_algorithmic": eag["total"] * tiles / t_ecold / 1e9,
                   "deltalog_speedup": t_ecold / t_cold,
+                  # the speed-up if each step ran at its access shape's probe rate (decode: tile
+                  # plus mean log read; eager: tile read and written back)
+                  "deltalog_speedup_at_probe_rates": (eag["total"] / ceil["tile_rw_gbs"])
+                                                     / (mdl["total"] / ceil["tile_read_log_gbs"]),
                   "cache_resident": {"ms_per_step": t_ewarm * 1e3, "deltalog_speedup": t_ewarm / t_warm}},
         "copy_ceiling_gbs": copy,
         "prefill": result.get("prefill"),
