@@ -165,6 +165,21 @@ def test_head_size_combinations(w, dk, dv):
 
 
 @pytest.mark.parametrize("w", [1, 3, 4])
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64), (64, 64), (128, 128)])
+@pytest.mark.parametrize("L", [24, 40])
+def test_log_entries_loaded_ahead(w, dk, dv, L):
+    """Logs longer than the fold stage: the decode step loads up to 32 or 64 entries ahead of
+    the base (chosen from L) and folds in several staged passes; ragged fills cover every
+    depth of the log."""
+    steps = 2 * L + 5
+    inp = make_inputs(w, steps, batch=3, heads=2, log_len=L, pool=steps, dk=dk, dv=dv,
+                      fill0=np.array([0, L // 3, L - 2], np.int32))
+    pool, outs = run_deltalog(inp, steps)
+    assert np.all(pool.fill.cpu().numpy() == ((inp.fill0 + steps) % L)[:, None])
+    _compare(inp, steps, pool, outs)
+
+
+@pytest.mark.parametrize("w", [1, 3, 4])
 def test_unit_zero_and_tiny_decay(w):
     inp = make_inputs(w, 48, batch=2, heads=2, log_len=8, pool=48)
     d = inp.decay
