@@ -22,10 +22,15 @@ of the fold, and the fp64 CPU oracle on the host cores.
   python bench.py [--gpus 1] [--steps 1024] [--warmup 32] [--workload 2]
                   [--no-cpu-baseline] [--graph]
                   [--only deltalog|warm|eager|ceiling|copy|prefill|merge]
-                  [--base-dtype f32|bf16] [--log-len L]
+                  [--base-dtype f32|bf16] [--log-len L] [--trace]
 
 `--only merge` times dl_merge_on on full logs with each arithmetic unit of the
 fold (vector FMAs, fp32 MFMA) and prints their times.
+
+`--trace` runs the cache-cold leg on the tracing build (libdeltalog_trace.so, made
+by `python -m linear_attention_recurrent_amd.build --trace`) and prints, for two
+consecutive launches at half-full logs and two that fold, each workgroup's phase
+times and the launch's timeline (span, start spread, gap between the launches).
 """
 from __future__ import annotations
 
@@ -319,6 +324,85 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
     return out
 
 
+TRACE_TICK_NS = 10.0  # s_memrealtime counts at 100 MHz
+
+
+def trace_summary(buf, tiles: int) -> dict:
+    """Timeline of two consecutive decode launches from the tracing build's stamps:
+    buf[launch][workgroup] = (start, after the log-coefficient phase, after the column
+    sums, end, hardware id)."""
+    us = TRACE_TICK_NS / 1e3
+    order = sorted(range(2), key=lambda i: int(buf[i, :, 0].min()))
+    t0 = int(buf[order[0], :, 0].min())
+    pct = lambda a, q: float(np.percentile(a, q)) * us
+    launches = []
+    for i in order:
+        t = buf[i, :, :4].astype(np.int64) - t0
+        ph = np.diff(t, axis=1)
+        hw = buf[i, :, 4]
+        cu = ((hw >> np.uint64(32)) << np.uint64(8)) | ((hw >> np.uint64(8)) & np.uint64(0xF)) << np.uint64(4) \
+            | ((hw >> np.uint64(13)) & np.uint64(0x7)) << np.uint64(1) | ((hw >> np.uint64(12)) & np.uint64(0x1))
+        launches.append({
+            "start_us": float(t[:, 0].min()) * us, "end_us": float(t[:, 3].max()) * us,
+            "span_us": float(t[:, 3].max() - t[:, 0].min()) * us,
+            "start_spread_us": {"p50": pct(t[:, 0] - t[:, 0].min(), 50), "p90": pct(t[:, 0] - t[:, 0].min(), 90),
+                                "max": float(t[:, 0].max() - t[:, 0].min()) * us},
+            "workgroup_us": {"p50": pct(t[:, 3] - t[:, 0], 50), "p90": pct(t[:, 3] - t[:, 0], 90)},
+            "phase_us_p50": {"log_coefficients": pct(ph[:, 0], 50), "column_sums": pct(ph[:, 1], 50),
+                             "output_append_fold": pct(ph[:, 2], 50)},
+            "phase_us_p90": {"log_coefficients": pct(ph[:, 0], 90), "column_sums": pct(ph[:, 1], 90),
+                             "output_append_fold": pct(ph[:, 2], 90)},
+            "compute_units_used": int(len(np.unique(cu))),
+        })
+    return {"launches": launches, "gap_us": launches[1]["start_us"] - launches[0]["end_us"],
+            "workgroups_per_launch": tiles}
+
+
+def trace_leg(args, inp, ios, base_dt) -> dict:
+    """The cache-cold leg on the tracing build: warm up whole fold periods of every pool,
+    then stop twice, after two launches at fill L/2 and after two that fold, and read the
+    stamps of those two launches each time."""
+    import ctypes
+
+    import torch
+
+    from linear_attention_recurrent_amd import build, deltalog as dl
+    lib = dl.load_library(build.TRACE_LIB, make_default=True)
+    lib.dl_trace_copy.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    lib.dl_trace_copy.restype = ctypes.c_int
+    dev = torch.device("cuda", 0)
+    B, H, dk, dv, L, var = inp.batch, inp.heads, inp.dk, inp.dv, inp.log_len, inp.variant
+    tiles = B * H
+    if tiles > 65536:
+        raise SystemExit("--trace records at most 65,536 workgroups per launch")
+    eb = 2 if base_dt == dl.BASE_BF16 else 4
+    NP = 1 + -(-MALL_BYTES // (tiles * (eb * dk * dv + L * entry_bytes(var, dk, dv) + 4)))
+    pools = [dl.DeltaLogPool(var, B, H, dk, dv, L, dev, base_dt) for _ in range(NP)]
+    for p_ in pools:
+        dl.dl_init_state(p_, torch.from_numpy(inp.s0).to(dev), inp.fill0)
+    P = len(ios)
+    t = 0
+
+    def run_to(stop):
+        nonlocal t
+        while t < stop:
+            dl.dl_decode_step(pools[t % NP], ios[t % P])
+            t += 1
+        torch.cuda.synchronize()
+        buf = np.zeros((2, tiles, 5), dtype=np.uint64)
+        rc = lib.dl_trace_copy(buf.ctypes.data, tiles)
+        if rc != 0:
+            raise RuntimeError(f"dl_trace_copy failed ({rc})")
+        return trace_summary(buf, tiles)
+    warm = NP * L * max(1, -(-args.warmup // (NP * L)))
+    out = {"mid_log": run_to(warm + NP * (L // 2) + 2)}  # the last two launches: fill L/2
+    out["fold"] = run_to(warm + 2 * NP * L)  # the last two launches: fill L - 1, they fold
+    out["note"] = ("tracing build: each workgroup's thread 0 stamps s_memrealtime (100 MHz) at its start, "
+                   "after the log-coefficient barrier, after the column-sum barrier and at its end; "
+                   f"{NP} pools in turn (cache-cold), log length {L}")
+    return out
+
+
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD's published figure
 PREFILL_CHUNK = 32
 
@@ -538,6 +622,8 @@ def main():
     ap.add_argument("--base-dtype", choices=["f32", "bf16"], default="f32",
                     help="storage of the dense base: fp32 (exact path) or bf16 (low-bit base, "
                          "rounded at each fold; log and arithmetic stay fp32)")
+    ap.add_argument("--trace", action="store_true",
+                    help="time the cache-cold leg's launches workgroup by workgroup on the tracing build")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -547,7 +633,7 @@ def main():
         sys.exit(2)
 
     cpu = None
-    if not args.no_cpu_baseline and args.only is None:
+    if not args.no_cpu_baseline and args.only is None and not args.trace:
         cpu = cpu_baseline(args.workload)  # before any GPU work: forked workers never touch the GPU
 
     import torch
@@ -587,6 +673,9 @@ def main():
         return
     if args.only == "prefill":
         print(json.dumps(prefill_leg(args, inp, T, base_dt)))
+        return
+    if args.trace:
+        print(json.dumps(trace_leg(args, inp, ios, base_dt)))
         return
 
     # Cache-cold (the headline): NP independent pools used in turn, so that between two

@@ -54,7 +54,7 @@ int check_io(const dl_dims* d, const dl_step_io* io) {
 }
 
 dl::PoolArgs pool_args(const dl_dims* d, const dl_pool* p) {
-  return dl::PoolArgs{p->base, p->log_k, p->log_u, p->log_c, p->fill, d->heads, d->log_len};
+  return dl::PoolArgs{p->base, p->log_k, p->log_u, p->log_c, p->fill, d->heads, d->log_len, d->batch * d->heads};
 }
 
 bool bf16_base(const dl_dims* d) { return d->base_dtype == DL_BASE_BF16;

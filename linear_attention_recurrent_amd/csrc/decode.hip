@@ -27,6 +27,32 @@
 
 namespace dl {
 
+#ifdef DL_TRACE
+// Per-workgroup timestamps, in the opt-in tracing build only (libdeltalog_trace.so):
+// s_memrealtime (a 100 MHz clock shared by every CU) at the workgroup's start (0), after
+// the barrier that ends the log-coefficient phase (1), after the barrier that ends the
+// column sums (2) and at its end (3), plus its hardware id (4), for workgroups < 65,536
+// of two launches: the buffer is chosen by the parity of the step's query pointer over
+// the slot size tiles * dk * 2 bytes, so consecutive steps of an input pool that holds
+// the steps back to back alternate between the two.
+__device__ unsigned long long g_trace[2][65536][5];
+__device__ __forceinline__ void trace_stamp(int k, const void* q, int tiles, int dk) {
+  if (threadIdx.x == 0 && blockIdx.x < 65536) {
+    const int par = (int)(((uintptr_t)q / ((size_t)tiles * dk * 2)) & 1);
+    g_trace[par][blockIdx.x][k] = __builtin_amdgcn_s_memrealtime();
+    if (k == 3) {
+      unsigned hw, xcc;
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+      g_trace[par][blockIdx.x][4] = ((unsigned long long)xcc << 32) | hw;
+    }
+  }
+}
+#define DL_STAMP(k) trace_stamp(k, s.q, p.tiles, DK)
+#else
+#define DL_STAMP(k) ((void)0)
+#endif
+
 // Read coefficients of one log entry j, computed by a group of LPE lanes that
 // each hold 8 key channels:
 //   GDN    sigma^k_j = 2^(c_t - c_j) (k_j . k_t),   sigma^q_j = 2^(c_t - c_j) (k_j . q_t)
@@ -402,6 +428,7 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
       for (int rr = 0; rr < RPC; ++rr) buf[c][rr] = BIO::load(tb, gidx(c, rr));
   }
   __syncthreads();
+  DL_STAMP(1);
 
   // ---- 4. column sums: the base matvec (streamed, or from the resident tile), then the log part.
   float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), aq = ak;
@@ -459,6 +486,7 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
     if constexpr (VAR != DL_RWKV6) *reinterpret_cast<float4*>(&sh.red[wave][1][cg * 4]) = aq;
   }
   __syncthreads();
+  DL_STAMP(2);
 
   // ---- 5. per-column results, output, append (column lanes / entry lanes).
   if (tid < DV) {
@@ -552,6 +580,7 @@ template <int VAR, int DK, int DV, bool BF, int PF>
 __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, StepArgs s) {
   using G = SGeo<DK, DV, PF>;
   __shared__ DecodeLds<DK, DV, (VAR == DL_GDN ? 1 : DK), G::NW, G::MC> sh;
+  DL_STAMP(0);
   const int tile = blockIdx.x;
   const int n = p.fill[tile];  // same for the whole workgroup
   if (n < 0 || n >= p.L) return;  // a fill outside [0, L) (a pool never started): touch nothing
@@ -559,6 +588,10 @@ __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, 
     decode_tile<VAR, DK, DV, BF, PF, true>(p, s, tile, n, sh);
   else
     decode_tile<VAR, DK, DV, BF, PF, false>(p, s, tile, n, sh);
+#ifdef DL_TRACE
+  __syncthreads();
+  DL_STAMP(3);
+#endif
 }
 
 // dl_merge: fold the logs of tiles holding at least min_fill entries.
@@ -680,3 +713,17 @@ hipError_t launch_init(int variant, bool bf16_base, int dk, int dv, int tiles, c
 }
 
 }  // namespace dl
+
+#ifdef DL_TRACE
+// Copy the timestamps of workgroups [0, nwg) of both buffers to `host` ([2][nwg][5]
+// uint64).  Only in the tracing build.  Returns 0 or the HIP error code.
+extern "C" int dl_trace_copy(unsigned long long* host, int nwg) {
+  if (nwg < 0 || nwg > 65536) return -1;
+  for (int par = 0; par < 2; ++par) {
+    const hipError_t e = hipMemcpyFromSymbol(host + (size_t)par * nwg * 5, HIP_SYMBOL(dl::g_trace),
+                                             (size_t)nwg * 5 * 8, (size_t)par * 65536 * 5 * 8, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return (int)e;
+  }
+  return 0;
+}
+#endif

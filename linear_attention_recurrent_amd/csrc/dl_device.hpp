@@ -253,6 +253,7 @@ struct PoolArgs {
   int32_t* fill;
   int heads;
   int L;
+  int tiles;  // batch * heads
 };
 
 // Arguments of the prefill kernels: a prompt of `tokens` rows per sequence,

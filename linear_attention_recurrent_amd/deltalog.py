@@ -58,8 +58,10 @@ class DeltaLogError(RuntimeError):
 _lib = None
 
 
-def load_library(path: Optional[str] = None) -> ctypes.CDLL:
-    """Load libdeltalog.so (once) and declare its signatures."""
+def load_library(path: Optional[str] = None, make_default: bool = False) -> ctypes.CDLL:
+    """Load libdeltalog.so (once) and declare its signatures.  A `path` loads that build
+    of the library instead (the tracing build, say); with make_default it serves every
+    later call of this module."""
     global _lib
     if _lib is not None and path is None:
         return _lib
@@ -81,7 +83,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     for f in (lib.dl_init_state, lib.dl_decode_step, lib.dl_merge, lib.dl_merge_on, lib.dl_merge_unit,
               lib.dl_eager_step, lib.dl_prefill):
         f.restype = ctypes.c_int
-    if path is None:
+    if path is None or make_default:
         _lib = lib
     return lib
 
@@ -95,8 +97,16 @@ def _check(rc: int, what: str) -> None:
         raise DeltaLogError(rc, what)
 
 
-def _stream(stream) -> int:
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, device=None) -> int:
+    """The hipStream_t to enqueue on: `stream` (a torch stream or a raw handle), else the
+    current stream of `device` (read without building a torch Stream object, which
+    costs microseconds per call on the step path)."""
     if stream is None:
+        if _raw_stream is not None and device is not None:
+            return _raw_stream(device.index)
         return torch.cuda.current_stream().cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
@@ -145,6 +155,9 @@ class DeltaLogPool:
         self.c_dims = Dims(self.variant, B, H, self.dk, self.dv, L, self.base_dtype)
         self.c_pool = Pool(self.base.data_ptr(), self.log_k.data_ptr(), self.log_u.data_ptr(),
                            self.log_c.data_ptr(), self.fill.data_ptr())
+        # by-reference arguments built once: the decode step is called every token
+        self.dims_ref = ctypes.byref(self.c_dims)
+        self.pool_ref = ctypes.byref(self.c_pool)
 
     def tensors(self) -> dict:
         return dict(base=self.base, log_k=self.log_k, log_u=self.log_u, log_c=self.log_c, fill=self.fill)
@@ -205,9 +218,10 @@ def dl_init_state(pool: DeltaLogPool, init_base: Optional[torch.Tensor] = None,
 
 def dl_decode_step(pool: DeltaLogPool, io: StepIO, stream=None) -> None:
     """One decode step (append, or fold on the step that fills the log) for every tile."""
-    rc = load_library().dl_decode_step(ctypes.byref(pool.c_dims), ctypes.byref(pool.c_pool),
-                                       ctypes.byref(io), _stream(stream))
-    _check(rc, "dl_decode_step")
+    lib = _lib if _lib is not None else load_library()
+    rc = lib.dl_decode_step(pool.dims_ref, pool.pool_ref, ctypes.byref(io), _stream(stream, pool.device))
+    if rc != DL_OK:
+        raise DeltaLogError(rc, "dl_decode_step")
 
 
 def dl_merge(pool: DeltaLogPool, min_fill: int = 1, stream=None) -> None:

@@ -273,6 +273,28 @@ def test_rwkv6_decode_continues_after_prefill():
 
 
 # ------------------------------------------- full sizes, sampled tiles ------
+@pytest.mark.parametrize("w", [2, 3, 4, 6])
+def test_long_prompts(w):
+    """Prompts of 16,384 tokens (512 chunks; the bench's are 2,048-4,096), every tile
+    of a small batch, prompt rows cycling over 512 drawn steps: the carried state's error
+    must not grow with the number of chunks."""
+    T = 16384
+    inp = make_inputs(w, T, batch=2, heads=2, pool=512)
+    up = Uploaded(inp)
+    pool = new_pool(inp, up=up)
+    idx = torch.arange(T, device=dev()) % inp.pool
+    tm = lambda x: None if x is None else x.index_select(0, idx).transpose(0, 1).contiguous()
+    out = torch.empty((inp.batch, T, inp.heads, inp.dv), dtype=torch.float32, device=dev())
+    io = dl.make_prefill_io(pool, tm(up.q), tm(up.k), tm(up.v), tm(up.decay), tm(up.beta), out, tm(up.eta),
+                            inp.eps, bonus=up.bonus)
+    dl.dl_prefill(pool, io)
+    torch.cuda.synchronize()
+    got_o = out.cpu().numpy().transpose(1, 0, 2, 3)  # [T][batch][heads][dv]
+    ref_S, ref_o = oracle.run_eager(inp, T)
+    _close(f"outputs, workload {w}, T={T}", got_o, ref_o, (-1,))
+    _close(f"state, workload {w}, T={T}", pool.base.cpu().numpy(), ref_S, (-2, -1))
+
+
 @pytest.mark.parametrize("w,T", [(2, 4096), (3, 4096), (4, 2048)])
 def test_full_size_prefill_sampled_tiles(w, T):
     """The shapes the bench times (every tile of the workload, prompt rows cycling over
