@@ -4,8 +4,8 @@ TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import this module.
 
 This is DeltaLog's representation as the DeltaLog page ("DeltaLog: Deferred
 Materialization of Recurrent States for Linear Attention Decoding", Abstract)
-describes it: the recurrent state is split into a dense base and a log of
-bounded length holding the latest low-rank updates; a typical decode step only
+describes it: the recurrent state is held as two parts, a dense base plus a
+bounded-length log holding the latest low-rank updates; a typical decode step only
 adds an update's factors to the log, and now and then a merge folds the logged
 updates into the base, so the dense state the model sees is the eager one.
 The page's AI Summary says the same of appends taking the place of full

@@ -2,8 +2,8 @@
 from the rounding alone.  Test infrastructure: it drives the fp64 oracle only.
 
 The low-bit base (LeapQuant abstract, on the card page titled "A Persistent-State
-Dataflow Accelerator for Memory-Bound Linear Attention Decode on FPGA": a fixed
-low-bit state read together with high-precision buffered updates) is rounded to
+Dataflow Accelerator for Memory-Bound Linear Attention Decode on FPGA": outputs
+come from a state stored in few bits plus pending updates kept at full precision) is rounded to
 bf16 where it is written: once at the start and once per fold.  Write S_t for the
 exact state and S_t + E_t for the state a bf16-base run stands for.
 
