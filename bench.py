@@ -367,6 +367,8 @@ def trace_leg(args, inp, ios, base_dt) -> dict:
     import torch
 
     from linear_attention_recurrent_amd import build, deltalog as dl
+    if not os.path.exists(build.TRACE_LIB):
+        raise SystemExit(f"{build.TRACE_LIB} is not built: run `python -m linear_attention_recurrent_amd.build --trace`")
     lib = dl.load_library(build.TRACE_LIB, make_default=True)
     lib.dl_trace_copy.argtypes = [ctypes.c_void_p, ctypes.c_int]
     lib.dl_trace_copy.restype = ctypes.c_int

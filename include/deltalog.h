@@ -217,7 +217,8 @@ typedef struct {
  * decay-weighted products inside a chunk are split around a reference token
  * per half chunk and run on matrix units when no channel decays by more than
  * 2^-60 over half a chunk, else they are formed pair by pair.  Errors:
- * DL_EINVAL for tokens < 0, null q/k/v/decay/out, or eps < 0 with eta set;
+ * DL_EINVAL for tokens < 0, heads > 131071 (a chunk's rows of one sequence are
+ * addressed with 32-bit offsets), null q/k/v/decay/out, or eps < 0 with eta set;
  * DL_EUNSUPPORTED if beta/eta/bonus do not match the variant (GDN/KDA: exactly
  * one of beta and eta, no bonus; RWKV6: bonus only).  tokens == 0 only folds
  * the logs and looks at no prompt pointer. */

@@ -177,6 +177,9 @@ int dl_prefill(const dl_dims* dims, const dl_pool* pool, const dl_prefill_io* io
   int rc = check_dims(dims);
   if (rc != DL_OK) return rc;
   if (io == nullptr || io->tokens < 0) return DL_EINVAL;
+  // the prefill kernels address one chunk's rows of a sequence (32 tokens x heads rows
+  // of up to 512 bytes) with 32-bit offsets
+  if (static_cast<int64_t>(dims->heads) * 32 * 512 > INT32_MAX) return DL_EINVAL;
   if (dims->batch == 0) return DL_OK;
   if ((rc = check_pool(pool, dims->variant)) != DL_OK) return rc;
   if (io->tokens > 0) {  // an empty prompt only folds: its pointers are not looked at

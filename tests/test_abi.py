@@ -177,6 +177,8 @@ def test_prefill_errors(lib):
     d = _dims(dl)
     p = _pool(dl)
     assert _prefill(lib, d, p, _pio(dl, T=-1)) == dl.DL_EINVAL
+    assert _prefill(lib, _dims(dl, batch=1, heads=131072), p, _pio(dl)) == dl.DL_EINVAL  # 32-bit chunk offsets
+    assert _prefill(lib, _dims(dl, batch=0, heads=131072), p, _pio(dl)) == dl.DL_EINVAL
     assert lib.dl_prefill(ctypes.byref(d), ctypes.byref(p), None, None) == dl.DL_EINVAL
     assert _prefill(lib, _dims(dl, variant=1), p, _pio(dl, decay=A + 4)) == dl.DL_EALIGN  # KDA decay rows: 16 B
     d2 = _dims(dl, variant=2, dk=64, dv=64)
