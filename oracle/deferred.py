@@ -43,8 +43,8 @@ def round_to_bf16(x) -> np.ndarray:
 
     For the low-bit base (LeapQuant abstract, on the card page titled "A
     Persistent-State Dataflow Accelerator for Memory-Bound Linear Attention
-    Decode on FPGA": outputs come from a fixed low-bit state plus high-precision
-    buffered updates, and the state is quantised once per window).  Written from
+    Decode on FPGA": outputs read a state stored in few bits together with pending
+    updates held at full precision, and the state is re-quantised once per window).  Written from
     the format's definition: x = m 2^e with m in [0.5, 1); keep m to 2^-8.
     Exact for the normal range (bf16 shares float32's exponent range); values
     below 2^-126 keep 8 significant bits here, where bf16 would flush them
