@@ -279,8 +279,9 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
     torch sum over 1 GiB, and the probes of libdlprobe.so (one workgroup per tile, every
     load issued first, no arithmetic) over the base tensors of `pools`, used in turn as the
     decode step uses them: the tile read alone, the tile read plus `log_bytes` of log per
-    tile (the mean the step reads), and the tile read and written back (the eager step's
-    traffic)."""
+    tile (the mean the step reads), the tile read and written back (the eager step's
+    traffic), and the same bytes streamed through LDS by one persistent workgroup per CU
+    with one 64 KiB unit in flight."""
     import ctypes
 
     import torch
@@ -297,6 +298,7 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
     lib.dl_probe_tile_read.argtypes = [vp, ci, ci, vp, vp]
     lib.dl_probe_tile_read_log.argtypes = [vp, ci, ci, vp, ci, ci, vp, vp]
     lib.dl_probe_tile_rw.argtypes = [vp, ci, ci, vp]
+    lib.dl_probe_tile_stream.argtypes = [vp, ci, ci, vp, vp]
     sink = torch.zeros(256, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
     NP = len(pools)
@@ -316,12 +318,19 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
                           (tile_bytes + lb) * tiles),
         "tile_rw": (lambda t: check(lib.dl_probe_tile_rw(pools[t % NP].base.data_ptr(), tile_bytes, tiles, stream),
                                     "dl_probe_tile_rw"), 2 * tile_bytes * tiles),
+        # the same bytes as 64 KiB units streamed by one persistent workgroup per CU through LDS
+        "tile_stream": (lambda t: check(lib.dl_probe_tile_stream(pools[t % NP].base.data_ptr(),
+                                                                 tile_bytes * tiles // 65536, 256, sink.data_ptr(),
+                                                                 stream), "dl_probe_tile_stream"),
+                        tile_bytes * tiles // 65536 * 65536),
     }
     for name, (fn, nbytes) in legs.items():
         secs = time_loop(fn, launches, 2 * NP)
         out[f"{name}_gbs"] = nbytes * launches / secs / 1e9
     out["probe_shape"] = (f"{tiles} tiles of {tile_bytes} B per launch, {NP} pools in turn; read_log adds {lb} B "
-                          f"of log per tile; rw writes the tile back (the eager step's traffic)")
+                          f"of log per tile; rw writes the tile back (the eager step's traffic); stream reads "
+                          f"the same bytes as 64 KiB units with 256 persistent workgroups, one unit in flight "
+                          f"per CU through LDS")
     return out
 
 
@@ -804,6 +813,7 @@ def main():
                        "met": achieved / HBM_PEAK_GBS >= 0.70,
                        "frac_of_tile_read_ceiling": achieved / ceil["tile_read_gbs"],
                        "frac_of_tile_read_log_ceiling": achieved / ceil["tile_read_log_gbs"],
+                       "frac_of_tile_stream_ceiling": achieved / ceil["tile_stream_gbs"],
                        "frac_of_torch_sum_ceiling": achieved / ceil["torch_sum_gbs"]},
         "read_ceiling_gbs": ceil,
         "cache_resident": {"value": tiles / t_warm, "ms_per_step": t_warm * 1e3, "timed_steps": Kw,
