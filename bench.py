@@ -281,7 +281,7 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
     decode step uses them: the tile read alone, the tile read plus `log_bytes` of log per
     tile (the mean the step reads), the tile read and written back (the eager step's
     traffic), and the same bytes streamed through LDS by one persistent workgroup per CU
-    with one 64 KiB unit in flight."""
+    with three 16 KiB units in flight."""
     import ctypes
 
     import torch
@@ -318,19 +318,20 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
                           (tile_bytes + lb) * tiles),
         "tile_rw": (lambda t: check(lib.dl_probe_tile_rw(pools[t % NP].base.data_ptr(), tile_bytes, tiles, stream),
                                     "dl_probe_tile_rw"), 2 * tile_bytes * tiles),
-        # the same bytes as 64 KiB units streamed by one persistent workgroup per CU through LDS
+        # the same bytes as 16 KiB units streamed through LDS by one persistent workgroup per
+        # CU, three units in flight
         "tile_stream": (lambda t: check(lib.dl_probe_tile_stream(pools[t % NP].base.data_ptr(),
-                                                                 tile_bytes * tiles // 65536, 256, sink.data_ptr(),
+                                                                 tile_bytes * tiles // 16384, 256, sink.data_ptr(),
                                                                  stream), "dl_probe_tile_stream"),
-                        tile_bytes * tiles // 65536 * 65536),
+                        tile_bytes * tiles // 16384 * 16384),
     }
     for name, (fn, nbytes) in legs.items():
         secs = time_loop(fn, launches, 2 * NP)
         out[f"{name}_gbs"] = nbytes * launches / secs / 1e9
     out["probe_shape"] = (f"{tiles} tiles of {tile_bytes} B per launch, {NP} pools in turn; read_log adds {lb} B "
                           f"of log per tile; rw writes the tile back (the eager step's traffic); stream reads "
-                          f"the same bytes as 64 KiB units with 256 persistent workgroups, one unit in flight "
-                          f"per CU through LDS")
+                          f"the same bytes as 16 KiB units with 256 persistent workgroups, three units in "
+                          f"flight per CU through LDS")
     return out
 
 

@@ -9,9 +9,9 @@
 //   read + log    the tile, then `log_bytes` more from the tile's own region of a
 //                 second array (the base read plus the log entries a step reads)
 //   read + write  the tile, written back in place (the eager step's traffic)
-//   stream        64 KiB tiles read by persistent workgroups (one per CU), each tile
-//                 loaded straight into LDS while the previous one is read from the
-//                 other LDS buffer: one tile in flight per CU, no registers held
+//   stream        the same bytes as 16 KiB units read by persistent workgroups (one
+//                 per CU) through four LDS buffers, each unit loaded straight into
+//                 LDS: three units in flight per CU, no registers held
 // Loaded values feed a sum that is stored only if it equals a value no sum of
 // finite inputs hits in practice, so the loads cannot be dropped; the write-back
 // scales by 1 - 2^-24 rounded, so it rewrites every value (the stored values change
@@ -80,45 +80,49 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // Four 16-byte LDS reads at byte offsets a, a + S, a + 2S, a + 3S, waited for inside
 // the same asm block (the compiler would otherwise wait for every outstanding
-// direct-to-LDS load before any LDS read, emptying the pipeline).
-#define PROBE_LDS_READ4(r0, r1, r2, r3, a, S)                                                            \
-  asm volatile("ds_read_b128 %0, %4\n ds_read_b128 %1, %4 offset:" #S "\n ds_read_b128 %2, %4 offset:(2*" #S \
-               ")\n ds_read_b128 %3, %4 offset:(3*" #S ")\n s_waitcnt lgkmcnt(0)"                              \
-               : "=v"(r0), "=v"(r1), "=v"(r2), "=v"(r3)                                                  \
-               : "v"(a))
+// direct-to-LDS load before any LDS read it issues, emptying the pipeline).
+#define PROBE_LDS_READ4(r0, r1, r2, r3, a, S)                                                          \
+  asm volatile("ds_read_b128 %0, %4\n ds_read_b128 %1, %4 offset:%5\n ds_read_b128 %2, %4 offset:%6\n" \
+               " ds_read_b128 %3, %4 offset:%7\n s_waitcnt lgkmcnt(0)"                                 \
+               : "=v"(r0), "=v"(r1), "=v"(r2), "=v"(r3)                                                \
+               : "v"(a), "n"(S), "n"(2 * (S)), "n"(3 * (S)))
 
-constexpr int kStreamThreads = 512;
-constexpr int kStreamTileF4 = 4096;  // 64 KiB
+constexpr int kStreamThreads = 256;
+constexpr int kStreamBufs = 4;                      // three units in flight while one is read
+constexpr int kStreamUnitF4 = 4 * kStreamThreads;  // 16 KiB: four 16-byte pieces per thread
 
-__global__ void __launch_bounds__(kStreamThreads) tile_stream_kernel(const float4* __restrict__ src, int tiles,
+__global__ void __launch_bounds__(kStreamThreads) tile_stream_kernel(const float4* __restrict__ src, int units,
                                                                      float* sink) {
-  __shared__ float4 buf[2][kStreamTileF4];
+  __shared__ float4 buf[kStreamBufs][kStreamUnitF4];
   const int tid = threadIdx.x, wave = tid >> 6;
   const int G = gridDim.x, wg = blockIdx.x;
-  auto issue = [&](int t, int b) {  // 8 x 16 bytes per thread, 1 KiB per wave instruction
-    const float4* g = src + (size_t)t * kStreamTileF4 + tid;
+  auto issue = [&](int u, int b) {  // 4 x 16 bytes per thread, 1 KiB per wave instruction
+    const float4* g = src + (size_t)u * kStreamUnitF4 + tid;
 #pragma unroll
-    for (int f = 0; f < 8; ++f)
+    for (int f = 0; f < 4; ++f)
       __builtin_amdgcn_global_load_lds(g + f * kStreamThreads,
                                        (lds_void*)(&buf[b][f * kStreamThreads + wave * 64]), 16, 0, 0);
   };
+#pragma unroll
+  for (int k = 0; k < kStreamBufs - 1; ++k)
+    if (wg + k * G < units) issue(wg + k * G, k);
   float s = 0.f;
   int b = 0;
-  if (wg < tiles) issue(wg, 0);
-  for (int t = wg; t < tiles; t += G, b ^= 1) {
-    if (t + G < tiles) {
-      issue(t + G, b ^ 1);
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // this tile's loads have landed
+  for (int u = wg; u < units; u += G) {
+    const int un = u + (kStreamBufs - 1) * G;
+    if (un < units) {
+      issue(un, (b + kStreamBufs - 1) % kStreamBufs);
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");  // this unit's 4 loads have landed, 12 still in flight
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __builtin_amdgcn_s_barrier();
     const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&buf[b][tid]));
-    float4 x0, x1, x2, x3, x4, x5, x6, x7;
-    PROBE_LDS_READ4(x0, x1, x2, x3, a, 8192);
-    PROBE_LDS_READ4(x4, x5, x6, x7, a + 32768, 8192);
-    s += (x0.x + x1.y) + (x2.z + x3.w) + (x4.x + x5.y) + (x6.z + x7.w);
+    float4 x0, x1, x2, x3;
+    PROBE_LDS_READ4(x0, x1, x2, x3, a, kStreamThreads * 16);
+    s += (x0.x + x1.y) + (x2.z + x3.w);
     __builtin_amdgcn_s_barrier();  // every wave is done with this buffer before it is refilled
+    b = (b + 1) % kStreamBufs;
   }
   if (s == 1.2345678e30f) sink[wg & 255] = s;
 }
@@ -149,14 +153,13 @@ int dl_probe_tile_read_log(const void* src, int tile_bytes, int tiles, const voi
                    static_cast<hipStream_t>(stream));
 }
 
-// Read `tiles` consecutive 64 KiB tiles at `src` (device, 16-byte aligned) with
-// `wgs` persistent workgroups of 512 threads (at most one per CU: each holds two
-// 64 KiB LDS buffers), one tile in flight per workgroup.  Returns 0, -1 for bad
-// arguments, -4 if the launch failed.
-int dl_probe_tile_stream(const void* src, int tiles, int wgs, void* sink, void* stream) {
-  if (!src || !sink || tiles <= 0 || wgs <= 0 || !aligned16(src)) return -1;
+// Read `units` consecutive 16 KiB units at `src` (device, 16-byte aligned) with
+// `wgs` persistent workgroups of 256 threads (64 KiB of LDS each), three units in
+// flight per workgroup.  Returns 0, -1 for bad arguments, -4 if the launch failed.
+int dl_probe_tile_stream(const void* src, int units, int wgs, void* sink, void* stream) {
+  if (!src || !sink || units <= 0 || wgs <= 0 || !aligned16(src)) return -1;
   tile_stream_kernel<<<wgs, kStreamThreads, 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const float4*>(src), tiles, static_cast<float*>(sink));
+      static_cast<const float4*>(src), units, static_cast<float*>(sink));
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
