@@ -41,6 +41,26 @@ def test_every_declared_symbol_is_exported(lib):
     assert exported == set(declared_functions()), exported
 
 
+def test_side_libraries_export_their_calls():
+    """The benchmark's probe library and the tracing build (both outside the ABI) load
+    and export what bench.py calls; the tracing build also exports the whole ABI."""
+    pkg = os.path.join(ROOT, "linear_attention_recurrent_amd")
+    probe = os.path.join(pkg, "libdlprobe.so")
+    trace = os.path.join(pkg, "libdeltalog_trace.so")
+    for path in (probe, trace):
+        if not os.path.exists(path):
+            pytest.fail(f"{os.path.basename(path)} is not built: run `python -m linear_attention_recurrent_amd.build --trace`")
+    exported = lambda path: set(re.findall(r"\sT\s+(dl_\w+)$", os.popen(f"nm -D --defined-only {path}").read(),
+                                           flags=re.M))
+    assert exported(probe) == {"dl_probe_tile_read", "dl_probe_tile_read_log", "dl_probe_tile_rw",
+                               "dl_probe_tile_stream"}
+    assert exported(trace) == set(declared_functions()) | {"dl_trace_copy"}
+    ctypes.CDLL(probe)
+    t = ctypes.CDLL(trace)
+    t.dl_trace_copy.argtypes = [ctypes.c_void_p, ctypes.c_int]
+    assert t.dl_trace_copy(None, -1) == -1  # argument check, no GPU call
+
+
 def test_status_strings(lib):
     from linear_attention_recurrent_amd import deltalog as dl
     for code, tag in [(dl.DL_OK, "DL_OK"), (dl.DL_EINVAL, "DL_EINVAL"), (dl.DL_EUNSUPPORTED, "DL_EUNSUPPORTED"),
