@@ -139,6 +139,22 @@ def test_full_size_sampled_tiles_4096_steps(w):
     _compare(inp, 4096, pool, outs, sel=sel)
 
 
+def test_serving_shape_full_size_ragged_fills():
+    """One layer of the 48-layer serving pool at its full size: GDN, B = 512, H = 32,
+    128/128, L = 16, start fills ragged per sequence, the largest single launch the
+    bench times (16,384 tiles).  512 steps (32 fold periods); fills checked everywhere,
+    states and outputs on tiles across the batch and the heads."""
+    steps = 512
+    inp = make_inputs(5, steps, pool=16, log_len=16)
+    B, H = inp.batch, inp.heads
+    assert B * H == 16384 and len(set(inp.fill0.tolist())) > 1
+    sel = [(0, 0), (1, H - 1), (B // 4, 3), (B // 2, H // 2), (3 * B // 4, 7), (B - 1, 0), (B - 1, H - 1)]
+    pool, outs = run_deltalog(inp, steps, sel=sel)
+    fill = pool.fill.cpu().numpy()
+    assert np.all(fill == (inp.fill0[:, None] + steps) % inp.log_len)
+    _compare(inp, steps, pool, outs, sel=sel)
+
+
 # ------------------------------------------------------------- edge cases ----
 @pytest.mark.parametrize("variant_w", [1, 3, 4])
 @pytest.mark.parametrize("L", [1, 2, 3, 128])
