@@ -15,8 +15,10 @@ headline is the median of --repeats (5) such timed windows, all listed.
 Also measured in the same run: the same step on one pool (its working set can
 stay in the last-level cache: reported as cache-resident), the eager comparator
 (dl_eager_step, read and write the whole state every step) on the same inputs,
-cold and cache-resident, read-only ceilings (a torch sum over 1 GiB, and the
-tile-read probe of libdlprobe.so over the same pools), plain copies,
+cold and cache-resident, read ceilings over the same pools (a torch sum over
+1 GiB; the probes of libdlprobe.so: one workgroup per tile reading it, with its
+log, or writing it back, and persistent workgroups streaming the same bytes
+through LDS), plain copies,
 dl_prefill of a long prompt, dl_merge_on on full logs with each arithmetic unit
 of the fold, and the fp64 CPU oracle on the host cores.
 
