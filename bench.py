@@ -673,6 +673,9 @@ def main():
         return
 
     if args.workload == 5:
+        if args.trace or args.only not in (None, "deltalog"):
+            raise SystemExit("the serving pool (--workload 5) runs its own leg only: no --trace or --only other than "
+                             "deltalog")
         print(json.dumps(serving_leg(args, cpu)))
         return
 
