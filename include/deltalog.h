@@ -88,8 +88,9 @@ typedef struct {
   int32_t base_dtype; /* DL_BASE_F32, or DL_BASE_BF16: a low-bit base.  The log and all
                          arithmetic stay fp32; the base is rounded to bf16 (to nearest,
                          ties to even) only where it is written: at init and at folds.
-                         Outputs then see the fixed low-bit base plus fp32 buffered
-                         updates (LeapQuant abstract, on the FPGA-titled card page). */
+                         Every output then reads the bf16 base together with the
+                         pending updates kept in fp32 (the scheme of the LeapQuant
+                         abstract, on the FPGA-titled card page). */
 } dl_dims;
 
 /* The per-layer state pool (all device, caller-owned).  G = 1 for GDN, dk otherwise. */
@@ -134,9 +135,10 @@ int dl_init_state(const dl_dims *dims, const dl_pool *pool, const float *init_ba
  * the read and output come from base plus log; the step appends one compact
  * update; a step that fills the log merges it into the base).  Reads the base
  * but never writes it except on merging steps; writes io->out, one log entry
- * per tile, and the fills.  Errors: DL_EINVAL for null q/k/v/decay/out or pool
- * arrays, or eps < 0 with eta set; DL_EUNSUPPORTED if beta/eta/bonus presence does
- * not match the variant (GDN/KDA: exactly one of beta and eta; RWKV6: bonus only). */
+ * per tile, and the fills.  A tile whose fill lies outside [0, L) (a pool that was
+ * never started) is left untouched.  Errors: DL_EINVAL for null q/k/v/decay/out or
+ * pool arrays, or eps < 0 with eta set; DL_EUNSUPPORTED if beta/eta/bonus presence
+ * does not match the variant (GDN/KDA: exactly one of beta and eta; RWKV6: bonus only). */
 int dl_decode_step(const dl_dims *dims, const dl_pool *pool, const dl_step_io *io, void *stream);
 
 /* Merge modes: the two named values of dl_merge's min_fill. */
@@ -147,8 +149,9 @@ enum {
   DL_MERGE_ALL = 1  /* fold every non-empty log: min_fill = 1                               */
 };
 
-/* Fold the log of every tile whose fill is >= min_fill (1 <= min_fill <= L)
- * into its base and set its fill to 0 (DeltaLog Abstract: the merge that
+/* Fold the log of every tile whose fill is >= min_fill (0 <= min_fill <= L; a
+ * tile whose fill lies outside [0, L) is left untouched) into its base and set
+ * its fill to 0 (DeltaLog Abstract: the merge that
  * moves logged updates into the base).  min_fill = DL_MERGE_ALL (1) folds
  * every non-empty log, after which `base` holds the dense state S_t of every
  * tile (for a checkpoint, or to read the state); min_fill = DL_MERGE_DUE (0)
