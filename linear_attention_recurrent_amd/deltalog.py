@@ -5,6 +5,24 @@ The calls have the C names and meanings declared in include/deltalog.h
 device memory and the stream; every step of the decode path runs in the HIP
 kernels of libdeltalog.so.  There is no CPU fallback: if the library is not
 built, or no GPU is present, these calls raise.
+
+One GDN layer, 4 sequences x 8 heads, dk = dv = 128, log length 16:
+
+    import torch
+    from linear_attention_recurrent_amd import deltalog as dl
+
+    dev = torch.device("cuda", 0)
+    pool = dl.DeltaLogPool(dl.GDN, 4, 8, 128, 128, 16, dev)  # fp32 base; BASE_BF16 for bf16
+    dl.dl_init_state(pool)                                   # zero state, empty logs
+    out = torch.empty(4, 8, 128, device=dev)
+    for q, k, v, alpha, beta in tokens:                      # bf16 [4, 8, 128]; fp32 [4, 8]
+        dl.dl_decode_step(pool, pool.step_io(q, k, v, alpha, beta, None, out))
+        ...                                                  # out holds this token's outputs
+    dl.dl_merge(pool, dl.MERGE_ALL)                          # pool.base: the dense states
+
+A StepIO holds raw device pointers: the tensors it was made from must stay alive
+(and unchanged in shape) until the work enqueued with it has run.  Calls enqueue
+on torch's current stream of the pool's device unless a stream is passed.
 """
 from __future__ import annotations
 
