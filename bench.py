@@ -283,7 +283,10 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
     decode step uses them: the tile read alone, the tile read plus `log_bytes` of log per
     tile (the mean the step reads), the tile read and written back (the eager step's
     traffic), and the same bytes streamed through LDS by one persistent workgroup per CU
-    with three 16 KiB units in flight."""
+    with three 16 KiB units in flight.  For 128 x 128 fp32 tiles also the owned stream:
+    persistent workgroups that each own whole tiles, as a decode step does, one wave
+    streaming their units into LDS and four forming the column sums, and the same kernel
+    taking the units in the stream's order instead."""
     import ctypes
 
     import torch
@@ -301,6 +304,7 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
     lib.dl_probe_tile_read_log.argtypes = [vp, ci, ci, vp, ci, ci, vp, vp]
     lib.dl_probe_tile_rw.argtypes = [vp, ci, ci, vp]
     lib.dl_probe_tile_stream.argtypes = [vp, ci, ci, vp, vp]
+    lib.dl_probe_owned_stream.argtypes = [vp, ci, ci, vp, ci, vp]
     sink = torch.zeros(256, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
     NP = len(pools)
@@ -327,13 +331,23 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
                                                                  stream), "dl_probe_tile_stream"),
                         tile_bytes * tiles // 16384 * 16384),
     }
+    owned = tile_bytes == 65536 and tiles % 256 == 0 and pools[0].base.dtype == torch.float32
+    if owned:  # 128 x 128 fp32 tiles: the tile-owning stream, and its unit order for comparison
+        colsums = torch.empty(tiles * 128, dtype=torch.float32, device=dev)
+        for order, name in ((0, "owned_stream"), (1, "owned_stream_unit_order")):
+            legs[name] = (lambda t, o=order: check(lib.dl_probe_owned_stream(pools[t % NP].base.data_ptr(), tiles, o,
+                                                                             colsums.data_ptr(), 256, stream),
+                                                   "dl_probe_owned_stream"), tile_bytes * tiles)
     for name, (fn, nbytes) in legs.items():
         secs = time_loop(fn, launches, 2 * NP)
         out[f"{name}_gbs"] = nbytes * launches / secs / 1e9
     out["probe_shape"] = (f"{tiles} tiles of {tile_bytes} B per launch, {NP} pools in turn; read_log adds {lb} B "
                           f"of log per tile; rw writes the tile back (the eager step's traffic); stream reads "
                           f"the same bytes as 16 KiB units with 256 persistent workgroups, three units in "
-                          f"flight per CU through LDS")
+                          f"flight per CU through LDS"
+                          + ("; owned_stream: 256 persistent workgroups owning whole tiles, one wave streaming "
+                             "16 KiB units into LDS three ahead, four forming column sums; its unit_order leg "
+                             "reads the pool's units in the stream's order" if owned else ""))
     return out
 
 
@@ -820,6 +834,8 @@ def main():
                        "frac_of_tile_read_ceiling": achieved / ceil["tile_read_gbs"],
                        "frac_of_tile_read_log_ceiling": achieved / ceil["tile_read_log_gbs"],
                        "frac_of_tile_stream_ceiling": achieved / ceil["tile_stream_gbs"],
+                       "frac_of_owned_stream_ceiling": (achieved / ceil["owned_stream_gbs"]
+                                                        if "owned_stream_gbs" in ceil else None),
                        "frac_of_torch_sum_ceiling": achieved / ceil["torch_sum_gbs"]},
         "read_ceiling_gbs": ceil,
         "cache_resident": {"value": tiles / t_warm, "ms_per_step": t_warm * 1e3, "timed_steps": Kw,

@@ -12,6 +12,13 @@
 //   stream        the same bytes as 16 KiB units read by persistent workgroups (one
 //                 per CU) through four LDS buffers, each unit loaded straight into
 //                 LDS: three units in flight per CU, no registers held
+//   owned stream  persistent workgroups (one per CU) that own whole 128 x 128 fp32
+//                 tiles, as a decode step does: one wave streams each tile's four
+//                 16 KiB units straight into a ring of eight LDS buffers, three
+//                 ahead of the one read, and four waves form the tile's column sums
+//                 from LDS (a decode step's base matvec with nothing around it); or,
+//                 for comparison, the same kernel taking the pool's units in the
+//                 stream order above
 // Loaded values feed a sum that is stored only if it equals a value no sum of
 // finite inputs hits in practice, so the loads cannot be dropped; the write-back
 // scales by 1 - 2^-24 rounded, so it rewrites every value (the stored values change
@@ -127,6 +134,110 @@ __global__ void __launch_bounds__(kStreamThreads) tile_stream_kernel(const float
   if (s == 1.2345678e30f) sink[wg & 255] = s;
 }
 
+// ---------------------------------------------------------------- owned stream
+// Workgroup of 320 threads: wave 0 only issues direct-to-LDS loads, from inline asm so
+// that the compiler neither counts them nor waits for them (it would otherwise wait for
+// every such load in flight before any LDS read); its own s_waitcnt before each barrier
+// holds the units issued after the one about to be read (16 instructions of 1 KiB per
+// unit).  Waves 1..4 never load from global memory: every LDS read of theirs follows a
+// barrier that wave 0 reaches only once the unit has landed.  One barrier per unit.
+// Column sums:  out[t][c] = sum_r B_t[r][c] y(t, r),  y(t, r) = 1 + ((131 t + r) mod 7) / 8.
+// ORDER 0: workgroup w owns tiles w, w + G, ... (units in order).  ORDER 1: workgroup w
+// reads units w, w + G, w + 2G, ... of the pool and sums each run of four as "tile"
+// w + i G with unit j of the run at rows 32 j..32 j + 31 (needs G | tiles).
+constexpr int kOwnThreads = 320;
+constexpr int kOwnRing = 8;
+constexpr int kOwnAhead = 3;         // units in flight beyond the one awaited
+constexpr int kOwnUnitF4 = 1024;     // 16 KiB
+constexpr int kOwnUnitsPerTile = 4;  // 128 x 128 fp32
+
+__device__ __forceinline__ float own_weight(int t, int r) { return 1.f + (float)((t * 131 + r) % 7) * 0.125f; }
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is written by the asm and declared clobbered
+// Sixteen 1 KiB direct-to-LDS loads: lane l of load f copies the 16 bytes at g + f * 64 + l
+// (float4 units) to LDS byte lds + f * 1024 + 16 l (the hardware adds 16 l to m0).
+__device__ __forceinline__ void own_issue_unit(const float4* g, uint32_t lds) {
+#pragma unroll
+  for (int f = 0; f < 16; f += 4)
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %4, off\n\t"
+        "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, off\n\t"
+        "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, off\n\t"
+        "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %7, off" ::"s"(lds + f * 1024),
+        "s"(lds + (f + 1) * 1024), "s"(lds + (f + 2) * 1024), "s"(lds + (f + 3) * 1024), "v"(g + f * 64),
+        "v"(g + (f + 1) * 64), "v"(g + (f + 2) * 64), "v"(g + (f + 3) * 64)
+        : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int ORDER>
+__global__ void __launch_bounds__(kOwnThreads) owned_stream_kernel(const float4* __restrict__ src, int tiles,
+                                                                   float* __restrict__ out) {
+  __shared__ float4 ring[kOwnRing][kOwnUnitF4];
+  __shared__ float red[4][128];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = gridDim.x, wg = blockIdx.x;
+  const int ntile = tiles > wg ? (tiles - wg + G - 1) / G : 0;
+  const int K = ntile * kOwnUnitsPerTile;  // units this workgroup reads, in phase order
+  auto unit_at = [&](int k) -> size_t {    // pool index of the unit read in phase k
+    if (ORDER == 1) return (size_t)wg + (size_t)k * G;
+    return ((size_t)wg + (size_t)(k / kOwnUnitsPerTile) * G) * kOwnUnitsPerTile + k % kOwnUnitsPerTile;
+  };
+  auto issue = [&](int k) {
+    own_issue_unit(src + unit_at(k) * kOwnUnitF4 + lane, (uint32_t)(uintptr_t)&ring[k % kOwnRing][0]);
+  };
+  int issued = 0;
+  if (wave == 0) {
+    issued = K < kOwnAhead ? K : kOwnAhead;
+    for (int k = 0; k < issued; ++k) issue(k);
+  }
+  // consumer wave c = wave - 1, lane (h, q): rows 8c + 4h + i (i < 4) of each unit, columns 4q..4q+3
+  const int c = wave - 1, h = lane >> 5, q = lane & 31;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int ph = 0; ph <= K; ++ph) {  // phase K only finishes the last tile
+    if (wave == 0 && ph < K) {
+      const int want = ph + kOwnAhead + 1 < K ? ph + kOwnAhead + 1 : K;
+      while (issued < want) issue(issued++);  // unit k takes the slot of unit k - 8, read 5 or more phases ago
+      const int after = issued - ph - 1;      // units issued after unit ph
+      if (after >= 3) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
+      else if (after == 2) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+      else if (after == 1) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (wave == 0) continue;
+    const int i = ph / kOwnUnitsPerTile, u = ph % kOwnUnitsPerTile;
+    if (u == 0 && i > 0 && lane < 32) {  // tile i - 1, columns 32c..32c+31
+      const int col = 32 * c + lane;
+      const float sum = (red[0][col] + red[1][col]) + (red[2][col] + red[3][col]);
+      __builtin_nontemporal_store(sum, out + ((size_t)wg + (size_t)(i - 1) * G) * 128 + col);
+    }
+    if (ph == K) continue;
+    const int t = wg + i * G;
+    const float4* sl = &ring[ph % kOwnRing][0];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 8 * c + 4 * h + r;
+      const float4 x = sl[row * 32 + q];
+      const float y = own_weight(t, 32 * u + row);
+      acc.x = fmaf(y, x.x, acc.x);
+      acc.y = fmaf(y, x.y, acc.y);
+      acc.z = fmaf(y, x.z, acc.z);
+      acc.w = fmaf(y, x.w, acc.w);
+    }
+    if (u == kOwnUnitsPerTile - 1) {  // red is read in the next phase and rewritten four phases later
+      acc.x += __shfl_xor(acc.x, 32);
+      acc.y += __shfl_xor(acc.y, 32);
+      acc.z += __shfl_xor(acc.z, 32);
+      acc.w += __shfl_xor(acc.w, 32);
+      if (h == 0) *reinterpret_cast<float4*>(&red[c][4 * q]) = acc;
+      acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -160,6 +271,24 @@ int dl_probe_tile_stream(const void* src, int units, int wgs, void* sink, void* 
   if (!src || !sink || units <= 0 || wgs <= 0 || !aligned16(src)) return -1;
   tile_stream_kernel<<<wgs, kStreamThreads, 0, static_cast<hipStream_t>(stream)>>>(
       static_cast<const float4*>(src), units, static_cast<float*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// Stream `tiles` 128 x 128 fp32 tiles at `src` (device, 16-byte aligned, 64 KiB each)
+// through LDS with `wgs` persistent workgroups of 320 threads (130 KiB of LDS each, so
+// one per CU) and write their column sums, as defined at owned_stream_kernel, to `out`
+// (device, tiles x 128 floats).  order 0: whole tiles per workgroup; order 1: the pool's
+// 16 KiB units strided over the workgroups (needs tiles % wgs == 0).  Returns 0, -1 for
+// bad arguments, -4 if the launch failed.
+int dl_probe_owned_stream(const void* src, int tiles, int order, void* out, int wgs, void* stream) {
+  if (!src || !out || tiles <= 0 || wgs <= 0 || !aligned16(src) || !aligned16(out)) return -1;
+  if (order != 0 && order != 1) return -1;
+  if (order == 1 && tiles % wgs) return -1;
+  auto st = static_cast<hipStream_t>(stream);
+  const float4* s = static_cast<const float4*>(src);
+  float* o = static_cast<float*>(out);
+  if (order == 0) owned_stream_kernel<0><<<wgs, kOwnThreads, 0, st>>>(s, tiles, o);
+  else owned_stream_kernel<1><<<wgs, kOwnThreads, 0, st>>>(s, tiles, o);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -53,9 +53,17 @@ def test_side_libraries_export_their_calls():
     exported = lambda path: set(re.findall(r"\sT\s+(dl_\w+)$", os.popen(f"nm -D --defined-only {path}").read(),
                                            flags=re.M))
     assert exported(probe) == {"dl_probe_tile_read", "dl_probe_tile_read_log", "dl_probe_tile_rw",
-                               "dl_probe_tile_stream"}
+                               "dl_probe_tile_stream", "dl_probe_owned_stream"}
     assert exported(trace) == set(declared_functions()) | {"dl_trace_copy"}
-    ctypes.CDLL(probe)
+    p = ctypes.CDLL(probe)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    p.dl_probe_owned_stream.argtypes = [vp, ci, ci, vp, ci, vp]
+    # argument checks, all rejected before any GPU call: null or misaligned buffers, no
+    # tiles or workgroups, an unknown order, the unit order with tiles not a multiple of wgs
+    for args in ((None, 512, 0, 0x10000, 256), (0x10000, 512, 0, None, 256), (0x10004, 512, 0, 0x10000, 256),
+                 (0x10000, 0, 0, 0x10000, 256), (0x10000, 512, 0, 0x10000, 0), (0x10000, 512, 2, 0x10000, 256),
+                 (0x10000, 300, 1, 0x10000, 256)):
+        assert p.dl_probe_owned_stream(*args, None) == -1
     t = ctypes.CDLL(trace)
     t.dl_trace_copy.argtypes = [ctypes.c_void_p, ctypes.c_int]
     assert t.dl_trace_copy(None, -1) == -1  # argument check, no GPU call
