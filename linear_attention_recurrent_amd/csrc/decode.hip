@@ -53,6 +53,16 @@ __device__ __forceinline__ void trace_stamp(int k, const void* q, int tiles, int
 #define DL_STAMP(k) ((void)0)
 #endif
 
+// Threads per workgroup of the decode step and the merge: 512 for GDN with an fp32 base
+// at 128 x 128 (80 VGPRs, three workgroups per CU: six waves per SIMD where 256 threads
+// at 131 VGPRs give three; a cold step 1.2 % faster), else the geometry's default (at
+// 512 threads KDA needs 143 VGPRs, one workgroup per CU, and a bf16 base step was 4 %
+// slower).
+template <int VAR, int DK, int DV, bool BF>
+constexpr int step_threads() { return VAR == DL_GDN && !BF && DK * DV >= 16384 ? 512 : 0; }
+template <int VAR, int DK, int DV, bool BF, int PF = 0>
+using StepGeo = SGeo<DK, DV, PF, step_threads<VAR, DK, DV, BF>()>;
+
 // Read coefficients of one log entry j, computed by a group of LPE lanes that
 // each hold 8 key channels:
 //   GDN    sigma^k_j = 2^(c_t - c_j) (k_j . k_t),   sigma^q_j = 2^(c_t - c_j) (k_j . q_t)
@@ -61,12 +71,12 @@ __device__ __forceinline__ void trace_stamp(int k, const void* q, int tiles, int
 // Lane 0 of the group stores them to s_sig[0][j] and s_sig[1][j].  When
 // `stage` is set, the group also stores the entry's fold weights
 // w_j[i] = 2^(c_t[i] - c_j[i]) k_j[i] to s_w (rows permuted).
-template <int VAR, int DK, int DV, int CWN>
+template <int VAR, int DK, int DV, bool BF, int CWN>
 __device__ __forceinline__ void log_coefs(const uint4 kj8, const float (&cj)[CWN], const float (&kt)[8],
                                           const float (&qt)[8], const float (&ct)[CWN],
                                           const float (&cprev)[CWN], float (*s_sig)[DL_MAX_LOG_LEN],
                                           int j, int ch, bool stage, float* s_w) {
-  using G = SGeo<DK, DV>;
+  using G = StepGeo<VAR, DK, DV, BF>;
   float kj[8];
   unpack8(kj8, kj);
   float a = 0.f, b = 0.f;
@@ -117,11 +127,11 @@ __device__ __forceinline__ void log_coefs(const uint4 kj8, const float (&cj)[CWN
 // (s_kcur, already permuted, and s_ucur).  Every thread takes part: all of its
 // loads (16-byte pieces of key, decay and factor rows; slots outside the stage
 // read zeros through out-of-range offsets) are issued before any is used.
-template <int VAR, int DK, int DV, bool HAS_CUR>
+template <int VAR, int DK, int DV, bool BF, bool HAS_CUR>
 __device__ __forceinline__ void stage_entries(const PoolArgs& p, int tile, int e0, int cnt, int nlog,
                                               const float* s_cnow, const float* s_kcur,
                                               const float* s_ucur, float* s_w, float* s_uu) {
-  using G = SGeo<DK, DV>;
+  using G = StepGeo<VAR, DK, DV, BF>;
   constexpr bool VEC = VAR != DL_GDN;
   constexpr int CW = VEC ? DK : 1;
   using UT = std::conditional_t<VAR == DL_RWKV6, uint16_t, float>;
@@ -185,7 +195,7 @@ __device__ __forceinline__ void stage_entries(const PoolArgs& p, int tile, int e
 template <int VAR, int DK, int DV, bool BF>
 __device__ __forceinline__ void fold_pass(typename BaseIO<BF>::T* tb, int nent, bool scale, const float* s_g,
                                           const float* s_w, const float* s_uu) {
-  using G = SGeo<DK, DV>;
+  using G = StepGeo<VAR, DK, DV, BF>;
   using BIO = BaseIO<BF>;
   constexpr int RPC = G::RPC;
   const int tid = threadIdx.x;
@@ -235,13 +245,13 @@ template <int VAR, int DK, int DV, bool BF, bool HAS_CUR>
 __device__ __forceinline__ void fold_staged(const PoolArgs& p, int tile, int nlog,
                                             const float* s_ct, const float* s_g, const float* s_kcur,
                                             const float* s_ucur, float* s_w, float* s_uu) {
-  using G = SGeo<DK, DV>;
+  using G = StepGeo<VAR, DK, DV, BF>;
   auto* tb = BaseIO<BF>::tile(p.base, (size_t)tile * DK * DV);
   const int total = nlog + (HAS_CUR ? 1 : 0);
   for (int e0 = 0; e0 < total; e0 += G::MC) {
     const int cnt = min(G::MC, total - e0);
     __syncthreads();  // the previous stage's LDS reads are done
-    stage_entries<VAR, DK, DV, HAS_CUR>(p, tile, e0, cnt, nlog, s_ct, s_kcur, s_ucur, s_w, s_uu);
+    stage_entries<VAR, DK, DV, BF, HAS_CUR>(p, tile, e0, cnt, nlog, s_ct, s_kcur, s_ucur, s_w, s_uu);
     __syncthreads();
     fold_pass<VAR, DK, DV, BF>(tb, cnt, e0 == 0, s_g, s_w, s_uu);
   }
@@ -271,7 +281,7 @@ struct DecodeLds {
 // and only the output, one log entry and the fill are written.
 template <int VAR, int DK, int DV, bool BF, int PF, bool FOLD, typename Lds>
 __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s, int tile, int n, Lds& sh) {
-  using G = SGeo<DK, DV, PF>;
+  using G = StepGeo<VAR, DK, DV, BF, PF>;
   using BIO = BaseIO<BF>;
   constexpr bool VEC = VAR != DL_GDN;  // per-key-channel decay
   constexpr int CW = VEC ? DK : 1;     // floats per log_c entry
@@ -409,7 +419,7 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
 #pragma unroll
     for (int e = 0; e < G::EPF; ++e) {
       const int j = eg + G::NG * e;
-      if (j < n) log_coefs<VAR, DK, DV>(kj8[e], cj[e], kt, qt, ct, cprev, sh.sig, j, ch, reg_stage, sh.w);
+      if (j < n) log_coefs<VAR, DK, DV, BF>(kj8[e], cj[e], kt, qt, ct, cprev, sh.sig, j, ch, reg_stage, sh.w);
     }
     // later passes, only when L > NG*EPF + 1
     for (int j = eg + G::NG * G::EPF; j < n; j += G::NG) {
@@ -417,7 +427,7 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
       if constexpr (VEC) load8(p.log_c + (lbase + j) * DK + ch * 8, cjj);
       else cjj[0] = p.log_c[lbase + j];
       const uint4 kjj = *reinterpret_cast<const uint4*>(p.log_k + (lbase + j) * DK + ch * 8);
-      log_coefs<VAR, DK, DV>(kjj, cjj, kt, qt, ct, cprev, sh.sig, j, ch, false, sh.w);
+      log_coefs<VAR, DK, DV, BF>(kjj, cjj, kt, qt, ct, cprev, sh.sig, j, ch, false, sh.w);
     }
   }
   if constexpr (FOLD) {
@@ -551,7 +561,7 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
       const int cnt = min(G::MC, total - e0);
       if (!reg_stage) {
         __syncthreads();  // the previous stage's LDS reads are done
-        stage_entries<VAR, DK, DV, true>(p, tile, e0, cnt, n, sh.ct, sh.kcur, sh.ucur, sh.w, sh.uu);
+        stage_entries<VAR, DK, DV, BF, true>(p, tile, e0, cnt, n, sh.ct, sh.kcur, sh.ucur, sh.w, sh.uu);
       }
       __syncthreads();
       for (int m = 0; m < cnt; ++m) {
@@ -577,8 +587,8 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
 // PF: log entries loaded ahead of the base (the launcher picks it from L so that a
 // step finds every entry of its log among them, up to 64).
 template <int VAR, int DK, int DV, bool BF, int PF>
-__global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, StepArgs s) {
-  using G = SGeo<DK, DV, PF>;
+__global__ void __launch_bounds__((StepGeo<VAR, DK, DV, BF>::NT)) decode_kernel(PoolArgs p, StepArgs s) {
+  using G = StepGeo<VAR, DK, DV, BF, PF>;
   __shared__ DecodeLds<DK, DV, (VAR == DL_GDN ? 1 : DK), G::NW, G::MC> sh;
   DL_STAMP(0);
   const int tile = blockIdx.x;
@@ -596,8 +606,8 @@ __global__ void __launch_bounds__((SGeo<DK, DV>::NT)) decode_kernel(PoolArgs p, 
 
 // dl_merge: fold the logs of tiles holding at least min_fill entries.
 template <int VAR, int DK, int DV, bool BF>
-__global__ void __launch_bounds__((SGeo<DK, DV>::NT)) merge_kernel(PoolArgs p, int min_fill) {
-  using G = SGeo<DK, DV>;
+__global__ void __launch_bounds__((StepGeo<VAR, DK, DV, BF>::NT)) merge_kernel(PoolArgs p, int min_fill) {
+  using G = StepGeo<VAR, DK, DV, BF>;
   constexpr bool VEC = VAR != DL_GDN;
   constexpr int CW = VEC ? DK : 1;
   const int tid = threadIdx.x;
@@ -676,8 +686,8 @@ hipError_t launch_decode(int variant, bool bf16_base, int dk, int dv, int tiles,
   do {                                                                                                 \
     const void* f = reinterpret_cast<const void*>(&decode_kernel<V, K, D, B, 0>);                      \
     if (p.L - 1 > 32) f = reinterpret_cast<const void*>(&decode_kernel<V, K, D, B, 64>);               \
-    else if (p.L - 1 > SGeo<K, D>::PF) f = reinterpret_cast<const void*>(&decode_kernel<V, K, D, B, 32>); \
-    err = hipLaunchKernel(f, dim3(tiles), dim3(SGeo<K, D>::NT), args, 0, stream);                      \
+    else if (p.L - 1 > StepGeo<V, K, D, B>::PF) f = reinterpret_cast<const void*>(&decode_kernel<V, K, D, B, 32>); \
+    err = hipLaunchKernel(f, dim3(tiles), dim3(StepGeo<V, K, D, B>::NT), args, 0, stream);             \
   } while (0)
   DL_VARIANTS(variant, bf16_base, dk, dv, CALL_DECODE);
 #undef CALL_DECODE
@@ -692,7 +702,7 @@ hipError_t launch_merge(int variant, bool bf16_base, int dk, int dv, int tiles, 
   void* args[] = {&pa, &mf};
 #define CALL_MERGE(V, B, K, D)                                                                    \
   err = hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<V, K, D, B>), dim3(tiles),    \
-                        dim3(SGeo<K, D>::NT), args, 0, stream)
+                        dim3(StepGeo<V, K, D, B>::NT), args, 0, stream)
   DL_VARIANTS(variant, bf16_base, dk, dv, CALL_MERGE);
 #undef CALL_MERGE
   return err;

@@ -36,10 +36,11 @@ struct Geo {
 // In LDS, per-row vectors are stored permuted by perm(i) = (i % RG)*RPT + i/RG,
 // which makes the RPC rows of one chunk of one thread four consecutive floats.
 // PF_ is the number of log entries whose keys, decays and factors a decode step
-// loads before the base (at least the fold stage size).
-template <int DK, int DV, int PF_ = 0>
+// loads before the base (at least the fold stage size).  NT_, when nonzero, sets the
+// threads per workgroup; otherwise 256 for tiles of at least 8,192 entries, else 128.
+template <int DK, int DV, int PF_ = 0, int NT_ = 0>
 struct SGeo {
-  static constexpr int NT = (DK * DV >= 8192) ? 256 : 128;  // threads per workgroup
+  static constexpr int NT = NT_ > 0 ? NT_ : (DK * DV >= 8192) ? 256 : 128;  // threads per workgroup
   static constexpr int CG = DV / 4;                          // float4 column groups
   static constexpr int RG = NT / CG;                         // row groups
   static constexpr int RPT = DK / RG;                        // rows per thread
