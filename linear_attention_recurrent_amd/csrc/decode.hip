@@ -53,15 +53,27 @@ __device__ __forceinline__ void trace_stamp(int k, const void* q, int tiles, int
 #define DL_STAMP(k) ((void)0)
 #endif
 
-// Threads per workgroup of the decode step and the merge: 512 for GDN with an fp32 base
-// at 128 x 128 (80 VGPRs, three workgroups per CU: six waves per SIMD where 256 threads
-// at 131 VGPRs give three; a cold step 1.2 % faster), else the geometry's default (at
-// 512 threads KDA needs 143 VGPRs, one workgroup per CU, and a bf16 base step was 4 %
-// slower).
-template <int VAR, int DK, int DV, bool BF>
-constexpr int step_threads() { return VAR == DL_GDN && !BF && DK * DV >= 16384 ? 512 : 0; }
+// Threads per workgroup of the decode step (PF: its log prefetch) and of the merge (PF 0)
+// at 128 x 128 with an fp32 base, where 512 threads halve each thread's share of the tile:
+//   GDN: 512 (80 VGPRs: three workgroups per CU, six waves per SIMD where 256 threads at
+//     131 VGPRs give three; cold steps 0.5-1.2 % faster, the vector merge up to 11 %);
+//   KDA with PF 0 (logs of up to 17 entries): 512, held to 128 VGPRs (four waves per SIMD,
+//     step_waves) so that two workgroups share a CU: 16 waves where 256 threads at 146
+//     VGPRs give 12 (cold steps 3.7 % faster); with more prefetched entries the cap spills.
+// Otherwise the geometry's default: with a bf16 base the GDN step was 4 % slower at 512
+// threads and the KDA vector merge up to 14 %.
+template <int VAR, int DK, int DV, bool BF, int PF>
+constexpr int step_threads() {
+  return DK * DV < 16384 || BF ? 0 : VAR == DL_GDN || (VAR == DL_KDA && PF == 0) ? 512 : 0;
+}
+// Waves per SIMD the register budget must allow: 4 for KDA at 512 threads (above), else
+// no bound.
+template <int VAR, int DK, int DV, bool BF, int PF>
+constexpr int step_waves() {
+  return VAR != DL_KDA || DK * DV < 16384 ? 1 : step_threads<VAR, DK, DV, BF, PF>() == 512 ? 4 : 1;
+}
 template <int VAR, int DK, int DV, bool BF, int PF = 0>
-using StepGeo = SGeo<DK, DV, PF, step_threads<VAR, DK, DV, BF>()>;
+using StepGeo = SGeo<DK, DV, PF, step_threads<VAR, DK, DV, BF, PF>()>;
 
 // Read coefficients of one log entry j, computed by a group of LPE lanes that
 // each hold 8 key channels:
@@ -70,13 +82,14 @@ using StepGeo = SGeo<DK, DV, PF, step_threads<VAR, DK, DV, BF>()>;
 //   RWKV6  sigma^r_j = sum_i k_j[i] 2^(c_{t-1}[i] - c_j[i]) r_t[i]
 // Lane 0 of the group stores them to s_sig[0][j] and s_sig[1][j].  When
 // `stage` is set, the group also stores the entry's fold weights
-// w_j[i] = 2^(c_t[i] - c_j[i]) k_j[i] to s_w (rows permuted).
-template <int VAR, int DK, int DV, bool BF, int CWN>
+// w_j[i] = 2^(c_t[i] - c_j[i]) k_j[i] to s_w (rows permuted as for a workgroup of NT
+// threads, the calling kernel's).
+template <int VAR, int DK, int DV, int NT, int CWN>
 __device__ __forceinline__ void log_coefs(const uint4 kj8, const float (&cj)[CWN], const float (&kt)[8],
                                           const float (&qt)[8], const float (&ct)[CWN],
                                           const float (&cprev)[CWN], float (*s_sig)[DL_MAX_LOG_LEN],
                                           int j, int ch, bool stage, float* s_w) {
-  using G = StepGeo<VAR, DK, DV, BF>;
+  using G = SGeo<DK, DV, 0, NT>;
   float kj[8];
   unpack8(kj8, kj);
   float a = 0.f, b = 0.f;
@@ -126,12 +139,13 @@ __device__ __forceinline__ void log_coefs(const uint4 kj8, const float (&cj)[CWN
 // s_uu[m][j] = u_e[j]; entry nlog, when asked for, is the current update
 // (s_kcur, already permuted, and s_ucur).  Every thread takes part: all of its
 // loads (16-byte pieces of key, decay and factor rows; slots outside the stage
-// read zeros through out-of-range offsets) are issued before any is used.
-template <int VAR, int DK, int DV, bool BF, bool HAS_CUR>
+// read zeros through out-of-range offsets) are issued before any is used.  NT: the
+// threads of the calling kernel's workgroup.
+template <int VAR, int DK, int DV, int NT, bool HAS_CUR>
 __device__ __forceinline__ void stage_entries(const PoolArgs& p, int tile, int e0, int cnt, int nlog,
                                               const float* s_cnow, const float* s_kcur,
                                               const float* s_ucur, float* s_w, float* s_uu) {
-  using G = StepGeo<VAR, DK, DV, BF>;
+  using G = SGeo<DK, DV, 0, NT>;
   constexpr bool VEC = VAR != DL_GDN;
   constexpr int CW = VEC ? DK : 1;
   using UT = std::conditional_t<VAR == DL_RWKV6, uint16_t, float>;
@@ -251,7 +265,7 @@ __device__ __forceinline__ void fold_staged(const PoolArgs& p, int tile, int nlo
   for (int e0 = 0; e0 < total; e0 += G::MC) {
     const int cnt = min(G::MC, total - e0);
     __syncthreads();  // the previous stage's LDS reads are done
-    stage_entries<VAR, DK, DV, BF, HAS_CUR>(p, tile, e0, cnt, nlog, s_ct, s_kcur, s_ucur, s_w, s_uu);
+    stage_entries<VAR, DK, DV, G::NT, HAS_CUR>(p, tile, e0, cnt, nlog, s_ct, s_kcur, s_ucur, s_w, s_uu);
     __syncthreads();
     fold_pass<VAR, DK, DV, BF>(tb, cnt, e0 == 0, s_g, s_w, s_uu);
   }
@@ -419,7 +433,7 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
 #pragma unroll
     for (int e = 0; e < G::EPF; ++e) {
       const int j = eg + G::NG * e;
-      if (j < n) log_coefs<VAR, DK, DV, BF>(kj8[e], cj[e], kt, qt, ct, cprev, sh.sig, j, ch, reg_stage, sh.w);
+      if (j < n) log_coefs<VAR, DK, DV, G::NT>(kj8[e], cj[e], kt, qt, ct, cprev, sh.sig, j, ch, reg_stage, sh.w);
     }
     // later passes, only when L > NG*EPF + 1
     for (int j = eg + G::NG * G::EPF; j < n; j += G::NG) {
@@ -427,7 +441,7 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
       if constexpr (VEC) load8(p.log_c + (lbase + j) * DK + ch * 8, cjj);
       else cjj[0] = p.log_c[lbase + j];
       const uint4 kjj = *reinterpret_cast<const uint4*>(p.log_k + (lbase + j) * DK + ch * 8);
-      log_coefs<VAR, DK, DV, BF>(kjj, cjj, kt, qt, ct, cprev, sh.sig, j, ch, false, sh.w);
+      log_coefs<VAR, DK, DV, G::NT>(kjj, cjj, kt, qt, ct, cprev, sh.sig, j, ch, false, sh.w);
     }
   }
   if constexpr (FOLD) {
@@ -561,7 +575,7 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
       const int cnt = min(G::MC, total - e0);
       if (!reg_stage) {
         __syncthreads();  // the previous stage's LDS reads are done
-        stage_entries<VAR, DK, DV, BF, true>(p, tile, e0, cnt, n, sh.ct, sh.kcur, sh.ucur, sh.w, sh.uu);
+        stage_entries<VAR, DK, DV, G::NT, true>(p, tile, e0, cnt, n, sh.ct, sh.kcur, sh.ucur, sh.w, sh.uu);
       }
       __syncthreads();
       for (int m = 0; m < cnt; ++m) {
@@ -587,7 +601,8 @@ __device__ __forceinline__ void decode_tile(const PoolArgs& p, const StepArgs& s
 // PF: log entries loaded ahead of the base (the launcher picks it from L so that a
 // step finds every entry of its log among them, up to 64).
 template <int VAR, int DK, int DV, bool BF, int PF>
-__global__ void __launch_bounds__((StepGeo<VAR, DK, DV, BF>::NT)) decode_kernel(PoolArgs p, StepArgs s) {
+__global__ void __launch_bounds__((StepGeo<VAR, DK, DV, BF, PF>::NT), (step_waves<VAR, DK, DV, BF, PF>()))
+decode_kernel(PoolArgs p, StepArgs s) {
   using G = StepGeo<VAR, DK, DV, BF, PF>;
   __shared__ DecodeLds<DK, DV, (VAR == DL_GDN ? 1 : DK), G::NW, G::MC> sh;
   DL_STAMP(0);
@@ -685,9 +700,15 @@ hipError_t launch_decode(int variant, bool bf16_base, int dk, int dv, int tiles,
 #define CALL_DECODE(V, B, K, D)                                                                        \
   do {                                                                                                 \
     const void* f = reinterpret_cast<const void*>(&decode_kernel<V, K, D, B, 0>);                      \
-    if (p.L - 1 > 32) f = reinterpret_cast<const void*>(&decode_kernel<V, K, D, B, 64>);               \
-    else if (p.L - 1 > StepGeo<V, K, D, B>::PF) f = reinterpret_cast<const void*>(&decode_kernel<V, K, D, B, 32>); \
-    err = hipLaunchKernel(f, dim3(tiles), dim3(StepGeo<V, K, D, B>::NT), args, 0, stream);             \
+    int nt = StepGeo<V, K, D, B, 0>::NT;  /* the threads of the kernel picked */                      \
+    if (p.L - 1 > 32) {                                                                                \
+      f = reinterpret_cast<const void*>(&decode_kernel<V, K, D, B, 64>);                               \
+      nt = StepGeo<V, K, D, B, 64>::NT;                                                                \
+    } else if (p.L - 1 > StepGeo<V, K, D, B>::PF) {                                                    \
+      f = reinterpret_cast<const void*>(&decode_kernel<V, K, D, B, 32>);                               \
+      nt = StepGeo<V, K, D, B, 32>::NT;                                                                \
+    }                                                                                                  \
+    err = hipLaunchKernel(f, dim3(tiles), dim3(nt), args, 0, stream);                                  \
   } while (0)
   DL_VARIANTS(variant, bf16_base, dk, dv, CALL_DECODE);
 #undef CALL_DECODE
