@@ -196,6 +196,21 @@ def test_log_entries_loaded_ahead(w, dk, dv, L):
 
 
 @pytest.mark.parametrize("w", [1, 3, 4])
+@pytest.mark.parametrize("L", [17, 18])
+def test_log_length_at_the_prefetch_boundary(w, L):
+    """L = 17 is the longest log the decode step's first variant covers (16 entries loaded
+    ahead of the base, the fold in two staged passes; 512 threads per workgroup for GDN and
+    KDA with an fp32 base at 128 x 128); L = 18 is the first that takes the 32-entry variant
+    (256 threads for KDA).  Ragged fills put tiles at both ends of the log."""
+    steps = 2 * L + 5
+    inp = make_inputs(w, steps, batch=3, heads=2, log_len=L, pool=steps, dk=128, dv=128,
+                      fill0=np.array([0, L // 2, L - 2], np.int32))
+    pool, outs = run_deltalog(inp, steps)
+    assert np.all(pool.fill.cpu().numpy() == ((inp.fill0 + steps) % L)[:, None])
+    _compare(inp, steps, pool, outs)
+
+
+@pytest.mark.parametrize("w", [1, 3, 4])
 def test_unit_zero_and_tiny_decay(w):
     inp = make_inputs(w, 48, batch=2, heads=2, log_len=8, pool=48)
     d = inp.decay
