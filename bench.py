@@ -285,8 +285,9 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
     traffic), and the same bytes streamed through LDS by one persistent workgroup per CU
     with three 16 KiB units in flight.  For 128 x 128 fp32 tiles also the owned stream:
     persistent workgroups that each own whole tiles, as a decode step does, one wave
-    streaming their units into LDS and four forming the column sums, and the same kernel
-    taking the units in the stream's order instead."""
+    streaming their units into LDS and four forming the column sums (tiles strided over the
+    workgroups, the same with each tile's units in a rotated order, or a contiguous run of
+    tiles per workgroup), and the same kernel taking the units in the stream's order."""
     import ctypes
 
     import torch
@@ -334,7 +335,8 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
     owned = tile_bytes == 65536 and tiles % 256 == 0 and pools[0].base.dtype == torch.float32
     if owned:  # 128 x 128 fp32 tiles: the tile-owning stream, and its unit order for comparison
         colsums = torch.empty(tiles * 128, dtype=torch.float32, device=dev)
-        for order, name in ((0, "owned_stream"), (1, "owned_stream_unit_order")):
+        for order, name in ((0, "owned_stream"), (1, "owned_stream_unit_order"), (2, "owned_stream_rotated"),
+                            (3, "owned_stream_contiguous")):
             legs[name] = (lambda t, o=order: check(lib.dl_probe_owned_stream(pools[t % NP].base.data_ptr(), tiles, o,
                                                                              colsums.data_ptr(), 256, stream),
                                                    "dl_probe_owned_stream"), tile_bytes * tiles)
@@ -347,7 +349,8 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
                           f"flight per CU through LDS"
                           + ("; owned_stream: 256 persistent workgroups owning whole tiles, one wave streaming "
                              "16 KiB units into LDS three ahead, four forming column sums; its unit_order leg "
-                             "reads the pool's units in the stream's order" if owned else ""))
+                             "reads the pool's units in the stream's order, rotated starts each tile at unit "
+                             "w mod 4, contiguous gives each workgroup a run of whole tiles" if owned else ""))
     return out
 
 

@@ -144,7 +144,9 @@ __global__ void __launch_bounds__(kStreamThreads) tile_stream_kernel(const float
 // Column sums:  out[t][c] = sum_r B_t[r][c] y(t, r),  y(t, r) = 1 + ((131 t + r) mod 7) / 8.
 // ORDER 0: workgroup w owns tiles w, w + G, ... (units in order).  ORDER 1: workgroup w
 // reads units w, w + G, w + 2G, ... of the pool and sums each run of four as "tile"
-// w + i G with unit j of the run at rows 32 j..32 j + 31 (needs G | tiles).
+// w + i G with unit j of the run at rows 32 j..32 j + 31 (needs G | tiles).  ORDER 2: as
+// 0, each tile's units read starting at unit w mod 4.  ORDER 3: workgroup w owns the
+// contiguous tiles w P .. w P + P - 1, P = ceil(tiles / G).
 constexpr int kOwnThreads = 320;
 constexpr int kOwnRing = 8;
 constexpr int kOwnAhead = 3;         // units in flight beyond the one awaited
@@ -179,11 +181,16 @@ __global__ void __launch_bounds__(kOwnThreads) owned_stream_kernel(const float4*
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = gridDim.x, wg = blockIdx.x;
-  const int ntile = tiles > wg ? (tiles - wg + G - 1) / G : 0;
+  const int per = (tiles + G - 1) / G;
+  const int ntile = ORDER == 3 ? max(0, min(per, tiles - wg * per)) : tiles > wg ? (tiles - wg + G - 1) / G : 0;
   const int K = ntile * kOwnUnitsPerTile;  // units this workgroup reads, in phase order
+  auto tile_of = [&](int i) { return ORDER == 3 ? wg * per + i : wg + i * G; };
+  auto unit_of = [&](int k) {              // the unit of its tile read in phase k
+    return ORDER == 2 ? (k + wg) % kOwnUnitsPerTile : k % kOwnUnitsPerTile;
+  };
   auto unit_at = [&](int k) -> size_t {    // pool index of the unit read in phase k
     if (ORDER == 1) return (size_t)wg + (size_t)k * G;
-    return ((size_t)wg + (size_t)(k / kOwnUnitsPerTile) * G) * kOwnUnitsPerTile + k % kOwnUnitsPerTile;
+    return (size_t)tile_of(k / kOwnUnitsPerTile) * kOwnUnitsPerTile + unit_of(k);
   };
   auto issue = [&](int k) {
     own_issue_unit(src + unit_at(k) * kOwnUnitF4 + lane, (uint32_t)(uintptr_t)&ring[k % kOwnRing][0]);
@@ -212,16 +219,16 @@ __global__ void __launch_bounds__(kOwnThreads) owned_stream_kernel(const float4*
     if (u == 0 && i > 0 && lane < 32) {  // tile i - 1, columns 32c..32c+31
       const int col = 32 * c + lane;
       const float sum = (red[0][col] + red[1][col]) + (red[2][col] + red[3][col]);
-      __builtin_nontemporal_store(sum, out + ((size_t)wg + (size_t)(i - 1) * G) * 128 + col);
+      __builtin_nontemporal_store(sum, out + (size_t)tile_of(i - 1) * 128 + col);
     }
     if (ph == K) continue;
-    const int t = wg + i * G;
+    const int t = tile_of(i), ur = ORDER == 1 ? u : unit_of(ph);
     const float4* sl = &ring[ph % kOwnRing][0];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 8 * c + 4 * h + r;
       const float4 x = sl[row * 32 + q];
-      const float y = own_weight(t, 32 * u + row);
+      const float y = own_weight(t, 32 * ur + row);
       acc.x = fmaf(y, x.x, acc.x);
       acc.y = fmaf(y, x.y, acc.y);
       acc.z = fmaf(y, x.z, acc.z);
@@ -277,18 +284,21 @@ int dl_probe_tile_stream(const void* src, int units, int wgs, void* sink, void* 
 // Stream `tiles` 128 x 128 fp32 tiles at `src` (device, 16-byte aligned, 64 KiB each)
 // through LDS with `wgs` persistent workgroups of 320 threads (130 KiB of LDS each, so
 // one per CU) and write their column sums, as defined at owned_stream_kernel, to `out`
-// (device, tiles x 128 floats).  order 0: whole tiles per workgroup; order 1: the pool's
-// 16 KiB units strided over the workgroups (needs tiles % wgs == 0).  Returns 0, -1 for
-// bad arguments, -4 if the launch failed.
+// (device, tiles x 128 floats).  order 0: whole tiles per workgroup, strided; 1: the
+// pool's 16 KiB units strided over the workgroups (needs tiles % wgs == 0); 2: as 0, each
+// tile's units in a rotated order; 3: contiguous runs of whole tiles per workgroup.
+// Returns 0, -1 for bad arguments, -4 if the launch failed.
 int dl_probe_owned_stream(const void* src, int tiles, int order, void* out, int wgs, void* stream) {
   if (!src || !out || tiles <= 0 || wgs <= 0 || !aligned16(src) || !aligned16(out)) return -1;
-  if (order != 0 && order != 1) return -1;
+  if (order < 0 || order > 3) return -1;
   if (order == 1 && tiles % wgs) return -1;
   auto st = static_cast<hipStream_t>(stream);
   const float4* s = static_cast<const float4*>(src);
   float* o = static_cast<float*>(out);
   if (order == 0) owned_stream_kernel<0><<<wgs, kOwnThreads, 0, st>>>(s, tiles, o);
-  else owned_stream_kernel<1><<<wgs, kOwnThreads, 0, st>>>(s, tiles, o);
+  else if (order == 1) owned_stream_kernel<1><<<wgs, kOwnThreads, 0, st>>>(s, tiles, o);
+  else if (order == 2) owned_stream_kernel<2><<<wgs, kOwnThreads, 0, st>>>(s, tiles, o);
+  else owned_stream_kernel<3><<<wgs, kOwnThreads, 0, st>>>(s, tiles, o);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

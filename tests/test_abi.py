@@ -61,7 +61,8 @@ def test_side_libraries_export_their_calls():
     # argument checks, all rejected before any GPU call: null or misaligned buffers, no
     # tiles or workgroups, an unknown order, the unit order with tiles not a multiple of wgs
     for args in ((None, 512, 0, 0x10000, 256), (0x10000, 512, 0, None, 256), (0x10004, 512, 0, 0x10000, 256),
-                 (0x10000, 0, 0, 0x10000, 256), (0x10000, 512, 0, 0x10000, 0), (0x10000, 512, 2, 0x10000, 256),
+                 (0x10000, 0, 0, 0x10000, 256), (0x10000, 512, 0, 0x10000, 0), (0x10000, 512, 4, 0x10000, 256),
+                 (0x10000, 512, -1, 0x10000, 256),
                  (0x10000, 300, 1, 0x10000, 256)):
         assert p.dl_probe_owned_stream(*args, None) == -1
     t = ctypes.CDLL(trace)

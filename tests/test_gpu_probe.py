@@ -30,7 +30,8 @@ def weights(tiles, device):
     return 1 + torch.remainder(131 * t + r, 7) / 8
 
 
-@pytest.mark.parametrize("tiles,wgs,order", [(512, 256, 0), (300, 256, 0), (301, 7, 0), (512, 256, 1), (770, 35, 1)])
+@pytest.mark.parametrize("tiles,wgs,order", [(512, 256, 0), (300, 256, 0), (301, 7, 0), (512, 256, 1), (770, 35, 1),
+                                              (512, 256, 2), (301, 7, 2), (300, 256, 3), (301, 7, 3)])
 def test_owned_stream_column_sums(probe, tiles, wgs, order):
     dev = torch.device("cuda", 0)
     g = torch.Generator(device=dev).manual_seed(tiles * 131 + wgs + order)
@@ -40,7 +41,7 @@ def test_owned_stream_column_sums(probe, tiles, wgs, order):
     assert probe.dl_probe_owned_stream(pool.data_ptr(), tiles, order, out.data_ptr(), wgs,
                                        torch.cuda.current_stream().cuda_stream) == 0
     torch.cuda.synchronize()
-    if order == 0:
+    if order != 1:  # whole tiles per workgroup, in any order: each tile's own rows
         rows = pool.double()
     else:  # "tile" T = w + i G gathers units w + (4i + j) G, j < 4, as its rows 32j..32j+31
         T = torch.arange(tiles, device=dev)
