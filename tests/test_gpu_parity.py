@@ -258,8 +258,11 @@ def test_merge_min_fill_then_continue():
     _close("state after partial merge", materialized_state(pool), oracle.run_eager(inp, 120)[0], (-2, -1))
 
 
-def test_reruns_are_bit_identical():
-    inp = make_inputs(2, 200, batch=3, heads=4, pool=200, fill0=np.array([0, 5, 11], np.int32))
+@pytest.mark.parametrize("w", [2, 3, 4])
+def test_reruns_are_bit_identical(w):
+    """Every cross-lane and cross-wave sum of the step (512 threads for GDN and KDA at
+    128 x 128) adds in a fixed order: the same steps twice give the same bits."""
+    inp = make_inputs(w, 200, batch=3, heads=4, pool=200, fill0=np.array([0, 5, 11], np.int32))
     up = Uploaded(inp)
     p1, o1 = run_deltalog(inp, 200, up=up)
     p2, o2 = run_deltalog(inp, 200, up=up)
