@@ -282,8 +282,9 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
     load issued first, no arithmetic) over the base tensors of `pools`, used in turn as the
     decode step uses them: the tile read alone, the tile read plus `log_bytes` of log per
     tile (the mean the step reads), the tile read and written back (the eager step's
-    traffic), and the same bytes streamed through LDS by one persistent workgroup per CU
-    with three 16 KiB units in flight.  For 128 x 128 fp32 tiles also the owned stream:
+    traffic), the same bytes read as 16 KiB blocks by one workgroup each (tiles larger
+    than that), and the same bytes streamed through LDS by one persistent workgroup per
+    CU with three 16 KiB units in flight.  For 128 x 128 fp32 tiles also the owned stream:
     persistent workgroups that each own whole tiles, as a decode step does, one wave
     streaming their units into LDS and four forming the column sums (tiles strided over the
     workgroups, the same with each tile's units in a rotated order, or a contiguous run of
@@ -332,6 +333,11 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
                                                                  stream), "dl_probe_tile_stream"),
                         tile_bytes * tiles // 16384 * 16384),
     }
+    if tile_bytes > 16384:  # the same bytes read as 16 KiB blocks, one workgroup each
+        legs["block16k_read"] = (lambda t: check(lib.dl_probe_tile_read(pools[t % NP].base.data_ptr(), 16384,
+                                                                         tiles * tile_bytes // 16384, sink.data_ptr(),
+                                                                         stream), "dl_probe_tile_read"),
+                                 tile_bytes * tiles)
     owned = tile_bytes == 65536 and tiles % 256 == 0 and pools[0].base.dtype == torch.float32
     if owned:  # 128 x 128 fp32 tiles: the tile-owning stream, and its unit order for comparison
         colsums = torch.empty(tiles * 128, dtype=torch.float32, device=dev)
@@ -344,7 +350,8 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
         secs = time_loop(fn, launches, 2 * NP)
         out[f"{name}_gbs"] = nbytes * launches / secs / 1e9
     out["probe_shape"] = (f"{tiles} tiles of {tile_bytes} B per launch, {NP} pools in turn; read_log adds {lb} B "
-                          f"of log per tile; rw writes the tile back (the eager step's traffic); stream reads "
+                          f"of log per tile; rw writes the tile back (the eager step's traffic); block16k_read "
+                          f"reads the same bytes as 16 KiB blocks, one workgroup each; stream reads "
                           f"the same bytes as 16 KiB units with 256 persistent workgroups, three units in "
                           f"flight per CU through LDS"
                           + ("; owned_stream: 256 persistent workgroups owning whole tiles, one wave streaming "
