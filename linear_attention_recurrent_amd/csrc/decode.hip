@@ -57,14 +57,15 @@ __device__ __forceinline__ void trace_stamp(int k, const void* q, int tiles, int
 // at 128 x 128 with an fp32 base, where 512 threads halve each thread's share of the tile:
 //   GDN: 512 (80 VGPRs: three workgroups per CU, six waves per SIMD where 256 threads at
 //     131 VGPRs give three; cold steps 0.5-1.2 % faster, the vector merge up to 11 %);
-//   KDA with PF 0 (logs of up to 17 entries): 512, held to 128 VGPRs (four waves per SIMD,
-//     step_waves) so that two workgroups share a CU: 16 waves where 256 threads at 146
-//     VGPRs give 12 (cold steps 3.7 % faster); with more prefetched entries the cap spills.
+//   KDA with PF 0 or 32 (logs of up to 33 entries): 512, held to 128 VGPRs (four waves per
+//     SIMD, step_waves) so that two workgroups share a CU: 16 waves where 256 threads at
+//     146 VGPRs give 12 (cold steps 3.7 % faster at L = 16, 3.3 % at L = 32); with 64
+//     prefetched entries the cap spills.
 // Otherwise the geometry's default: with a bf16 base the GDN step was 4 % slower at 512
 // threads and the KDA vector merge up to 14 %.
 template <int VAR, int DK, int DV, bool BF, int PF>
 constexpr int step_threads() {
-  return DK * DV < 16384 || BF ? 0 : VAR == DL_GDN || (VAR == DL_KDA && PF == 0) ? 512 : 0;
+  return DK * DV < 16384 || BF ? 0 : VAR == DL_GDN || (VAR == DL_KDA && PF <= 32) ? 512 : 0;
 }
 // Waves per SIMD the register budget must allow: 4 for KDA at 512 threads (above), else
 // no bound.
