@@ -201,7 +201,8 @@ def test_log_length_at_the_prefetch_boundary(w, L):
     """L = 17 is the longest log the decode step's first variant covers (16 entries loaded
     ahead of the base, the fold in two staged passes; 512 threads per workgroup for GDN and
     KDA with an fp32 base at 128 x 128); L = 18 is the first that takes the 32-entry variant
-    (256 threads for KDA).  Ragged fills put tiles at both ends of the log."""
+    (512 threads for KDA as well, 256 for RWKV6).  Ragged fills put tiles at both ends of
+    the log."""
     steps = 2 * L + 5
     inp = make_inputs(w, steps, batch=3, heads=2, log_len=L, pool=steps, dk=128, dv=128,
                       fill0=np.array([0, L // 2, L - 2], np.int32))
