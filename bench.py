@@ -288,7 +288,9 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
     persistent workgroups that each own whole tiles, as a decode step does, one wave
     streaming their units into LDS and four forming the column sums (tiles strided over the
     workgroups, the same with each tile's units in a rotated order, or a contiguous run of
-    tiles per workgroup), and the same kernel taking the units in the stream's order."""
+    tiles per workgroup), and the same kernel taking the units in the stream's order; and
+    one workgroup per 16 KiB quarter tile storing its partial column sums, without and with
+    their sum per tile inside the launch (agent-scope fences and a count)."""
     import ctypes
 
     import torch
@@ -307,6 +309,7 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
     lib.dl_probe_tile_rw.argtypes = [vp, ci, ci, vp]
     lib.dl_probe_tile_stream.argtypes = [vp, ci, ci, vp, vp]
     lib.dl_probe_owned_stream.argtypes = [vp, ci, ci, vp, ci, vp]
+    lib.dl_probe_quarter_split.argtypes = [vp, ci, ci, vp, vp, vp, vp]
     sink = torch.zeros(256, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
     NP = len(pools)
@@ -346,6 +349,16 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
             legs[name] = (lambda t, o=order: check(lib.dl_probe_owned_stream(pools[t % NP].base.data_ptr(), tiles, o,
                                                                              colsums.data_ptr(), 256, stream),
                                                    "dl_probe_owned_stream"), tile_bytes * tiles)
+        # one workgroup per 16 KiB quarter, in pool order; partial column sums stored, and
+        # with the exchange added up per tile inside the launch behind agent-scope fences
+        qpart = torch.empty(tiles * 4 * 256, dtype=torch.float32, device=dev)
+        qcnt = torch.zeros(tiles, dtype=torch.int32, device=dev)
+        qout = torch.empty(tiles * 256, dtype=torch.float32, device=dev)
+        for ex, name in ((0, "quarter_split"), (1, "quarter_split_exchange")):
+            legs[name] = (lambda t, e=ex: check(lib.dl_probe_quarter_split(pools[t % NP].base.data_ptr(), tiles, e,
+                                                                           qpart.data_ptr(), qcnt.data_ptr(),
+                                                                           qout.data_ptr(), stream),
+                                                "dl_probe_quarter_split"), tile_bytes * tiles)
     for name, (fn, nbytes) in legs.items():
         secs = time_loop(fn, launches, 2 * NP)
         out[f"{name}_gbs"] = nbytes * launches / secs / 1e9
@@ -357,7 +370,10 @@ def read_ceilings(pools, tiles, tile_bytes, log_bytes, launches):
                           + ("; owned_stream: 256 persistent workgroups owning whole tiles, one wave streaming "
                              "16 KiB units into LDS three ahead, four forming column sums; its unit_order leg "
                              "reads the pool's units in the stream's order, rotated starts each tile at unit "
-                             "w mod 4, contiguous gives each workgroup a run of whole tiles" if owned else ""))
+                             "w mod 4, contiguous gives each workgroup a run of whole tiles; quarter_split: one "
+                             "workgroup per 16 KiB quarter in pool order storing partial column sums, its "
+                             "exchange leg adding each tile's four up inside the launch behind agent-scope "
+                             "fences" if owned else ""))
     return out
 
 

@@ -19,6 +19,11 @@
 //                 from LDS (a decode step's base matvec with nothing around it); or,
 //                 for comparison, the same kernel taking the pool's units in the
 //                 stream order above
+//   quarter split one workgroup per 16 KiB quarter (32 rows) of a 128 x 128 fp32 tile,
+//                 the quarters of a tile in consecutive workgroups (so that all of
+//                 them sweep one contiguous region): partial column sums of the
+//                 quarter, stored; optionally added up across the four workgroups
+//                 of the tile by the last to arrive, behind agent-scope fences
 // Loaded values feed a sum that is stored only if it equals a value no sum of
 // finite inputs hits in practice, so the loads cannot be dropped; the write-back
 // scales by 1 - 2^-24 rounded, so it rewrites every value (the stored values change
@@ -245,6 +250,75 @@ __global__ void __launch_bounds__(kOwnThreads) owned_stream_kernel(const float4*
   }
 }
 
+// ---------------------------------------------------------------- quarter split
+// Workgroup b (256 threads) reads quarter q = b mod 4 of tile t = b / 4 (rows 32 q ..
+// 32 q + 31), forms its column sums with two row weights,
+//   part[b][c] = sum_r B_t[r][c] own_weight(t, r),  part[b][128 + c] = sum_r B_t[r][c] qs_weight(t, r),
+// and stores them.  With EXCHANGE, every thread then fences at agent scope (release),
+// thread 0 adds 1 to cnt[t], and the workgroup that finds 3 there fences again (acquire),
+// writes out[t] = the sum of the tile's four partials and sets cnt[t] back to 0: a tile's
+// column sums finished inside the launch, correct under the HIP memory model (on this chip
+// an agent-scope fence writes the L2 back and invalidates it).  No workgroup waits for
+// another.
+__device__ __forceinline__ float qs_weight(int t, int r) { return 0.5f + (float)((t * 17 + r) % 5) * 0.25f; }
+
+template <bool EXCHANGE>
+__global__ void __launch_bounds__(256) quarter_split_kernel(const float4* __restrict__ src, float* __restrict__ part,
+                                                            unsigned* __restrict__ cnt, float* __restrict__ out) {
+  __shared__ float4 red[4][2][32];
+  __shared__ unsigned s_old;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int b = blockIdx.x, t = b >> 2, q = b & 3;
+  const int cg = tid & 31, rg = tid >> 5;  // column quad; rows 4 rg .. 4 rg + 3 of the quarter
+  const float4* blk = src + (size_t)b * 1024;
+  float4 x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = blk[(4 * rg + i) * 32 + cg];
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), c = a;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 32 * q + 4 * rg + i;
+    const float y = own_weight(t, r), z = qs_weight(t, r);
+    a.x = fmaf(y, x[i].x, a.x); a.y = fmaf(y, x[i].y, a.y); a.z = fmaf(y, x[i].z, a.z); a.w = fmaf(y, x[i].w, a.w);
+    c.x = fmaf(z, x[i].x, c.x); c.y = fmaf(z, x[i].y, c.y); c.z = fmaf(z, x[i].z, c.z); c.w = fmaf(z, x[i].w, c.w);
+  }
+  a.x += __shfl_xor(a.x, 32); a.y += __shfl_xor(a.y, 32); a.z += __shfl_xor(a.z, 32); a.w += __shfl_xor(a.w, 32);
+  c.x += __shfl_xor(c.x, 32); c.y += __shfl_xor(c.y, 32); c.z += __shfl_xor(c.z, 32); c.w += __shfl_xor(c.w, 32);
+  if (lane < 32) {
+    red[wave][0][lane] = a;
+    red[wave][1][lane] = c;
+  }
+  __syncthreads();
+  if (tid < 64) {  // thread (v, quad): v 0 the own_weight sums, 1 the qs_weight sums
+    const int v = tid >> 5, qd = tid & 31;
+    float4 sum = red[0][v][qd];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      const float4 o = red[w][v][qd];
+      sum.x += o.x; sum.y += o.y; sum.z += o.z; sum.w += o.w;
+    }
+    reinterpret_cast<float4*>(part + (size_t)b * 256)[tid] = sum;
+  }
+  if constexpr (EXCHANGE) {
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_old = atomicAdd(&cnt[t], 1u);
+    __syncthreads();
+    if (s_old != 3) return;
+    __threadfence();
+    if (tid < 64) {
+      float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const float4 o = reinterpret_cast<const float4*>(part + ((size_t)t * 4 + qq) * 256)[tid];
+        sum.x += o.x; sum.y += o.y; sum.z += o.z; sum.w += o.w;
+      }
+      reinterpret_cast<float4*>(out + (size_t)t * 256)[tid] = sum;
+    }
+    if (tid == 0) cnt[t] = 0;  // ready for the next launch on the stream
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -299,6 +373,28 @@ int dl_probe_owned_stream(const void* src, int tiles, int order, void* out, int 
   else if (order == 1) owned_stream_kernel<1><<<wgs, kOwnThreads, 0, st>>>(s, tiles, o);
   else if (order == 2) owned_stream_kernel<2><<<wgs, kOwnThreads, 0, st>>>(s, tiles, o);
   else owned_stream_kernel<3><<<wgs, kOwnThreads, 0, st>>>(s, tiles, o);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// Quarter-split column sums of `tiles` 128 x 128 fp32 tiles at `src` (device, 16-byte
+// aligned), one 256-thread workgroup per 16 KiB quarter, as defined at
+// quarter_split_kernel: the partials go to `part` (device, tiles x 4 x 256 floats); with
+// `exchange` nonzero the four partials of each tile are also added up inside the launch
+// into `out` (device, tiles x 256 floats), counted in `cnt` (device, tiles unsigned
+// ints, all zero on entry; left zero).  Returns 0, -1 for bad arguments, -4 if the launch
+// failed.
+int dl_probe_quarter_split(const void* src, int tiles, int exchange, void* part, void* cnt, void* out,
+                           void* stream) {
+  if (!src || !part || tiles <= 0 || !aligned16(src) || !aligned16(part)) return -1;
+  if (exchange && (!cnt || !out || !aligned16(out))) return -1;
+  if (static_cast<int64_t>(tiles) * 4 > INT32_MAX) return -1;
+  auto st = static_cast<hipStream_t>(stream);
+  const float4* s = static_cast<const float4*>(src);
+  if (exchange)
+    quarter_split_kernel<true><<<tiles * 4, 256, 0, st>>>(s, static_cast<float*>(part), static_cast<unsigned*>(cnt),
+                                                          static_cast<float*>(out));
+  else
+    quarter_split_kernel<false><<<tiles * 4, 256, 0, st>>>(s, static_cast<float*>(part), nullptr, nullptr);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

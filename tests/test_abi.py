@@ -53,7 +53,7 @@ def test_side_libraries_export_their_calls():
     exported = lambda path: set(re.findall(r"\sT\s+(dl_\w+)$", os.popen(f"nm -D --defined-only {path}").read(),
                                            flags=re.M))
     assert exported(probe) == {"dl_probe_tile_read", "dl_probe_tile_read_log", "dl_probe_tile_rw",
-                               "dl_probe_tile_stream", "dl_probe_owned_stream"}
+                               "dl_probe_tile_stream", "dl_probe_owned_stream", "dl_probe_quarter_split"}
     assert exported(trace) == set(declared_functions()) | {"dl_trace_copy"}
     p = ctypes.CDLL(probe)
     vp, ci = ctypes.c_void_p, ctypes.c_int
@@ -65,6 +65,12 @@ def test_side_libraries_export_their_calls():
                  (0x10000, 512, -1, 0x10000, 256),
                  (0x10000, 300, 1, 0x10000, 256)):
         assert p.dl_probe_owned_stream(*args, None) == -1
+    p.dl_probe_quarter_split.argtypes = [vp, ci, ci, vp, vp, vp, vp]
+    for args in ((None, 512, 0, 0x10000, None, None), (0x10000, 512, 0, None, None, None),
+                 (0x10004, 512, 0, 0x10000, None, None), (0x10000, 0, 0, 0x10000, None, None),
+                 (0x10000, 512, 1, 0x10000, None, 0x10000), (0x10000, 512, 1, 0x10000, 0x10000, None),
+                 (0x10000, 512, 1, 0x10000, 0x10000, 0x10004)):
+        assert p.dl_probe_quarter_split(*args, None) == -1
     t = ctypes.CDLL(trace)
     t.dl_trace_copy.argtypes = [ctypes.c_void_p, ctypes.c_int]
     assert t.dl_trace_copy(None, -1) == -1  # argument check, no GPU call

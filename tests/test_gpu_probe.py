@@ -52,3 +52,37 @@ def test_owned_stream_column_sums(probe, tiles, wgs, order):
     assert torch.isfinite(out).all()
     err = ((out.double() - ref).abs().max() / ref.abs().max()).item()
     assert err < 1e-5, err
+
+
+@pytest.mark.parametrize("tiles,exchange", [(512, 0), (300, 1), (2048, 1)])
+def test_quarter_split_column_sums(probe, tiles, exchange):
+    """Quarter-split partial column sums, and with the exchange the four quarters of each
+    tile added up inside the launch by the last workgroup to arrive (counts left zero)."""
+    probe.dl_probe_quarter_split.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev).manual_seed(tiles + exchange)
+    pool = torch.randn(tiles, 128, 128, device=dev, generator=g)
+    part = torch.full((tiles, 4, 256), float("nan"), device=dev)
+    cnt = torch.zeros(tiles, dtype=torch.int32, device=dev)
+    out = torch.full((tiles, 256), float("nan"), device=dev)
+    print(f"quarter split: tiles {tiles} exchange {exchange}", flush=True)
+    for _ in range(2):  # the second launch starts from the counts the first left
+        assert probe.dl_probe_quarter_split(pool.data_ptr(), tiles, exchange, part.data_ptr(), cnt.data_ptr(),
+                                            out.data_ptr(), torch.cuda.current_stream().cuda_stream) == 0
+        torch.cuda.synchronize()
+    t = torch.arange(tiles, device=dev, dtype=torch.float64).view(-1, 1)
+    r = torch.arange(128, device=dev, dtype=torch.float64).view(1, -1)
+    w1 = 1 + torch.remainder(131 * t + r, 7) / 8
+    w2 = 0.5 + torch.remainder(17 * t + r, 5) / 4
+    B = pool.double()
+    quarters = [torch.cat([(B[:, 32 * q:32 * q + 32] * w[:, 32 * q:32 * q + 32].unsqueeze(-1)).sum(1)
+                           for w in (w1, w2)], dim=1) for q in range(4)]
+    ref_part = torch.stack(quarters, dim=1)
+    err = ((part.double() - ref_part).abs().max() / ref_part.abs().max()).item()
+    assert err < 1e-5, err
+    if exchange:
+        ref = ref_part.sum(1)
+        err = ((out.double() - ref).abs().max() / ref.abs().max()).item()
+        assert err < 1e-5, err
+        assert bool((cnt == 0).all())
